@@ -1,0 +1,81 @@
+"""The oracle's pins have teeth: plant a plausible mistake in a copy of the
+oracle source (a flipped decision, a transposed ratio, a wrong residual sign
+or row, a dropped temperature, a wrong tie rule, a wrong tree recursion...),
+build it, and check that at least one pin fails.  Runs on the CPU only; the
+mistakes are planted in the oracle, never in GPU code.
+"""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from tests import test_oracle_pins as pins
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "sv_oracle.cpp")
+
+CHAIN_PINS = [
+    lambda: pins.test_chain_round_is_lossless(2, 2, 0.6, 0.3, 0.3, 13),
+    lambda: pins.test_chain_round_is_lossless(3, 1, 1.0, 0.5, 0.0, 15),
+    pins.test_single_step_acceptance_law,
+    pins.test_softmax_with_temperature_matches_library,
+    pins.test_chain_shaped_tree_is_chain,
+    pins.test_greedy_equals_chain_on_one_hot_rows,
+]
+TREE_PINS = [
+    lambda: pins.test_tree_round_with_iid_siblings_is_lossless([-1, 0, 0, 0], 1, 23, 0.8),
+    lambda: pins.test_tree_round_with_iid_siblings_is_lossless([-1, 0, 1, 1, 0], 1, 24, 1.3),
+    pins.test_chain_shaped_tree_is_chain,
+]
+
+MUTANTS = [
+    # (name, original text, planted text, pins expected to catch it)
+    ("decision inverted", "if (!(r[j] < a)) break;", "if (!(r[j] > a)) break;", CHAIN_PINS),
+    ("ratio transposed", "if (qx > 0.0) return px / qx;", "if (px > 0.0) return qx / px;", CHAIN_PINS),
+    ("residual sign", "w[v] = std::max(0.0, P[n][v] - Q[n][v]);", "w[v] = std::max(0.0, Q[n][v] - P[n][v]);",
+     CHAIN_PINS),
+    ("residual row", "w[v] = std::max(0.0, P[n][v] - Q[n][v]);",
+     "w[v] = std::max(0.0, P[n + 1][v] - Q[n][v]);", CHAIN_PINS),
+    ("bonus row", "    w = P[gamma];\n", "    w = P[gamma - 1];\n", CHAIN_PINS),
+    ("temperature dropped", "p[v] = std::exp((load_logit(base, dtype, row_off + v) - M) / T);",
+     "p[v] = std::exp(load_logit(base, dtype, row_off + v) - M);", CHAIN_PINS),
+    ("softmax not normalised", "  for (int v = 0; v < V; ++v) p[v] /= S;\n", "\n", CHAIN_PINS),
+    ("inverse CDF off by one", "      return (int)v;\n    }\n  }\n  int last",
+     "      return (int)std::min(v + 1, w.size() - 1);\n    }\n  }\n  int last", CHAIN_PINS),
+    ("acceptance counter index", "draw_uniform(seed, (uint32_t)(j + 1), (uint32_t)b, 0, round, 0);",
+     "draw_uniform(seed, (uint32_t)j, (uint32_t)b, 0, round, 0);", [pins.test_chain_shaped_tree_is_chain]),
+    ("tree recursion step", "const double c_next = c + D;", "const double c_next = c + 1.0;", TREE_PINS),
+    ("tree mass not updated", "        D = G;\n", "\n", TREE_PINS),
+    ("tree residual not renormalised", "const double pcur = std::max(0.0, p[tok] - c * q[tok]) / D;",
+     "const double pcur = std::max(0.0, p[tok] - c * q[tok]);", TREE_PINS),
+    ("tree draws from p after rejections", "for (int v = 0; v < in.V; ++v) w[v] = std::max(0.0, p[v] - c * q[v]);",
+     "for (int v = 0; v < in.V; ++v) w[v] = p[v];", TREE_PINS),
+    ("multi ties to highest k", "if (results[k].n > best_n) {", "if (results[k].n >= best_n) {",
+     [pins.test_multi_k1_is_chain_and_each_candidate_is_its_chain]),
+    ("greedy ties to highest index", "    if (z > best) {\n      best = z;", "    if (z >= best) {\n      best = z;",
+     [pins.test_greedy_ties_lowest_index_and_signed_zero, pins.test_greedy_equals_chain_on_one_hot_rows]),
+    ("fan-out unstable order", "std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return z[a] > z[b]; });",
+     "std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return z[a] >= z[b] && a != b && z[a] == z[b] ? a > b : z[a] > z[b]; });",
+     [pins.test_fanout_is_stable_sort]),
+    ("geometric fan-out floor", "F_out[k] = (int32_t)std::ceil(f);", "F_out[k] = (int32_t)std::floor(f);",
+     [pins.test_geometric_fanout_closed_form]),
+]
+
+
+@pytest.mark.parametrize("name,old,new,catchers", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_planted_mistake_is_caught(tmp_path, name, old, new, catchers):
+    src = open(SRC).read()
+    assert src.count(old) == 1, f"mutation site for '{name}' not unique"
+    mutant = tmp_path / "mutant.cpp"
+    mutant.write_text(src.replace(old, new))
+    so = str(tmp_path / "libmutant.so")
+    subprocess.run(["g++", "-O1", "-std=c++17", "-fPIC", "-shared", "-ffp-contract=off", str(mutant), "-o", so],
+                   check=True)
+    caught = []
+    with oracle.use_library(so):
+        for pin in catchers:
+            try:
+                pin()
+            except (AssertionError, oracle.OracleError):
+                caught.append(pin)
+    assert caught, f"no pin caught the planted mistake '{name}'"

@@ -1,0 +1,360 @@
+"""Pins of the CPU oracle to what the pages and the mathematics fix (no GPU).
+
+Each test checks the oracle against something other than itself: exact
+enumeration of its output distribution against the target's chain rule,
+closed forms for acceptance statistics, reductions to library routines,
+known-answer vectors and an independent Philox implementation.
+"""
+import math
+import os
+import subprocess
+
+import numpy as np
+import pytest
+import scipy.special
+
+import oracle
+from tests import enum_pins as E
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+GOLDEN = os.path.join(HERE, "golden")
+
+
+# --------------------------------------------------------------------------
+# Philox4x32-10 (SC'11): known-answer vectors and PyTorch's header engine
+# --------------------------------------------------------------------------
+def _kat_rows():
+    rows = []
+    with open(os.path.join(GOLDEN, "philox_kat.txt")) as f:
+        for ln in f:
+            if ln.startswith("#") or not ln.strip():
+                continue
+            v = [int(x, 16) for x in ln.split()]
+            rows.append((v[0:4], v[4:6], v[6:10]))
+    return rows
+
+
+def test_philox_known_answers():
+    rows = _kat_rows()
+    assert len(rows) == 3
+    for ctr, key, want in rows:
+        assert list(oracle.philox4x32_10(ctr, key)) == want
+
+
+def test_philox_matches_pytorch_engine(tmp_path):
+    import torch.utils.cpp_extension as ce
+    exe = str(tmp_path / "philox_ref")
+    subprocess.run(["g++", "-O1", "-std=c++17", "-I" + ce.include_paths()[0],
+                    os.path.join(HERE, "philox_torch_ref.cpp"), "-o", exe], check=True)
+    rng = np.random.default_rng(7)
+    cases = rng.integers(0, 2 ** 32, size=(300, 6), dtype=np.uint64)
+    cases[:20, :4] = rng.integers(0, 64, size=(20, 4))  # small counters like the verifier's
+    text = "\n".join(" ".join(str(int(x)) for x in row) for row in cases) + "\n"
+    res = subprocess.run([exe], input=text, capture_output=True, text=True, check=True)
+    got = [list(map(int, ln.split())) for ln in res.stdout.strip().splitlines()]
+    assert len(got) == len(cases)
+    for row, ref in zip(cases, got):
+        assert list(oracle.philox4x32_10(row[:4], row[4:6])) == ref
+
+
+def test_uniform_grid_and_uniformity():
+    # U = (w >> 8) * 2^-24 of the first Philox word of counter (idx, b, k, round<<2|tag)
+    seed = 0x1234_5678_9ABC_DEF0
+    w = oracle.philox4x32_10([3, 5, 7, (9 << 2) | 1], [seed & 0xFFFFFFFF, seed >> 32])[0]
+    assert oracle.uniform(seed, 3, 5, 7, 9, 1) == (int(w) >> 8) / 2.0 ** 24
+    us = np.array([oracle.uniform(0, j, b, 0, 0, 0) for j in range(1, 65) for b in range(400)])
+    assert us.min() >= 0.0 and us.max() < 1.0
+    counts, _ = np.histogram(us, bins=32, range=(0, 1))
+    chi2 = ((counts - len(us) / 32) ** 2 / (len(us) / 32)).sum()
+    assert chi2 < 70.0  # 31 dof: p ~ 1e-4 tail
+
+
+# --------------------------------------------------------------------------
+# Losslessness by exact enumeration (draft-verification page §2.1 proof):
+# the sequence produced by repeated rounds has exactly the target's law.
+# --------------------------------------------------------------------------
+@pytest.mark.parametrize("gamma,m,T,pz,qz,seed", [
+    (1, 3, 1.0, 0.0, 0.0, 11),
+    (2, 3, 1.0, 0.0, 0.0, 12),
+    (2, 2, 0.6, 0.3, 0.3, 13),   # zeros in p (never accepted) and q (residual must supply them)
+    (3, 2, 1.7, 0.0, 0.4, 14),
+    (3, 1, 1.0, 0.5, 0.0, 15),
+])
+def test_chain_round_is_lossless(gamma, m, T, pz, qz, seed):
+    tab = E.Tables(5, seed, p_zero=pz, q_zero=qz)
+    d = E.chain_sequence_distribution(tab, gamma, m, T=T)
+    assert E.max_marginal_error(tab, d, m) < 1e-12
+
+
+@pytest.mark.parametrize("parent,m,seed,T", [
+    ([-1, 0, 0], 2, 21, 1.0),            # two i.i.d. siblings under the root
+    ([-1, 0, 0, 1], 2, 22, 1.0),         # siblings + depth 2
+    ([-1, 0, 0, 0], 1, 23, 0.8),         # three siblings
+    ([-1, 0, 1, 1, 0], 1, 24, 1.3),      # siblings at depth 2 under the first child
+])
+def test_tree_round_with_iid_siblings_is_lossless(parent, m, seed, T):
+    tab = E.Tables(5, seed, q_zero=0.2)
+    d = E.tree_sequence_distribution(tab, parent, m, T=T)
+    assert E.max_marginal_error(tab, d, m) < 1e-12
+
+
+def test_single_step_acceptance_law():
+    """gamma = 1: P(accept) = sum min(p, q) (page §2.2) and the emitted token ~ p (page §2.1)."""
+    tab = E.Tables(6, 31, q_zero=0.3)
+    p, q = tab.p(()), tab.q(())
+    acc = 0.0
+    emitted = np.zeros(6)
+    T = 1.0
+    for x in range(6):
+        if q[x] == 0:
+            continue
+        tgt = np.stack([E.logits_of(p, T), E.logits_of(tab.p((x,)), T)])
+        drf = E.logits_of(q, T)[None]
+
+        def run(r, u, tgt=tgt, drf=drf, x=x):
+            o = oracle.chain_core(tgt, drf, np.array([x]), T, r, u)
+            return ((x,) if o["n"] else ()) + (o["t"],), o["a"], o["w"]
+
+        for e, pr in E.enumerate_cells(run, 1, 6).items():
+            if len(e) == 2:
+                acc += q[x] * pr
+            emitted[e[0]] += q[x] * pr
+    beta = np.minimum(p, q).sum()
+    assert abs(acc - beta) < 1e-14
+    assert abs(beta - (1 - 0.5 * np.abs(p - q).sum())) < 1e-14
+    assert np.max(np.abs(emitted - p)) < 1e-14
+
+
+# --------------------------------------------------------------------------
+# Acceptance statistics with Philox uniforms (page §2.2, §2.3, §3; the
+# truncated-geometric law on the SpecBranch page's motivation section)
+# --------------------------------------------------------------------------
+def _fixed_rows(V, gamma, seed, same=False):
+    rng = np.random.default_rng(seed)
+    P = [rng.dirichlet(np.full(V, 0.5)) for _ in range(gamma + 1)]
+    Q = [rng.dirichlet(np.full(V, 0.5)) for _ in range(gamma)]
+    if same:
+        P = [P[0]] * (gamma + 1)
+        Q = [Q[0]] * gamma
+    return P, Q
+
+
+def _run_fixed(P, Q, B, seed, T=1.0):
+    gamma, V = len(Q), len(P[0])
+    rng = np.random.default_rng(seed)
+    tgt = np.broadcast_to(np.stack([E.logits_of(p, T) for p in P]), (B, gamma + 1, V)).copy()
+    drf = np.broadcast_to(np.stack([E.logits_of(q, T) for q in Q]), (B, gamma, V)).copy()
+    tok = np.stack([rng.choice(V, size=B, p=Q[j]) for j in range(gamma)], axis=1).astype(np.int32)
+    o = oracle.verify_chain(tgt, drf, tok, T, seed=seed, round_=3, dtype="f64")
+    return o, tok
+
+
+def test_positionwise_acceptance_equals_overlap():
+    V, gamma, B = 12, 4, 40000
+    P, Q = _fixed_rows(V, gamma, 41)
+    o, _ = _run_fixed(P, Q, B, 41)
+    n = o["n"]
+    assert n.min() >= 0 and n.max() <= gamma  # 1 <= emitted <= gamma + 1
+    for j in range(gamma):
+        reached = (n >= j).sum()
+        acc = (n >= j + 1).sum()
+        beta = np.minimum(P[j], Q[j]).sum()
+        sd = math.sqrt(beta * (1 - beta) / reached)
+        assert abs(acc / reached - beta) < 4 * sd + 1e-3
+
+
+def test_expected_length_product_of_accepts():
+    V, gamma, B = 10, 5, 40000
+    P, Q = _fixed_rows(V, gamma, 42)
+    o, _ = _run_fixed(P, Q, B, 42)
+    beta = np.array([np.minimum(P[j], Q[j]).sum() for j in range(gamma)])
+    cum = np.cumprod(beta)
+    En = cum.sum()  # c1 + c1 c2 + ...
+    n = o["n"].astype(float)
+    assert abs(n.mean() - En) < 4 * n.std() / math.sqrt(B)
+    probs = [(1 - beta[0])] + [cum[k - 1] * (1 - beta[k]) for k in range(1, gamma)] + [cum[-1]]
+    for k, pk in enumerate(probs):
+        frac = (o["n"] == k).mean()
+        assert abs(frac - pk) < 4 * math.sqrt(pk * (1 - pk) / B) + 1e-3
+
+
+def test_iid_alpha_closed_form_and_truncated_geometric():
+    V, gamma, B = 8, 6, 40000
+    P, Q = _fixed_rows(V, gamma, 43, same=True)
+    alpha = np.minimum(P[0], Q[0]).sum()
+    o, _ = _run_fixed(P, Q, B, 43)
+    tokens = o["n"] + 1.0
+    want = (1 - alpha ** (gamma + 1)) / (1 - alpha)
+    assert abs(tokens.mean() - want) < 4 * tokens.std() / math.sqrt(B)
+    for k in range(gamma + 1):
+        pk = (1 - alpha) * alpha ** k if k < gamma else alpha ** gamma
+        frac = (o["n"] == k).mean()
+        assert abs(frac - pk) < 4 * math.sqrt(pk * (1 - pk) / B) + 1e-3
+
+
+def test_softmax_with_temperature_matches_library():
+    rng = np.random.default_rng(5)
+    B, gamma, V = 3, 4, 257
+    for T in (0.3, 0.8, 1.0, 2.5):
+        tgt = rng.normal(0, 3, (B, gamma + 1, V))
+        drf = tgt[:, :gamma] + rng.normal(0, 1, (B, gamma, V))
+        tgt[0, 1, :100] = -np.inf  # masked logits are probability 0
+        tok = rng.integers(0, V, (B, gamma)).astype(np.int32)
+        o = oracle.verify_chain(tgt, drf, tok, T, 0, 0, "f64")
+        p_ref = scipy.special.softmax(tgt[:, :gamma] / T, axis=-1)
+        q_ref = scipy.special.softmax(drf / T, axis=-1)
+        pg = np.take_along_axis(p_ref, tok[..., None], -1)[..., 0]
+        qg = np.take_along_axis(q_ref, tok[..., None], -1)[..., 0]
+        assert np.allclose(o["p"], pg, rtol=1e-12, atol=0)
+        assert np.allclose(o["q"], qg, rtol=1e-12, atol=0)
+
+
+def test_bf16_and_f32_inputs_convert_exactly():
+    rng = np.random.default_rng(6)
+    V, gamma = 64, 3
+    f32 = rng.normal(0, 3, (1, gamma + 1, V)).astype(np.float32)
+    bits = (f32.view(np.uint32) >> 16).astype(np.uint16)  # truncation gives exact bf16 values
+    as_f64 = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+    tok = rng.integers(0, V, (1, gamma)).astype(np.int32)
+    a = oracle.verify_chain(bits, bits[:, :gamma].copy(), tok, 1.0, 9, 1, "bf16")
+    b = oracle.verify_chain(as_f64, as_f64[:, :gamma].copy(), tok, 1.0, 9, 1, "f64")
+    assert np.array_equal(a["p"], b["p"]) and a["t"][0] == b["t"][0] and a["n"][0] == b["n"][0]
+    c = oracle.verify_chain(f32, f32[:, :gamma].copy(), tok, 1.0, 9, 1, "f32")
+    d = oracle.verify_chain(f32.astype(np.float64), f32[:, :gamma].astype(np.float64), tok, 1.0, 9, 1, "f64")
+    assert np.array_equal(c["p"], d["p"]) and c["t"][0] == d["t"][0]
+
+
+# --------------------------------------------------------------------------
+# Greedy (page §2.2, §4): the chain rule fed one-hot p and q is an id match
+# --------------------------------------------------------------------------
+def _onehot_logits(idx, V):
+    z = np.full(V, -1e4)
+    z[idx] = 0.0
+    return z
+
+
+def test_greedy_equals_chain_on_one_hot_rows():
+    rng = np.random.default_rng(8)
+    B, gamma, V = 40, 6, 50
+    tgt = rng.normal(0, 2, (B, gamma + 1, V))
+    g = tgt.argmax(-1)
+    tok = np.where(rng.random((B, gamma)) < 0.7, g[:, :gamma], rng.integers(0, V, (B, gamma))).astype(np.int32)
+    og = oracle.verify_greedy(tgt, tok, "f64")
+    assert np.array_equal(og["argmax"], g)
+    P1 = np.stack([[_onehot_logits(g[b, j], V) for j in range(gamma + 1)] for b in range(B)])
+    Q1 = np.stack([[_onehot_logits(tok[b, j], V) for j in range(gamma)] for b in range(B)])
+    for seed in (0, 1, 99):
+        oc = oracle.verify_chain(P1, Q1, tok, 1.0, seed, 0, "f64")
+        assert np.array_equal(oc["n"], og["n"]) and np.array_equal(oc["t"], og["t"])
+
+
+def test_greedy_ties_lowest_index_and_signed_zero():
+    V = 32
+    rows = np.full((1, 3, V), -5.0)
+    rows[0, 0, [7, 3, 20]] = 2.0           # ties -> 3
+    rows[0, 1, 9] = -0.0
+    rows[0, 1, 4] = 0.0                    # -0 == +0 -> 4
+    rows[0, 2, :] = 1.0                    # all equal -> 0
+    o = oracle.verify_greedy(rows, np.array([[3, 4]], np.int32), "f64")
+    assert list(o["argmax"][0]) == [3, 4, 0] == [int(np.argmax(r)) for r in rows[0]]
+    assert o["n"][0] == 2 and o["t"][0] == 0
+    bits = np.full((2, 5, V), 0x3F80, np.uint16)  # bf16 1.0 everywhere
+    bits[1, 2, 17] = 0x4000  # 2.0
+    o = oracle.verify_greedy(bits, np.array([[0, 0, 0, 1], [0, 0, 17, 0]], np.int32), "bf16")
+    assert list(o["n"]) == [3, 4] and list(o["t"]) == [0, 0]
+
+
+# --------------------------------------------------------------------------
+# Multi-candidate and tree reductions
+# --------------------------------------------------------------------------
+def test_multi_k1_is_chain_and_each_candidate_is_its_chain():
+    rng = np.random.default_rng(9)
+    B, K, gamma, V = 6, 4, 5, 40
+    tgt = rng.normal(0, 2, (B, K, gamma + 1, V))
+    drf = tgt[:, 0, :gamma] + rng.normal(0, 1, (B, gamma, V))
+    tok = rng.integers(0, V, (B, K, gamma)).astype(np.int32)
+    om = oracle.verify_multi(tgt, drf, tok, 0.9, 77, 5, "f64")
+    for k in range(K):
+        # candidate k alone, with the acceptance uniforms drawn at counter k
+        r = np.array([[oracle.uniform(77, j + 1, b, k, 5, 0) for j in range(gamma)] for b in range(B)])
+        o1 = oracle.verify_multi(tgt[:, k:k + 1].copy(), drf, tok[:, k:k + 1].copy(), 0.9, 77, 5, "f64",
+                                 r=r[:, None, :])
+        assert np.array_equal(o1["n"], om["n_cand"][:, k])
+    assert np.array_equal(om["n"], om["n_cand"].max(1))
+    assert np.array_equal(om["k"], np.argmax(om["n_cand"], 1))  # lowest k among the longest
+    o1 = oracle.verify_multi(tgt[:, :1].copy(), drf, tok[:, :1].copy(), 0.9, 77, 5, "f64")
+    oc = oracle.verify_chain(tgt[:, 0].copy(), drf, tok[:, 0].copy(), 0.9, 77, 5, "f64")
+    for key in ("n", "t", "mdec", "mcdf"):
+        assert np.array_equal(o1[key], oc[key])
+    assert np.array_equal(o1["p"][:, 0], oc["p"]) and np.array_equal(o1["q"][:, 0], oc["q"])
+
+
+def test_chain_shaped_tree_is_chain():
+    rng = np.random.default_rng(10)
+    B, gamma, V = 30, 6, 60
+    for T in (1.0, 0.7):
+        tgt = rng.normal(0, 2, (B, gamma + 1, V))
+        drf = tgt[:, :gamma] + rng.normal(0, 1.5, (B, gamma, V))
+        tok = rng.integers(0, V, (B, gamma)).astype(np.int32)
+        oc = oracle.verify_chain(tgt, drf, tok, T, 5, 2, "f64")
+        N = gamma + 1
+        tdrf = np.concatenate([drf, drf[:, -1:]], axis=1)
+        node_tok = np.concatenate([np.zeros((B, 1), np.int32), tok], 1)
+        parent = np.tile(np.arange(-1, N - 1, dtype=np.int32), (B, 1))
+        ot = oracle.verify_tree(tgt, tdrf, node_tok, parent, gamma, T, 5, 2, "f64")
+        assert np.array_equal(ot["len"], oc["n"]) and np.array_equal(ot["t"], oc["t"])
+        assert np.array_equal(ot["mdec"], oc["mdec"]) and np.array_equal(ot["mcdf"], oc["mcdf"])
+        for b in range(B):
+            L = oc["n"][b]
+            assert list(ot["path"][b][:L]) == list(range(1, L + 1))
+            seen = min(L + 1, gamma)
+            assert np.array_equal(ot["p"][b, 1:1 + seen], oc["p"][b, :seen])
+
+
+def test_tree_residual_recursion_matches_repeated_residuals():
+    """(p - c_i q)^+ / D_i equals norm(max(0, p_cur - q)) applied i times."""
+    rng = np.random.default_rng(11)
+    for _ in range(50):
+        V = 30
+        p = rng.dirichlet(np.full(V, 0.4))
+        q = rng.dirichlet(np.full(V, 0.4))
+        cur = p.copy()
+        c, D = 0.0, 1.0
+        for _i in range(6):
+            nxt = np.maximum(0, cur - q)
+            if nxt.sum() <= 0:
+                break
+            cur = nxt / nxt.sum()
+            c = c + D
+            D = np.maximum(0, p - c * q).sum()
+            assert np.max(np.abs(np.maximum(0, p - c * q) / D - cur)) < 1e-12
+
+
+# --------------------------------------------------------------------------
+# Fan-out (SSD review §3 and Theorem 12)
+# --------------------------------------------------------------------------
+def test_geometric_fanout_closed_form():
+    with open(os.path.join(GOLDEN, "geometric_fanout.txt")) as f:
+        for ln in f:
+            if ln.startswith("#") or not ln.strip():
+                continue
+            lhs, rhs = ln.split(":")
+            F0, a_p, r, K, cap = lhs.split()
+            want = [int(x) for x in rhs.split()]
+            got = oracle.geometric_fanout(int(F0), float(a_p), float(r), int(K), bool(int(cap)))
+            assert list(got) == want
+
+
+def test_fanout_is_stable_sort():
+    rng = np.random.default_rng(12)
+    R, V, Fmax = 40, 300, 8
+    bits = rng.integers(0x3F00, 0x3F08, size=(R, V)).astype(np.uint16)  # bf16 with many ties
+    bits[::3] = rng.integers(0, 0xFFFF, size=bits[::3].shape).astype(np.uint16) & 0x7F7F  # finite, mixed sign
+    vals = (bits.astype(np.uint32) << 16).view(np.float32)
+    F = rng.integers(0, Fmax + 1, R).astype(np.int32)
+    ids, got_vals = oracle.fanout_topk(bits, F, Fmax, "bf16")
+    for r in range(R):
+        order = np.argsort(-vals[r].astype(np.float64), kind="stable")
+        assert list(ids[r][:F[r]]) == list(order[:F[r]])
+        assert (ids[r][F[r]:] == -1).all()
+        assert np.array_equal(got_vals[r][:F[r]], vals[r][order[:F[r]]])
