@@ -1,0 +1,215 @@
+/*
+ * specverify.h -- C ABI of the MI355X (gfx950) draft-verification library.
+ *
+ * One call runs the data-parallel acceptance step of lossless speculative
+ * decoding on the GPU: temperature softmax of target and draft logit rows,
+ * acceptance of each draft token with probability min(1, p(x)/q(x)) against a
+ * counter-based uniform, the longest accepted prefix, and the correction token
+ * drawn from norm(max(0, p - q)) at the first rejection, or the bonus token
+ * drawn from the next target row when every draft is accepted.
+ *
+ * Definitions followed (page title, section):
+ *   - llm-infra-atlas "01 · Draft-then-verify: lossless algorithm core":
+ *     §1 (one round, Leviathan Algorithm 1), §2.1 (accept with
+ *     min(1, p/q), residual norm(max(0, p - q))), §2.2 (greedy = argmax-id
+ *     match), §4 (bonus row; filters applied to both p and q; pseudocode).
+ *   - "SpecDiff-2: Scaling Diffusion Drafter Alignment for Faster Speculative
+ *     Decoding", Core method (K candidates from shared position marginals,
+ *     the verifier keeps the best one).
+ *   - "PRESTO: prefix-aligned tree drafting for diffusion speculative
+ *     decoding", §2.1 (token tree, accept sequentially from the root until a
+ *     mismatch).
+ *   - "Speculative Speculative Decoding (SSD) / Saguaro" review, §3 (fan-out:
+ *     top-F_k tokens of the draft logits per lookahead position k) and
+ *     Theorem 12 (geometric F_k).
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ *  - Tensor pointers are DEVICE pointers owned by the caller.  The library
+ *    never allocates or frees device memory on these paths; scratch space is
+ *    the caller's workspace `ws` of `ws_bytes` bytes (size from
+ *    sv_workspace_size).  A new workspace must be zero-filled once
+ *    (sv_workspace_init, or any zero fill); every call leaves it ready for
+ *    the next call of any op and any shape.  Calls that share one workspace
+ *    must not overlap in time (same stream, or ordered by events).
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every call is asynchronous: SV_OK means "validated and enqueued".
+ *    Launch failures are reported as SV_EHIP; device-side input errors set
+ *    bits in the workspace's error word (sv_get_device_error).
+ *  - Logit rows: `dt` is SV_BF16 or SV_F32; row r of a logit tensor starts
+ *    at base + r * stride elements; the base address and stride * element
+ *    size must be multiples of 16 bytes (SV_EALIGN otherwise); stride >= V.
+ *    -inf logits mean probability 0; NaN is outside the contract.
+ *  - Temperature T > 0 and finite scales target AND draft logits (z / T).
+ *  - Uniforms: Philox4x32-10 (Salmon et al., SC'11), key = (seed low 32
+ *    bits, seed high 32 bits), counter = (idx, b, k, (round << 2) | tag);
+ *    the first output word w gives U = (w >> 8) * 2^-24.  tag 0: acceptance
+ *    uniform of chain position idx = j (1-based) of candidate k, or of tree
+ *    node idx (k = 0); tag 1: the one sampling uniform of sequence b
+ *    (idx = k = 0).  round must be < 2^30.  Same inputs, seed and round give
+ *    bit-identical outputs.
+ *  - Decisions: accept draft x at a position iff U < p(x)/q(x) (q(x) = 0
+ *    with p(x) > 0 always accepts).  Draws: inverse CDF in index order, the
+ *    smallest v whose cumulative weight exceeds U * (total weight).
+ *  - Device-side preconditions (not checked on the host): token ids in
+ *    [0, V); every row has a finite logit; tree parent arrays valid.  A
+ *    violation never causes an out-of-bounds access: it sets a bit in the
+ *    error word and the affected decision rejects.
+ */
+#ifndef SPECVERIFY_H
+#define SPECVERIFY_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef int32_t sv_status;
+enum {
+  SV_OK = 0,
+  SV_EINVAL = 1,       /* bad size, null pointer, T <= 0, stride < V, ... */
+  SV_EDTYPE = 2,       /* dtype not SV_BF16 / SV_F32 */
+  SV_EALIGN = 3,       /* logit base or row stride not 16-byte aligned */
+  SV_EWORKSPACE = 4,   /* ws is NULL or ws_bytes below sv_workspace_size */
+  SV_EUNSUPPORTED = 5, /* beyond this build's limits (see SV_MAX_*) */
+  SV_EHIP = 6          /* a HIP launch or copy failed */
+};
+
+typedef int32_t sv_dtype;
+enum { SV_F32 = 0, SV_BF16 = 1 };
+
+typedef int32_t sv_op;
+enum { SV_OP_CHAIN = 0, SV_OP_GREEDY = 1, SV_OP_MULTI = 2, SV_OP_TREE = 3, SV_OP_FANOUT = 4 };
+
+/* Limits of this build. */
+#define SV_MAX_GAMMA 64        /* draft positions per chain */
+#define SV_MAX_K 64            /* candidates per sequence */
+#define SV_MAX_N 1024          /* tree nodes per sequence (root included) */
+#define SV_MAX_FANOUT 64       /* F_max of sv_fanout_topk */
+#define SV_MAX_V (1 << 24)     /* vocabulary size */
+#define SV_MAX_SEQ 32768       /* sequences per call (rows per call for fan-out: 65536) */
+
+/* Device error-word bits (sv_get_device_error). */
+#define SV_DERR_TOKEN 1        /* a token id outside [0, V) was seen */
+#define SV_DERR_TREE 2         /* parent array invalid, or a path longer than max_depth */
+#define SV_DERR_FANOUT 4       /* F[r] outside [0, F_max] */
+#define SV_DERR_ROW 8          /* a needed row has no finite logit */
+
+int32_t sv_version(void);
+const char* sv_status_string(sv_status s);
+
+/*
+ * Workspace bytes for one call of `op` with the given shape.  gamma_or_N is
+ * gamma (chain, greedy, multi) or N (tree); B is the number of sequences (or
+ * R, the number of rows, for fan-out); K is used by multi only; F_max by
+ * fan-out only.  Returns SV_EINVAL / SV_EUNSUPPORTED for shapes the
+ * corresponding call would reject.
+ */
+sv_status sv_workspace_size(sv_op op, sv_dtype dt, int32_t B, int32_t K, int32_t gamma_or_N, int32_t V,
+                            int32_t F_max, size_t* bytes);
+
+/* Zero-fill a workspace on `stream` (a kernel, safe inside graph capture). */
+sv_status sv_workspace_init(void* ws, size_t ws_bytes, void* stream);
+
+/* Synchronise `stream`, read and clear the workspace's device error word. */
+sv_status sv_get_device_error(void* ws, int32_t* flags, void* stream);
+
+/*
+ * Chain verification (draft-verification page §1 steps 3-5, §2.1, §4).
+ *   tgt   [B, gamma+1, V] rows p_1..p_{gamma+1}; row (b, j) at b*(gamma+1)+j
+ *   drf   [B, gamma, V]   rows q_1..q_gamma;     row (b, j) at b*gamma+j
+ *   draft_tok [B, gamma] int32, x_j drawn by the drafter from q_j
+ * Outputs (device):
+ *   out_n   [B] number of accepted drafts n (0..gamma); emitted tokens are
+ *           x_1..x_n followed by out_tok
+ *   out_tok [B] correction drawn from max(0, p_{n+1} - q_{n+1}) (from
+ *           p_{n+1} if that mass rounds to 0), or the bonus from p_{gamma+1}
+ *   out_p, out_q [B, gamma] float, p_j(x_j) and q_j(x_j) for every j; may be
+ *           NULL (both or either)
+ * Reads each needed row once (rows 1..gamma of both tensors), then one row
+ * pair (or the bonus row) per sequence.
+ */
+sv_status sv_verify_chain(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride, int64_t drf_stride,
+                          const int32_t* draft_tok, int32_t B, int32_t gamma, int32_t V, float T, uint64_t seed,
+                          uint32_t round, int32_t* out_n, int32_t* out_tok, float* out_p, float* out_q, void* ws,
+                          size_t ws_bytes, void* stream);
+
+/*
+ * Greedy verification at temperature 0 (draft-verification page §2.2, §4:
+ * p and q are one-hot, so acceptance is an id comparison).
+ *   tgt [B, gamma+1, V], draft_tok [B, gamma]
+ *   g_j = the smallest index attaining the maximum of target row j (values
+ *   compared as numbers, -0 == +0); out_n = number of leading j with
+ *   x_j == g_j; out_tok = g_{n+1}; out_argmax [B, gamma+1] (may be NULL).
+ */
+sv_status sv_verify_greedy(const void* tgt, sv_dtype dt, int64_t stride, const int32_t* draft_tok, int32_t B,
+                           int32_t gamma, int32_t V, int32_t* out_n, int32_t* out_tok, int32_t* out_argmax, void* ws,
+                           size_t ws_bytes, void* stream);
+
+/*
+ * Multi-candidate self-selection (SpecDiff-2 page, Core method): K drafts per
+ * sequence sampled from shared draft marginals, each verified as a chain
+ * against its own target rows with its own acceptance uniforms (counter
+ * k = candidate); the longest accepted streak is kept (lowest k on ties) and
+ * its correction / bonus is drawn with the sequence's sampling uniform.
+ * K = 1 gives exactly sv_verify_chain's outputs.
+ *   tgt [B, K, gamma+1, V], row (b, k, j) at (b*K + k)*(gamma+1) + j
+ *   drf [B, gamma, V] shared by the K candidates
+ *   draft_tok [B, K, gamma]
+ * Outputs: out_k [B] kept candidate, out_n [B], out_tok [B],
+ *   out_n_cand [B, K] (may be NULL), out_p / out_q [B, K, gamma] (may be NULL).
+ */
+sv_status sv_verify_multi(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride, int64_t drf_stride,
+                          const int32_t* draft_tok, int32_t B, int32_t K, int32_t gamma, int32_t V, float T,
+                          uint64_t seed, uint32_t round, int32_t* out_k, int32_t* out_n, int32_t* out_tok,
+                          int32_t* out_n_cand, float* out_p, float* out_q, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Tree verification (PRESTO page §2.1; draft-verification page §2.1 rule at
+ * every child).  Node 0 is the root (its token is ignored); parent[i] < i for
+ * i >= 1.  Node u's rows P_u (tgt) and Q_u (drf) are the target and draft
+ * distributions of u's children.  From the root, children are tried in
+ * increasing node index: child c is accepted iff U_c < p_cur(tok_c) /
+ * q(tok_c); after a rejection the residual becomes
+ * p_cur <- norm(max(0, p_cur - q)), i.e. (p - c_i q)^+ / D_i with
+ * c_{i+1} = c_i + D_i and D_i its mass (one pass over the row pair).
+ * An accepted child becomes the current node.  When every child is
+ * rejected the correction is drawn from the last residual; a node without
+ * children gives the bonus draw from its P row.
+ *   tgt, drf [B, N, V], row (b, i) at b*N + i (leaf draft rows are not read)
+ *   node_tok, parent [B, N] int32
+ * Outputs: out_len [B] accepted path length (<= max_depth), out_path
+ *   [B, max_depth] accepted node ids in order (-1 padded), out_tok [B];
+ *   out_p / out_q [B, N] (may be NULL): p(tok_i), q(tok_i) of the base
+ *   distributions for every child i that was tried (others untouched).
+ */
+sv_status sv_verify_tree(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride, int64_t drf_stride,
+                         const int32_t* node_tok, const int32_t* parent, int32_t B, int32_t N, int32_t max_depth,
+                         int32_t V, float T, uint64_t seed, uint32_t round, int32_t* out_len, int32_t* out_path,
+                         int32_t* out_tok, float* out_p, float* out_q, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Top-F fan-out (SSD / Saguaro review §3): for each row r the F[r] largest
+ * logits, ordered by value descending and index ascending on ties.
+ *   logits [R, V]; F [R] device int32 with 0 <= F[r] <= F_max
+ *   out_ids [R, F_max] (-1 padded); out_vals [R, F_max] float (may be NULL,
+ *   -inf padded)
+ */
+sv_status sv_fanout_topk(const void* logits, sv_dtype dt, int64_t stride, int32_t R, int32_t V, const int32_t* F,
+                         int32_t F_max, int32_t* out_ids, float* out_vals, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Host helper, SSD / Saguaro review Theorem 12: F_k = ceil(F0 * a_p^(k/(1+r)))
+ * for k < K; F_K uses the capped term F0 * a_p^(K/(1+r)) * (1-a_p)^(-1/(1+r))
+ * when capped_last != 0, the plain term otherwise.  Writes K+1 values to the
+ * HOST array F_out and returns their sum (-1 on invalid arguments).
+ */
+int32_t sv_geometric_fanout(int32_t F0, double a_p, double r, int32_t K, int32_t capped_last, int32_t* F_out);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SPECVERIFY_H */

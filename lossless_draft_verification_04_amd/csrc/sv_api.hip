@@ -1,0 +1,399 @@
+// sv_api.hip -- the C ABI of libspecverify: host-side argument checks,
+// workspace planning and kernel launches on the caller's stream.
+//
+// Every check below runs before any HIP call, so invalid arguments are
+// rejected synchronously and nothing is enqueued.
+#include <cmath>
+#include <cstdlib>
+#include <cstring>
+
+#include "sv_device.hpp"
+#include "sv_internal.h"
+
+namespace sv {
+
+namespace {
+
+constexpr int kBlockVecs = 256;  // smallest row part (vectors) worth a block
+
+int env_int(const char* name, int dflt) {
+  const char* v = std::getenv(name);
+  if (!v || !*v) return dflt;
+  const int x = std::atoi(v);
+  return x > 0 ? x : dflt;
+}
+
+// Blocks the streaming passes aim for (the chip has 256 CUs; a few blocks
+// per CU keep enough loads in flight and even out the tail).  Overridable
+// for tuning sweeps with SV_STATS_BLOCKS / SV_SAMPLE_BLOCKS.
+int stats_blocks() {
+  static const int v = env_int("SV_STATS_BLOCKS", 2048);
+  return v;
+}
+int sample_blocks() {
+  static const int v = env_int("SV_SAMPLE_BLOCKS", 1024);
+  return v;
+}
+
+int per_vec(sv_dtype dt) { return dt == SV_BF16 ? 8 : 4; }
+int elem_bytes(sv_dtype dt) { return dt == SV_BF16 ? 2 : 4; }
+
+size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
+
+// Split rows of nvec vectors into parts so that rows * parts ~ target.
+void split(int64_t rows, int64_t nvec, int target, int32_t* nch, int64_t* vpc) {
+  int64_t n = rows > 0 ? (target + rows - 1) / rows : 1;
+  const int64_t cap = nvec / kBlockVecs > 1 ? nvec / kBlockVecs : 1;
+  if (n > cap) n = cap;
+  if (n < 1) n = 1;
+  int64_t per = (nvec + n - 1) / n;
+  if (per < 1) per = 1;
+  *vpc = per;
+  *nch = (int32_t)((nvec + per - 1) / per);
+}
+
+bool bad_dtype(sv_dtype dt) { return dt != SV_BF16 && dt != SV_F32; }
+
+sv_status check_rows(const void* base, int64_t stride, int32_t V, sv_dtype dt) {
+  if (!base) return SV_EINVAL;
+  if (stride < V) return SV_EINVAL;
+  if (reinterpret_cast<uintptr_t>(base) % 16 != 0) return SV_EALIGN;
+  if ((stride * elem_bytes(dt)) % 16 != 0) return SV_EALIGN;
+  return SV_OK;
+}
+
+bool bad_temperature(float T) { return !(T > 0.f) || !std::isfinite(T); }
+
+sv_status plan_chain(sv_dtype dt, int32_t B, int32_t K, int32_t gamma, int32_t V, Plan* pl) {
+  if (bad_dtype(dt)) return SV_EDTYPE;
+  if (B < 0 || K < 1 || gamma < 1 || V < 1) return SV_EINVAL;
+  if (B > SV_MAX_SEQ || K > SV_MAX_K || gamma > SV_MAX_GAMMA || V > SV_MAX_V) return SV_EUNSUPPORTED;
+  pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
+  const int64_t rows = (int64_t)B * (K + 1) * gamma;
+  split(rows, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
+  split(B, pl->nvec, sample_blocks(), &pl->nch2, &pl->vpc2);
+  pl->grid1 = rows * pl->nch1;
+  pl->grid2 = (int64_t)B * pl->nch2;
+  if (pl->grid1 > INT32_MAX || pl->grid2 > INT32_MAX) return SV_EUNSUPPORTED;
+  if ((int64_t)(K + 1) * gamma * pl->nch1 > UINT32_MAX / 2) return SV_EUNSUPPORTED;
+  size_t off = kWsFixed;
+  pl->off_part1 = off;
+  off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
+  pl->off_jobs = off;
+  off = align_up(off + (size_t)B * 64, 256);
+  pl->off_part2 = off;
+  off = align_up(off + (size_t)B * pl->nch2 * sizeof(Partial), 256);
+  pl->bytes = off;
+  return SV_OK;
+}
+
+sv_status plan_greedy(sv_dtype dt, int32_t B, int32_t gamma, int32_t V, Plan* pl) {
+  if (bad_dtype(dt)) return SV_EDTYPE;
+  if (B < 0 || gamma < 1 || V < 1) return SV_EINVAL;
+  if (B > SV_MAX_SEQ || gamma > SV_MAX_GAMMA || V > SV_MAX_V) return SV_EUNSUPPORTED;
+  pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
+  const int64_t rows = (int64_t)B * (gamma + 1);
+  split(rows, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
+  pl->grid1 = rows * pl->nch1;
+  if (pl->grid1 > INT32_MAX) return SV_EUNSUPPORTED;
+  size_t off = kWsFixed;
+  pl->off_part1 = off;
+  off = align_up(off + (size_t)rows * pl->nch1 * 8, 256);
+  pl->bytes = off;
+  return SV_OK;
+}
+
+constexpr int kWalkThreads = 512;
+constexpr int kWalkMaxTiles = 8192;
+
+sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, Plan* pl) {
+  if (bad_dtype(dt)) return SV_EDTYPE;
+  if (B < 0 || N < 1 || V < 1) return SV_EINVAL;
+  if (B > SV_MAX_SEQ || N > SV_MAX_N || V > SV_MAX_V) return SV_EUNSUPPORTED;
+  pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
+  if ((pl->nvec + kWalkThreads - 1) / kWalkThreads > kWalkMaxTiles) return SV_EUNSUPPORTED;
+  const int64_t rows = (int64_t)B * N * 2;
+  // only nodes with children are streamed; size the parts for about half
+  split(rows / 2 > 0 ? rows / 2 : 1, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
+  pl->grid1 = rows * pl->nch1;
+  pl->grid2 = B;
+  if (pl->grid1 > INT32_MAX) return SV_EUNSUPPORTED;
+  size_t off = kWsFixed;
+  pl->off_part1 = off;
+  off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
+  pl->bytes = off;
+  return SV_OK;
+}
+
+sv_status plan_fanout(sv_dtype dt, int32_t R, int32_t V, int32_t F_max, Plan* pl) {
+  if (bad_dtype(dt)) return SV_EDTYPE;
+  if (R < 0 || V < 1 || F_max < 1) return SV_EINVAL;
+  if (R > (int32_t)kWsCounters || V > SV_MAX_V || F_max > SV_MAX_FANOUT) return SV_EUNSUPPORTED;
+  pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
+  split(R, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
+  pl->grid1 = (int64_t)R * pl->nch1;
+  if (pl->grid1 > INT32_MAX) return SV_EUNSUPPORTED;
+  size_t off = kWsFixed;
+  pl->off_part1 = off;
+  off = align_up(off + (size_t)R * pl->nch1 * F_max * 8, 256);
+  pl->bytes = off;
+  return SV_OK;
+}
+
+sv_status check_ws(const void* ws, size_t ws_bytes, const Plan& pl) {
+  if (!ws || ws_bytes < pl.bytes) return SV_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return SV_EALIGN;
+  return SV_OK;
+}
+
+float log2e_over(float T) { return (float)(1.4426950408889634 / (double)T); }
+
+__global__ void fill_zero_kernel(uint32_t* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x) p[i] = 0u;
+}
+
+}  // namespace
+
+hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 4;
+  if (n == 0) return hipSuccess;
+  size_t blocks = (n + 255) / 256;
+  if (blocks > 4096) blocks = 4096;
+  fill_zero_kernel<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(static_cast<uint32_t*>(ws), n);
+  return hipGetLastError();
+}
+
+}  // namespace sv
+
+using namespace sv;
+
+extern "C" {
+
+int32_t sv_version(void) { return 1; }
+
+const char* sv_status_string(sv_status s) {
+  switch (s) {
+    case SV_OK: return "ok";
+    case SV_EINVAL: return "invalid argument";
+    case SV_EDTYPE: return "unsupported dtype";
+    case SV_EALIGN: return "logit rows or workspace not 16-byte aligned";
+    case SV_EWORKSPACE: return "workspace missing or too small";
+    case SV_EUNSUPPORTED: return "shape beyond this build's limits";
+    case SV_EHIP: return "HIP launch or copy failed";
+    default: return "unknown status";
+  }
+}
+
+sv_status sv_workspace_size(sv_op op, sv_dtype dt, int32_t B, int32_t K, int32_t gamma_or_N, int32_t V,
+                            int32_t F_max, size_t* bytes) {
+  if (!bytes) return SV_EINVAL;
+  Plan pl;
+  sv_status st;
+  switch (op) {
+    case SV_OP_CHAIN: st = plan_chain(dt, B, 1, gamma_or_N, V, &pl); break;
+    case SV_OP_MULTI: st = plan_chain(dt, B, K, gamma_or_N, V, &pl); break;
+    case SV_OP_GREEDY: st = plan_greedy(dt, B, gamma_or_N, V, &pl); break;
+    case SV_OP_TREE: st = plan_tree(dt, B, gamma_or_N, V, &pl); break;
+    case SV_OP_FANOUT: st = plan_fanout(dt, B, V, F_max, &pl); break;
+    default: return SV_EINVAL;
+  }
+  if (st != SV_OK) return st;
+  *bytes = pl.bytes;
+  return SV_OK;
+}
+
+sv_status sv_workspace_init(void* ws, size_t ws_bytes, void* stream) {
+  if (!ws || ws_bytes < kWsFixed) return SV_EWORKSPACE;
+  if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return SV_EALIGN;
+  return launch_fill_zero(ws, ws_bytes, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+sv_status sv_get_device_error(void* ws, int32_t* flags, void* stream) {
+  if (!ws || !flags) return SV_EINVAL;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t h = 0;
+  if (hipMemcpyAsync(&h, ws, sizeof h, hipMemcpyDeviceToHost, s) != hipSuccess) return SV_EHIP;
+  if (hipStreamSynchronize(s) != hipSuccess) return SV_EHIP;
+  *flags = h;
+  if (h != 0 && launch_fill_zero(ws, 4, s) != hipSuccess) return SV_EHIP;
+  return SV_OK;
+}
+
+static sv_status verify_chain_like(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride,
+                                   int64_t drf_stride, const int32_t* tok, int32_t B, int32_t K, int32_t gamma,
+                                   int32_t V, float T, uint64_t seed, uint32_t round, int32_t* out_k, int32_t* out_n,
+                                   int32_t* out_tok, int32_t* out_n_cand, float* out_p, float* out_q, void* ws,
+                                   size_t ws_bytes, void* stream) {
+  Plan pl;
+  sv_status st = plan_chain(dt, B, K, gamma, V, &pl);
+  if (st != SV_OK) return st;
+  if (bad_temperature(T) || round >= (1u << 30)) return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  if ((st = check_rows(tgt, tgt_stride, V, dt)) != SV_OK) return st;
+  if ((st = check_rows(drf, drf_stride, V, dt)) != SV_OK) return st;
+  if (!tok || !out_n || !out_tok) return SV_EINVAL;
+  if ((st = check_ws(ws, ws_bytes, pl)) != SV_OK) return st;
+  char* w = static_cast<char*>(ws);
+  ChainParams p;
+  p.tgt = tgt;
+  p.drf = drf;
+  p.tgt_sb = tgt_stride * elem_bytes(dt);
+  p.drf_sb = drf_stride * elem_bytes(dt);
+  p.tok = tok;
+  p.B = B;
+  p.K = K;
+  p.gamma = gamma;
+  p.V = V;
+  p.c = log2e_over(T);
+  p.seed = seed;
+  p.round = round;
+  p.out_k = out_k;
+  p.out_n = out_n;
+  p.out_tok = out_tok;
+  p.out_n_cand = out_n_cand;
+  p.out_p = out_p;
+  p.out_q = out_q;
+  p.err = reinterpret_cast<int32_t*>(w);
+  p.cnt1 = reinterpret_cast<uint32_t*>(w + kWsHeader);
+  p.cnt2 = p.cnt1 + kWsCounters / 2;
+  p.part1 = w + pl.off_part1;
+  p.jobs = w + pl.off_jobs;
+  p.part2 = w + pl.off_part2;
+  p.nch1 = pl.nch1;
+  p.nch2 = pl.nch2;
+  p.vpc1 = pl.vpc1;
+  p.vpc2 = pl.vpc2;
+  p.nvec = pl.nvec;
+  return launch_chain(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+sv_status sv_verify_chain(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride, int64_t drf_stride,
+                          const int32_t* draft_tok, int32_t B, int32_t gamma, int32_t V, float T, uint64_t seed,
+                          uint32_t round, int32_t* out_n, int32_t* out_tok, float* out_p, float* out_q, void* ws,
+                          size_t ws_bytes, void* stream) {
+  return verify_chain_like(tgt, drf, dt, tgt_stride, drf_stride, draft_tok, B, 1, gamma, V, T, seed, round, nullptr,
+                           out_n, out_tok, nullptr, out_p, out_q, ws, ws_bytes, stream);
+}
+
+sv_status sv_verify_multi(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride, int64_t drf_stride,
+                          const int32_t* draft_tok, int32_t B, int32_t K, int32_t gamma, int32_t V, float T,
+                          uint64_t seed, uint32_t round, int32_t* out_k, int32_t* out_n, int32_t* out_tok,
+                          int32_t* out_n_cand, float* out_p, float* out_q, void* ws, size_t ws_bytes, void* stream) {
+  if (!out_k) return SV_EINVAL;
+  return verify_chain_like(tgt, drf, dt, tgt_stride, drf_stride, draft_tok, B, K, gamma, V, T, seed, round, out_k,
+                           out_n, out_tok, out_n_cand, out_p, out_q, ws, ws_bytes, stream);
+}
+
+sv_status sv_verify_greedy(const void* tgt, sv_dtype dt, int64_t stride, const int32_t* draft_tok, int32_t B,
+                           int32_t gamma, int32_t V, int32_t* out_n, int32_t* out_tok, int32_t* out_argmax, void* ws,
+                           size_t ws_bytes, void* stream) {
+  Plan pl;
+  sv_status st = plan_greedy(dt, B, gamma, V, &pl);
+  if (st != SV_OK) return st;
+  if (B == 0) return SV_OK;
+  if ((st = check_rows(tgt, stride, V, dt)) != SV_OK) return st;
+  if (!draft_tok || !out_n || !out_tok) return SV_EINVAL;
+  if ((st = check_ws(ws, ws_bytes, pl)) != SV_OK) return st;
+  char* w = static_cast<char*>(ws);
+  GreedyParams p;
+  p.tgt = tgt;
+  p.tgt_sb = stride * elem_bytes(dt);
+  p.tok = draft_tok;
+  p.B = B;
+  p.gamma = gamma;
+  p.V = V;
+  p.out_n = out_n;
+  p.out_tok = out_tok;
+  p.out_argmax = out_argmax;
+  p.err = reinterpret_cast<int32_t*>(w);
+  p.cnt = reinterpret_cast<uint32_t*>(w + kWsHeader);
+  p.part = w + pl.off_part1;
+  p.nch = pl.nch1;
+  p.vpc = pl.vpc1;
+  p.nvec = pl.nvec;
+  return launch_greedy(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+sv_status sv_verify_tree(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride, int64_t drf_stride,
+                         const int32_t* node_tok, const int32_t* parent, int32_t B, int32_t N, int32_t max_depth,
+                         int32_t V, float T, uint64_t seed, uint32_t round, int32_t* out_len, int32_t* out_path,
+                         int32_t* out_tok, float* out_p, float* out_q, void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  sv_status st = plan_tree(dt, B, N, V, &pl);
+  if (st != SV_OK) return st;
+  if (max_depth < 1 || max_depth > SV_MAX_N) return SV_EINVAL;
+  if (bad_temperature(T) || round >= (1u << 30)) return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  if ((st = check_rows(tgt, tgt_stride, V, dt)) != SV_OK) return st;
+  if ((st = check_rows(drf, drf_stride, V, dt)) != SV_OK) return st;
+  if (!node_tok || !parent || !out_len || !out_path || !out_tok) return SV_EINVAL;
+  if ((st = check_ws(ws, ws_bytes, pl)) != SV_OK) return st;
+  char* w = static_cast<char*>(ws);
+  TreeParams p;
+  p.tgt = tgt;
+  p.drf = drf;
+  p.tgt_sb = tgt_stride * elem_bytes(dt);
+  p.drf_sb = drf_stride * elem_bytes(dt);
+  p.tok = node_tok;
+  p.parent = parent;
+  p.B = B;
+  p.N = N;
+  p.max_depth = max_depth;
+  p.V = V;
+  p.c = log2e_over(T);
+  p.seed = seed;
+  p.round = round;
+  p.out_len = out_len;
+  p.out_path = out_path;
+  p.out_tok = out_tok;
+  p.out_p = out_p;
+  p.out_q = out_q;
+  p.err = reinterpret_cast<int32_t*>(w);
+  p.part = w + pl.off_part1;
+  p.nch = pl.nch1;
+  p.vpc = pl.vpc1;
+  p.nvec = pl.nvec;
+  return launch_tree(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+sv_status sv_fanout_topk(const void* logits, sv_dtype dt, int64_t stride, int32_t R, int32_t V, const int32_t* F,
+                         int32_t F_max, int32_t* out_ids, float* out_vals, void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  sv_status st = plan_fanout(dt, R, V, F_max, &pl);
+  if (st != SV_OK) return st;
+  if (R == 0) return SV_OK;
+  if ((st = check_rows(logits, stride, V, dt)) != SV_OK) return st;
+  if (!F || !out_ids) return SV_EINVAL;
+  if ((st = check_ws(ws, ws_bytes, pl)) != SV_OK) return st;
+  char* w = static_cast<char*>(ws);
+  FanoutParams p;
+  p.logits = logits;
+  p.sb = stride * elem_bytes(dt);
+  p.R = R;
+  p.V = V;
+  p.F = F;
+  p.F_max = F_max;
+  p.out_ids = out_ids;
+  p.out_vals = out_vals;
+  p.err = reinterpret_cast<int32_t*>(w);
+  p.cnt = reinterpret_cast<uint32_t*>(w + kWsHeader);
+  p.part = w + pl.off_part1;
+  p.nch = pl.nch1;
+  p.vpc = pl.vpc1;
+  p.nvec = pl.nvec;
+  return launch_fanout(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+int32_t sv_geometric_fanout(int32_t F0, double a_p, double r, int32_t K, int32_t capped_last, int32_t* F_out) {
+  if (!F_out || F0 < 0 || K < 0 || !(a_p > 0.0) || !(a_p < 1.0) || !(r >= 0.0)) return -1;
+  int32_t sum = 0;
+  for (int32_t k = 0; k <= K; ++k) {
+    double f = (double)F0 * std::pow(a_p, (double)k / (1.0 + r));
+    if (k == K && capped_last) f *= std::pow(1.0 - a_p, -1.0 / (1.0 + r));
+    F_out[k] = (int32_t)std::ceil(f);
+    sum += F_out[k];
+  }
+  return sum;
+}
+
+}  // extern "C"

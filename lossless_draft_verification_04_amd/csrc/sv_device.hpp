@@ -1,0 +1,478 @@
+// sv_device.hpp -- device-side building blocks of the gfx950 verification
+// kernels: Philox uniforms, 16-byte row loads, wave/block reductions and
+// scans, online row statistics and the block-wide inverse-CDF search.
+//
+// Internal to libspecverify; shares nothing with the CPU oracle.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+constexpr int kWave = 64;
+constexpr float kNegInf = -__builtin_huge_valf();
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// Element formats: one 16-byte load holds 8 bf16 or 4 fp32 logits.
+// bf16 -> fp32 is exact: the 16 bits are the high half of the fp32 pattern;
+// in a little-endian 32-bit word the lower-indexed element is the low half.
+// ---------------------------------------------------------------------------
+template <int DT>
+struct Fmt;
+template <>
+struct Fmt<SV_BF16> {
+  static constexpr int kPerVec = 8;
+  static constexpr int kBytes = 2;
+};
+template <>
+struct Fmt<SV_F32> {
+  static constexpr int kPerVec = 4;
+  static constexpr int kBytes = 4;
+};
+
+template <int DT>
+__device__ __forceinline__ void unpack(const u32x4 d, float* x) {
+  if constexpr (DT == SV_BF16) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = __uint_as_float(d[i] << 16);
+      x[2 * i + 1] = __uint_as_float(d[i] & 0xffff0000u);
+    }
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) x[i] = __uint_as_float(d[i]);
+  }
+}
+
+__device__ __forceinline__ const void* row_ptr(const void* base, int64_t row, int64_t stride_bytes) {
+  return static_cast<const char*>(base) + row * stride_bytes;
+}
+
+__device__ __forceinline__ u32x4 load_vec(const void* row, int64_t vi) {
+  return reinterpret_cast<const u32x4*>(row)[vi];
+}
+
+// One logit as fp32 (gather of a single token).
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* row, int64_t i) {
+  if constexpr (DT == SV_BF16) {
+    const uint16_t h = reinterpret_cast<const uint16_t*>(row)[i];
+    return __uint_as_float((uint32_t)h << 16);
+  } else {
+    return reinterpret_cast<const float*>(row)[i];
+  }
+}
+
+// 2^x on the hardware exp unit (no denormal fix-up; terms that small are
+// below 2^-126 of the row maximum and do not matter to any sum here).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// ---------------------------------------------------------------------------
+// Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of
+// (c0,c1,c2,c3) -> (hi(B c2)^c1^k0, lo(B c2), hi(A c0)^c3^k1, lo(A c0)),
+// A = 0xD2511F53, B = 0xCD9E8D57, key bumped by (0x9E3779B9, 0xBB67AE85)
+// between rounds.  Only the first output word is used.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ uint32_t philox_word0(uint32_t c0, uint32_t c1, uint32_t c2, uint32_t c3, uint32_t k0,
+                                                 uint32_t k1) {
+#pragma unroll
+  for (int i = 0; i < 10; ++i) {
+    if (i > 0) {
+      k0 += 0x9E3779B9u;
+      k1 += 0xBB67AE85u;
+    }
+    const uint32_t lo_a = 0xD2511F53u * c0, hi_a = __umulhi(0xD2511F53u, c0);
+    const uint32_t lo_b = 0xCD9E8D57u * c2, hi_b = __umulhi(0xCD9E8D57u, c2);
+    const uint32_t n0 = hi_b ^ c1 ^ k0;
+    const uint32_t n2 = hi_a ^ c3 ^ k1;
+    c0 = n0;
+    c1 = lo_b;
+    c2 = n2;
+    c3 = lo_a;
+  }
+  return c0;
+}
+
+// Verifier uniform on the 2^-24 grid: key = seed (low, high), counter =
+// (idx, b, k, (round << 2) | tag).
+__device__ __forceinline__ double uniform24(uint64_t seed, uint32_t idx, uint32_t b, uint32_t k, uint32_t round,
+                                            uint32_t tag) {
+  const uint32_t w = philox_word0(idx, b, k, (round << 2) | tag, (uint32_t)seed, (uint32_t)(seed >> 32));
+  return (double)(w >> 8) * (1.0 / 16777216.0);
+}
+
+// a = p(x) / q(x); q(x) = 0 accepts iff p(x) > 0.
+__device__ __forceinline__ double accept_ratio(double p, double q) {
+  if (q > 0.0) return p / q;
+  return p > 0.0 ? __builtin_huge_val() : 0.0;
+}
+
+// ---------------------------------------------------------------------------
+// Wave / block collectives (block of NT threads = NT/64 waves).
+// ---------------------------------------------------------------------------
+template <typename T>
+__device__ __forceinline__ T wave_max(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+template <typename T>
+__device__ __forceinline__ T wave_min(T v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ float wave_fmax(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
+  return v;
+}
+__device__ __forceinline__ double wave_sum(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+template <int NT>
+__device__ float block_fmax(float v) {
+  __shared__ float red[NT / kWave];
+  v = wave_fmax(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+  __syncthreads();
+  float r = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / kWave; ++i) r = fmaxf(r, red[i]);
+  return r;
+}
+
+// Sum in a fixed order (wave butterfly, then waves in index order):
+// deterministic for a given launch shape.
+template <int NT>
+__device__ double block_sum(double v) {
+  __shared__ double red[NT / kWave];
+  v = wave_sum(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+  __syncthreads();
+  double r = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / kWave; ++i) r += red[i];
+  return r;
+}
+
+template <int NT>
+__device__ int64_t block_max_i64(int64_t v) {
+  __shared__ int64_t red[NT / kWave];
+  v = wave_max(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+  __syncthreads();
+  int64_t r = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / kWave; ++i) r = max(r, red[i]);
+  return r;
+}
+
+template <int NT>
+__device__ int64_t block_min_i64(int64_t v) {
+  __shared__ int64_t red[NT / kWave];
+  v = wave_min(v);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
+  __syncthreads();
+  int64_t r = red[0];
+#pragma unroll
+  for (int i = 1; i < NT / kWave; ++i) r = min(r, red[i]);
+  return r;
+}
+
+// Exclusive prefix sum over the block in thread order; returns the total.
+template <int NT>
+__device__ double block_exclusive_scan(double v, double* excl) {
+  __shared__ double wtot[NT / kWave];
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  double inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double y = __shfl_up(inc, o, kWave);
+    if (lane >= o) inc += y;
+  }
+  __syncthreads();
+  if (lane == kWave - 1) wtot[w] = inc;
+  __syncthreads();
+  double before = 0.0, total = 0.0;
+#pragma unroll
+  for (int i = 0; i < NT / kWave; ++i) {
+    if (i < w) before += wtot[i];
+    total += wtot[i];
+  }
+  *excl = before + (inc - v);
+  return total;
+}
+
+// ---------------------------------------------------------------------------
+// Row statistics.  For logits z and c = log2(e) / T, a row's temperature
+// softmax is p(v) = 2^(z_v c - c M) / S with M = max z and
+// S = sum_v 2^(z_v c - c M).  A partial over part of a row is (M, S) with
+// S relative to the fp32 product cm = c * M; partials merge by rescaling
+// with 2^(cm_a - cm_b).
+// ---------------------------------------------------------------------------
+struct Partial {
+  float m;   // max raw logit of the part (-inf if none finite)
+  float pad;
+  double s;  // sum of 2^(z c - c m) over the part
+};
+
+struct RowStat {
+  float cm;  // c * (row max), the shift used for every term
+  float pad;
+  double S;  // sum_v 2^(z_v c - cm); 0 if the row has no finite logit
+};
+
+// Online (max, sum) over vectors [v0, v1) of one row by a block of NT
+// threads; U vectors in flight per thread.  Every thread returns the
+// block's partial.
+template <int DT, int NT, int U>
+__device__ Partial range_stats(const void* row, int V, int64_t v0, int64_t v1, float c) {
+  constexpr int E = Fmt<DT>::kPerVec;
+  const int tid = threadIdx.x;
+  const int64_t nfull = V / E;
+  const int64_t vf = v1 < nfull ? v1 : nfull;
+  float m = kNegInf;
+  float s = 0.f;
+  int64_t v = v0 + tid;
+  for (; v + (int64_t)(U - 1) * NT < vf; v += (int64_t)U * NT) {
+    u32x4 d[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) d[u] = load_vec(row, v + (int64_t)u * NT);
+    float x[U * E];
+#pragma unroll
+    for (int u = 0; u < U; ++u) unpack<DT>(d[u], x + u * E);
+    float gm = x[0];
+#pragma unroll
+    for (int e = 1; e < U * E; ++e) gm = fmaxf(gm, x[e]);
+    if (gm > m) {
+      s *= fast_exp2(c * m - c * gm);
+      m = gm;
+    }
+    if (m != kNegInf) {
+      const float cm = c * m;
+      float t[U * E];
+#pragma unroll
+      for (int e = 0; e < U * E; ++e) t[e] = fast_exp2(__builtin_fmaf(x[e], c, -cm));
+#pragma unroll
+      for (int w = U * E / 2; w > 0; w >>= 1)
+#pragma unroll
+        for (int e = 0; e < w; ++e) t[e] += t[e + w];
+      s += t[0];
+    }
+  }
+  for (; v < v1; v += NT) {
+    float x[E];
+    unpack<DT>(load_vec(row, v), x);
+    if (v >= nfull) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (v * E + e >= V) x[e] = kNegInf;
+    }
+    float gm = x[0];
+#pragma unroll
+    for (int e = 1; e < E; ++e) gm = fmaxf(gm, x[e]);
+    if (gm > m) {
+      s *= fast_exp2(c * m - c * gm);
+      m = gm;
+    }
+    if (m != kNegInf) {
+      const float cm = c * m;
+      float acc = 0.f;
+#pragma unroll
+      for (int e = 0; e < E; ++e) acc += fast_exp2(__builtin_fmaf(x[e], c, -cm));
+      s += acc;
+    }
+  }
+  const float M = block_fmax<NT>(m);
+  const double mine = (m == kNegInf) ? 0.0 : (double)s * (double)fast_exp2(c * m - c * M);
+  const double S = block_sum<NT>(mine);
+  Partial p;
+  p.m = M;
+  p.pad = 0.f;
+  p.s = S;
+  return p;
+}
+
+// Merge part statistics (in part order) into the row statistic.
+__device__ __forceinline__ RowStat merge_parts(const Partial* parts, int n, float c) {
+  float M = kNegInf;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, parts[i].m);
+  RowStat r;
+  r.pad = 0.f;
+  if (M == kNegInf) {
+    r.cm = 0.f;
+    r.S = 0.0;
+    return r;
+  }
+  r.cm = c * M;
+  double S = 0.0;
+  for (int i = 0; i < n; ++i) {
+    if (parts[i].m == kNegInf) continue;
+    S += parts[i].s * exp2((double)(c * parts[i].m) - (double)r.cm);
+  }
+  r.S = S;
+  return r;
+}
+
+// p(v) of one gathered logit under a row statistic (0 for an empty row).
+__device__ __forceinline__ double prob_of(float z, float c, const RowStat& st) {
+  if (!(st.S > 0.0)) return 0.0;
+  return (double)exp2f(__builtin_fmaf(z, c, -st.cm)) / st.S;
+}
+
+// ---------------------------------------------------------------------------
+// Weights of the final draw, one 16-byte vector at a time (elements past V
+// get weight 0).
+//   residual: w = max(0, p - coef * q), p and q normalised by their row
+//             statistics (coef = 1 for a chain, c_i for a tree node);
+//   plain:    w = 2^(z c - cm) (bonus draw / fallback, unnormalised).
+// ---------------------------------------------------------------------------
+struct DrawSpec {
+  const void* rowP;
+  const void* rowQ;  // null for a plain draw
+  float c;           // log2(e) / T
+  float cmP, invSP;  // residual: p = 2^(zP c - cmP) * invSP; plain: shift cmP, invSP unused
+  float cmQ, invSQ;
+  float coef;
+};
+
+template <int DT>
+__device__ __forceinline__ void draw_weights_from(const DrawSpec& sp, int V, int64_t vi, const u32x4 dp,
+                                                  const u32x4 dq, float* w) {
+  constexpr int E = Fmt<DT>::kPerVec;
+  float zp[E];
+  unpack<DT>(dp, zp);
+  if (sp.rowQ) {
+    float zq[E];
+    unpack<DT>(dq, zq);
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      const float pw = fast_exp2(__builtin_fmaf(zp[e], sp.c, -sp.cmP)) * sp.invSP;
+      const float qw = fast_exp2(__builtin_fmaf(zq[e], sp.c, -sp.cmQ)) * sp.invSQ;
+      w[e] = fmaxf(__builtin_fmaf(-sp.coef, qw, pw), 0.f);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < E; ++e) w[e] = fast_exp2(__builtin_fmaf(zp[e], sp.c, -sp.cmP));
+  }
+  if ((vi + 1) * E > V) {
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (vi * E + e >= V) w[e] = 0.f;
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void draw_weights(const DrawSpec& sp, int V, int64_t vi, float* w) {
+  const u32x4 dp = load_vec(sp.rowP, vi);
+  const u32x4 dq = sp.rowQ ? load_vec(sp.rowQ, vi) : dp;
+  draw_weights_from<DT>(sp, V, vi, dp, dq, w);
+}
+
+// Sum of draw weights over vectors [v0, v1) by a block (double accumulation).
+template <int DT, int NT>
+__device__ double range_weight_sum(const DrawSpec& sp, int V, int64_t v0, int64_t v1) {
+  constexpr int E = Fmt<DT>::kPerVec;
+  double acc = 0.0;
+  for (int64_t v = v0 + threadIdx.x; v < v1; v += NT) {
+    float w[E];
+    draw_weights<DT>(sp, V, v, w);
+    double own = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e) own += (double)w[e];
+    acc += own;
+  }
+  return block_sum<NT>(acc);
+}
+
+// Inverse-CDF search over vectors [v0, v1) in index order: the first element
+// whose running weight exceeds `target`.  Tiles of NT vectors; in each tile
+// the block scans per-thread sums, and the thread whose interval holds the
+// target walks its own elements.  If rounding leaves the target beyond the
+// range's weight, the last positive element is returned.  All threads return
+// the same index.
+template <int DT, int NT>
+__device__ int64_t block_search(const DrawSpec& sp, int V, int64_t v0, int64_t v1, double target) {
+  constexpr int E = Fmt<DT>::kPerVec;
+  double cum = 0.0;
+  int64_t last_pos = -1;
+  for (int64_t base = v0; base < v1; base += NT) {
+    const int64_t v = base + threadIdx.x;
+    float w[E];
+#pragma unroll
+    for (int e = 0; e < E; ++e) w[e] = 0.f;
+    if (v < v1) draw_weights<DT>(sp, V, v, w);
+    double own = 0.0;
+    int64_t my_last = -1;
+#pragma unroll
+    for (int e = 0; e < E; ++e) {
+      own += (double)w[e];
+      if (w[e] > 0.f) my_last = v * E + e;
+    }
+    double excl;
+    const double total = block_exclusive_scan<NT>(own, &excl);
+    const int64_t tile_last = block_max_i64<NT>(my_last);
+    if (tile_last >= 0) last_pos = tile_last;
+    if (cum + total > target) {
+      const double t_local = target - cum - excl;
+      int64_t found = INT64_MAX;
+      if (own > 0.0 && t_local >= 0.0 && t_local < own) {
+        double run = 0.0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          run += (double)w[e];
+          if (found == INT64_MAX && run > t_local) found = v * E + e;
+        }
+        if (found == INT64_MAX) found = my_last;
+      }
+      const int64_t r = block_min_i64<NT>(found);
+      return r != INT64_MAX ? r : tile_last;
+    }
+    cum += total;
+  }
+  return last_pos;
+}
+
+// Release this block's global writes / acquire other blocks' (agent scope,
+// so the per-XCD L2 caches are written back / invalidated as needed).
+__device__ __forceinline__ void fence_acq_rel_agent() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent"); }
+
+// Count one arrival on `counter`; true in every thread of the block that
+// arrived last (of `total`).  That block resets the counter to 0 itself.
+template <int NT>
+__device__ bool arrive_last(uint32_t* counter, uint32_t total) {
+  __shared__ int last;
+  fence_acq_rel_agent();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    last = (old == total - 1);
+  }
+  __syncthreads();
+  if (last) fence_acq_rel_agent();
+  return last != 0;
+}
+
+__device__ __forceinline__ void set_error(int32_t* err, int32_t bit) {
+  __hip_atomic_fetch_or(err, bit, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+}  // namespace sv

@@ -1,0 +1,157 @@
+// sv_fanout.hip -- top-F fan-out of draft rows on gfx950.
+//
+// SSD / Saguaro review §3: the speculation cache holds the top-F_k tokens of
+// the draft logits at every lookahead position k.  Here: for each row r the
+// F[r] largest logits, value descending, index ascending on ties.
+//
+// One launch: a block per (row part).  Each wave keeps its current top-F in
+// registers, one entry per lane (lane i = i-th best), and streams its share of
+// the part in increasing index order.  A lane's 16-byte vector is a candidate
+// only if its largest element beats the wave's F-th best so far (elements are
+// seen in index order, so an equal value can never displace an earlier
+// entry); candidates are inserted one element at a time with a lane shift.
+// Most vectors cost one max and one compare.  The block merges its waves'
+// lists; the last block of a row merges the parts' lists and writes them.
+#include "sv_device.hpp"
+#include "sv_internal.h"
+
+namespace sv {
+
+constexpr int kFNT = 256;
+
+struct TopEntry {
+  float val;
+  int32_t idx;
+};
+
+constexpr int32_t kNoIdx = 0x7fffffff;
+
+__device__ __forceinline__ bool top_better(float va, int32_t ia, float vb, int32_t ib) {
+  return va > vb || (va == vb && ia < ib);
+}
+
+// Insert (v, i) into the wave's sorted list (lane l holds entry l; lanes
+// >= F hold the empty entry).  Wave-uniform arguments.
+__device__ __forceinline__ void wave_insert(float& lv, int32_t& li, float v, int32_t i, int F, int lane) {
+  const bool here = top_better(v, i, lv, li) && lane < F;
+  const uint64_t m = __ballot(here);
+  if (!m) return;
+  const int pos = __builtin_ctzll(m);
+  const float up_v = __shfl_up(lv, 1, kWave);
+  const int32_t up_i = __shfl_up(li, 1, kWave);
+  if (lane < F) {
+    if (lane > pos) {
+      lv = up_v;
+      li = up_i;
+    } else if (lane == pos) {
+      lv = v;
+      li = i;
+    }
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
+  constexpr int E = Fmt<DT>::kPerVec;
+  const int r = blockIdx.x / a.nch;
+  const int ch = blockIdx.x - r * a.nch;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  int F = a.F[r];
+  if (F < 0 || F > a.F_max) {
+    if (threadIdx.x == 0 && ch == 0) set_error(a.err, SV_DERR_FANOUT);
+    F = F < 0 ? 0 : a.F_max;
+  }
+  const void* row = row_ptr(a.logits, r, a.sb);
+  float lv = kNegInf;
+  int32_t li = kNoIdx;
+  int count = 0;  // entries held (wave-uniform)
+  float thr = kNegInf;
+  const int64_t v0 = (int64_t)ch * a.vpc;
+  const int64_t v1 = v0 + a.vpc < a.nvec ? v0 + a.vpc : a.nvec;
+  if (F > 0) {
+    // each wave walks its own 64-vector windows in increasing order
+    const int nw = kFNT / kWave;
+    for (int64_t base = v0 + (int64_t)wave * kWave; base < v1; base += (int64_t)nw * kWave) {
+      const int64_t v = base + lane;
+      float x[E];
+      float vm = kNegInf;
+      bool valid = v < v1;
+      if (valid) {
+        unpack<DT>(load_vec(row, v), x);
+        if ((v + 1) * E > a.V) {
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (v * E + e >= a.V) x[e] = kNegInf;
+        }
+        vm = x[0];
+#pragma unroll
+        for (int e = 1; e < E; ++e) vm = fmaxf(vm, x[e]);
+      }
+      const bool cand = valid && (count < F || vm > thr);
+      uint64_t cm = __ballot(cand);
+      while (cm) {
+        const int src = __builtin_ctzll(cm);
+        cm &= cm - 1;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          const float xe = __shfl(x[e], src, kWave);
+          const int64_t gi = (base + src) * E + e;
+          if (gi < a.V && (count < F || xe > thr)) {
+            wave_insert(lv, li, xe, (int32_t)gi, F, lane);
+            if (count < F) ++count;
+            thr = __shfl(lv, F - 1, kWave);
+          }
+        }
+      }
+    }
+  }
+  // merge the block's waves into wave 0's list
+  __shared__ TopEntry s_list[kFNT / kWave][SV_MAX_FANOUT];
+  __syncthreads();
+  if (lane < SV_MAX_FANOUT) {
+    s_list[wave][lane].val = lv;
+    s_list[wave][lane].idx = li;
+  }
+  __syncthreads();
+  TopEntry* parts = static_cast<TopEntry*>(a.part) + (int64_t)r * a.nch * a.F_max;
+  if (wave == 0 && F > 0) {
+    for (int w = 1; w < kFNT / kWave; ++w)
+      for (int e = 0; e < F; ++e) {
+        const TopEntry t = s_list[w][e];
+        if (t.idx != kNoIdx) wave_insert(lv, li, t.val, t.idx, F, lane);
+      }
+  }
+  if (wave == 0 && lane < a.F_max) {
+    TopEntry t;
+    t.val = lane < F ? lv : kNegInf;
+    t.idx = lane < F ? li : kNoIdx;
+    parts[(int64_t)ch * a.F_max + lane] = t;
+  }
+  if (!arrive_last<kFNT>(&a.cnt[r], (uint32_t)a.nch)) return;
+  if (wave == 0) {
+    float fv = kNegInf;
+    int32_t fi = kNoIdx;
+    for (int c = 0; c < a.nch; ++c)
+      for (int e = 0; e < F; ++e) {
+        const TopEntry t = parts[(int64_t)c * a.F_max + e];
+        if (t.idx != kNoIdx) wave_insert(fv, fi, t.val, t.idx, F, lane);
+      }
+    if (lane < a.F_max) {
+      const bool keep = lane < F && fi != kNoIdx;
+      a.out_ids[(int64_t)r * a.F_max + lane] = keep ? fi : -1;
+      if (a.out_vals) a.out_vals[(int64_t)r * a.F_max + lane] = keep ? fv : kNegInf;
+    }
+    if (lane == 0) __hip_atomic_store(&a.cnt[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+hipError_t launch_fanout(const FanoutParams& p, sv_dtype dt, const Plan& plan, hipStream_t s) {
+  if (dt == SV_BF16)
+    fanout_kernel<SV_BF16><<<dim3((unsigned)plan.grid1), dim3(kFNT), 0, s>>>(p);
+  else
+    fanout_kernel<SV_F32><<<dim3((unsigned)plan.grid1), dim3(kFNT), 0, s>>>(p);
+  return hipGetLastError();
+}
+
+}  // namespace sv

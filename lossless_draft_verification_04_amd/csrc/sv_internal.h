@@ -1,0 +1,110 @@
+// sv_internal.h -- host-side launch parameters shared by the library's
+// translation units (not part of the public C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "specverify.h"
+
+namespace sv {
+
+// Fixed workspace header: error word, then a counter region that every op
+// leaves zeroed on exit, then op-specific scratch.
+constexpr size_t kWsHeader = 256;
+constexpr size_t kWsCounters = 65536;  // uint32 counters
+constexpr size_t kWsFixed = kWsHeader + kWsCounters * sizeof(uint32_t);
+
+struct ChainParams {
+  const void* tgt;
+  const void* drf;
+  int64_t tgt_sb, drf_sb;  // row strides in bytes
+  const int32_t* tok;
+  int32_t B, K, gamma, V;
+  float c;  // log2(e) / T
+  uint64_t seed;
+  uint32_t round;
+  int32_t* out_k;
+  int32_t* out_n;
+  int32_t* out_tok;
+  int32_t* out_n_cand;
+  float* out_p;
+  float* out_q;
+  int32_t* err;
+  uint32_t* cnt1;
+  uint32_t* cnt2;
+  void* part1;
+  void* jobs;
+  void* part2;
+  int32_t nch1, nch2;
+  int64_t vpc1, vpc2, nvec;
+};
+
+struct GreedyParams {
+  const void* tgt;
+  int64_t tgt_sb;
+  const int32_t* tok;
+  int32_t B, gamma, V;
+  int32_t* out_n;
+  int32_t* out_tok;
+  int32_t* out_argmax;
+  int32_t* err;
+  uint32_t* cnt;
+  void* part;
+  int32_t nch;
+  int64_t vpc, nvec;
+};
+
+struct TreeParams {
+  const void* tgt;
+  const void* drf;
+  int64_t tgt_sb, drf_sb;
+  const int32_t* tok;
+  const int32_t* parent;
+  int32_t B, N, max_depth, V;
+  float c;
+  uint64_t seed;
+  uint32_t round;
+  int32_t* out_len;
+  int32_t* out_path;
+  int32_t* out_tok;
+  float* out_p;
+  float* out_q;
+  int32_t* err;
+  void* part;
+  int32_t nch;
+  int64_t vpc, nvec;
+};
+
+struct FanoutParams {
+  const void* logits;
+  int64_t sb;
+  int32_t R, V;
+  const int32_t* F;
+  int32_t F_max;
+  int32_t* out_ids;
+  float* out_vals;
+  int32_t* err;
+  uint32_t* cnt;
+  void* part;
+  int32_t nch;
+  int64_t vpc, nvec;
+};
+
+// Workspace plans (chunking + scratch sizes), computed identically by
+// sv_workspace_size and the entry points.
+struct Plan {
+  int32_t nch1 = 1, nch2 = 1;
+  int64_t vpc1 = 0, vpc2 = 0, nvec = 0;
+  size_t off_part1 = 0, off_jobs = 0, off_part2 = 0;
+  size_t bytes = 0;
+  int64_t grid1 = 0, grid2 = 0;
+};
+
+hipError_t launch_chain(const ChainParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
+hipError_t launch_greedy(const GreedyParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
+hipError_t launch_tree(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
+hipError_t launch_fanout(const FanoutParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
+hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s);
+
+}  // namespace sv
