@@ -14,7 +14,9 @@ namespace sv {
 
 namespace {
 
-constexpr int kBlockVecs = 256;  // smallest row part (vectors) worth a block
+constexpr int kBlockVecs = 1024;   // smallest row part (vectors): 4 in flight per thread of a 256-thread block
+constexpr int kMaxSampleParts = 512;  // parts of the draw pass per sequence (LDS staging in the sample kernel)
+constexpr int kDrawVecs = 256;        // smallest part of the draw pass (one vector per thread)
 
 int env_int(const char* name, int dflt) {
   const char* v = std::getenv(name);
@@ -23,15 +25,17 @@ int env_int(const char* name, int dflt) {
   return x > 0 ? x : dflt;
 }
 
-// Blocks the streaming passes aim for (the chip has 256 CUs; a few blocks
-// per CU keep enough loads in flight and even out the tail).  Overridable
-// for tuning sweeps with SV_STATS_BLOCKS / SV_SAMPLE_BLOCKS.
+// Blocks the streaming passes aim for (the chip has 256 CUs; four blocks of
+// 256 threads per CU with four 16-byte loads in flight per thread keep the
+// HBM busy; fewer, longer parts also mean fewer parts to merge).  The draw
+// pass uses more, smaller parts so its final in-part search is short.
+// Overridable for tuning sweeps with SV_STATS_BLOCKS / SV_SAMPLE_BLOCKS.
 int stats_blocks() {
-  static const int v = env_int("SV_STATS_BLOCKS", 2048);
+  static const int v = env_int("SV_STATS_BLOCKS", 1024);
   return v;
 }
 int sample_blocks() {
-  static const int v = env_int("SV_SAMPLE_BLOCKS", 1024);
+  static const int v = env_int("SV_SAMPLE_BLOCKS", 2048);
   return v;
 }
 
@@ -40,10 +44,11 @@ int elem_bytes(sv_dtype dt) { return dt == SV_BF16 ? 2 : 4; }
 
 size_t align_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
-// Split rows of nvec vectors into parts so that rows * parts ~ target.
-void split(int64_t rows, int64_t nvec, int target, int32_t* nch, int64_t* vpc) {
+// Split rows of nvec vectors into parts of at least min_vecs vectors so that
+// rows * parts ~ target.
+void split(int64_t rows, int64_t nvec, int target, int32_t* nch, int64_t* vpc, int64_t min_vecs = kBlockVecs) {
   int64_t n = rows > 0 ? (target + rows - 1) / rows : 1;
-  const int64_t cap = nvec / kBlockVecs > 1 ? nvec / kBlockVecs : 1;
+  const int64_t cap = nvec / min_vecs > 1 ? nvec / min_vecs : 1;
   if (n > cap) n = cap;
   if (n < 1) n = 1;
   int64_t per = (nvec + n - 1) / n;
@@ -71,7 +76,12 @@ sv_status plan_chain(sv_dtype dt, int32_t B, int32_t K, int32_t gamma, int32_t V
   pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
   const int64_t rows = (int64_t)B * (K + 1) * gamma;
   split(rows, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
-  split(B, pl->nvec, sample_blocks(), &pl->nch2, &pl->vpc2);
+  // the draw pass re-reads one part in its last block: keep parts small
+  split(B, pl->nvec, sample_blocks(), &pl->nch2, &pl->vpc2, kDrawVecs);
+  if (pl->nch2 > kMaxSampleParts) {
+    pl->vpc2 = (pl->nvec + kMaxSampleParts - 1) / kMaxSampleParts;
+    pl->nch2 = (int32_t)((pl->nvec + pl->vpc2 - 1) / pl->vpc2);
+  }
   pl->grid1 = rows * pl->nch1;
   pl->grid2 = (int64_t)B * pl->nch2;
   if (pl->grid1 > INT32_MAX || pl->grid2 > INT32_MAX) return SV_EUNSUPPORTED;
@@ -103,24 +113,29 @@ sv_status plan_greedy(sv_dtype dt, int32_t B, int32_t gamma, int32_t V, Plan* pl
   return SV_OK;
 }
 
-constexpr int kWalkThreads = 512;
-constexpr int kWalkMaxTiles = 8192;
+constexpr int kWalkSlices = 64;  // slices of a walk pass per sequence
+constexpr int kWalkBlocks = 256;  // walk blocks per call (one per CU when co-resident)
 
 sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, Plan* pl) {
   if (bad_dtype(dt)) return SV_EDTYPE;
   if (B < 0 || N < 1 || V < 1) return SV_EINVAL;
   if (B > SV_MAX_SEQ || N > SV_MAX_N || V > SV_MAX_V) return SV_EUNSUPPORTED;
   pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
-  if ((pl->nvec + kWalkThreads - 1) / kWalkThreads > kWalkMaxTiles) return SV_EUNSUPPORTED;
   const int64_t rows = (int64_t)B * N * 2;
   // only nodes with children are streamed; size the parts for about half
   split(rows / 2 > 0 ? rows / 2 : 1, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
   pl->grid1 = rows * pl->nch1;
-  pl->grid2 = B;
-  if (pl->grid1 > INT32_MAX) return SV_EUNSUPPORTED;
+  // walk blocks per sequence: a power of two dividing the slice count
+  int G = 1;
+  while (G * 2 <= kWalkSlices && (int64_t)B * G * 2 <= kWalkBlocks) G *= 2;
+  pl->nch2 = G;
+  pl->grid2 = (int64_t)B * G;
+  if (pl->grid1 > INT32_MAX || pl->grid2 > INT32_MAX) return SV_EUNSUPPORTED;
   size_t off = kWsFixed;
   pl->off_part1 = off;
   off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
+  pl->off_part2 = off;  // walk exchange slots
+  off = align_up(off + (size_t)B * 2 * kWalkSlices * sizeof(Partial), 256);
   pl->bytes = off;
   return SV_OK;
 }
@@ -349,8 +364,12 @@ sv_status sv_verify_tree(const void* tgt, const void* drf, sv_dtype dt, int64_t 
   p.out_p = out_p;
   p.out_q = out_q;
   p.err = reinterpret_cast<int32_t*>(w);
+  p.cnt1 = reinterpret_cast<uint32_t*>(w + kWsHeader);
+  p.cnt2 = p.cnt1 + kWsCounters / 2;
   p.part = w + pl.off_part1;
+  p.xch = w + pl.off_part2;
   p.nch = pl.nch1;
+  p.G = pl.nch2;
   p.vpc = pl.vpc1;
   p.nvec = pl.nvec;
   return launch_tree(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;

@@ -24,6 +24,7 @@ namespace sv {
 
 constexpr int kNT = 256;
 constexpr int kU = 4;
+constexpr int kMaxSampleParts = 512;  // parts of the draw pass per sequence (host plan caps nch2)
 
 struct Job {
   int64_t rowP;  // target row of the draw
@@ -33,31 +34,98 @@ struct Job {
   double u;
 };
 
+// Parts of one sequence staged in LDS by the deciding block (all loads in
+// flight together instead of one dependent load per part).
+constexpr int kStage = 1024;
+
+struct StagedParts {
+  float m[kStage];
+  double s[kStage];
+};
+
+// Row statistic from parts [first, first + n) of the staged set (or straight
+// from global memory when the sequence has more parts than fit).
+__device__ __forceinline__ RowStat merge_staged(const StagedParts& st, bool staged, const Partial* gparts, int first,
+                                                int n, float c) {
+  if (!staged) return merge_parts(gparts + first, n, c);
+  float M = kNegInf;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, st.m[first + i]);
+  RowStat r;
+  r.pad = 0.f;
+  if (M == kNegInf) {
+    r.cm = 0.f;
+    r.S = 0.0;
+    return r;
+  }
+  r.cm = c * M;
+  double S = 0.0;
+  for (int i = 0; i < n; ++i)
+    if (st.m[first + i] != kNegInf) S += st.s[first + i] * exp2((double)(c * st.m[first + i]) - (double)r.cm);
+  r.S = S;
+  return r;
+}
+
 template <int DT>
 __device__ void chain_decide(const ChainParams& a, int b) {
+  __shared__ StagedParts st;
   __shared__ RowStat sQ[SV_MAX_GAMMA];
   __shared__ int sN[SV_MAX_K];
   const int rows = (a.K + 1) * a.gamma;
   const int Kg = a.K * a.gamma;
-  const Partial* pb = static_cast<const Partial*>(a.part1) + (int64_t)b * rows * a.nch1;
-  for (int j = threadIdx.x; j < a.gamma; j += kNT) sQ[j] = merge_parts(pb + (int64_t)(Kg + j) * a.nch1, a.nch1, a.c);
-  __syncthreads();
+  const int nparts = rows * a.nch1;
+  const bool staged = nparts <= kStage;
+  const Partial* pb = static_cast<const Partial*>(a.part1) + (int64_t)b * nparts;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
+
+  // Gathers of the first candidates' logits do not depend on any statistic:
+  // issue them before waiting on the parts.
+  float zp0 = 0.f, zq0 = 0.f;
+  int32_t x0 = -1;
+  if (wave < a.K && lane < a.gamma) {
+    const int64_t o = ((int64_t)b * a.K + wave) * a.gamma + lane;
+    x0 = a.tok[o];
+    if (x0 >= 0 && x0 < a.V) {
+      zp0 = load_elem<DT>(row_ptr(a.tgt, ((int64_t)b * a.K + wave) * (a.gamma + 1) + lane, a.tgt_sb), x0);
+      zq0 = load_elem<DT>(row_ptr(a.drf, (int64_t)b * a.gamma + lane, a.drf_sb), x0);
+    }
+  }
+  if (staged) {
+    for (int i = threadIdx.x; i < nparts; i += kNT) {
+      const Partial pi = get_partial(pb + i);
+      st.m[i] = pi.m;
+      st.s[i] = pi.s;
+    }
+  }
+  __syncthreads();
+  for (int j = threadIdx.x; j < a.gamma; j += kNT)
+    sQ[j] = merge_staged(st, staged, pb, (Kg + j) * a.nch1, a.nch1, a.c);
+  __syncthreads();
   for (int k = wave; k < a.K; k += kNT / kWave) {
     bool acc = false;
     if (lane < a.gamma) {
       const int j = lane;
-      const RowStat sp = merge_parts(pb + (int64_t)(k * a.gamma + j) * a.nch1, a.nch1, a.c);
+      const RowStat sp = merge_staged(st, staged, pb, (k * a.gamma + j) * a.nch1, a.nch1, a.c);
       const RowStat sq = sQ[j];
       const int64_t o = ((int64_t)b * a.K + k) * a.gamma + j;
-      const int32_t x = a.tok[o];
+      int32_t x;
+      float zp, zq;
+      if (k == wave) {
+        x = x0;
+        zp = zp0;
+        zq = zq0;
+      } else {
+        x = a.tok[o];
+        zp = zq = 0.f;
+        if (x >= 0 && x < a.V) {
+          zp = load_elem<DT>(row_ptr(a.tgt, ((int64_t)b * a.K + k) * (a.gamma + 1) + j, a.tgt_sb), x);
+          zq = load_elem<DT>(row_ptr(a.drf, (int64_t)b * a.gamma + j, a.drf_sb), x);
+        }
+      }
       double p = 0.0, q = 0.0;
       if (x >= 0 && x < a.V) {
-        const void* rp = row_ptr(a.tgt, ((int64_t)b * a.K + k) * (a.gamma + 1) + j, a.tgt_sb);
-        const void* rq = row_ptr(a.drf, (int64_t)b * a.gamma + j, a.drf_sb);
-        p = prob_of(load_elem<DT>(rp, x), a.c, sp);
-        q = prob_of(load_elem<DT>(rq, x), a.c, sq);
+        p = prob_of(zp, a.c, sp);
+        q = prob_of(zq, a.c, sq);
       } else {
         set_error(a.err, SV_DERR_TOKEN);
       }
@@ -86,7 +154,7 @@ __device__ void chain_decide(const ChainParams& a, int b) {
     Job jb;
     jb.rowP = ((int64_t)b * a.K + best) * (a.gamma + 1) + n;
     if (n < a.gamma) {
-      const RowStat sp = merge_parts(pb + (int64_t)(best * a.gamma + n) * a.nch1, a.nch1, a.c);
+      const RowStat sp = merge_staged(st, staged, pb, (best * a.gamma + n) * a.nch1, a.nch1, a.c);
       jb.rowQ = (int64_t)b * a.gamma + n;
       jb.cmP = sp.cm;
       jb.SP = sp.S;
@@ -123,7 +191,7 @@ __global__ __launch_bounds__(kNT) void chain_stats_kernel(ChainParams a) {
   const int64_t v0 = (int64_t)ch * a.vpc1;
   const int64_t v1 = v0 + a.vpc1 < a.nvec ? v0 + a.vpc1 : a.nvec;
   const Partial part = range_stats<DT, kNT, kU>(row, a.V, v0, v1, a.c);
-  if (threadIdx.x == 0) static_cast<Partial*>(a.part1)[(int64_t)b * per_seq + (int64_t)lr * a.nch1 + ch] = part;
+  if (threadIdx.x == 0) put_partial(static_cast<Partial*>(a.part1) + (int64_t)b * per_seq + (int64_t)lr * a.nch1 + ch, part);
   if (!arrive_last<kNT>(&a.cnt1[b], (uint32_t)per_seq)) return;
   chain_decide<DT>(a, b);
 }
@@ -168,27 +236,38 @@ __global__ __launch_bounds__(kNT) void chain_sample_kernel(ChainParams a) {
     part = range_stats<DT, kNT, kU>(row_ptr(a.tgt, jb.rowP, a.tgt_sb), a.V, v0, v1, a.c);
   }
   Partial* parts = static_cast<Partial*>(a.part2) + (int64_t)b * a.nch2;
-  if (threadIdx.x == 0) parts[ch] = part;
+  if (threadIdx.x == 0) put_partial(parts + ch, part);
   if (!arrive_last<kNT>(&a.cnt2[b], (uint32_t)a.nch2)) return;
 
-  // Last block of sequence b: locate the part holding u * S, search in it.
+  // Last block of sequence b: stage the parts (weights of the draw per part,
+  // in part order) in LDS, locate the part holding u * S, search in it.
+  __shared__ double s_w[kMaxSampleParts];
+  __shared__ float s_pm[kMaxSampleParts];
   __shared__ double s_target;
   __shared__ int64_t s_v0, s_v1;
   __shared__ float s_cm;
   __shared__ int s_mode;  // 0 residual, 1 plain (bonus), 2 plain over P with the row statistic
+  for (int i = threadIdx.x; i < a.nch2; i += kNT) {
+    const Partial pi = get_partial(parts + i);
+    s_pm[i] = pi.m;
+    s_w[i] = pi.s;
+  }
+  __syncthreads();
   if (threadIdx.x == 0) {
     double total = 0.0;
     float cm = 0.f;
     int mode = resid ? 0 : 1;
     if (resid) {
-      for (int i = 0; i < a.nch2; ++i) total += parts[i].s;
+      for (int i = 0; i < a.nch2; ++i) total += s_w[i];
       if (!(total > 0.0)) mode = 2;  // residual mass rounded to 0: draw from p_{n+1}
     } else {
       float M = kNegInf;
-      for (int i = 0; i < a.nch2; ++i) M = fmaxf(M, parts[i].m);
+      for (int i = 0; i < a.nch2; ++i) M = fmaxf(M, s_pm[i]);
       cm = a.c * M;
-      for (int i = 0; i < a.nch2; ++i)
-        if (parts[i].m != kNegInf) total += parts[i].s * exp2((double)(a.c * parts[i].m) - (double)cm);
+      for (int i = 0; i < a.nch2; ++i) {
+        s_w[i] = s_pm[i] == kNegInf ? 0.0 : s_w[i] * exp2((double)(a.c * s_pm[i]) - (double)cm);
+        total += s_w[i];
+      }
     }
     if (mode == 2) {
       s_mode = 2;
@@ -202,10 +281,7 @@ __global__ __launch_bounds__(kNT) void chain_sample_kernel(ChainParams a) {
       int pick = -1, last_pos = -1;
       double cum_last = 0.0;
       for (int i = 0; i < a.nch2; ++i) {
-        const double w = resid ? parts[i].s
-                               : (parts[i].m == kNegInf
-                                      ? 0.0
-                                      : parts[i].s * exp2((double)(a.c * parts[i].m) - (double)cm));
+        const double w = s_w[i];
         if (w > 0.0) {
           last_pos = i;
           cum_last = cum;

@@ -311,26 +311,6 @@ __device__ Partial range_stats(const void* row, int V, int64_t v0, int64_t v1, f
   return p;
 }
 
-// Merge part statistics (in part order) into the row statistic.
-__device__ __forceinline__ RowStat merge_parts(const Partial* parts, int n, float c) {
-  float M = kNegInf;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, parts[i].m);
-  RowStat r;
-  r.pad = 0.f;
-  if (M == kNegInf) {
-    r.cm = 0.f;
-    r.S = 0.0;
-    return r;
-  }
-  r.cm = c * M;
-  double S = 0.0;
-  for (int i = 0; i < n; ++i) {
-    if (parts[i].m == kNegInf) continue;
-    S += parts[i].s * exp2((double)(c * parts[i].m) - (double)r.cm);
-  }
-  r.S = S;
-  return r;
-}
 
 // p(v) of one gathered logit under a row statistic (0 for an empty row).
 __device__ __forceinline__ double prob_of(float z, float c, const RowStat& st) {
@@ -387,88 +367,169 @@ __device__ __forceinline__ void draw_weights(const DrawSpec& sp, int V, int64_t 
   draw_weights_from<DT>(sp, V, vi, dp, dq, w);
 }
 
-// Sum of draw weights over vectors [v0, v1) by a block (double accumulation).
+// Sum of draw weights over vectors [v0, v1) by a block (double accumulation),
+// kDrawU vectors per row in flight per thread (clamped addresses, masked
+// contributions, so the loads are unconditional and overlap).
+constexpr int kDrawU = 4;
+
 template <int DT, int NT>
 __device__ double range_weight_sum(const DrawSpec& sp, int V, int64_t v0, int64_t v1) {
   constexpr int E = Fmt<DT>::kPerVec;
   double acc = 0.0;
-  for (int64_t v = v0 + threadIdx.x; v < v1; v += NT) {
-    float w[E];
-    draw_weights<DT>(sp, V, v, w);
-    double own = 0.0;
+  if (v1 <= v0) return block_sum<NT>(0.0);
+  for (int64_t base = v0 + threadIdx.x; base < v1; base += (int64_t)kDrawU * NT) {
+    u32x4 dp[kDrawU], dq[kDrawU];
 #pragma unroll
-    for (int e = 0; e < E; ++e) own += (double)w[e];
-    acc += own;
+    for (int u = 0; u < kDrawU; ++u) {
+      const int64_t v = base + (int64_t)u * NT;
+      const int64_t vc = v < v1 ? v : v1 - 1;
+      dp[u] = load_vec(sp.rowP, vc);
+      if (sp.rowQ) dq[u] = load_vec(sp.rowQ, vc);
+    }
+#pragma unroll
+    for (int u = 0; u < kDrawU; ++u) {
+      const int64_t v = base + (int64_t)u * NT;
+      if (v < v1) {
+        float w[E];
+        draw_weights_from<DT>(sp, V, v, dp[u], dq[u], w);
+        double own = 0.0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) own += (double)w[e];
+        acc += own;
+      }
+    }
   }
   return block_sum<NT>(acc);
 }
 
 // Inverse-CDF search over vectors [v0, v1) in index order: the first element
-// whose running weight exceeds `target`.  Tiles of NT vectors; in each tile
-// the block scans per-thread sums, and the thread whose interval holds the
-// target walks its own elements.  If rounding leaves the target beyond the
-// range's weight, the last positive element is returned.  All threads return
-// the same index.
+// whose running weight exceeds `target`.  Tiles of NT vectors, kDrawU tiles'
+// loads in flight at once; in each tile the block scans per-thread sums, and
+// the thread whose interval holds the target walks its own elements.  If
+// rounding leaves the target beyond the range's weight, the last positive
+// element is returned.  All threads return the same index.
 template <int DT, int NT>
 __device__ int64_t block_search(const DrawSpec& sp, int V, int64_t v0, int64_t v1, double target) {
   constexpr int E = Fmt<DT>::kPerVec;
   double cum = 0.0;
   int64_t last_pos = -1;
-  for (int64_t base = v0; base < v1; base += NT) {
-    const int64_t v = base + threadIdx.x;
-    float w[E];
+  for (int64_t base0 = v0; base0 < v1; base0 += (int64_t)kDrawU * NT) {
+    u32x4 dp[kDrawU], dq[kDrawU];
 #pragma unroll
-    for (int e = 0; e < E; ++e) w[e] = 0.f;
-    if (v < v1) draw_weights<DT>(sp, V, v, w);
-    double own = 0.0;
-    int64_t my_last = -1;
-#pragma unroll
-    for (int e = 0; e < E; ++e) {
-      own += (double)w[e];
-      if (w[e] > 0.f) my_last = v * E + e;
+    for (int u = 0; u < kDrawU; ++u) {
+      const int64_t v = base0 + (int64_t)u * NT + threadIdx.x;
+      const int64_t vc = v < v1 ? v : v1 - 1;
+      dp[u] = load_vec(sp.rowP, vc);
+      if (sp.rowQ) dq[u] = load_vec(sp.rowQ, vc);
     }
-    double excl;
-    const double total = block_exclusive_scan<NT>(own, &excl);
-    const int64_t tile_last = block_max_i64<NT>(my_last);
-    if (tile_last >= 0) last_pos = tile_last;
-    if (cum + total > target) {
-      const double t_local = target - cum - excl;
-      int64_t found = INT64_MAX;
-      if (own > 0.0 && t_local >= 0.0 && t_local < own) {
-        double run = 0.0;
+    for (int u = 0; u < kDrawU; ++u) {
+      const int64_t base = base0 + (int64_t)u * NT;
+      if (base >= v1) break;  // block-uniform
+      const int64_t v = base + threadIdx.x;
+      float w[E];
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          run += (double)w[e];
-          if (found == INT64_MAX && run > t_local) found = v * E + e;
-        }
-        if (found == INT64_MAX) found = my_last;
+      for (int e = 0; e < E; ++e) w[e] = 0.f;
+      if (v < v1) draw_weights_from<DT>(sp, V, v, dp[u], dq[u], w);
+      double own = 0.0;
+      int64_t my_last = -1;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        own += (double)w[e];
+        if (w[e] > 0.f) my_last = v * E + e;
       }
-      const int64_t r = block_min_i64<NT>(found);
-      return r != INT64_MAX ? r : tile_last;
+      double excl;
+      const double total = block_exclusive_scan<NT>(own, &excl);
+      const int64_t tile_last = block_max_i64<NT>(my_last);
+      if (tile_last >= 0) last_pos = tile_last;
+      if (cum + total > target) {
+        const double t_local = target - cum - excl;
+        int64_t found = INT64_MAX;
+        if (own > 0.0 && t_local >= 0.0 && t_local < own) {
+          double run = 0.0;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            run += (double)w[e];
+            if (found == INT64_MAX && run > t_local) found = v * E + e;
+          }
+          if (found == INT64_MAX) found = my_last;
+        }
+        const int64_t r = block_min_i64<NT>(found);
+        return r != INT64_MAX ? r : tile_last;
+      }
+      cum += total;
     }
-    cum += total;
   }
   return last_pos;
 }
 
-// Release this block's global writes / acquire other blocks' (agent scope,
-// so the per-XCD L2 caches are written back / invalidated as needed).
-__device__ __forceinline__ void fence_acq_rel_agent() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "agent"); }
+// ---------------------------------------------------------------------------
+// Hand-off between the blocks of one launch.  Parts written by one block and
+// merged by another travel through device-scope (agent) atomic stores and
+// loads only: on gfx950 those are performed at the device-coherent level
+// (they write through / re-fetch past the per-XCD L2), so no agent-scope
+// fence - which would write back or invalidate a whole L2 per block - is
+// needed.  Each block waits for its own stores to complete before counting
+// its arrival; the last block to arrive reads every part.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void st_dev(uint64_t* p, uint64_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint64_t ld_dev(const uint64_t* p) {
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
-// Count one arrival on `counter`; true in every thread of the block that
-// arrived last (of `total`).  That block resets the counter to 0 itself.
+__device__ __forceinline__ void put_partial(Partial* dst, const Partial& v) {
+  uint64_t* d = reinterpret_cast<uint64_t*>(dst);
+  st_dev(d, (uint64_t)__float_as_uint(v.m));
+  st_dev(d + 1, (uint64_t)__double_as_longlong(v.s));
+}
+__device__ __forceinline__ Partial get_partial(const Partial* src) {
+  const uint64_t* d = reinterpret_cast<const uint64_t*>(src);
+  Partial v;
+  v.m = __uint_as_float((uint32_t)ld_dev(d));
+  v.pad = 0.f;
+  v.s = __longlong_as_double((long long)ld_dev(d + 1));
+  return v;
+}
+
+// Count one arrival on `counter` once this block's hand-off stores have
+// completed; true in every thread of the block that arrived last (of
+// `total`).  That block resets the counter to 0 itself.
 template <int NT>
 __device__ bool arrive_last(uint32_t* counter, uint32_t total) {
   __shared__ int last;
-  fence_acq_rel_agent();
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);  // this wave's stores are complete (device-visible)
   __syncthreads();
   if (threadIdx.x == 0) {
-    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t old = __hip_atomic_fetch_add(counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     last = (old == total - 1);
   }
   __syncthreads();
-  if (last) fence_acq_rel_agent();
   return last != 0;
+}
+
+// Merge the parts of one row (in part order) into the row statistic; parts
+// are read with device-scope loads (written by other blocks of the launch).
+__device__ inline RowStat merge_parts(const Partial* parts, int n, float c) {
+  float M = kNegInf;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, get_partial(parts + i).m);
+  RowStat r;
+  r.pad = 0.f;
+  if (M == kNegInf) {
+    r.cm = 0.f;
+    r.S = 0.0;
+    return r;
+  }
+  r.cm = c * M;
+  double S = 0.0;
+  for (int i = 0; i < n; ++i) {
+    const Partial pi = get_partial(parts + i);
+    if (pi.m == kNegInf) continue;
+    S += pi.s * exp2((double)(c * pi.m) - (double)r.cm);
+  }
+  r.S = S;
+  return r;
 }
 
 __device__ __forceinline__ void set_error(int32_t* err, int32_t bit) {

@@ -26,6 +26,17 @@ struct TopEntry {
 
 constexpr int32_t kNoIdx = 0x7fffffff;
 
+__device__ __forceinline__ void put_entry(TopEntry* dst, float val, int32_t idx) {
+  st_dev(reinterpret_cast<uint64_t*>(dst), (uint64_t)__float_as_uint(val) | ((uint64_t)(uint32_t)idx << 32));
+}
+__device__ __forceinline__ TopEntry get_entry(const TopEntry* src) {
+  const uint64_t w = ld_dev(reinterpret_cast<const uint64_t*>(src));
+  TopEntry t;
+  t.val = __uint_as_float((uint32_t)w);
+  t.idx = (int32_t)(uint32_t)(w >> 32);
+  return t;
+}
+
 __device__ __forceinline__ bool top_better(float va, int32_t ia, float vb, int32_t ib) {
   return va > vb || (va == vb && ia < ib);
 }
@@ -70,37 +81,49 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
   const int64_t v0 = (int64_t)ch * a.vpc;
   const int64_t v1 = v0 + a.vpc < a.nvec ? v0 + a.vpc : a.nvec;
   if (F > 0) {
-    // each wave walks its own 64-vector windows in increasing order
-    const int nw = kFNT / kWave;
-    for (int64_t base = v0 + (int64_t)wave * kWave; base < v1; base += (int64_t)nw * kWave) {
-      const int64_t v = base + lane;
-      float x[E];
-      float vm = kNegInf;
-      bool valid = v < v1;
-      if (valid) {
-        unpack<DT>(load_vec(row, v), x);
-        if ((v + 1) * E > a.V) {
+    // each wave walks its own 64-vector windows in increasing order, with
+    // the loads of kWin windows in flight at once
+    constexpr int kWin = 4;
+    const int64_t stride = (int64_t)(kFNT / kWave) * kWave;
+    for (int64_t base0 = v0 + (int64_t)wave * kWave; base0 < v1; base0 += stride * kWin) {
+      u32x4 d[kWin];
 #pragma unroll
-          for (int e = 0; e < E; ++e)
-            if (v * E + e >= a.V) x[e] = kNegInf;
-        }
-        vm = x[0];
-#pragma unroll
-        for (int e = 1; e < E; ++e) vm = fmaxf(vm, x[e]);
+      for (int u = 0; u < kWin; ++u) {
+        const int64_t v = base0 + u * stride + lane;
+        d[u] = load_vec(row, v < v1 ? v : v1 - 1);  // unconditional (clamped) so the loads overlap
       }
-      const bool cand = valid && (count < F || vm > thr);
-      uint64_t cm = __ballot(cand);
-      while (cm) {
-        const int src = __builtin_ctzll(cm);
-        cm &= cm - 1;
 #pragma unroll
-        for (int e = 0; e < E; ++e) {
-          const float xe = __shfl(x[e], src, kWave);
-          const int64_t gi = (base + src) * E + e;
-          if (gi < a.V && (count < F || xe > thr)) {
-            wave_insert(lv, li, xe, (int32_t)gi, F, lane);
-            if (count < F) ++count;
-            thr = __shfl(lv, F - 1, kWave);
+      for (int u = 0; u < kWin; ++u) {
+        const int64_t base = base0 + u * stride;
+        const int64_t v = base + lane;
+        float x[E];
+        float vm = kNegInf;
+        const bool valid = v < v1;
+        if (valid) {
+          unpack<DT>(d[u], x);
+          if ((v + 1) * E > a.V) {
+#pragma unroll
+            for (int e = 0; e < E; ++e)
+              if (v * E + e >= a.V) x[e] = kNegInf;
+          }
+          vm = x[0];
+#pragma unroll
+          for (int e = 1; e < E; ++e) vm = fmaxf(vm, x[e]);
+        }
+        const bool cand = valid && (count < F || vm > thr);
+        uint64_t cm = __ballot(cand);
+        while (cm) {
+          const int src = __builtin_ctzll(cm);
+          cm &= cm - 1;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const float xe = __shfl(x[e], src, kWave);
+            const int64_t gi = (base + src) * E + e;
+            if (gi < a.V && (count < F || xe > thr)) {
+              wave_insert(lv, li, xe, (int32_t)gi, F, lane);
+              if (count < F) ++count;
+              thr = __shfl(lv, F - 1, kWave);
+            }
           }
         }
       }
@@ -122,19 +145,15 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
         if (t.idx != kNoIdx) wave_insert(lv, li, t.val, t.idx, F, lane);
       }
   }
-  if (wave == 0 && lane < a.F_max) {
-    TopEntry t;
-    t.val = lane < F ? lv : kNegInf;
-    t.idx = lane < F ? li : kNoIdx;
-    parts[(int64_t)ch * a.F_max + lane] = t;
-  }
+  if (wave == 0 && lane < a.F_max) put_entry(parts + (int64_t)ch * a.F_max + lane, lane < F ? lv : kNegInf,
+                                             lane < F ? li : kNoIdx);
   if (!arrive_last<kFNT>(&a.cnt[r], (uint32_t)a.nch)) return;
   if (wave == 0) {
     float fv = kNegInf;
     int32_t fi = kNoIdx;
     for (int c = 0; c < a.nch; ++c)
       for (int e = 0; e < F; ++e) {
-        const TopEntry t = parts[(int64_t)c * a.F_max + e];
+        const TopEntry t = get_entry(parts + (int64_t)c * a.F_max + e);
         if (t.idx != kNoIdx) wave_insert(fv, fi, t.val, t.idx, F, lane);
       }
     if (lane < a.F_max) {

@@ -22,6 +22,17 @@ struct ArgPart {
   int32_t idx;
 };
 
+__device__ __forceinline__ void put_arg(ArgPart* dst, const ArgPart& v) {
+  st_dev(reinterpret_cast<uint64_t*>(dst), (uint64_t)__float_as_uint(v.val) | ((uint64_t)(uint32_t)v.idx << 32));
+}
+__device__ __forceinline__ ArgPart get_arg(const ArgPart* src) {
+  const uint64_t w = ld_dev(reinterpret_cast<const uint64_t*>(src));
+  ArgPart v;
+  v.val = __uint_as_float((uint32_t)w);
+  v.idx = (int32_t)(uint32_t)(w >> 32);
+  return v;
+}
+
 // (value desc, index asc)
 __device__ __forceinline__ bool arg_better(float va, int64_t ia, float vb, int64_t ib) {
   return va > vb || (va == vb && ia < ib);
@@ -135,19 +146,22 @@ __global__ __launch_bounds__(kGNT) void greedy_kernel(GreedyParams a) {
   const int64_t v1 = v0 + a.vpc < a.nvec ? v0 + a.vpc : a.nvec;
   const ArgPart part = range_argmax<DT, kGNT, kGU>(row, a.V, v0, v1);
   ArgPart* parts = static_cast<ArgPart*>(a.part) + (int64_t)b * per_seq;
-  if (threadIdx.x == 0) parts[(int64_t)j * a.nch + ch] = part;
+  if (threadIdx.x == 0) put_arg(parts + (int64_t)j * a.nch + ch, part);
   if (!arrive_last<kGNT>(&a.cnt[b], (uint32_t)per_seq)) return;
 
   __shared__ int32_t g[SV_MAX_GAMMA + 1];
   for (int jj = threadIdx.x; jj < rows; jj += kGNT) {
     const ArgPart* pr = parts + (int64_t)jj * a.nch;
-    float bv = pr[0].val;
-    int32_t bi = pr[0].idx;
-    for (int c = 1; c < a.nch; ++c)
-      if (pr[c].val > bv) {  // parts are in index order: strict > keeps the lowest index
-        bv = pr[c].val;
-        bi = pr[c].idx;
+    const ArgPart p0 = get_arg(pr);
+    float bv = p0.val;
+    int32_t bi = p0.idx;
+    for (int c = 1; c < a.nch; ++c) {
+      const ArgPart pc = get_arg(pr + c);
+      if (pc.val > bv) {  // parts are in index order: strict > keeps the lowest index
+        bv = pc.val;
+        bi = pc.idx;
       }
+    }
     g[jj] = bi;
     if (a.out_argmax) a.out_argmax[(int64_t)b * rows + jj] = bi;
   }

@@ -13,10 +13,11 @@
 // Two launches per call:
 //  1. stats: a block per (node, target|draft, row part) of every node that
 //     has children (leaf rows are skipped), streaming each row once.
-//  2. walk: one 512-thread block per sequence merges the parts of the node
-//     it stands on, decides children in order, and makes one pass over the
-//     node's row pair per rejection; the pass keeps per-tile weight sums in
-//     LDS so the final draw only re-reads one tile.
+//  2. walk: G blocks per sequence (cooperative launch) replay the walk in
+//     lockstep: merge the parts of the node they stand on, decide its
+//     children in order, and split one pass over the node's row pair per
+//     rejection into slices; the slice sums are exchanged, so the final draw
+//     only re-reads one slice.
 #include "sv_device.hpp"
 #include "sv_internal.h"
 
@@ -24,9 +25,6 @@ namespace sv {
 
 constexpr int kTNT = 256;
 constexpr int kTU = 4;
-constexpr int kWNT = 512;        // walk block
-constexpr int kMaxTiles = 8192;  // LDS tile sums of one row pass (tiles of kWNT vectors)
-constexpr int kGroup = 8;        // tiles per pass step (vectors in flight per thread)
 
 template <int DT>
 __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
@@ -46,156 +44,212 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
   const int64_t v0 = (int64_t)ch * a.vpc;
   const int64_t v1 = v0 + a.vpc < a.nvec ? v0 + a.vpc : a.nvec;
   const Partial part = range_stats<DT, kTNT, kTU>(row, a.V, v0, v1, a.c);
-  if (threadIdx.x == 0) static_cast<Partial*>(a.part)[(((int64_t)b * a.N + u) * 2 + which) * a.nch + ch] = part;
+  if (threadIdx.x == 0) put_partial(static_cast<Partial*>(a.part) + (((int64_t)b * a.N + u) * 2 + which) * a.nch + ch, part);
 }
 
-// Per-tile sums of the draw weights over a whole row.  A tile is kWNT
-// vectors (one per thread); kGroup tiles' loads are issued before any of
-// them is reduced, so each thread keeps kGroup (x2 for a residual) 16-byte
-// loads in flight.  Returns the total.
-template <int DT>
-__device__ double tile_pass(const DrawSpec& sp, int V, int64_t nvec, int ntiles, double* s_tiles) {
-  constexpr int E = Fmt<DT>::kPerVec;
-  __shared__ double red[kGroup][kWNT / kWave];
-  const int lane = threadIdx.x & (kWave - 1);
-  const int wave = threadIdx.x / kWave;
-  double total = 0.0;
-  for (int t0 = 0; t0 < ntiles; t0 += kGroup) {
-    u32x4 dp[kGroup], dq[kGroup];
-#pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      const int64_t v = (int64_t)(t0 + g) * kWNT + threadIdx.x;
-      if (v < nvec) {
-        dp[g] = load_vec(sp.rowP, v);
-        if (sp.rowQ) dq[g] = load_vec(sp.rowQ, v);
+// ---------------------------------------------------------------------------
+// Walk.  A sequence's row passes are split into kSlices slices, handled by
+// the G blocks of that sequence (G = 1 .. kSlices, co-resident by a
+// cooperative launch when G > 1).  After each pass the blocks exchange their
+// slice sums through device-scope stores and meet at a per-sequence barrier;
+// every block then holds the same slice sums and, since every decision is a
+// deterministic function of global data and of those sums (same order, same
+// arithmetic), every block replays the identical walk.  Only block 0 writes
+// the per-child outputs; only the owner of the slice holding the draw
+// searches it.
+// ---------------------------------------------------------------------------
+constexpr int kWNT = 256;       // walk block
+constexpr int kSlices = 64;     // slices of a row pass per sequence
+constexpr uint32_t kSpinLimit = 1u << 22;
+
+struct WalkCtx {
+  const TreeParams* a;
+  int b, g, G;
+  int64_t spv;            // vectors per slice
+  uint32_t* arrive;       // per-sequence arrival counter (monotone within a call)
+  Partial* xch;           // [2][kSlices] exchange slots of this sequence
+  int pass;               // exchanges so far
+};
+
+// Exchange this block's slice parts; afterwards s_m / s_s hold all kSlices
+// parts (slice order) in every block of the sequence.
+__device__ void exchange(WalkCtx& w, const Partial* mine, float* s_m, double* s_s) {
+  const int per = kSlices / w.G;
+  Partial* slot = w.xch + (w.pass & 1) * kSlices;
+  if (threadIdx.x < per) put_partial(slot + w.g * per + threadIdx.x, mine[threadIdx.x]);
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(w.arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint32_t want = (uint32_t)w.G * (uint32_t)(w.pass + 1);
+    uint32_t spins = 0;
+    while (__hip_atomic_load(w.arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+      if (++spins > kSpinLimit) {
+        set_error(w.a->err, SV_DERR_TIMEOUT);
+        break;
       }
+      __builtin_amdgcn_s_sleep(2);
     }
-    double own[kGroup];
-#pragma unroll
-    for (int g = 0; g < kGroup; ++g) {
-      own[g] = 0.0;
-      const int64_t v = (int64_t)(t0 + g) * kWNT + threadIdx.x;
-      if (v < nvec) {
-        float w[E];
-        draw_weights_from<DT>(sp, V, v, dp[g], dq[g], w);
-#pragma unroll
-        for (int e = 0; e < E; ++e) own[g] += (double)w[e];
-      }
-    }
-#pragma unroll
-    for (int g = 0; g < kGroup; ++g) own[g] = wave_sum(own[g]);
-    __syncthreads();
-    if (lane == 0) {
-#pragma unroll
-      for (int g = 0; g < kGroup; ++g) red[g][wave] = own[g];
-    }
-    __syncthreads();
-    if (threadIdx.x < kGroup && t0 + (int)threadIdx.x < ntiles) {
-      double s = 0.0;
-      for (int w = 0; w < kWNT / kWave; ++w) s += red[threadIdx.x][w];
-      s_tiles[t0 + threadIdx.x] = s;
-    }
-    __syncthreads();
-    for (int g = 0; g < kGroup && t0 + g < ntiles; ++g) total += s_tiles[t0 + g];
   }
+  __syncthreads();
+  if (threadIdx.x < kSlices) {
+    const Partial p = get_partial(slot + threadIdx.x);
+    s_m[threadIdx.x] = p.m;
+    s_s[threadIdx.x] = p.s;
+  }
+  __syncthreads();
+  ++w.pass;
+}
+
+__device__ __forceinline__ void slice_range(const WalkCtx& w, int s, int64_t* v0, int64_t* v1) {
+  *v0 = (int64_t)s * w.spv;
+  const int64_t e = *v0 + w.spv;
+  *v1 = e < w.a->nvec ? e : w.a->nvec;
+  if (*v0 > w.a->nvec) *v0 = w.a->nvec;
+}
+
+// One residual pass: this block's slices of sum_v max(0, p - coef q).
+template <int DT>
+__device__ double residual_pass(WalkCtx& w, const DrawSpec& sp, float* s_m, double* s_s) {
+  __shared__ Partial mine[kSlices];
+  const int per = kSlices / w.G;
+  for (int i = 0; i < per; ++i) {
+    int64_t v0, v1;
+    slice_range(w, w.g * per + i, &v0, &v1);
+    const double sum = range_weight_sum<DT, kWNT>(sp, w.a->V, v0, v1);
+    if (threadIdx.x == 0) {
+      mine[i].m = 0.f;
+      mine[i].pad = 0.f;
+      mine[i].s = sum;
+    }
+  }
+  __syncthreads();
+  exchange(w, mine, s_m, s_s);
+  double total = 0.0;
+  for (int i = 0; i < kSlices; ++i) total += s_s[i];
   return total;
 }
 
-// Draw from the weights whose tile sums are in s_tiles (total `total`).
+// Draw from slice weights s_s (total `total`): locate the slice holding
+// u * total, and let its owner block search it.  Returns the token in the
+// owner block (-1 elsewhere).
 template <int DT>
-__device__ int64_t tile_draw(const DrawSpec& sp, int V, int64_t nvec, int ntiles, const double* s_tiles, double total,
-                             double u) {
-  __shared__ int s_tile;
-  __shared__ double s_loc;
-  if (threadIdx.x == 0) {
-    const double target = u * total;
-    double cum = 0.0, cum_last = 0.0;
-    int pick = -1, last = -1;
-    for (int t = 0; t < ntiles; ++t) {
-      const double w = s_tiles[t];
-      if (w > 0.0) {
-        last = t;
-        cum_last = cum;
-      }
-      if (pick < 0 && cum + w > target) {
-        pick = t;
-        s_loc = target - cum;
-      }
-      cum += w;
+__device__ int64_t slice_draw(const WalkCtx& w, const DrawSpec& sp, const double* s_s, double total, double u) {
+  const double target = u * total;
+  double cum = 0.0, cum_last = 0.0, loc = 0.0;
+  int pick = -1, last = -1;
+  for (int i = 0; i < kSlices; ++i) {
+    const double x = s_s[i];
+    if (x > 0.0) {
+      last = i;
+      cum_last = cum;
     }
-    if (pick < 0) {
-      pick = last < 0 ? 0 : last;
-      s_loc = cum - cum_last;
+    if (pick < 0 && cum + x > target) {
+      pick = i;
+      loc = target - cum;
     }
-    s_tile = pick;
+    cum += x;
   }
-  __syncthreads();
-  const int64_t v0 = (int64_t)s_tile * kWNT;
-  const int64_t v1 = v0 + kWNT < nvec ? v0 + kWNT : nvec;
-  return block_search<DT, kWNT>(sp, V, v0, v1, s_loc);
+  if (pick < 0) {
+    pick = last < 0 ? 0 : last;
+    loc = cum - cum_last;
+  }
+  const int per = kSlices / w.G;
+  if (pick / per != w.g) return -1;
+  int64_t v0, v1;
+  slice_range(w, pick, &v0, &v1);
+  return block_search<DT, kWNT>(sp, w.a->V, v0, v1, loc);
 }
 
 template <int DT>
 __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
-  const int b = blockIdx.x;
+  WalkCtx w;
+  w.a = &a;
+  w.G = a.G;
+  w.b = blockIdx.x / a.G;
+  w.g = blockIdx.x - w.b * a.G;
+  w.spv = (a.nvec + kSlices - 1) / kSlices;
+  w.arrive = a.cnt1 + w.b;
+  w.xch = static_cast<Partial*>(a.xch) + (int64_t)w.b * 2 * kSlices;
+  w.pass = 0;
+  const int b = w.b;
+  const bool writer = (w.g == 0);
   const int64_t rowbase = (int64_t)b * a.N;
   const Partial* parts = static_cast<const Partial*>(a.part);
   __shared__ int s_kids[SV_MAX_N];
-  __shared__ int s_nkids;
-  __shared__ RowStat s_P, s_Q;
-  __shared__ int s_acc;
-  __shared__ double s_tiles[kMaxTiles];
   __shared__ int32_t s_path[SV_MAX_N];
-
-  const int ntiles = (int)((a.nvec + kWNT - 1) / kWNT);  // <= kMaxTiles (checked on the host)
+  __shared__ float s_m[kSlices];
+  __shared__ double s_s[kSlices];
+  __shared__ int s_cnt;
   const double us = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
 
   int node = 0, depth = 0;
   int64_t t = -1;
   for (;;) {
-    // children of `node`, in increasing index
-    const int i = node + 1 + (int)threadIdx.x;
-    int flag = 0;
-    if (i < a.N) {
-      const int32_t pi = a.parent[rowbase + i];
-      flag = (pi == node);
-      if (pi < 0 || pi >= i) set_error(a.err, SV_DERR_TREE);
-    }
-    double excl;
-    const double nk_d = block_exclusive_scan<kWNT>((double)flag, &excl);
-    if (flag) s_kids[(int)excl] = i;
-    const int nk = (int)nk_d;
-    if (threadIdx.x == 0) s_nkids = nk;
+    // children of `node` in increasing index
+    if (threadIdx.x == 0) s_cnt = 0;
     __syncthreads();
-
+    for (int base = node + 1; base < a.N; base += kWNT) {
+      const int i = base + (int)threadIdx.x;
+      int flag = 0;
+      if (i < a.N) {
+        const int32_t pi = a.parent[rowbase + i];
+        flag = (pi == node);
+        if (writer && (pi < 0 || pi >= i)) set_error(a.err, SV_DERR_TREE);
+      }
+      double excl;
+      const double tot = block_exclusive_scan<kWNT>((double)flag, &excl);
+      if (flag) s_kids[s_cnt + (int)excl] = i;
+      __syncthreads();
+      if (threadIdx.x == 0) s_cnt += (int)tot;
+      __syncthreads();
+    }
+    const int nk = s_cnt;
     const void* rowP = row_ptr(a.tgt, rowbase + node, a.tgt_sb);
     if (nk == 0 || depth >= a.max_depth) {
-      if (nk > 0) set_error(a.err, SV_DERR_TREE);
-      // bonus draw from P_node: its statistic first (leaf rows were not in
-      // the stats pass), then tile sums with that shift, then the draw
-      const Partial st = range_stats<DT, kWNT, 4>(rowP, a.V, 0, a.nvec, a.c);
+      if (nk > 0 && writer) set_error(a.err, SV_DERR_TREE);
+      // bonus draw from P_node: online slice statistics, then the draw with
+      // the merged shift (rows of nodes without children were not streamed)
+      __shared__ Partial mine[kSlices];
+      const int per = kSlices / w.G;
+      for (int i = 0; i < per; ++i) {
+        int64_t v0, v1;
+        slice_range(w, w.g * per + i, &v0, &v1);
+        const Partial st = range_stats<DT, kWNT, 4>(rowP, a.V, v0, v1, a.c);
+        if (threadIdx.x == 0) mine[i] = st;
+      }
+      __syncthreads();
+      exchange(w, mine, s_m, s_s);
+      float M = kNegInf;
+      for (int i = 0; i < kSlices; ++i) M = fmaxf(M, s_m[i]);
+      const float cm = a.c * M;
+      __shared__ double s_w[kSlices];
+      double total = 0.0;
+      if (threadIdx.x == 0) {
+        for (int i = 0; i < kSlices; ++i) {
+          s_w[i] = s_m[i] == kNegInf ? 0.0 : s_s[i] * exp2((double)(a.c * s_m[i]) - (double)cm);
+        }
+      }
+      __syncthreads();
+      for (int i = 0; i < kSlices; ++i) total += s_w[i];
+      if (M == kNegInf && writer) set_error(a.err, SV_DERR_ROW);
       DrawSpec sp;
       sp.rowP = rowP;
       sp.rowQ = nullptr;
       sp.c = a.c;
-      sp.cmP = a.c * st.m;
+      sp.cmP = cm;
       sp.invSP = 1.f;
       sp.cmQ = 0.f;
       sp.invSQ = 1.f;
       sp.coef = 0.f;
-      if (st.m == kNegInf) set_error(a.err, SV_DERR_ROW);
-      const double total = tile_pass<DT>(sp, a.V, a.nvec, ntiles, s_tiles);
-      t = tile_draw<DT>(sp, a.V, a.nvec, ntiles, s_tiles, total, us);
+      t = slice_draw<DT>(w, sp, s_w, total, us);
       break;
     }
     const void* rowQ = row_ptr(a.drf, rowbase + node, a.drf_sb);
-    if (threadIdx.x == 0) {
-      s_P = merge_parts(parts + ((rowbase + node) * 2 + 0) * a.nch, a.nch, a.c);
-      s_Q = merge_parts(parts + ((rowbase + node) * 2 + 1) * a.nch, a.nch, a.c);
-      if (!(s_P.S > 0.0) || !(s_Q.S > 0.0)) set_error(a.err, SV_DERR_ROW);
-    }
-    __syncthreads();
-    const RowStat P = s_P, Q = s_Q;
+    const RowStat P = merge_parts(parts + ((rowbase + node) * 2 + 0) * a.nch, a.nch, a.c);
+    const RowStat Q = merge_parts(parts + ((rowbase + node) * 2 + 1) * a.nch, a.nch, a.c);
+    if (writer && threadIdx.x == 0 && (!(P.S > 0.0) || !(Q.S > 0.0))) set_error(a.err, SV_DERR_ROW);
     DrawSpec sp;
     sp.rowP = rowP;
     sp.rowQ = rowQ;
@@ -205,42 +259,39 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     sp.cmQ = Q.cm;
     sp.invSQ = Q.S > 0.0 ? (float)(1.0 / Q.S) : 0.f;
     double c = 0.0, D = 1.0, total = 0.0;
-    bool tiles_ok = false;  // s_tiles hold the weights of the current residual
+    bool sums_ok = false;  // s_s holds the slice sums of the current residual
     int accepted = -1;
     for (int kk = 0; kk < nk; ++kk) {
       const int ch = s_kids[kk];
-      if (threadIdx.x == 0) {
-        const int32_t x = a.tok[rowbase + ch];
-        double pt = 0.0, qt = 0.0;
-        if (x >= 0 && x < a.V) {
-          pt = prob_of(load_elem<DT>(rowP, x), a.c, P);
-          qt = prob_of(load_elem<DT>(rowQ, x), a.c, Q);
-        } else {
-          set_error(a.err, SV_DERR_TOKEN);
-        }
+      const int32_t x = a.tok[rowbase + ch];
+      double pt = 0.0, qt = 0.0;
+      if (x >= 0 && x < a.V) {
+        pt = prob_of(load_elem<DT>(rowP, x), a.c, P);
+        qt = prob_of(load_elem<DT>(rowQ, x), a.c, Q);
+      } else if (writer && threadIdx.x == 0) {
+        set_error(a.err, SV_DERR_TOKEN);
+      }
+      if (writer && threadIdx.x == 0) {
         if (a.out_p) a.out_p[rowbase + ch] = (float)pt;
         if (a.out_q) a.out_q[rowbase + ch] = (float)qt;
-        const double pcur = fmax(0.0, pt - c * qt) / D;
-        const double r = uniform24(a.seed, (uint32_t)ch, (uint32_t)b, 0, a.round, 0);
-        s_acc = r < accept_ratio(pcur, qt);
       }
-      __syncthreads();
-      if (s_acc) {
+      const double pcur = fmax(0.0, pt - c * qt) / D;
+      const double r = uniform24(a.seed, (uint32_t)ch, (uint32_t)b, 0, a.round, 0);
+      if (r < accept_ratio(pcur, qt)) {
         accepted = ch;
         break;
       }
       const double cn = c + D;
       sp.coef = (float)cn;
-      const double G = tile_pass<DT>(sp, a.V, a.nvec, ntiles, s_tiles);
+      const double G = residual_pass<DT>(w, sp, s_m, s_s);
       if (G > 0.0) {
         c = cn;
         D = G;
         total = G;
-        tiles_ok = true;
+        sums_ok = true;
       } else {
-        tiles_ok = false;  // residual mass rounded to 0: keep the previous residual
+        sums_ok = false;  // residual mass rounded to 0: keep the previous residual
       }
-      __syncthreads();
     }
     if (accepted >= 0) {
       if (threadIdx.x == 0) s_path[depth] = accepted;
@@ -251,28 +302,45 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     }
     // every child rejected: draw from (p - c q)^+
     sp.coef = (float)c;
-    if (!tiles_ok) total = tile_pass<DT>(sp, a.V, a.nvec, ntiles, s_tiles);
-    t = tile_draw<DT>(sp, a.V, a.nvec, ntiles, s_tiles, total, us);
+    if (!sums_ok) total = residual_pass<DT>(w, sp, s_m, s_s);
+    t = slice_draw<DT>(w, sp, s_s, total, us);
     break;
   }
   __syncthreads();
-  for (int d = threadIdx.x; d < a.max_depth; d += kWNT)
-    a.out_path[(int64_t)b * a.max_depth + d] = d < depth ? s_path[d] : -1;
+  if (writer) {
+    for (int d = threadIdx.x; d < a.max_depth; d += kWNT)
+      a.out_path[(int64_t)b * a.max_depth + d] = d < depth ? s_path[d] : -1;
+    if (threadIdx.x == 0) a.out_len[b] = depth;
+  }
+  if (t >= 0 && threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
+  // the last block of the sequence to leave resets its counters
   if (threadIdx.x == 0) {
-    a.out_len[b] = depth;
-    a.out_tok[b] = (int32_t)t;
+    const uint32_t old = __hip_atomic_fetch_add(a.cnt2 + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (uint32_t)w.G - 1) {
+      __hip_atomic_store(w.arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(a.cnt2 + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
   }
 }
 
-hipError_t launch_tree(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s) {
-  if (dt == SV_BF16) {
-    tree_stats_kernel<SV_BF16><<<dim3((unsigned)plan.grid1), dim3(kTNT), 0, s>>>(p);
-    tree_walk_kernel<SV_BF16><<<dim3((unsigned)plan.grid2), dim3(kWNT), 0, s>>>(p);
-  } else {
-    tree_stats_kernel<SV_F32><<<dim3((unsigned)plan.grid1), dim3(kTNT), 0, s>>>(p);
-    tree_walk_kernel<SV_F32><<<dim3((unsigned)plan.grid2), dim3(kWNT), 0, s>>>(p);
+template <int DT>
+hipError_t launch_tree_t(const TreeParams& p, const Plan& plan, hipStream_t s) {
+  tree_stats_kernel<DT><<<dim3((unsigned)plan.grid1), dim3(kTNT), 0, s>>>(p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.G == 1) {
+    tree_walk_kernel<DT><<<dim3((unsigned)plan.grid2), dim3(kWNT), 0, s>>>(p);
+    return hipGetLastError();
   }
-  return hipGetLastError();
+  // G blocks per sequence wait on each other: they must be co-resident
+  TreeParams arg = p;
+  void* args[] = {&arg};
+  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tree_walk_kernel<DT>), dim3((unsigned)plan.grid2),
+                                    dim3(kWNT), args, 0, s);
+}
+
+hipError_t launch_tree(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s) {
+  return dt == SV_BF16 ? launch_tree_t<SV_BF16>(p, plan, s) : launch_tree_t<SV_F32>(p, plan, s);
 }
 
 }  // namespace sv
