@@ -35,7 +35,7 @@ int stats_blocks() {
   return v;
 }
 int sample_blocks() {
-  static const int v = env_int("SV_SAMPLE_BLOCKS", 2048);
+  static const int v = env_int("SV_SAMPLE_BLOCKS", 1024);
   return v;
 }
 
@@ -113,8 +113,9 @@ sv_status plan_greedy(sv_dtype dt, int32_t B, int32_t gamma, int32_t V, Plan* pl
   return SV_OK;
 }
 
-constexpr int kWalkSlices = 64;  // slices of a walk pass per sequence
+constexpr int kWalkMaxG = 64;     // walk blocks (one slice of every row pass each) per sequence
 constexpr int kWalkBlocks = 256;  // walk blocks per call (one per CU when co-resident)
+constexpr int kWalkMaxParts = 64; // stats parts per row the walk stages
 
 sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, Plan* pl) {
   if (bad_dtype(dt)) return SV_EDTYPE;
@@ -124,10 +125,14 @@ sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, Plan* pl) {
   const int64_t rows = (int64_t)B * N * 2;
   // only nodes with children are streamed; size the parts for about half
   split(rows / 2 > 0 ? rows / 2 : 1, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
+  if (pl->nch1 > kWalkMaxParts) {
+    pl->vpc1 = (pl->nvec + kWalkMaxParts - 1) / kWalkMaxParts;
+    pl->nch1 = (int32_t)((pl->nvec + pl->vpc1 - 1) / pl->vpc1);
+  }
   pl->grid1 = rows * pl->nch1;
-  // walk blocks per sequence: a power of two dividing the slice count
+  // walk blocks per sequence: as many as keep the whole walk co-resident
   int G = 1;
-  while (G * 2 <= kWalkSlices && (int64_t)B * G * 2 <= kWalkBlocks) G *= 2;
+  while (G * 2 <= kWalkMaxG && (int64_t)B * G * 2 <= kWalkBlocks) G *= 2;
   pl->nch2 = G;
   pl->grid2 = (int64_t)B * G;
   if (pl->grid1 > INT32_MAX || pl->grid2 > INT32_MAX) return SV_EUNSUPPORTED;
@@ -135,7 +140,7 @@ sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, Plan* pl) {
   pl->off_part1 = off;
   off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
   pl->off_part2 = off;  // walk exchange slots
-  off = align_up(off + (size_t)B * 2 * kWalkSlices * sizeof(Partial), 256);
+  off = align_up(off + (size_t)B * 2 * kWalkMaxG * sizeof(Partial), 256);
   pl->bytes = off;
   return SV_OK;
 }

@@ -4,7 +4,8 @@
 // residual norm(max(0, p - q)), bonus row p_{gamma+1}); SpecDiff-2 page, Core
 // method (K candidates over shared draft marginals, keep the longest streak).
 //
-// Two launches per call:
+// Three launches per call (back-to-back launches on one stream cost about
+// nothing; a dependent pass inside one launch would cost a cross-block wait):
 //  1. stats: one block per (row part); every needed logit row (target rows
 //     1..gamma of every candidate, draft rows 1..gamma) is streamed once with
 //     16-byte loads and reduced to a mergeable (max, sum 2^(z c - c max))
@@ -12,9 +13,10 @@
 //     the parts, gathers p(x_j) and q(x_j), draws the acceptance uniforms,
 //     finds each candidate's first rejection with a wave ballot, keeps the
 //     best candidate and records which row(s) the final draw needs.
-//  2. sample: blocks over parts of that row pair (or the bonus row); each
-//     sums the draw weights of its part; the last block of the sequence
-//     locates the part holding u * S and searches inside it.
+//  2. draw parts: blocks over parts of that row pair (or the bonus row) sum
+//     the draw weights of their part.
+//  3. draw finish: one block per sequence locates the part holding u * S and
+//     searches inside it (one part re-read).
 // The bonus row p_{gamma+1} is only read when every draft of the kept
 // candidate is accepted.
 #include "sv_device.hpp"
@@ -218,8 +220,10 @@ __device__ DrawSpec job_spec(const ChainParams& a, const Job& jb, float cm_plain
   return sp;
 }
 
+// Draw pass, part sums: one block per (sequence, part) of the row pair of
+// the draw (or of the bonus row), no cross-block hand-off.
 template <int DT>
-__global__ __launch_bounds__(kNT) void chain_sample_kernel(ChainParams a) {
+__global__ __launch_bounds__(kNT) void chain_draw_parts_kernel(ChainParams a) {
   const int b = blockIdx.x / a.nch2;
   const int ch = blockIdx.x - b * a.nch2;
   const Job jb = static_cast<const Job*>(a.jobs)[b];
@@ -235,12 +239,17 @@ __global__ __launch_bounds__(kNT) void chain_sample_kernel(ChainParams a) {
   } else {
     part = range_stats<DT, kNT, kU>(row_ptr(a.tgt, jb.rowP, a.tgt_sb), a.V, v0, v1, a.c);
   }
-  Partial* parts = static_cast<Partial*>(a.part2) + (int64_t)b * a.nch2;
-  if (threadIdx.x == 0) put_partial(parts + ch, part);
-  if (!arrive_last<kNT>(&a.cnt2[b], (uint32_t)a.nch2)) return;
+  if (threadIdx.x == 0) static_cast<Partial*>(a.part2)[(int64_t)b * a.nch2 + ch] = part;
+}
 
-  // Last block of sequence b: stage the parts (weights of the draw per part,
-  // in part order) in LDS, locate the part holding u * S, search in it.
+// Draw pass, finish: one block per sequence stages the part sums, locates
+// the part holding u * S and searches inside it.
+template <int DT>
+__global__ __launch_bounds__(kNT) void chain_draw_finish_kernel(ChainParams a) {
+  const int b = blockIdx.x;
+  const Job jb = static_cast<const Job*>(a.jobs)[b];
+  const bool resid = jb.rowQ >= 0 && jb.SP > 0.0 && jb.SQ > 0.0;
+  const Partial* parts = static_cast<const Partial*>(a.part2) + (int64_t)b * a.nch2;
   __shared__ double s_w[kMaxSampleParts];
   __shared__ float s_pm[kMaxSampleParts];
   __shared__ double s_target;
@@ -248,9 +257,8 @@ __global__ __launch_bounds__(kNT) void chain_sample_kernel(ChainParams a) {
   __shared__ float s_cm;
   __shared__ int s_mode;  // 0 residual, 1 plain (bonus), 2 plain over P with the row statistic
   for (int i = threadIdx.x; i < a.nch2; i += kNT) {
-    const Partial pi = get_partial(parts + i);
-    s_pm[i] = pi.m;
-    s_w[i] = pi.s;
+    s_pm[i] = parts[i].m;
+    s_w[i] = parts[i].s;
   }
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -309,19 +317,18 @@ __global__ __launch_bounds__(kNT) void chain_sample_kernel(ChainParams a) {
     sp.cmP = s_cm;
   }
   const int64_t t = block_search<DT, kNT>(sp, a.V, s_v0, s_v1, s_target);
-  if (threadIdx.x == 0) {
-    a.out_tok[b] = (int32_t)t;
-    __hip_atomic_store(&a.cnt2[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
 }
 
 hipError_t launch_chain(const ChainParams& p, sv_dtype dt, const Plan& plan, hipStream_t s) {
   if (dt == SV_BF16) {
     chain_stats_kernel<SV_BF16><<<dim3((unsigned)plan.grid1), dim3(kNT), 0, s>>>(p);
-    chain_sample_kernel<SV_BF16><<<dim3((unsigned)plan.grid2), dim3(kNT), 0, s>>>(p);
+    chain_draw_parts_kernel<SV_BF16><<<dim3((unsigned)plan.grid2), dim3(kNT), 0, s>>>(p);
+    chain_draw_finish_kernel<SV_BF16><<<dim3((unsigned)p.B), dim3(kNT), 0, s>>>(p);
   } else {
     chain_stats_kernel<SV_F32><<<dim3((unsigned)plan.grid1), dim3(kNT), 0, s>>>(p);
-    chain_sample_kernel<SV_F32><<<dim3((unsigned)plan.grid2), dim3(kNT), 0, s>>>(p);
+    chain_draw_parts_kernel<SV_F32><<<dim3((unsigned)plan.grid2), dim3(kNT), 0, s>>>(p);
+    chain_draw_finish_kernel<SV_F32><<<dim3((unsigned)p.B), dim3(kNT), 0, s>>>(p);
   }
   return hipGetLastError();
 }

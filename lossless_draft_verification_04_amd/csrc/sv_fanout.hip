@@ -6,11 +6,14 @@
 //
 // One launch: a block per (row part).  Each wave keeps its current top-F in
 // registers, one entry per lane (lane i = i-th best), and streams its share of
-// the part in increasing index order.  A lane's 16-byte vector is a candidate
-// only if its largest element beats the wave's F-th best so far (elements are
-// seen in index order, so an equal value can never displace an earlier
-// entry); candidates are inserted one element at a time with a lane shift.
-// Most vectors cost one max and one compare.  The block merges its waves'
+// the part in increasing index order.  The list starts as the top-F of the
+// wave's first 64-vector window (F rounds of a wave-wide selection).  After
+// that a lane's 16-byte vector is a candidate only if its largest element
+// beats the wave's F-th best so far (elements are seen in index order, so an
+// equal value can never displace an earlier entry); a candidate lane flags
+// its qualifying elements, which are read with register lane reads and
+// inserted one at a time with a lane shift.  Most vectors cost one max and
+// one compare.  The block merges its waves'
 // lists; the last block of a row merges the parts' lists and writes them.
 #include "sv_device.hpp"
 #include "sv_internal.h"
@@ -110,19 +113,70 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
 #pragma unroll
           for (int e = 1; e < E; ++e) vm = fmaxf(vm, x[e]);
         }
-        const bool cand = valid && (count < F || vm > thr);
-        uint64_t cm = __ballot(cand);
+        if (count == 0) {
+          // first window of this wave: take its top-F directly, F rounds of a
+          // wave-wide (value desc, index asc) selection
+          uint32_t taken = 0;
+          for (int k = 0; k < F; ++k) {
+            float bv = kNegInf;
+            int32_t bi = kNoIdx;
+            if (valid) {
+#pragma unroll
+              for (int e = 0; e < E; ++e) {
+                const int64_t gi = v * E + e;
+                if (!((taken >> e) & 1u) && gi < a.V && (bi == kNoIdx || x[e] > bv)) {
+                  bv = x[e];
+                  bi = (int32_t)gi;
+                }
+              }
+            }
+            float wv = bv;
+            int32_t wi = bi;
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1) {
+              const float ov = __shfl_xor(wv, o, kWave);
+              const int32_t oi = __shfl_xor(wi, o, kWave);
+              if (oi != kNoIdx && (wi == kNoIdx || top_better(ov, oi, wv, wi))) {
+                wv = ov;
+                wi = oi;
+              }
+            }
+            if (wi == kNoIdx) break;  // the window has fewer than F elements
+            if (lane == k) {
+              lv = wv;
+              li = wi;
+            }
+            if (bi == wi) taken |= 1u << (wi - (int32_t)(v * E));
+            ++count;
+          }
+          if (count == F) thr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), F - 1));
+          continue;
+        }
+        // later windows: a lane is a candidate only if its largest element
+        // beats the F-th best so far; it then flags which of its elements do
+        uint32_t mine = 0;
+        if (valid && (count < F || vm > thr)) {
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if ((count < F || x[e] > thr) && v * E + e < a.V) mine |= 1u << e;
+        }
+        uint64_t cm = __ballot(mine != 0);
         while (cm) {
           const int src = __builtin_ctzll(cm);
           cm &= cm - 1;
+          uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)mine, src);
+          while (bits) {
+            const int e = __builtin_ctz(bits);
+            bits &= bits - 1;
+            // register read from one (uniform) lane: no LDS round trip
+            float xe = 0.f;
 #pragma unroll
-          for (int e = 0; e < E; ++e) {
-            const float xe = __shfl(x[e], src, kWave);
-            const int64_t gi = (base + src) * E + e;
-            if (gi < a.V && (count < F || xe > thr)) {
-              wave_insert(lv, li, xe, (int32_t)gi, F, lane);
+            for (int q = 0; q < E; ++q)
+              if (q == e) xe = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[q]), src));
+            if (count < F || xe > thr) {
+              wave_insert(lv, li, xe, (int32_t)((base + src) * E + e), F, lane);
               if (count < F) ++count;
-              thr = __shfl(lv, F - 1, kWave);
+              thr = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), F - 1));
             }
           }
         }

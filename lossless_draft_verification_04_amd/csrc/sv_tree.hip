@@ -48,39 +48,38 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
 }
 
 // ---------------------------------------------------------------------------
-// Walk.  A sequence's row passes are split into kSlices slices, handled by
-// the G blocks of that sequence (G = 1 .. kSlices, co-resident by a
-// cooperative launch when G > 1).  After each pass the blocks exchange their
-// slice sums through device-scope stores and meet at a per-sequence barrier;
-// every block then holds the same slice sums and, since every decision is a
-// deterministic function of global data and of those sums (same order, same
-// arithmetic), every block replays the identical walk.  Only block 0 writes
-// the per-child outputs; only the owner of the slice holding the draw
-// searches it.
+// Walk.  The G blocks of a sequence (G = 1 .. 64, co-resident by a
+// cooperative launch when G > 1) each own one slice of every row pass.
+// After a pass the blocks exchange their slice sums through device-scope
+// stores and meet at a per-sequence barrier; every block then holds the same
+// sums and, since every decision is a deterministic function of global data
+// and of those sums (same order, same arithmetic), every block replays the
+// identical walk.  Block 0 writes the per-child outputs; the owner of the
+// slice holding the draw searches it.
 // ---------------------------------------------------------------------------
-constexpr int kWNT = 256;       // walk block
-constexpr int kSlices = 64;     // slices of a row pass per sequence
+constexpr int kWNT = 256;  // walk block
+constexpr int kMaxG = 64;  // walk blocks (slices) per sequence
 constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr int kMaxParts = 64;  // stats parts per row staged by the walk
 
 struct WalkCtx {
   const TreeParams* a;
   int b, g, G;
-  int64_t spv;            // vectors per slice
-  uint32_t* arrive;       // per-sequence arrival counter (monotone within a call)
-  Partial* xch;           // [2][kSlices] exchange slots of this sequence
-  int pass;               // exchanges so far
+  int64_t v0, v1;     // this block's slice of every row pass
+  uint32_t* arrive;   // per-sequence arrival counter (monotone within a call)
+  Partial* xch;       // [2][kMaxG] exchange slots of this sequence
+  int pass;           // exchanges so far
 };
 
-// Exchange this block's slice parts; afterwards s_m / s_s hold all kSlices
-// parts (slice order) in every block of the sequence.
-__device__ void exchange(WalkCtx& w, const Partial* mine, float* s_m, double* s_s) {
-  const int per = kSlices / w.G;
-  Partial* slot = w.xch + (w.pass & 1) * kSlices;
-  if (threadIdx.x < per) put_partial(slot + w.g * per + threadIdx.x, mine[threadIdx.x]);
+// Exchange this block's slice part; afterwards s_m / s_s hold all G parts
+// (slice order) in every block of the sequence.
+__device__ void exchange(WalkCtx& w, const Partial& mine, float* s_m, double* s_s) {
+  Partial* slot = w.xch + (w.pass & 1) * kMaxG;
+  if (threadIdx.x == 0) put_partial(slot + w.g, mine);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && w.G > 1) {
     __hip_atomic_fetch_add(w.arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     const uint32_t want = (uint32_t)w.G * (uint32_t)(w.pass + 1);
     uint32_t spins = 0;
@@ -89,12 +88,12 @@ __device__ void exchange(WalkCtx& w, const Partial* mine, float* s_m, double* s_
         set_error(w.a->err, SV_DERR_TIMEOUT);
         break;
       }
-      __builtin_amdgcn_s_sleep(2);
+      __builtin_amdgcn_s_sleep(1);
     }
   }
   __syncthreads();
-  if (threadIdx.x < kSlices) {
-    const Partial p = get_partial(slot + threadIdx.x);
+  if (threadIdx.x < w.G) {
+    const Partial p = w.G > 1 ? get_partial(slot + threadIdx.x) : mine;
     s_m[threadIdx.x] = p.m;
     s_s[threadIdx.x] = p.s;
   }
@@ -102,45 +101,16 @@ __device__ void exchange(WalkCtx& w, const Partial* mine, float* s_m, double* s_
   ++w.pass;
 }
 
-__device__ __forceinline__ void slice_range(const WalkCtx& w, int s, int64_t* v0, int64_t* v1) {
-  *v0 = (int64_t)s * w.spv;
-  const int64_t e = *v0 + w.spv;
-  *v1 = e < w.a->nvec ? e : w.a->nvec;
-  if (*v0 > w.a->nvec) *v0 = w.a->nvec;
-}
-
-// One residual pass: this block's slices of sum_v max(0, p - coef q).
+// Draw from slice weights s_w (G of them, total `total`): locate the slice
+// holding u * total; its owner block searches it and returns the token
+// (-1 in the other blocks).
 template <int DT>
-__device__ double residual_pass(WalkCtx& w, const DrawSpec& sp, float* s_m, double* s_s) {
-  __shared__ Partial mine[kSlices];
-  const int per = kSlices / w.G;
-  for (int i = 0; i < per; ++i) {
-    int64_t v0, v1;
-    slice_range(w, w.g * per + i, &v0, &v1);
-    const double sum = range_weight_sum<DT, kWNT>(sp, w.a->V, v0, v1);
-    if (threadIdx.x == 0) {
-      mine[i].m = 0.f;
-      mine[i].pad = 0.f;
-      mine[i].s = sum;
-    }
-  }
-  __syncthreads();
-  exchange(w, mine, s_m, s_s);
-  double total = 0.0;
-  for (int i = 0; i < kSlices; ++i) total += s_s[i];
-  return total;
-}
-
-// Draw from slice weights s_s (total `total`): locate the slice holding
-// u * total, and let its owner block search it.  Returns the token in the
-// owner block (-1 elsewhere).
-template <int DT>
-__device__ int64_t slice_draw(const WalkCtx& w, const DrawSpec& sp, const double* s_s, double total, double u) {
+__device__ int64_t slice_draw(const WalkCtx& w, const DrawSpec& sp, const double* s_w, double total, double u) {
   const double target = u * total;
   double cum = 0.0, cum_last = 0.0, loc = 0.0;
   int pick = -1, last = -1;
-  for (int i = 0; i < kSlices; ++i) {
-    const double x = s_s[i];
+  for (int i = 0; i < w.G; ++i) {
+    const double x = s_w[i];
     if (x > 0.0) {
       last = i;
       cum_last = cum;
@@ -155,11 +125,8 @@ __device__ int64_t slice_draw(const WalkCtx& w, const DrawSpec& sp, const double
     pick = last < 0 ? 0 : last;
     loc = cum - cum_last;
   }
-  const int per = kSlices / w.G;
-  if (pick / per != w.g) return -1;
-  int64_t v0, v1;
-  slice_range(w, pick, &v0, &v1);
-  return block_search<DT, kWNT>(sp, w.a->V, v0, v1, loc);
+  if (pick != w.g) return -1;
+  return block_search<DT, kWNT>(sp, w.a->V, w.v0, w.v1, loc);
 }
 
 template <int DT>
@@ -169,35 +136,49 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   w.G = a.G;
   w.b = blockIdx.x / a.G;
   w.g = blockIdx.x - w.b * a.G;
-  w.spv = (a.nvec + kSlices - 1) / kSlices;
+  {
+    const int64_t spv = (a.nvec + a.G - 1) / a.G;
+    w.v0 = (int64_t)w.g * spv < a.nvec ? (int64_t)w.g * spv : a.nvec;
+    w.v1 = w.v0 + spv < a.nvec ? w.v0 + spv : a.nvec;
+  }
   w.arrive = a.cnt1 + w.b;
-  w.xch = static_cast<Partial*>(a.xch) + (int64_t)w.b * 2 * kSlices;
+  w.xch = static_cast<Partial*>(a.xch) + (int64_t)w.b * 2 * kMaxG;
   w.pass = 0;
   const int b = w.b;
   const bool writer = (w.g == 0);
   const int64_t rowbase = (int64_t)b * a.N;
   const Partial* parts = static_cast<const Partial*>(a.part);
+  __shared__ int32_t s_par[SV_MAX_N];
+  __shared__ int32_t s_tok[SV_MAX_N];
   __shared__ int s_kids[SV_MAX_N];
   __shared__ int32_t s_path[SV_MAX_N];
-  __shared__ float s_m[kSlices];
-  __shared__ double s_s[kSlices];
+  __shared__ float s_zp[SV_MAX_N], s_zq[SV_MAX_N];
+  __shared__ float s_pm[2 * kMaxParts];
+  __shared__ double s_ps[2 * kMaxParts];
+  __shared__ RowStat s_P, s_Q;
+  __shared__ float s_m[kMaxG];
+  __shared__ double s_s[kMaxG];
   __shared__ int s_cnt;
   const double us = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
+
+  // the tree's shape and tokens, once
+  for (int i = threadIdx.x; i < a.N; i += kWNT) {
+    const int32_t pi = a.parent[rowbase + i];
+    s_par[i] = pi;
+    s_tok[i] = a.tok[rowbase + i];
+    if (writer && i > 0 && (pi < 0 || pi >= i)) set_error(a.err, SV_DERR_TREE);
+  }
+  __syncthreads();
 
   int node = 0, depth = 0;
   int64_t t = -1;
   for (;;) {
-    // children of `node` in increasing index
+    // children of `node` in increasing index (from LDS)
     if (threadIdx.x == 0) s_cnt = 0;
     __syncthreads();
     for (int base = node + 1; base < a.N; base += kWNT) {
       const int i = base + (int)threadIdx.x;
-      int flag = 0;
-      if (i < a.N) {
-        const int32_t pi = a.parent[rowbase + i];
-        flag = (pi == node);
-        if (writer && (pi < 0 || pi >= i)) set_error(a.err, SV_DERR_TREE);
-      }
+      const int flag = (i < a.N) && s_par[i] == node;
       double excl;
       const double tot = block_exclusive_scan<kWNT>((double)flag, &excl);
       if (flag) s_kids[s_cnt + (int)excl] = i;
@@ -209,31 +190,22 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     const void* rowP = row_ptr(a.tgt, rowbase + node, a.tgt_sb);
     if (nk == 0 || depth >= a.max_depth) {
       if (nk > 0 && writer) set_error(a.err, SV_DERR_TREE);
-      // bonus draw from P_node: online slice statistics, then the draw with
-      // the merged shift (rows of nodes without children were not streamed)
-      __shared__ Partial mine[kSlices];
-      const int per = kSlices / w.G;
-      for (int i = 0; i < per; ++i) {
-        int64_t v0, v1;
-        slice_range(w, w.g * per + i, &v0, &v1);
-        const Partial st = range_stats<DT, kWNT, 4>(rowP, a.V, v0, v1, a.c);
-        if (threadIdx.x == 0) mine[i] = st;
-      }
-      __syncthreads();
-      exchange(w, mine, s_m, s_s);
+      // bonus draw from P_node (not streamed by the stats pass): online slice
+      // statistics, exchanged, then the draw with the merged shift
+      const Partial st = range_stats<DT, kWNT, 4>(rowP, a.V, w.v0, w.v1, a.c);
+      exchange(w, st, s_m, s_s);
       float M = kNegInf;
-      for (int i = 0; i < kSlices; ++i) M = fmaxf(M, s_m[i]);
+      for (int i = 0; i < w.G; ++i) M = fmaxf(M, s_m[i]);
       const float cm = a.c * M;
-      __shared__ double s_w[kSlices];
       double total = 0.0;
-      if (threadIdx.x == 0) {
-        for (int i = 0; i < kSlices; ++i) {
-          s_w[i] = s_m[i] == kNegInf ? 0.0 : s_s[i] * exp2((double)(a.c * s_m[i]) - (double)cm);
-        }
-      }
       __syncthreads();
-      for (int i = 0; i < kSlices; ++i) total += s_w[i];
-      if (M == kNegInf && writer) set_error(a.err, SV_DERR_ROW);
+      if (threadIdx.x < w.G)
+        s_s[threadIdx.x] = s_m[threadIdx.x] == kNegInf ? 0.0
+                                                       : s_s[threadIdx.x] * exp2((double)(a.c * s_m[threadIdx.x]) -
+                                                                                 (double)cm);
+      __syncthreads();
+      for (int i = 0; i < w.G; ++i) total += s_s[i];
+      if (M == kNegInf && writer && threadIdx.x == 0) set_error(a.err, SV_DERR_ROW);
       DrawSpec sp;
       sp.rowP = rowP;
       sp.rowQ = nullptr;
@@ -243,12 +215,46 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       sp.cmQ = 0.f;
       sp.invSQ = 1.f;
       sp.coef = 0.f;
-      t = slice_draw<DT>(w, sp, s_w, total, us);
+      t = slice_draw<DT>(w, sp, s_s, total, us);
       break;
     }
     const void* rowQ = row_ptr(a.drf, rowbase + node, a.drf_sb);
-    const RowStat P = merge_parts(parts + ((rowbase + node) * 2 + 0) * a.nch, a.nch, a.c);
-    const RowStat Q = merge_parts(parts + ((rowbase + node) * 2 + 1) * a.nch, a.nch, a.c);
+    // one round of loads: the node's stats parts and every child's logits
+    const int np = a.nch <= kMaxParts ? a.nch : kMaxParts;
+    const Partial* pn = parts + (rowbase + node) * 2 * a.nch;
+    for (int i = threadIdx.x; i < 2 * np; i += kWNT) {
+      const Partial pi = get_partial(pn + (i < np ? i : a.nch + (i - np)));
+      s_pm[i] = pi.m;
+      s_ps[i] = pi.s;
+    }
+    for (int k = threadIdx.x; k < nk; k += kWNT) {
+      const int32_t x = s_tok[s_kids[k]];
+      float zp = 0.f, zq = 0.f;
+      if (x >= 0 && x < a.V) {
+        zp = load_elem<DT>(rowP, x);
+        zq = load_elem<DT>(rowQ, x);
+      }
+      s_zp[k] = zp;
+      s_zq[k] = zq;
+    }
+    __syncthreads();
+    if (threadIdx.x < 2) {
+      const float* pm = s_pm + threadIdx.x * np;
+      const double* ps = s_ps + threadIdx.x * np;
+      float M = kNegInf;
+      for (int i = 0; i < np; ++i) M = fmaxf(M, pm[i]);
+      RowStat r;
+      r.pad = 0.f;
+      r.cm = M == kNegInf ? 0.f : a.c * M;
+      double S = 0.0;
+      if (M != kNegInf)
+        for (int i = 0; i < np; ++i)
+          if (pm[i] != kNegInf) S += ps[i] * exp2((double)(a.c * pm[i]) - (double)r.cm);
+      r.S = S;
+      if (threadIdx.x == 0) s_P = r; else s_Q = r;
+    }
+    __syncthreads();
+    const RowStat P = s_P, Q = s_Q;
     if (writer && threadIdx.x == 0 && (!(P.S > 0.0) || !(Q.S > 0.0))) set_error(a.err, SV_DERR_ROW);
     DrawSpec sp;
     sp.rowP = rowP;
@@ -263,11 +269,11 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     int accepted = -1;
     for (int kk = 0; kk < nk; ++kk) {
       const int ch = s_kids[kk];
-      const int32_t x = a.tok[rowbase + ch];
+      const int32_t x = s_tok[ch];
       double pt = 0.0, qt = 0.0;
       if (x >= 0 && x < a.V) {
-        pt = prob_of(load_elem<DT>(rowP, x), a.c, P);
-        qt = prob_of(load_elem<DT>(rowQ, x), a.c, Q);
+        pt = prob_of(s_zp[kk], a.c, P);
+        qt = prob_of(s_zq[kk], a.c, Q);
       } else if (writer && threadIdx.x == 0) {
         set_error(a.err, SV_DERR_TOKEN);
       }
@@ -283,7 +289,13 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       }
       const double cn = c + D;
       sp.coef = (float)cn;
-      const double G = residual_pass<DT>(w, sp, s_m, s_s);
+      Partial mine;
+      mine.m = 0.f;
+      mine.pad = 0.f;
+      mine.s = range_weight_sum<DT, kWNT>(sp, a.V, w.v0, w.v1);
+      exchange(w, mine, s_m, s_s);
+      double G = 0.0;
+      for (int i = 0; i < w.G; ++i) G += s_s[i];
       if (G > 0.0) {
         c = cn;
         D = G;
@@ -302,7 +314,15 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     }
     // every child rejected: draw from (p - c q)^+
     sp.coef = (float)c;
-    if (!sums_ok) total = residual_pass<DT>(w, sp, s_m, s_s);
+    if (!sums_ok) {
+      Partial mine;
+      mine.m = 0.f;
+      mine.pad = 0.f;
+      mine.s = range_weight_sum<DT, kWNT>(sp, a.V, w.v0, w.v1);
+      exchange(w, mine, s_m, s_s);
+      total = 0.0;
+      for (int i = 0; i < w.G; ++i) total += s_s[i];
+    }
     t = slice_draw<DT>(w, sp, s_s, total, us);
     break;
   }
@@ -314,7 +334,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   }
   if (t >= 0 && threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
   // the last block of the sequence to leave resets its counters
-  if (threadIdx.x == 0) {
+  if (threadIdx.x == 0 && w.G > 1) {
     const uint32_t old = __hip_atomic_fetch_add(a.cnt2 + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (uint32_t)w.G - 1) {
       __hip_atomic_store(w.arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -160,6 +160,13 @@ def test_tree_small_shapes():
         PT.tree(wl, 7, 1)
 
 
+@pytest.mark.parametrize("B", [70, 130])  # 2 walk blocks per sequence, and 1
+def test_tree_many_sequences(B):
+    wl = W.tree_zipf(B=B, N=12, max_depth=5, V=2500, T=1.0, seed=44 + B)
+    PT.tree(wl, 3, 0)
+    PT.device_error_clear()
+
+
 def test_tree_chain_shaped_matches_chain_oracle():
     cw = W.chain_zipf(B=6, gamma=7, V=20000, T=1.0, seed=43)
     tw = W.chain_shaped_tree(cw)
@@ -214,3 +221,25 @@ def test_workspace_shared_across_ops_and_shapes():
     PT.greedy(W.greedy_zipf(B=50, gamma=3, V=8000, seed=63))
     PT.tree(tw, 2, 0)
     PT.chain(cw, 2, 0)
+
+
+# ----------------------------------------------------------------- graph replay
+def test_chain_graph_replays_match_eager():
+    """A captured sv_verify_chain call replays correctly several times, with
+    eager work and synchronisations between the replays."""
+    wl = W.chain_zipf(B=8, gamma=8, V=30000, T=0.8, seed=71)
+    g = wl.to(PT.DEV)
+    T = PT.f32(0.8)
+    eager = svx.sv_verify_chain(g["tgt"], g["drf"], g["tok"], T, seed=2, round_=5)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        cap = svx.sv_verify_chain(g["tgt"], g["drf"], g["tok"], T, seed=2, round_=5)
+    for rep in range(4):
+        graph.replay()
+        torch.cuda.synchronize()
+        for k in ("n", "tok", "p", "q"):
+            assert torch.equal(cap[k], eager[k]), (rep, k)
+        other = svx.sv_verify_greedy(g["tgt"], g["tok"])  # eager work between replays
+        torch.cuda.synchronize()
+        assert other["n"].numel() == 8
