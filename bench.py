@@ -7,10 +7,10 @@ Inputs are resident in HBM before the timed region; distinct copies of the
 inputs (>= 2 GB in total) are rotated so the 256 MB last-level cache cannot
 serve a repeat.
 
-Each input copy's call is captured once in a HIP graph and the timed loop
-replays the graphs, so host launch cost is not in the step time (the eager
-per-call numbers are reported beside it).  The tree row uses eager calls
-(its walk is a cooperative launch).
+One HIP graph holds one call per input copy and the timed loop replays it
+(plus a tail graph) so that exactly `steps` calls run; host launch cost is
+then not in the step time (the eager rate is reported beside it).  The tree
+row uses eager calls (its walk is a cooperative launch).
 
 Prints ONE JSON line.  `value` is verified draft positions per second (B *
 gamma per call).  `roofline` reports the call's algorithmic bytes (rows
@@ -40,6 +40,11 @@ from lossless_draft_verification_04_amd import workloads as W  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0
 ROTATE_BYTES = 2.2e9
+USE_GRAPHS = True
+PMC_RECORD = os.path.join(ROOT, "profiles", "chain_batched_pmc.json")
+KERNEL_SOURCES = [os.path.join(ROOT, "lossless_draft_verification_04_amd", "csrc", f)
+                  for f in ("sv_device.hpp", "sv_internal.h", "sv_api.hip", "sv_chain.hip")] + \
+                 [os.path.join(ROOT, "include", "specverify.h")]
 METRIC = "verified draft positions/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
 
 
@@ -52,50 +57,104 @@ def esize(dt):
 
 
 def n_copies(bytes_per_copy):
-    return max(2, int(np.ceil(ROTATE_BYTES / max(bytes_per_copy, 1))))
+    """Distinct input copies whose total exceeds the 256 MB last-level cache (at most 32)."""
+    return min(32, max(2, int(np.ceil(ROTATE_BYTES / max(bytes_per_copy, 1)))))
 
 
 def time_calls(fn, copies, steps, warmup):
-    """Run fn(copy) `warmup` times untimed, then `steps` times timed, each call
-    bracketed by HIP events on the launch stream.
+    """Run fn(copy) `warmup` times untimed, then `steps` times timed, with one
+    pair of HIP events on the launch stream around the timed calls.
 
-    Returns (ms_per_step wall, mean event ms per call, list of event ms)."""
+    Returns (ms_per_step wall, event ms per call)."""
     for i in range(warmup):
         fn(copies[i % len(copies)])
     torch.cuda.synchronize()
-    starts = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    ends = [torch.cuda.Event(enable_timing=True) for _ in range(steps)]
-    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0 = time.perf_counter()
+    a.record()
     for i in range(steps):
-        starts[i].record()
         fn(copies[i % len(copies)])
-        ends[i].record()
+    b.record()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) * 1e3 / steps
-    ev = [s.elapsed_time(e) for s, e in zip(starts, ends)]
-    return wall, float(np.mean(ev)), ev
+    return wall, a.elapsed_time(b) / steps
 
 
 def time_graphs(fn, copies, steps, warmup):
-    """Same as time_calls, but each input copy's call is captured once in a HIP
-    graph and the timed loop replays the graphs (no host launch cost per step)."""
+    """Capture one HIP graph holding one call per input copy (and a tail graph
+    for steps % copies), replay them so that exactly `steps` calls run, and
+    bracket every replay with HIP events on the launch stream.
+
+    Returns (ms_per_step wall, mean event ms per call)."""
+    if not USE_GRAPHS:
+        return time_calls(fn, copies, steps, warmup)
     fn(copies[0])  # workspace and code objects exist before capture
     torch.cuda.synchronize()
-    graphs = []
-    for c in copies:
+    L = len(copies)
+
+    def capture(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            fn(c)
-        graphs.append(g)
+            for c in copies[:n]:
+                fn(c)
+        return g
+
+    full = capture(L)
+    plan = [(full, L)] * (steps // L)
+    if steps % L:
+        plan.append((capture(steps % L), steps % L))
+    for _ in range(max(1, -(-warmup // L))):
+        full.replay()
     torch.cuda.synchronize()
-    return time_calls(lambda g: g.replay(), graphs, steps, warmup)
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in plan]
+    t0 = time.perf_counter()
+    for (g, _), (a, b) in zip(plan, ev):
+        a.record()
+        g.replay()
+        b.record()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) * 1e3 / steps
+    per_call = sum(a.elapsed_time(b) for a, b in ev) / steps
+    return wall, per_call
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic():
+    """HBM bytes per call from the committed rocprofv3 counter record, if it was
+    taken on the current kernel sources (null otherwise)."""
+    try:
+        with open(PMC_RECORD) as f:
+            rec = json.load(f)
+    except (OSError, ValueError):
+        return None
+    if rec.get("source_hash") != kernel_source_hash():
+        return None
+    return rec.get("hbm_bytes_per_call")
 
 
 def roofline(alg_bytes, ms):
     gbs = alg_bytes / (ms * 1e-3) / 1e9
     return dict(bound="hbm", achieved=round(gbs, 1), peak=HBM_PEAK_GBS, unit="GB/s", frac=round(gbs / HBM_PEAK_GBS, 4),
-                traffic=None)
+                traffic=measured_traffic())
+
+
+def copy_probe(mib, reps=5):
+    """Device-to-device copies of a known size, for scaling the traffic counters."""
+    n = mib * (1 << 20) // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    log(f"copy probe: {reps} copies of {mib} MiB ({mib * (1 << 20)} bytes read and written each)")
 
 
 # ------------------------------------------------------------------ chain
@@ -115,13 +174,12 @@ def bench_chain(wl, steps, warmup, seed=0):
     out = fn(copies[0])
     torch.cuda.synchronize()
     n = out["n"].cpu().numpy()
-    e_wall, e_ms, _ = time_calls(fn, copies, steps, warmup)
-    wall, ev_ms, _ = time_graphs(fn, copies, steps, warmup)
+    e_wall, _ = time_calls(fn, copies, steps, warmup)
+    wall, ev_ms = time_graphs(fn, copies, steps, warmup)
     pos = p["B"] * p["gamma"]
     alg = chain_alg_bytes(p, n)
     return dict(positions_per_call=pos, positions_per_s=pos / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
-                alg_bytes=alg, mean_accepted=float(n.mean()), copies=len(copies), eager_ms_per_step=e_wall,
-                eager_call_ms=e_ms), out
+                alg_bytes=alg, mean_accepted=float(n.mean()), copies=len(copies), eager_ms_per_step=e_wall), out
 
 
 def bench_greedy(wl, steps, warmup):
@@ -131,7 +189,7 @@ def bench_greedy(wl, steps, warmup):
     fn = lambda g: svx.sv_verify_greedy(g["tgt"], g["tok"], want_argmax=False)
     out = fn(copies[0])
     torch.cuda.synchronize()
-    wall, ev_ms, _ = time_graphs(fn, copies, steps, warmup)
+    wall, ev_ms = time_graphs(fn, copies, steps, warmup)
     pos = p["B"] * p["gamma"]
     alg = p["B"] * (p["gamma"] + 1) * p["V"] * esize(p["dtype"])
     return dict(positions_per_call=pos, positions_per_s=pos / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
@@ -147,7 +205,7 @@ def bench_multi(wl, steps, warmup):
     out = fn(copies[0])
     torch.cuda.synchronize()
     n = out["n"].cpu().numpy()
-    wall, ev_ms, _ = time_graphs(fn, copies, steps, warmup)
+    wall, ev_ms = time_graphs(fn, copies, steps, warmup)
     B, K, g, V = p["B"], p["K"], p["gamma"], p["V"]
     row = V * esize(p["dtype"])
     alg = (B * K * g + B * g) * row + sum(2 if int(x) < g else 1 for x in n) * row
@@ -188,7 +246,7 @@ def bench_tree(wl, steps, warmup):
     torch.cuda.synchronize()
     alg = tree_alg_bytes(wl, out)
     fn = lambda g: svx.sv_verify_tree(g["tgt"], g["drf"], g["tok"], g["parent"], p["max_depth"], T, want_pq=False)
-    wall, ev_ms, _ = time_calls(fn, copies, steps, warmup)
+    wall, ev_ms = time_calls(fn, copies, steps, warmup)
     pos = p["B"] * (p["N"] - 1)
     return dict(positions_per_call=pos, positions_per_s=pos / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
                 alg_bytes=alg, mean_accepted=float(out["len"].float().mean().item()), copies=len(copies))
@@ -207,7 +265,7 @@ def bench_fanout(wl, steps, warmup):
     fn = lambda g: svx.sv_fanout_topk(g["x"], g["F"], 8, want_vals=False)
     fn(copies[0])
     torch.cuda.synchronize()
-    wall, ev_ms, _ = time_graphs(fn, copies, steps, warmup)
+    wall, ev_ms = time_graphs(fn, copies, steps, warmup)
     alg = B * N * V * esize(p["dtype"])
     return dict(rows_per_call=B * N, rows_per_s=B * N / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
                 alg_bytes=alg, copies=len(copies))
@@ -248,7 +306,15 @@ def main():
     ap.add_argument("--no-variants", action="store_true", help="time only the headline workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=10.0, help="seconds of CPU oracle work")
+    ap.add_argument("--eager", action="store_true", help="time eager calls instead of graph replays (profiling runs)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0, help="also run copies of this size (counter calibration)")
+    ap.add_argument("--source-hash", action="store_true", help="print the kernel-source hash and exit")
     args = ap.parse_args()
+    if args.source_hash:
+        print(kernel_source_hash())
+        return
+    global USE_GRAPHS
+    USE_GRAPHS = not args.eager
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the verification step shards by sequence with no exchange, "
               "and this build runs no multi-GPU configuration.", file=sys.stderr)
@@ -282,6 +348,9 @@ def main():
             del w
             torch.cuda.empty_cache()
 
+    if args.copy_probe_mib:
+        copy_probe(args.copy_probe_mib)
+
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle")
@@ -289,8 +358,8 @@ def main():
         cpu["cores"] = 1
 
     rl = roofline(r["alg_bytes"], r["call_ms"])
-    rl["kernel"] = ("sv_verify_chain call (row-statistics + draw kernels), mean of HIP events around each "
-                    "graph replay on the launch stream")
+    rl["kernel"] = ("sv_verify_chain call (row-statistics + 2 draw kernels); duration = HIP events around the "
+                    "graph replays on the launch stream / calls")
     rl["alg_bytes_per_call"] = int(r["alg_bytes"])
     line = {
         "metric": METRIC,
@@ -309,9 +378,9 @@ def main():
                                "Zipf(1.1)+Gumbel target rows, draft noise sigma 0.5..2.5",
                    "B": 32, "gamma": 16, "V": 152064, "logits": "bf16", "device": dev_name,
                    "input_copies_rotated": r["copies"], "mean_accepted": round(r["mean_accepted"], 3),
-                   "launch": "each input copy's call captured once in a HIP graph; timed loop replays the graphs",
-                   "eager_ms_per_step": round(r["eager_ms_per_step"], 5),
-                   "eager_call_ms": round(r["eager_call_ms"], 5)},
+                   "launch": ("one HIP graph holds one call per input copy; the timed loop replays it so that "
+                              "exactly `steps` calls run" if USE_GRAPHS else "eager calls"),
+                   "eager_ms_per_step": round(r["eager_ms_per_step"], 5)},
         "roofline": rl,
         "cpu_baseline": cpu,
         "variants": variants,
