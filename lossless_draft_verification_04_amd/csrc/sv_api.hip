@@ -114,8 +114,9 @@ sv_status plan_greedy(sv_dtype dt, int32_t B, int32_t gamma, int32_t V, Plan* pl
 }
 
 constexpr int kWalkMaxG = 64;     // walk blocks (one slice of every row pass each) per sequence
-constexpr int kWalkBlocks = 256;  // walk blocks per call (one per CU when co-resident)
 constexpr int kWalkMaxParts = 64; // stats parts per row the walk stages
+constexpr int kWalkRing = 3;      // pass-total words per sequence (in the zeroed counter region)
+constexpr int32_t kWalkRingSeqs = (int32_t)(kWsCounters / 2 * sizeof(uint32_t) / (kWalkRing * sizeof(uint64_t)));
 
 sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, Plan* pl) {
   if (bad_dtype(dt)) return SV_EDTYPE;
@@ -123,26 +124,37 @@ sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, Plan* pl) {
   if (B > SV_MAX_SEQ || N > SV_MAX_N || V > SV_MAX_V) return SV_EUNSUPPORTED;
   pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
   const int64_t rows = (int64_t)B * N * 2;
-  // only nodes with children are streamed; size the parts for about half
-  split(rows / 2 > 0 ? rows / 2 : 1, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
+  // only rows of nodes with children are streamed (about half of them in a
+  // bushy tree): aim the part count at twice the usual block target
+  split(rows, pl->nvec, 2 * stats_blocks(), &pl->nch1, &pl->vpc1);
   if (pl->nch1 > kWalkMaxParts) {
     pl->vpc1 = (pl->nvec + kWalkMaxParts - 1) / kWalkMaxParts;
     pl->nch1 = (int32_t)((pl->nvec + pl->vpc1 - 1) / pl->vpc1);
   }
   pl->grid1 = rows * pl->nch1;
-  // walk blocks per sequence: as many as keep the whole walk co-resident
-  int G = 1;
-  while (G * 2 <= kWalkMaxG && (int64_t)B * G * 2 <= kWalkBlocks) G *= 2;
-  pl->nch2 = G;
-  pl->grid2 = (int64_t)B * G;
-  if (pl->grid1 > INT32_MAX || pl->grid2 > INT32_MAX) return SV_EUNSUPPORTED;
+  if (pl->grid1 > INT32_MAX) return SV_EUNSUPPORTED;
   size_t off = kWsFixed;
   pl->off_part1 = off;
   off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
-  pl->off_part2 = off;  // walk exchange slots
+  pl->off_part2 = off;  // walk slice slots
   off = align_up(off + (size_t)B * 2 * kWalkMaxG * sizeof(Partial), 256);
   pl->bytes = off;
   return SV_OK;
+}
+
+// Walk blocks per sequence: the largest power of two (<= 64) with B * G at
+// most the device's compute-unit count, so one launch's walk blocks are all
+// resident together.  G > 1 needs the sequence's pass-total ring, which lives
+// in the first half of the counter region.
+int walk_blocks_per_sequence(int32_t B) {
+  if (B > kWalkRingSeqs) return 1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    cus = 1;
+  int G = 1;
+  while (G * 2 <= kWalkMaxG && (int64_t)B * G * 2 <= cus) G *= 2;
+  return G;
 }
 
 sv_status plan_fanout(sv_dtype dt, int32_t R, int32_t V, int32_t F_max, Plan* pl) {
@@ -369,12 +381,12 @@ sv_status sv_verify_tree(const void* tgt, const void* drf, sv_dtype dt, int64_t 
   p.out_p = out_p;
   p.out_q = out_q;
   p.err = reinterpret_cast<int32_t*>(w);
-  p.cnt1 = reinterpret_cast<uint32_t*>(w + kWsHeader);
-  p.cnt2 = p.cnt1 + kWsCounters / 2;
+  p.ring = w + kWsHeader;  // counter region, first half
+  p.cnt2 = reinterpret_cast<uint32_t*>(w + kWsHeader) + kWsCounters / 2;
   p.part = w + pl.off_part1;
   p.xch = w + pl.off_part2;
   p.nch = pl.nch1;
-  p.G = pl.nch2;
+  p.G = walk_blocks_per_sequence(B);
   p.vpc = pl.vpc1;
   p.nvec = pl.nvec;
   return launch_tree(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;

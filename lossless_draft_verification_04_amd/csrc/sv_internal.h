@@ -71,10 +71,10 @@ struct TreeParams {
   float* out_p;
   float* out_q;
   int32_t* err;
-  uint32_t* cnt1;  // walk barrier arrivals per sequence
   uint32_t* cnt2;  // walk exits per sequence
   void* part;
-  void* xch;       // walk slice exchange, [B][2][64] parts
+  void* xch;       // walk slice slots, [B][2][64] parts
+  void* ring;      // walk pass totals, [B][3] words in the zeroed counter region
   int32_t nch;
   int32_t G;       // walk blocks per sequence
   int64_t vpc, nvec;

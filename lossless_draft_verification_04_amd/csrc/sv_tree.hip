@@ -13,11 +13,10 @@
 // Two launches per call:
 //  1. stats: a block per (node, target|draft, row part) of every node that
 //     has children (leaf rows are skipped), streaming each row once.
-//  2. walk: G blocks per sequence (cooperative launch) replay the walk in
-//     lockstep: merge the parts of the node they stand on, decide its
-//     children in order, and split one pass over the node's row pair per
-//     rejection into slices; the slice sums are exchanged, so the final draw
-//     only re-reads one slice.
+//  2. walk: G blocks per sequence replay the walk in lockstep: merge the
+//     parts of the node they stand on, decide its children in order, and
+//     split one pass over the node's row pair per rejection into slices; the
+//     pass totals are exchanged, so the final draw only re-reads one slice.
 #include "sv_device.hpp"
 #include "sv_internal.h"
 
@@ -48,57 +47,96 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
 }
 
 // ---------------------------------------------------------------------------
-// Walk.  The G blocks of a sequence (G = 1 .. 64, co-resident by a
-// cooperative launch when G > 1) each own one slice of every row pass.
-// After a pass the blocks exchange their slice sums through device-scope
-// stores and meet at a per-sequence barrier; every block then holds the same
-// sums and, since every decision is a deterministic function of global data
-// and of those sums (same order, same arithmetic), every block replays the
-// identical walk.  Block 0 writes the per-child outputs; the owner of the
-// slice holding the draw searches it.
+// Walk.  The G blocks of a sequence (G = 1 .. 64, at most one block per
+// compute unit over the whole launch, so all of them are resident together)
+// each own one slice of every row pass.  After a pass the blocks add
+// (1 << 56) + round(slice sum * 2^54) into one 64-bit word of a 3-word ring
+// per sequence: the top byte counts arrivals, the rest is the pass total in
+// fixed point, so one device-scope atomic per block both delivers the sum and
+// marks the arrival, and the total is the same bit pattern in every block
+// whatever the arrival order.  Every decision is a deterministic function of
+// global data and of these totals, so every block replays the identical walk.
+// Slice sums also go to device-scope slots (read only for the final draw).
+// Block 0 writes the per-child outputs; the owner of the slice holding the
+// draw searches it.  Waits are bounded: a block that waits too long sets
+// SV_DERR_TIMEOUT and goes on.
 // ---------------------------------------------------------------------------
 constexpr int kWNT = 256;  // walk block
 constexpr int kMaxG = 64;  // walk blocks (slices) per sequence
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr int kMaxParts = 64;  // stats parts per row staged by the walk
+constexpr int kRing = 3;       // pass-total words per sequence
+constexpr double kFix = 18014398509481984.0;  // 2^54: totals up to 4 fit under the arrival byte
+constexpr uint64_t kArrive = 1ull << 56;
 
 struct WalkCtx {
   const TreeParams* a;
   int b, g, G;
   int64_t v0, v1;     // this block's slice of every row pass
-  uint32_t* arrive;   // per-sequence arrival counter (monotone within a call)
-  Partial* xch;       // [2][kMaxG] exchange slots of this sequence
+  uint64_t* ring;     // [kRing] pass-total words of this sequence
+  Partial* xch;       // [2][kMaxG] slice slots of this sequence
   int pass;           // exchanges so far
+  bool late;          // a wait ran out: later exchanges do not wait
 };
 
-// Exchange this block's slice part; afterwards s_m / s_s hold all G parts
-// (slice order) in every block of the sequence.
-__device__ void exchange(WalkCtx& w, const Partial& mine, float* s_m, double* s_s) {
+// Exchange this block's slice part.  Returns the fixed-point total of the
+// parts' s (meaningful for residual passes, whose s is in [0, 1]); the parts
+// themselves are left in the slots of this pass's parity.
+__device__ double exchange(WalkCtx& w, const Partial& mine, bool sum) {
+  __shared__ double s_total;
   Partial* slot = w.xch + (w.pass & 1) * kMaxG;
+  // slice sums of a residual lie in [0, 1] (up to rounding); anything else
+  // (a row error upstream) is clamped so it cannot reach the arrival byte
+  const double s_in = sum && mine.s > 0.0 ? fmin(mine.s, 2.0) : 0.0;
+  const uint64_t fixed = (uint64_t)llrint(s_in * kFix);
+  if (w.G == 1) {
+    if (threadIdx.x == 0) put_partial(slot, mine);
+    __syncthreads();
+    ++w.pass;
+    return (double)fixed / kFix;
+  }
   if (threadIdx.x == 0) put_partial(slot + w.g, mine);
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  if (threadIdx.x == 0 && w.G > 1) {
-    __hip_atomic_fetch_add(w.arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint32_t want = (uint32_t)w.G * (uint32_t)(w.pass + 1);
+  if (threadIdx.x == 0) {
+    uint64_t* word = w.ring + (w.pass % kRing);
+    __hip_atomic_fetch_add(word, kArrive + fixed, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    uint64_t v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     uint32_t spins = 0;
-    while (__hip_atomic_load(w.arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < want) {
+    while (!w.late && (v >> 56) < (uint64_t)w.G) {
       if (++spins > kSpinLimit) {
         set_error(w.a->err, SV_DERR_TIMEOUT);
+        w.late = true;
         break;
       }
       __builtin_amdgcn_s_sleep(1);
+      v = __hip_atomic_load(word, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+    s_total = (double)(v & (kArrive - 1)) / kFix;
+    // every block has now added to this pass's word, hence has finished
+    // reading the previous one: block 0 clears it for reuse three passes on
+    if (w.g == 0 && w.pass >= 1) {
+      __hip_atomic_store(w.ring + ((w.pass - 1) % kRing), 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __builtin_amdgcn_s_waitcnt(0);
     }
   }
   __syncthreads();
+  const double t = s_total;
+  __syncthreads();
+  ++w.pass;
+  return t;
+}
+
+// Read the G slice parts of pass `pass` into s_m / s_s.
+__device__ void read_slices(const WalkCtx& w, int pass, float* s_m, double* s_s) {
+  const Partial* slot = w.xch + (pass & 1) * kMaxG;
   if (threadIdx.x < w.G) {
-    const Partial p = w.G > 1 ? get_partial(slot + threadIdx.x) : mine;
+    const Partial p = get_partial(slot + threadIdx.x);
     s_m[threadIdx.x] = p.m;
     s_s[threadIdx.x] = p.s;
   }
   __syncthreads();
-  ++w.pass;
 }
 
 // Draw from slice weights s_w (G of them, total `total`): locate the slice
@@ -141,9 +179,10 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     w.v0 = (int64_t)w.g * spv < a.nvec ? (int64_t)w.g * spv : a.nvec;
     w.v1 = w.v0 + spv < a.nvec ? w.v0 + spv : a.nvec;
   }
-  w.arrive = a.cnt1 + w.b;
+  w.ring = static_cast<uint64_t*>(a.ring) + (int64_t)w.b * kRing;
   w.xch = static_cast<Partial*>(a.xch) + (int64_t)w.b * 2 * kMaxG;
   w.pass = 0;
+  w.late = false;
   const int b = w.b;
   const bool writer = (w.g == 0);
   const int64_t rowbase = (int64_t)b * a.N;
@@ -193,7 +232,9 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       // bonus draw from P_node (not streamed by the stats pass): online slice
       // statistics, exchanged, then the draw with the merged shift
       const Partial st = range_stats<DT, kWNT, 4>(rowP, a.V, w.v0, w.v1, a.c);
-      exchange(w, st, s_m, s_s);
+      const int bp = w.pass;
+      exchange(w, st, false);
+      read_slices(w, bp, s_m, s_s);
       float M = kNegInf;
       for (int i = 0; i < w.G; ++i) M = fmaxf(M, s_m[i]);
       const float cm = a.c * M;
@@ -265,7 +306,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     sp.cmQ = Q.cm;
     sp.invSQ = Q.S > 0.0 ? (float)(1.0 / Q.S) : 0.f;
     double c = 0.0, D = 1.0, total = 0.0;
-    bool sums_ok = false;  // s_s holds the slice sums of the current residual
+    int sums_pass = -1;  // pass whose slice sums are those of the current residual
     int accepted = -1;
     for (int kk = 0; kk < nk; ++kk) {
       const int ch = s_kids[kk];
@@ -293,16 +334,15 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       mine.m = 0.f;
       mine.pad = 0.f;
       mine.s = range_weight_sum<DT, kWNT>(sp, a.V, w.v0, w.v1);
-      exchange(w, mine, s_m, s_s);
-      double G = 0.0;
-      for (int i = 0; i < w.G; ++i) G += s_s[i];
+      const int this_pass = w.pass;
+      const double G = exchange(w, mine, true);
       if (G > 0.0) {
         c = cn;
         D = G;
         total = G;
-        sums_ok = true;
+        sums_pass = this_pass;
       } else {
-        sums_ok = false;  // residual mass rounded to 0: keep the previous residual
+        sums_pass = -1;  // residual mass rounded to 0: keep the previous residual
       }
     }
     if (accepted >= 0) {
@@ -314,15 +354,15 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     }
     // every child rejected: draw from (p - c q)^+
     sp.coef = (float)c;
-    if (!sums_ok) {
+    if (sums_pass < 0) {
       Partial mine;
       mine.m = 0.f;
       mine.pad = 0.f;
       mine.s = range_weight_sum<DT, kWNT>(sp, a.V, w.v0, w.v1);
-      exchange(w, mine, s_m, s_s);
-      total = 0.0;
-      for (int i = 0; i < w.G; ++i) total += s_s[i];
+      sums_pass = w.pass;
+      total = exchange(w, mine, true);
     }
+    read_slices(w, sums_pass, s_m, s_s);
     t = slice_draw<DT>(w, sp, s_s, total, us);
     break;
   }
@@ -333,11 +373,11 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     if (threadIdx.x == 0) a.out_len[b] = depth;
   }
   if (t >= 0 && threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
-  // the last block of the sequence to leave resets its counters
+  // the last block of the sequence to leave clears the ring for the next call
   if (threadIdx.x == 0 && w.G > 1) {
     const uint32_t old = __hip_atomic_fetch_add(a.cnt2 + b, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     if (old == (uint32_t)w.G - 1) {
-      __hip_atomic_store(w.arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      for (int i = 0; i < kRing; ++i) __hip_atomic_store(w.ring + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       __hip_atomic_store(a.cnt2 + b, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
@@ -348,15 +388,11 @@ hipError_t launch_tree_t(const TreeParams& p, const Plan& plan, hipStream_t s) {
   tree_stats_kernel<DT><<<dim3((unsigned)plan.grid1), dim3(kTNT), 0, s>>>(p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  if (p.G == 1) {
-    tree_walk_kernel<DT><<<dim3((unsigned)plan.grid2), dim3(kWNT), 0, s>>>(p);
-    return hipGetLastError();
-  }
-  // G blocks per sequence wait on each other: they must be co-resident
-  TreeParams arg = p;
-  void* args[] = {&arg};
-  return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&tree_walk_kernel<DT>), dim3((unsigned)plan.grid2),
-                                    dim3(kWNT), args, 0, s);
+  // B * G <= compute units (chosen by the caller): the walk's blocks are all
+  // resident together on an otherwise idle device, and their waits are
+  // bounded either way
+  tree_walk_kernel<DT><<<dim3((unsigned)p.B * p.G), dim3(kWNT), 0, s>>>(p);
+  return hipGetLastError();
 }
 
 hipError_t launch_tree(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s) {
