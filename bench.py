@@ -43,7 +43,7 @@ ROTATE_BYTES = 2.2e9
 USE_GRAPHS = True
 PMC_RECORD = os.path.join(ROOT, "profiles", "chain_batched_pmc.json")
 KERNEL_SOURCES = [os.path.join(ROOT, "lossless_draft_verification_04_amd", "csrc", f)
-                  for f in ("sv_device.hpp", "sv_internal.h", "sv_api.hip", "sv_chain.hip")] + \
+                  for f in ("sv_device.hpp", "sv_walk.hpp", "sv_internal.h", "sv_api.hip", "sv_chain.hip")] + \
                  [os.path.join(ROOT, "include", "specverify.h")]
 METRIC = "verified draft positions/sec + achieved HBM GB/s (% of MI355X peak), 1 GPU"
 
@@ -358,7 +358,7 @@ def main():
         cpu["cores"] = 1
 
     rl = roofline(r["alg_bytes"], r["call_ms"])
-    rl["kernel"] = ("sv_verify_chain call (row-statistics + 2 draw kernels); duration = HIP events around the "
+    rl["kernel"] = ("sv_verify_chain call (row-statistics kernel + draw kernel); duration = HIP events around the "
                     "graph replays on the launch stream / calls")
     rl["alg_bytes_per_call"] = int(r["alg_bytes"])
     line = {

@@ -9,14 +9,14 @@
 
 #include "sv_device.hpp"
 #include "sv_internal.h"
+#include "sv_walk.hpp"
 
 namespace sv {
 
 namespace {
 
 constexpr int kBlockVecs = 1024;   // smallest row part (vectors): 4 in flight per thread of a 256-thread block
-constexpr int kMaxSampleParts = 512;  // parts of the draw pass per sequence (LDS staging in the sample kernel)
-constexpr int kDrawVecs = 256;        // smallest part of the draw pass (one vector per thread)
+constexpr int kMaxResident = 4096;  // bound on the blocks of a draw / walk launch (two slot words each)
 
 int env_int(const char* name, int dflt) {
   const char* v = std::getenv(name);
@@ -27,16 +27,17 @@ int env_int(const char* name, int dflt) {
 
 // Blocks the streaming passes aim for (the chip has 256 CUs; four blocks of
 // 256 threads per CU with four 16-byte loads in flight per thread keep the
-// HBM busy; fewer, longer parts also mean fewer parts to merge).  The draw
-// pass uses more, smaller parts so its final in-part search is short.
-// Overridable for tuning sweeps with SV_STATS_BLOCKS / SV_SAMPLE_BLOCKS.
+// HBM busy; fewer, longer parts also mean fewer parts to merge).
+// Overridable for tuning sweeps with SV_STATS_BLOCKS.
 int stats_blocks() {
   static const int v = env_int("SV_STATS_BLOCKS", 1024);
   return v;
 }
-int sample_blocks() {
-  static const int v = env_int("SV_SAMPLE_BLOCKS", 1024);
-  return v;
+// Upper bound on the draw / walk blocks per sequence (SV_DRAW_G caps it for
+// tuning sweeps).
+int draw_g_limit() {
+  static const int v = env_int("SV_DRAW_G", kMaxG);
+  return v < kMaxG ? v : kMaxG;
 }
 
 int per_vec(sv_dtype dt) { return dt == SV_BF16 ? 8 : 4; }
@@ -69,6 +70,43 @@ sv_status check_rows(const void* base, int64_t stride, int32_t V, sv_dtype dt) {
 
 bool bad_temperature(float T) { return !(T > 0.f) || !std::isfinite(T); }
 
+// slot words (two per block of a draw / walk launch) that fit in the first
+// half of the counter region
+constexpr int64_t kSlotWords = (int64_t)(kWsCounters / 2 * sizeof(uint32_t) / sizeof(uint64_t));
+static_assert(2 * (int64_t)kMaxResident <= kSlotWords, "slot words of a full launch fit the counter region");
+
+// Largest G a B-sequence launch may use (B * G <= kMaxResident).
+int32_t g_cap(int32_t B) {
+  if (B <= 0) return 1;
+  const int32_t g = kMaxResident / B;
+  return g < 1 ? 1 : (g > kMaxG ? kMaxG : g);
+}
+
+// Blocks per sequence of a draw / walk launch: as many as let all B * G
+// blocks be resident together (capacity = blocks the device holds at once),
+// within the slot region, and at most one per vector.
+int32_t choose_g(int32_t B, int64_t nvec, int capacity) {
+  if (B <= 0 || capacity <= 0) return 1;
+  int64_t g = capacity / B;
+  if (g > g_cap(B)) g = g_cap(B);
+  if (g > draw_g_limit()) g = draw_g_limit();
+  if (g > nvec) g = nvec;
+  return g < 1 ? 1 : (int32_t)g;
+}
+
+// G and the kernel variant: slices held in registers when they span at most
+// kSliceTiles tiles of 256 vectors at the held kernel's G, else streamed.
+void pick_slices(int32_t B, int64_t nvec, int cap_held, int cap_stream, int32_t* G, bool* held) {
+  const int32_t g = choose_g(B, nvec, cap_held);
+  if ((nvec + g - 1) / g <= (int64_t)kSliceTiles * 256) {
+    *G = g;
+    *held = true;
+  } else {
+    *G = choose_g(B, nvec, cap_stream);
+    *held = false;
+  }
+}
+
 sv_status plan_chain(sv_dtype dt, int32_t B, int32_t K, int32_t gamma, int32_t V, Plan* pl) {
   if (bad_dtype(dt)) return SV_EDTYPE;
   if (B < 0 || K < 1 || gamma < 1 || V < 1) return SV_EINVAL;
@@ -76,23 +114,13 @@ sv_status plan_chain(sv_dtype dt, int32_t B, int32_t K, int32_t gamma, int32_t V
   pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
   const int64_t rows = (int64_t)B * (K + 1) * gamma;
   split(rows, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
-  // the draw pass re-reads one part in its last block: keep parts small
-  split(B, pl->nvec, sample_blocks(), &pl->nch2, &pl->vpc2, kDrawVecs);
-  if (pl->nch2 > kMaxSampleParts) {
-    pl->vpc2 = (pl->nvec + kMaxSampleParts - 1) / kMaxSampleParts;
-    pl->nch2 = (int32_t)((pl->nvec + pl->vpc2 - 1) / pl->vpc2);
-  }
   pl->grid1 = rows * pl->nch1;
-  pl->grid2 = (int64_t)B * pl->nch2;
-  if (pl->grid1 > INT32_MAX || pl->grid2 > INT32_MAX) return SV_EUNSUPPORTED;
-  if ((int64_t)(K + 1) * gamma * pl->nch1 > UINT32_MAX / 2) return SV_EUNSUPPORTED;
+  if (pl->grid1 > INT32_MAX || (int64_t)B * kMaxG > INT32_MAX) return SV_EUNSUPPORTED;
   size_t off = kWsFixed;
   pl->off_part1 = off;
   off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
-  pl->off_jobs = off;
-  off = align_up(off + (size_t)B * 64, 256);
-  pl->off_part2 = off;
-  off = align_up(off + (size_t)B * pl->nch2 * sizeof(Partial), 256);
+  pl->off_part2 = off;  // gathered logits of the drafted tokens (target, then draft)
+  off = align_up(off + (size_t)2 * B * K * gamma * sizeof(float), 256);
   pl->bytes = off;
   return SV_OK;
 }
@@ -113,10 +141,7 @@ sv_status plan_greedy(sv_dtype dt, int32_t B, int32_t gamma, int32_t V, Plan* pl
   return SV_OK;
 }
 
-constexpr int kWalkMaxG = 64;     // walk blocks (one slice of every row pass each) per sequence
 constexpr int kWalkMaxParts = 64; // stats parts per row the walk stages
-constexpr int kWalkRing = 3;      // pass-total words per sequence (in the zeroed counter region)
-constexpr int32_t kWalkRingSeqs = (int32_t)(kWsCounters / 2 * sizeof(uint32_t) / (kWalkRing * sizeof(uint64_t)));
 
 sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, Plan* pl) {
   if (bad_dtype(dt)) return SV_EDTYPE;
@@ -136,25 +161,8 @@ sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, Plan* pl) {
   size_t off = kWsFixed;
   pl->off_part1 = off;
   off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
-  pl->off_part2 = off;  // walk slice slots
-  off = align_up(off + (size_t)B * 2 * kWalkMaxG * sizeof(Partial), 256);
   pl->bytes = off;
   return SV_OK;
-}
-
-// Walk blocks per sequence: the largest power of two (<= 64) with B * G at
-// most the device's compute-unit count, so one launch's walk blocks are all
-// resident together.  G > 1 needs the sequence's pass-total ring, which lives
-// in the first half of the counter region.
-int walk_blocks_per_sequence(int32_t B) {
-  if (B > kWalkRingSeqs) return 1;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
-    cus = 1;
-  int G = 1;
-  while (G * 2 <= kWalkMaxG && (int64_t)B * G * 2 <= cus) G *= 2;
-  return G;
 }
 
 sv_status plan_fanout(sv_dtype dt, int32_t R, int32_t V, int32_t F_max, Plan* pl) {
@@ -286,15 +294,14 @@ static sv_status verify_chain_like(const void* tgt, const void* drf, sv_dtype dt
   p.out_p = out_p;
   p.out_q = out_q;
   p.err = reinterpret_cast<int32_t*>(w);
-  p.cnt1 = reinterpret_cast<uint32_t*>(w + kWsHeader);
-  p.cnt2 = p.cnt1 + kWsCounters / 2;
   p.part1 = w + pl.off_part1;
-  p.jobs = w + pl.off_jobs;
-  p.part2 = w + pl.off_part2;
+  p.zg = reinterpret_cast<float*>(w + pl.off_part2);
+  p.zq = p.zg + (int64_t)B * K * gamma;
+  p.slots = w + kWsHeader;  // counter region, first half
+  p.cnt2 = reinterpret_cast<uint32_t*>(w + kWsHeader) + kWsCounters / 2;
   p.nch1 = pl.nch1;
-  p.nch2 = pl.nch2;
+  pick_slices(B, pl.nvec, chain_draw_capacity(dt, true), chain_draw_capacity(dt, false), &p.G, &p.held);
   p.vpc1 = pl.vpc1;
-  p.vpc2 = pl.vpc2;
   p.nvec = pl.nvec;
   return launch_chain(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
 }
@@ -381,12 +388,11 @@ sv_status sv_verify_tree(const void* tgt, const void* drf, sv_dtype dt, int64_t 
   p.out_p = out_p;
   p.out_q = out_q;
   p.err = reinterpret_cast<int32_t*>(w);
-  p.ring = w + kWsHeader;  // counter region, first half
+  p.slots = w + kWsHeader;  // counter region, first half
   p.cnt2 = reinterpret_cast<uint32_t*>(w + kWsHeader) + kWsCounters / 2;
   p.part = w + pl.off_part1;
-  p.xch = w + pl.off_part2;
   p.nch = pl.nch1;
-  p.G = walk_blocks_per_sequence(B);
+  pick_slices(B, pl.nvec, tree_walk_capacity(dt, true), tree_walk_capacity(dt, false), &p.G, &p.held);
   p.vpc = pl.vpc1;
   p.nvec = pl.nvec;
   return launch_tree(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;

@@ -31,13 +31,15 @@ struct ChainParams {
   float* out_p;
   float* out_q;
   int32_t* err;
-  uint32_t* cnt1;
-  uint32_t* cnt2;
-  void* part1;
-  void* jobs;
-  void* part2;
-  int32_t nch1, nch2;
-  int64_t vpc1, vpc2, nvec;
+  void* part1;     // stats parts, [B][rows][nch1]
+  float* zg;       // target logits of the drafted tokens, [B][K][gamma]
+  float* zq;       // draft logits of the drafted tokens, [B][K][gamma]
+  void* slots;     // draw slot words, [B][2][G] (zeroed counter region)
+  uint32_t* cnt2;  // draw exits per sequence (zeroed counter region)
+  int32_t nch1;
+  int32_t G;       // draw blocks per sequence
+  bool held;       // slices of at most kSliceTiles tiles, held in registers
+  int64_t vpc1, nvec;
 };
 
 struct GreedyParams {
@@ -73,10 +75,10 @@ struct TreeParams {
   int32_t* err;
   uint32_t* cnt2;  // walk exits per sequence
   void* part;
-  void* xch;       // walk slice slots, [B][2][64] parts
-  void* ring;      // walk pass totals, [B][3] words in the zeroed counter region
+  void* slots;     // walk slot words, [B][2][G] (zeroed counter region)
   int32_t nch;
   int32_t G;       // walk blocks per sequence
+  bool held;       // slices of at most kSliceTiles tiles, held in registers
   int64_t vpc, nvec;
 };
 
@@ -110,5 +112,19 @@ hipError_t launch_greedy(const GreedyParams& p, sv_dtype dt, const Plan& plan, h
 hipError_t launch_tree(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
 hipError_t launch_fanout(const FanoutParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
 hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s);
+
+// Blocks of one launch of the draw / walk kernel (held or streamed slices)
+// the current device holds at once (0 if unknown).
+int chain_draw_capacity(sv_dtype dt, bool held);
+int tree_walk_capacity(sv_dtype dt, bool held);
+
+// Blocks of kernel fn (block of nt threads) device dev holds at once.
+inline int device_capacity(const void* fn, int nt, int dev) {
+  int per_cu = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, fn, nt, 0) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  return per_cu * cus;
+}
 
 }  // namespace sv

@@ -1,0 +1,337 @@
+// sv_walk.hpp -- a sequence's draw split over G co-resident blocks.
+//
+// The final draw of every entry point is an inverse-CDF search in index order
+// over one weight row (draft-then-verify page §1 step 5 and §2.1: the
+// residual norm(max(0, p - q)) at the first rejection, or p_{gamma+1} when
+// every draft is accepted; for trees the residual after the rejected
+// siblings).  A row is split into G slices, one per block.  Each block holds
+// its slice in registers (up to kSliceTiles tiles of NT 16-byte vectors per
+// row; longer slices are re-read from memory on each use), sums its weights,
+// and the blocks exchange the slice sums; the block whose slice holds u * S
+// searches it.
+//
+// Exchange: one 64-bit slot word per (sequence, pass parity, block), in the
+// workspace region that is zero between calls.  After a pass each block
+// stores its value with the pass's tag in the low byte (a double with its
+// 8 lowest mantissa bits replaced, or a float in the high half) and its
+// first wave polls the G slots of the pass until every tag matches: one
+// device-scope store per block and no separate arrival counter.  Two pass
+// parities keep a slow block's slot from being overwritten while it is still
+// read; the last block of a sequence to leave clears its slots.  The G
+// blocks of a sequence must be resident together (the host sizes G so that
+// the whole launch fits on the device); waits are bounded and a block that
+// waits too long sets SV_DERR_TIMEOUT and stops waiting.
+#pragma once
+
+#include "sv_device.hpp"
+
+namespace sv {
+
+constexpr int kSliceTiles = 4;   // tiles per row a block holds in registers
+constexpr int kMaxG = 64;        // blocks (slices) per sequence
+constexpr uint32_t kSpinLimit = 1u << 22;
+constexpr uint64_t kTagMask = 0xffull;
+
+// Sum of N per-thread values over the block, each in a fixed order.
+template <int NT, int N>
+__device__ void block_sum_vec(const double* v, double* out) {
+  __shared__ double red[NT / kWave][N];
+  double x[N];
+#pragma unroll
+  for (int i = 0; i < N; ++i) x[i] = wave_sum(v[i]);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0)
+#pragma unroll
+    for (int i = 0; i < N; ++i) red[w][i] = x[i];
+  __syncthreads();
+#pragma unroll
+  for (int i = 0; i < N; ++i) {
+    double r = red[0][i];
+#pragma unroll
+    for (int k = 1; k < NT / kWave; ++k) r += red[k][i];
+    out[i] = r;
+  }
+}
+
+// One block's slice [v0, v1) of a row pair (rowQ null: a single row).
+// HELD: the slice spans at most kSliceTiles tiles and is kept in registers;
+// otherwise it is streamed from memory on each use (separate kernels, so the
+// streaming code's registers do not add to the held ones).
+template <int DT, int NT, bool HELD>
+struct Slice {
+  static constexpr int E = Fmt<DT>::kPerVec;
+  static constexpr int kT = HELD ? kSliceTiles : 1;
+  u32x4 p[kT], q[kT];
+  const void* rowP;
+  const void* rowQ;
+  int64_t v0, v1;
+  static constexpr bool held = HELD;
+
+  __device__ __forceinline__ void load(const void* rp, const void* rq, int64_t a, int64_t b) {
+    rowP = rp;
+    rowQ = rq;
+    v0 = a;
+    v1 = b > a ? b : a;
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      p[u] = u32x4{0u, 0u, 0u, 0u};
+      q[u] = p[u];
+    }
+    if constexpr (!HELD) return;
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      if (v0 + (int64_t)u * NT < v1) {  // block-uniform
+        const int64_t v = v0 + (int64_t)u * NT + threadIdx.x;
+        const int64_t vc = v < v1 ? v : v1 - 1;  // clamped: the loads are unconditional and overlap
+        p[u] = load_vec(rp, vc);
+        if (rq) q[u] = load_vec(rq, vc);
+      }
+    }
+  }
+
+  __device__ __forceinline__ bool valid(int u, int64_t* vi) const {
+    const int64_t v = v0 + (int64_t)u * NT + threadIdx.x;
+    *vi = v;
+    return v < v1;
+  }
+
+  // Sum of the draw weights of sp over the slice (block total, fixed order).
+  // sp.rowQ must be null, or the row pair the slice holds.
+  __device__ __forceinline__ double weight_sum(const DrawSpec& sp, int V) const {
+    if constexpr (!HELD) return range_weight_sum<DT, NT>(sp, V, v0, v1);
+    double acc = 0.0;
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      int64_t v;
+      if (valid(u, &v)) {
+        float w[E];
+        draw_weights_from<DT>(sp, V, v, p[u], q[u], w);
+        double own = 0.0;
+#pragma unroll
+        for (int e = 0; e < E; ++e) own += (double)w[e];
+        acc += own;
+      }
+    }
+    return block_sum<NT>(acc);
+  }
+
+  // Largest logit of row P over the slice (-inf if none).
+  __device__ __forceinline__ float max_logit(float c, int V) const {
+    if constexpr (!HELD) return range_stats<DT, NT, 4>(rowP, V, v0, v1, c).m;
+    float m = kNegInf;
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      int64_t v;
+      if (valid(u, &v)) {
+        float x[E];
+        unpack<DT>(p[u], x);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (v * E + e < V) m = fmaxf(m, x[e]);
+      }
+    }
+    return block_fmax<NT>(m);
+  }
+
+  // Inverse-CDF search over the slice in index order: the first element
+  // whose running weight exceeds `target`; if rounding leaves the target
+  // beyond the slice's weight, the last positive element (-1 if none).  The
+  // same index is returned in every thread.
+  // Last element with positive weight in held tile u of this thread (-1).
+  __device__ __forceinline__ int64_t last_positive(const DrawSpec& sp, int V, int u_sel) const {
+    int64_t last = -1;
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      int64_t v;
+      if ((u_sel < 0 || u == u_sel) && valid(u, &v)) {
+        float w[E];
+        draw_weights_from<DT>(sp, V, v, p[u], q[u], w);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (w[e] > 0.f) last = v * E + e;
+      }
+    }
+    return last;
+  }
+
+  __device__ __forceinline__ int64_t search(const DrawSpec& sp, int V, double target) const {
+    if constexpr (!HELD) return block_search<DT, NT>(sp, V, v0, v1, target);
+    double own[kT];
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      own[u] = 0.0;
+      int64_t v;
+      if (valid(u, &v)) {
+        float w[E];
+        draw_weights_from<DT>(sp, V, v, p[u], q[u], w);
+#pragma unroll
+        for (int e = 0; e < E; ++e) own[u] += (double)w[e];
+      }
+    }
+    double tot[kT];
+    block_sum_vec<NT, kT>(own, tot);
+    double cum = 0.0, loc = 0.0;
+    int pick = -1;
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      if (pick < 0 && cum + tot[u] > target) {
+        pick = u;
+        loc = target - cum;
+      }
+      cum += tot[u];
+    }
+    if (pick < 0) return block_max_i64<NT>(last_positive(sp, V, -1));
+    // the picked tile (block-uniform); every tile index stays a constant so
+    // the held vectors stay in registers
+    int64_t result = -1;
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      if (u == pick) {
+        double excl;
+        block_exclusive_scan<NT>(own[u], &excl);
+        const double t_local = loc - excl;
+        int64_t found = INT64_MAX;
+        int64_t v;
+        if (valid(u, &v) && own[u] > 0.0 && t_local >= 0.0 && t_local < own[u]) {
+          float w[E];
+          draw_weights_from<DT>(sp, V, v, p[u], q[u], w);
+          double run = 0.0;
+          int64_t last = -1;
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            run += (double)w[e];
+            if (found == INT64_MAX && run > t_local) found = v * E + e;
+            if (w[e] > 0.f) last = v * E + e;
+          }
+          if (found == INT64_MAX) found = last;
+        }
+        const int64_t r = block_min_i64<NT>(found);
+        // rounding left the target past every thread: the tile's last positive element
+        result = r != INT64_MAX ? r : block_max_i64<NT>(last_positive(sp, V, u));
+      }
+    }
+    return result;
+  }
+};
+
+// Exchange state of one block.
+struct Exchange {
+  uint64_t* slots;  // [2][G] slot words of this sequence, zero between calls
+  int32_t* err;
+  int G, g;
+  int pass;   // exchanges so far
+  bool late;  // a wait ran out: later exchanges do not wait (first wave only)
+};
+
+__device__ __forceinline__ Exchange make_exchange(void* slots, int32_t* err, int b, int G, int g) {
+  Exchange x;
+  x.slots = static_cast<uint64_t*>(slots) + (int64_t)b * 2 * G;
+  x.err = err;
+  x.G = G;
+  x.g = g;
+  x.pass = 0;
+  x.late = false;
+  return x;
+}
+
+__device__ __forceinline__ uint64_t pack_sum(double v) {
+  return (uint64_t)__double_as_longlong(v > 0.0 ? v : 0.0) & ~kTagMask;
+}
+__device__ __forceinline__ double unpack_sum(uint64_t w) { return __longlong_as_double((long long)(w & ~kTagMask)); }
+__device__ __forceinline__ uint64_t pack_max(float m) { return (uint64_t)__float_as_uint(m) << 32; }
+__device__ __forceinline__ float unpack_max(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
+
+// Publish this block's payload (low byte zero) for the current pass and
+// wait for the G payloads of the pass, left (without tags) in s_words[0..G).
+__device__ __forceinline__ void exchange(Exchange& x, uint64_t payload, uint64_t* s_words) {
+  const uint64_t tag = (uint64_t)(x.pass % 254) + 1;
+  __syncthreads();  // every wave is done with the previous exchange's s_words
+  if (threadIdx.x < kWave) {
+    const int l = threadIdx.x;
+    uint64_t* set = x.slots + (x.pass & 1) * x.G;
+    uint64_t w = payload;
+    bool ok = (l >= x.G) || (l == x.g);
+    if (x.G > 1) {
+      if (l == x.g) st_dev(set + l, payload | tag);
+      uint32_t spins = 0;
+      for (;;) {
+        if (!ok) {
+          w = ld_dev(set + l);
+          ok = (w & kTagMask) == tag;
+        }
+        if (__all(ok) || x.late) break;
+        if (++spins > kSpinLimit) {
+          if (l == 0) set_error(x.err, SV_DERR_TIMEOUT);
+          x.late = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+      }
+    }
+    if (l < x.G) s_words[l] = w & ~kTagMask;
+  }
+  __syncthreads();
+  ++x.pass;
+}
+
+// Slice values v_l = s_val[l] (l < G, in slice order): every wave computes
+// the same inclusive scan, so every thread gets the same total, and, for a
+// target, the slice holding it and the offset into it.  Rounding past the
+// end picks the end of the last slice with positive weight.
+__device__ __forceinline__ double slice_scan(const double* s_val, int G, double target, int* pick, double* loc) {
+  const int l = threadIdx.x & (kWave - 1);
+  const double v = l < G ? s_val[l] : 0.0;
+  double inc = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const double y = __shfl_up(inc, o, kWave);
+    if (l >= o) inc += y;
+  }
+  const double total = __shfl(inc, G - 1, kWave);
+  const uint64_t over = __ballot(l < G && inc > target);
+  if (over) {
+    const int p = __builtin_ctzll(over);
+    *pick = p;
+    *loc = target - (__shfl(inc, p, kWave) - __shfl(v, p, kWave));
+  } else {
+    const uint64_t pos = __ballot(l < G && v > 0.0);
+    const int p = pos ? 63 - __builtin_clzll(pos) : 0;
+    *pick = p;
+    *loc = __shfl(v, p, kWave);  // its end
+  }
+  return total;
+}
+
+// Exchange slice sums: every thread gets the total; s_val[0..G) holds the
+// slice values (for a later slice_scan).
+__device__ __forceinline__ double exchange_sum(Exchange& x, double mine, uint64_t* s_words, double* s_val) {
+  exchange(x, pack_sum(mine), s_words);
+  if ((int)threadIdx.x < x.G) s_val[threadIdx.x] = unpack_sum(s_words[threadIdx.x]);
+  __syncthreads();
+  int pick;
+  double loc;
+  return slice_scan(s_val, x.G, 0.0, &pick, &loc);
+}
+
+// Exchange slice maxima: every thread gets the maximum.
+__device__ __forceinline__ float exchange_max(Exchange& x, float mine, uint64_t* s_words) {
+  exchange(x, pack_max(mine), s_words);
+  const int l = threadIdx.x & (kWave - 1);
+  float m = l < x.G ? unpack_max(s_words[l]) : kNegInf;
+  return wave_fmax(m);
+}
+
+// Leave the exchange: the last block of the sequence to leave clears its
+// slot words (and its exit counter) for the next call.
+__device__ __forceinline__ void leave(Exchange& x, uint32_t* exit_counter) {
+  if (threadIdx.x == 0 && x.G > 1) {
+    const uint32_t old = __hip_atomic_fetch_add(exit_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (old == (uint32_t)x.G - 1) {
+      for (int i = 0; i < 2 * x.G; ++i) __hip_atomic_store(x.slots + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(exit_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+}
+
+}  // namespace sv

@@ -69,6 +69,20 @@ def test_chain_masked_logits():
         assert torch.isfinite(row[t[b]])
 
 
+def test_chain_one_draw_block_per_sequence():
+    # more sequences than the device holds draw blocks at once: G = 1
+    wl = W.chain_normal(B=1100, gamma=2, V=300, T=1.0, dtype="bf16", seed=17)
+    PT.chain(wl, 4, 1)
+    PT.device_error_clear()
+
+
+def test_chain_streamed_slices():
+    # slices longer than a block holds in registers: the streamed draw
+    wl = W.chain_zipf(B=400, gamma=2, V=50000, T=0.9, seed=18)
+    PT.chain(wl, 6, 0)
+    PT.device_error_clear()
+
+
 def test_chain_full_batched_workload():
     wl = W.chain_zipf(**W.CHAIN_BATCHED)
     for seed, rnd in [(0, 0), (5, 2)]:
@@ -160,10 +174,17 @@ def test_tree_small_shapes():
         PT.tree(wl, 7, 1)
 
 
-@pytest.mark.parametrize("B", [70, 130])  # 2 walk blocks per sequence, and 1
+@pytest.mark.parametrize("B", [70, 300])  # a few walk blocks per sequence, and one
 def test_tree_many_sequences(B):
     wl = W.tree_zipf(B=B, N=12, max_depth=5, V=2500, T=1.0, seed=44 + B)
     PT.tree(wl, 3, 0)
+    PT.device_error_clear()
+
+
+def test_tree_streamed_slices():
+    # slices longer than a block holds in registers: the streamed walk
+    wl = W.tree_zipf(B=70, N=10, max_depth=4, V=40000, T=1.0, seed=47)
+    PT.tree(wl, 5, 0)
     PT.device_error_clear()
 
 
