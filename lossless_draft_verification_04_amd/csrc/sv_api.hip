@@ -70,11 +70,6 @@ sv_status check_rows(const void* base, int64_t stride, int32_t V, sv_dtype dt) {
 
 bool bad_temperature(float T) { return !(T > 0.f) || !std::isfinite(T); }
 
-// slot words (two per block of a draw / walk launch) that fit in the first
-// half of the counter region
-constexpr int64_t kSlotWords = (int64_t)(kWsCounters / 2 * sizeof(uint32_t) / sizeof(uint64_t));
-static_assert(2 * (int64_t)kMaxResident <= kSlotWords, "slot words of a full launch fit the counter region");
-
 // Largest G a B-sequence launch may use (B * G <= kMaxResident).
 int32_t g_cap(int32_t B) {
   if (B <= 0) return 1;
@@ -121,6 +116,8 @@ sv_status plan_chain(sv_dtype dt, int32_t B, int32_t K, int32_t gamma, int32_t V
   off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
   pl->off_part2 = off;  // gathered logits of the drafted tokens (target, then draft)
   off = align_up(off + (size_t)2 * B * K * gamma * sizeof(float), 256);
+  pl->off_jobs = off;   // draw slot words
+  off = align_up(off + (size_t)B * 2 * g_cap(B) * sizeof(uint64_t), 256);
   pl->bytes = off;
   return SV_OK;
 }
@@ -161,6 +158,8 @@ sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, Plan* pl) {
   size_t off = kWsFixed;
   pl->off_part1 = off;
   off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
+  pl->off_jobs = off;  // walk slot words
+  off = align_up(off + (size_t)B * 2 * g_cap(B) * sizeof(uint64_t), 256);
   pl->bytes = off;
   return SV_OK;
 }
@@ -297,8 +296,7 @@ static sv_status verify_chain_like(const void* tgt, const void* drf, sv_dtype dt
   p.part1 = w + pl.off_part1;
   p.zg = reinterpret_cast<float*>(w + pl.off_part2);
   p.zq = p.zg + (int64_t)B * K * gamma;
-  p.slots = w + kWsHeader;  // counter region, first half
-  p.cnt2 = reinterpret_cast<uint32_t*>(w + kWsHeader) + kWsCounters / 2;
+  p.slots = w + pl.off_jobs;
   p.nch1 = pl.nch1;
   pick_slices(B, pl.nvec, chain_draw_capacity(dt, true), chain_draw_capacity(dt, false), &p.G, &p.held);
   p.vpc1 = pl.vpc1;
@@ -388,8 +386,7 @@ sv_status sv_verify_tree(const void* tgt, const void* drf, sv_dtype dt, int64_t 
   p.out_p = out_p;
   p.out_q = out_q;
   p.err = reinterpret_cast<int32_t*>(w);
-  p.slots = w + kWsHeader;  // counter region, first half
-  p.cnt2 = reinterpret_cast<uint32_t*>(w + kWsHeader) + kWsCounters / 2;
+  p.slots = w + pl.off_jobs;
   p.part = w + pl.off_part1;
   p.nch = pl.nch1;
   pick_slices(B, pl.nvec, tree_walk_capacity(dt, true), tree_walk_capacity(dt, false), &p.G, &p.held);

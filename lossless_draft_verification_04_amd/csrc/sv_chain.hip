@@ -49,6 +49,14 @@ struct StagedParts {
 __device__ __forceinline__ RowStat merge_staged(const StagedParts& st, bool staged, const Partial* gparts, int first,
                                                 int n, float c) {
   if (!staged) return merge_parts(gparts + first, n, c);
+  if (n == 1) {  // one part: the part is the row statistic
+    RowStat r;
+    r.pad = 0.f;
+    const float m = st.m[first];
+    r.cm = m == kNegInf ? 0.f : c * m;
+    r.S = m == kNegInf ? 0.0 : st.s[first];
+    return r;
+  }
   float M = kNegInf;
   for (int i = 0; i < n; ++i) M = fmaxf(M, st.m[first + i]);
   RowStat r;
@@ -182,6 +190,7 @@ __global__ __launch_bounds__(kNT) void chain_stats_kernel(ChainParams a) {
   const int ch = (int)(rem - (int64_t)lr * a.nch1);
   const int Kg = a.K * a.gamma;
   const bool is_tgt = lr < Kg;
+  zero_slots(a.slots, (int64_t)a.B * 2 * a.G, bid, kNT);  // for the draw launch
   const void* row;
   int j;
   if (is_tgt) {
@@ -253,11 +262,11 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
   sl.load(sp.rowP, resid ? sp.rowQ : nullptr, v0, v1);
   double total;
   if (resid) {
-    total = exchange_sum(x, sl.weight_sum(sp, a.V), s_words, s_val);
+    total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
     if (!(total > 0.0)) {
       // residual mass rounded to 0: draw from p_{n+1} itself
       sp.rowQ = nullptr;
-      total = exchange_sum(x, sl.weight_sum(sp, a.V), s_words, s_val);
+      total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
     }
   } else {
     // bonus draw (or a row without mass): the row's maximum from the
@@ -267,7 +276,7 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
     sp.rowQ = nullptr;
     sp.cmP = M == kNegInf ? 0.f : a.c * M;
     sp.invSP = 1.f;
-    total = exchange_sum(x, sl.weight_sum(sp, a.V), s_words, s_val);
+    total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
   }
   int pick;
   double loc;
@@ -276,7 +285,6 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
     const int64_t t = sl.search(sp, a.V, loc);
     if (threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
   }
-  leave(x, a.cnt2 + b);
 }
 
 template <int DT>

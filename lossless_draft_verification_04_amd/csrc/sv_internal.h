@@ -34,8 +34,7 @@ struct ChainParams {
   void* part1;     // stats parts, [B][rows][nch1]
   float* zg;       // target logits of the drafted tokens, [B][K][gamma]
   float* zq;       // draft logits of the drafted tokens, [B][K][gamma]
-  void* slots;     // draw slot words, [B][2][G] (zeroed counter region)
-  uint32_t* cnt2;  // draw exits per sequence (zeroed counter region)
+  void* slots;     // draw slot words, [B][2][G], zeroed by the stats launch
   int32_t nch1;
   int32_t G;       // draw blocks per sequence
   bool held;       // slices of at most kSliceTiles tiles, held in registers
@@ -73,9 +72,8 @@ struct TreeParams {
   float* out_p;
   float* out_q;
   int32_t* err;
-  uint32_t* cnt2;  // walk exits per sequence
   void* part;
-  void* slots;     // walk slot words, [B][2][G] (zeroed counter region)
+  void* slots;     // walk slot words, [B][2][G], zeroed by the stats launch
   int32_t nch;
   int32_t G;       // walk blocks per sequence
   bool held;       // slices of at most kSliceTiles tiles, held in registers

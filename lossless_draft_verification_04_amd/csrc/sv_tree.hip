@@ -38,6 +38,7 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
   rem -= (int64_t)u * per_node;
   const int which = (int)(rem / a.nch);
   const int ch = (int)(rem - (int64_t)which * a.nch);
+  zero_slots(a.slots, (int64_t)a.B * 2 * a.G, bid, kTNT);  // for the walk launch
   int has_kids = 0;
   for (int i = u + 1 + threadIdx.x; i < a.N; i += kTNT) has_kids |= (a.parent[(int64_t)b * a.N + i] == u);
   if (!__syncthreads_or(has_kids)) return;
@@ -130,7 +131,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       sp.cmQ = 0.f;
       sp.invSQ = 1.f;
       sp.coef = 0.f;
-      const double total = exchange_sum(x, sl.weight_sum(sp, a.V), s_words, s_val);
+      const double total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
       int pick;
       double loc;
       slice_scan(s_val, x.G, us * total, &pick, &loc);
@@ -210,7 +211,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       }
       const double cn = c + D;
       sp.coef = (float)cn;
-      const double Dn = exchange_sum(x, sl.weight_sum(sp, a.V), s_words, s_val);
+      const double Dn = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
       if (Dn > 0.0) {
         c = cn;
         D = Dn;
@@ -228,7 +229,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     }
     // every child rejected: draw from (p - c q)^+
     sp.coef = (float)c;
-    if (!sums_current) D = exchange_sum(x, sl.weight_sum(sp, a.V), s_words, s_val);
+    if (!sums_current) D = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
     int pick;
     double loc;
     slice_scan(s_val, x.G, us * D, &pick, &loc);
@@ -242,7 +243,6 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     if (threadIdx.x == 0) a.out_len[b] = depth;
   }
   if (t >= 0 && threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
-  leave(x, a.cnt2 + b);
 }
 
 template <int DT>

@@ -10,14 +10,14 @@
 // and the blocks exchange the slice sums; the block whose slice holds u * S
 // searches it.
 //
-// Exchange: one 64-bit slot word per (sequence, pass parity, block), in the
-// workspace region that is zero between calls.  After a pass each block
+// Exchange: one 64-bit slot word per (sequence, pass parity, block), zeroed
+// by the call's first launch.  After a pass each block
 // stores its value with the pass's tag in the low byte (a double with its
 // 8 lowest mantissa bits replaced, or a float in the high half) and its
 // first wave polls the G slots of the pass until every tag matches: one
 // device-scope store per block and no separate arrival counter.  Two pass
 // parities keep a slow block's slot from being overwritten while it is still
-// read; the last block of a sequence to leave clears its slots.  The G
+// read.  The G
 // blocks of a sequence must be resident together (the host sizes G so that
 // the whole launch fits on the device); waits are bounded and a block that
 // waits too long sets SV_DERR_TIMEOUT and stops waiting.
@@ -63,6 +63,8 @@ struct Slice {
   static constexpr int E = Fmt<DT>::kPerVec;
   static constexpr int kT = HELD ? kSliceTiles : 1;
   u32x4 p[kT], q[kT];
+  double own[kT];  // this thread's weight sum per tile (last prepare)
+  double tot[kT];  // the block's weight sum per tile (last prepare)
   const void* rowP;
   const void* rowQ;
   int64_t v0, v1;
@@ -96,24 +98,27 @@ struct Slice {
     return v < v1;
   }
 
-  // Sum of the draw weights of sp over the slice (block total, fixed order).
+  // Weight sums of sp over the slice: per thread and per tile (kept for a
+  // later search with the same sp) and the block total (fixed order).
   // sp.rowQ must be null, or the row pair the slice holds.
-  __device__ __forceinline__ double weight_sum(const DrawSpec& sp, int V) const {
+  __device__ __forceinline__ double prepare(const DrawSpec& sp, int V) {
     if constexpr (!HELD) return range_weight_sum<DT, NT>(sp, V, v0, v1);
-    double acc = 0.0;
 #pragma unroll
     for (int u = 0; u < kT; ++u) {
+      own[u] = 0.0;
       int64_t v;
       if (valid(u, &v)) {
         float w[E];
         draw_weights_from<DT>(sp, V, v, p[u], q[u], w);
-        double own = 0.0;
 #pragma unroll
-        for (int e = 0; e < E; ++e) own += (double)w[e];
-        acc += own;
+        for (int e = 0; e < E; ++e) own[u] += (double)w[e];
       }
     }
-    return block_sum<NT>(acc);
+    block_sum_vec<NT, kT>(own, tot);
+    double total = 0.0;
+#pragma unroll
+    for (int u = 0; u < kT; ++u) total += tot[u];
+    return total;
   }
 
   // Largest logit of row P over the slice (-inf if none).
@@ -134,11 +139,8 @@ struct Slice {
     return block_fmax<NT>(m);
   }
 
-  // Inverse-CDF search over the slice in index order: the first element
-  // whose running weight exceeds `target`; if rounding leaves the target
-  // beyond the slice's weight, the last positive element (-1 if none).  The
-  // same index is returned in every thread.
-  // Last element with positive weight in held tile u of this thread (-1).
+  // Last element with positive weight in held tile u_sel (every tile if
+  // negative) of this thread (-1 if none).
   __device__ __forceinline__ int64_t last_positive(const DrawSpec& sp, int V, int u_sel) const {
     int64_t last = -1;
 #pragma unroll
@@ -155,22 +157,12 @@ struct Slice {
     return last;
   }
 
+  // Inverse-CDF search over the slice in index order, with the sums of the
+  // last prepare (same sp): the first element whose running weight exceeds
+  // `target`; if rounding leaves the target beyond the slice's weight, the
+  // last positive element (-1 if none).  The same index in every thread.
   __device__ __forceinline__ int64_t search(const DrawSpec& sp, int V, double target) const {
     if constexpr (!HELD) return block_search<DT, NT>(sp, V, v0, v1, target);
-    double own[kT];
-#pragma unroll
-    for (int u = 0; u < kT; ++u) {
-      own[u] = 0.0;
-      int64_t v;
-      if (valid(u, &v)) {
-        float w[E];
-        draw_weights_from<DT>(sp, V, v, p[u], q[u], w);
-#pragma unroll
-        for (int e = 0; e < E; ++e) own[u] += (double)w[e];
-      }
-    }
-    double tot[kT];
-    block_sum_vec<NT, kT>(own, tot);
     double cum = 0.0, loc = 0.0;
     int pick = -1;
 #pragma unroll
@@ -217,7 +209,7 @@ struct Slice {
 
 // Exchange state of one block.
 struct Exchange {
-  uint64_t* slots;  // [2][G] slot words of this sequence, zero between calls
+  uint64_t* slots;  // [2][G] slot words of this sequence, zero at launch
   int32_t* err;
   int G, g;
   int pass;   // exchanges so far
@@ -322,16 +314,11 @@ __device__ __forceinline__ float exchange_max(Exchange& x, float mine, uint64_t*
   return wave_fmax(m);
 }
 
-// Leave the exchange: the last block of the sequence to leave clears its
-// slot words (and its exit counter) for the next call.
-__device__ __forceinline__ void leave(Exchange& x, uint32_t* exit_counter) {
-  if (threadIdx.x == 0 && x.G > 1) {
-    const uint32_t old = __hip_atomic_fetch_add(exit_counter, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (old == (uint32_t)x.G - 1) {
-      for (int i = 0; i < 2 * x.G; ++i) __hip_atomic_store(x.slots + i, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(exit_counter, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
+// Zero n slot words, spread over the blocks of a launch that precedes the
+// exchanges (one word per thread).
+__device__ __forceinline__ void zero_slots(void* slots, int64_t n, int64_t block, int nt) {
+  const int64_t i = block * nt + threadIdx.x;
+  if (i < n) static_cast<uint64_t*>(slots)[i] = 0ull;
 }
 
 }  // namespace sv
