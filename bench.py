@@ -9,8 +9,7 @@ serve a repeat.
 
 One HIP graph holds one call per input copy and the timed loop replays it
 (plus a tail graph) so that exactly `steps` calls run; host launch cost is
-then not in the step time (the eager rate is reported beside it).  The tree
-row uses eager calls (its walk is a cooperative launch).
+then not in the step time (the eager rate is reported beside it).
 
 Prints ONE JSON line.  `value` is verified draft positions per second (B *
 gamma per call).  `roofline` reports the call's algorithmic bytes (rows
@@ -215,13 +214,15 @@ def bench_multi(wl, steps, warmup):
 
 
 def tree_alg_bytes(wl, out):
-    """Rows of every node with children (target + draft), plus the rows the walk must re-read:
-    the node's row pair once per rejected child, or the last node's target row for a bonus draw.
-    Counted from one call's outputs (children tried = those with p(tok) written)."""
+    """Minimum HBM bytes of one call: the target and draft rows of every node with children (the row
+    statistics), plus the row pair of every node on the walked path where at least one child was
+    rejected (the residual passes and the final draw need that node's whole row pair), plus the target
+    row of the last node when the walk ends in a bonus draw.  Counted from one call's outputs: a
+    child was tried iff its p(tok) was written."""
     p = wl.params
     parent = wl.tensors["parent"]
     B, N = parent.shape
-    tried = (~torch.isnan(out["p"].cpu())).sum(1)
+    tried = ~torch.isnan(out["p"].cpu())
     length = out["len"].cpu()
     path = out["path"].cpu()
     rows = 0
@@ -229,8 +230,13 @@ def tree_alg_bytes(wl, out):
         par = parent[b].tolist()
         internal = set(x for x in par if x >= 0)
         rows += 2 * len(internal)
-        rows += 2 * int(tried[b] - length[b])  # one row-pair pass per rejection
-        last = int(path[b, length[b] - 1]) if length[b] > 0 else 0
+        walked = [0] + [int(path[b, d]) for d in range(int(length[b]))]
+        for i, node in enumerate(walked):
+            n_tried = sum(1 for c in range(1, N) if par[c] == node and bool(tried[b, c]))
+            accepted = 1 if i + 1 < len(walked) else 0
+            if n_tried - accepted > 0:
+                rows += 2  # the node's row pair, read once for its residual passes
+        last = walked[-1]
         if last not in internal or length[b] >= p["max_depth"]:
             rows += 1  # bonus draw from the last node's target row
     return rows * p["V"] * esize(p["dtype"])
@@ -246,7 +252,7 @@ def bench_tree(wl, steps, warmup):
     torch.cuda.synchronize()
     alg = tree_alg_bytes(wl, out)
     fn = lambda g: svx.sv_verify_tree(g["tgt"], g["drf"], g["tok"], g["parent"], p["max_depth"], T, want_pq=False)
-    wall, ev_ms = time_calls(fn, copies, steps, warmup)
+    wall, ev_ms = time_graphs(fn, copies, steps, warmup)
     pos = p["B"] * (p["N"] - 1)
     return dict(positions_per_call=pos, positions_per_s=pos / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
                 alg_bytes=alg, mean_accepted=float(out["len"].float().mean().item()), copies=len(copies))

@@ -117,7 +117,7 @@ sv_status plan_chain(sv_dtype dt, int32_t B, int32_t K, int32_t gamma, int32_t V
   pl->off_part2 = off;  // gathered logits of the drafted tokens (target, then draft)
   off = align_up(off + (size_t)2 * B * K * gamma * sizeof(float), 256);
   pl->off_jobs = off;   // draw slot words
-  off = align_up(off + (size_t)B * 2 * g_cap(B) * sizeof(uint64_t), 256);
+  off = align_up(off + (size_t)B * kSlotWords * g_cap(B) * sizeof(uint64_t), 256);
   pl->bytes = off;
   return SV_OK;
 }
@@ -159,7 +159,9 @@ sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, Plan* pl) {
   pl->off_part1 = off;
   off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
   pl->off_jobs = off;  // walk slot words
-  off = align_up(off + (size_t)B * 2 * g_cap(B) * sizeof(uint64_t), 256);
+  off = align_up(off + (size_t)B * kSlotWords * g_cap(B) * sizeof(uint64_t), 256);
+  pl->off_part2 = off;  // gathered child logits
+  off = align_up(off + (size_t)2 * B * N * sizeof(float), 256);
   pl->bytes = off;
   return SV_OK;
 }
@@ -387,6 +389,7 @@ sv_status sv_verify_tree(const void* tgt, const void* drf, sv_dtype dt, int64_t 
   p.out_q = out_q;
   p.err = reinterpret_cast<int32_t*>(w);
   p.slots = w + pl.off_jobs;
+  p.zc = reinterpret_cast<float*>(w + pl.off_part2);
   p.part = w + pl.off_part1;
   p.nch = pl.nch1;
   pick_slices(B, pl.nvec, tree_walk_capacity(dt, true), tree_walk_capacity(dt, false), &p.G, &p.held);

@@ -106,10 +106,10 @@ __device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_jo
       st.s[i] = pi.s;
     }
   }
-  __syncthreads();
+  lds_sync();
   for (int j = threadIdx.x; j < a.gamma; j += kNT)
     sQ[j] = merge_staged(st, staged, pb, (Kg + j) * a.nch1, a.nch1, a.c);
-  __syncthreads();
+  lds_sync();
   for (int k = wave; k < a.K; k += kNT / kWave) {
     bool acc = false;
     if (lane < a.gamma) {
@@ -149,7 +149,7 @@ __device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_jo
       if (writer && a.out_n_cand) a.out_n_cand[(int64_t)b * a.K + k] = n;
     }
   }
-  __syncthreads();
+  lds_sync();
   if (threadIdx.x == 0) {
     int best = 0;
     for (int k = 1; k < a.K; ++k)
@@ -176,7 +176,7 @@ __device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_jo
     jb.u = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
     *s_job = jb;
   }
-  __syncthreads();
+  lds_sync();
 }
 
 template <int DT>
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(kNT) void chain_stats_kernel(ChainParams a) {
   const int ch = (int)(rem - (int64_t)lr * a.nch1);
   const int Kg = a.K * a.gamma;
   const bool is_tgt = lr < Kg;
-  zero_slots(a.slots, (int64_t)a.B * 2 * a.G, bid, kNT);  // for the draw launch
+  zero_slots(a.slots, (int64_t)a.B * kSlotWords * a.G, bid, kNT);  // for the draw launch
   const void* row;
   int j;
   if (is_tgt) {
@@ -248,7 +248,7 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
   const int b = blockIdx.x / a.G;
   const int g = blockIdx.x - b * a.G;
   __shared__ Job s_job;
-  __shared__ uint64_t s_words[kMaxG];
+  __shared__ uint64_t s_words[kMaxG], s_w1[kMaxG];
   __shared__ double s_val[kMaxG];
   chain_decide<DT>(a, b, g == 0, &s_job);
   const Job jb = s_job;
@@ -261,6 +261,7 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
   Slice<DT, kNT, HELD> sl;
   sl.load(sp.rowP, resid ? sp.rowQ : nullptr, v0, v1);
   double total;
+  bool plain = false;
   if (resid) {
     total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
     if (!(total > 0.0)) {
@@ -269,19 +270,21 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
       total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
     }
   } else {
-    // bonus draw (or a row without mass): the row's maximum from the
-    // slices, then a plain draw with that shift
-    const float M = exchange_max(x, sl.max_logit(a.c, a.V), s_words);
+    // bonus draw (or a row without mass): the row's statistics from the
+    // slices in one exchange, then a plain draw with the row's shift
+    float M;
+    total = exchange_stats(x, sl.row_stats(a.c, a.V), a.c, s_words, s_w1, s_val, &M);
     if (g == 0 && threadIdx.x == 0 && M == kNegInf) set_error(a.err, SV_DERR_ROW);
     sp.rowQ = nullptr;
     sp.cmP = M == kNegInf ? 0.f : a.c * M;
     sp.invSP = 1.f;
-    total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
+    plain = true;
   }
   int pick;
   double loc;
   slice_scan(s_val, x.G, jb.u * total, &pick, &loc);
   if (pick == g) {
+    if (plain) sl.prepare(sp, a.V);  // the owner's weights under the row's shift
     const int64_t t = sl.search(sp, a.V, loc);
     if (threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
   }

@@ -118,6 +118,18 @@ __device__ __forceinline__ double accept_ratio(double p, double q) {
 // ---------------------------------------------------------------------------
 // Wave / block collectives (block of NT threads = NT/64 waves).
 // ---------------------------------------------------------------------------
+
+// Block barrier for data exchanged through LDS only: it waits for this
+// wave's LDS operations but not for its global loads or stores, so loads
+// issued ahead of it stay in flight (a plain __syncthreads also waits for
+// every outstanding global access, stores and loads being counted
+// together on this architecture).  Global memory shared between blocks is
+// ordered explicitly where it is handed off.
+__device__ __forceinline__ void lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
 template <typename T>
 __device__ __forceinline__ T wave_max(T v) {
 #pragma unroll
@@ -146,9 +158,9 @@ __device__ float block_fmax(float v) {
   __shared__ float red[NT / kWave];
   v = wave_fmax(v);
   const int w = threadIdx.x / kWave;
-  __syncthreads();
+  lds_sync();
   if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
-  __syncthreads();
+  lds_sync();
   float r = red[0];
 #pragma unroll
   for (int i = 1; i < NT / kWave; ++i) r = fmaxf(r, red[i]);
@@ -162,9 +174,9 @@ __device__ double block_sum(double v) {
   __shared__ double red[NT / kWave];
   v = wave_sum(v);
   const int w = threadIdx.x / kWave;
-  __syncthreads();
+  lds_sync();
   if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
-  __syncthreads();
+  lds_sync();
   double r = red[0];
 #pragma unroll
   for (int i = 1; i < NT / kWave; ++i) r += red[i];
@@ -176,9 +188,9 @@ __device__ int64_t block_max_i64(int64_t v) {
   __shared__ int64_t red[NT / kWave];
   v = wave_max(v);
   const int w = threadIdx.x / kWave;
-  __syncthreads();
+  lds_sync();
   if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
-  __syncthreads();
+  lds_sync();
   int64_t r = red[0];
 #pragma unroll
   for (int i = 1; i < NT / kWave; ++i) r = max(r, red[i]);
@@ -190,9 +202,9 @@ __device__ int64_t block_min_i64(int64_t v) {
   __shared__ int64_t red[NT / kWave];
   v = wave_min(v);
   const int w = threadIdx.x / kWave;
-  __syncthreads();
+  lds_sync();
   if ((threadIdx.x & (kWave - 1)) == 0) red[w] = v;
-  __syncthreads();
+  lds_sync();
   int64_t r = red[0];
 #pragma unroll
   for (int i = 1; i < NT / kWave; ++i) r = min(r, red[i]);
@@ -211,9 +223,9 @@ __device__ double block_exclusive_scan(double v, double* excl) {
     const double y = __shfl_up(inc, o, kWave);
     if (lane >= o) inc += y;
   }
-  __syncthreads();
+  lds_sync();
   if (lane == kWave - 1) wtot[w] = inc;
-  __syncthreads();
+  lds_sync();
   double before = 0.0, total = 0.0;
 #pragma unroll
   for (int i = 0; i < NT / kWave; ++i) {

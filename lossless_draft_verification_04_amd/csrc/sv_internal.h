@@ -34,7 +34,7 @@ struct ChainParams {
   void* part1;     // stats parts, [B][rows][nch1]
   float* zg;       // target logits of the drafted tokens, [B][K][gamma]
   float* zq;       // draft logits of the drafted tokens, [B][K][gamma]
-  void* slots;     // draw slot words, [B][2][G], zeroed by the stats launch
+  void* slots;     // draw slot words, [B][G][4], zeroed by the stats launch
   int32_t nch1;
   int32_t G;       // draw blocks per sequence
   bool held;       // slices of at most kSliceTiles tiles, held in registers
@@ -73,7 +73,8 @@ struct TreeParams {
   float* out_q;
   int32_t* err;
   void* part;
-  void* slots;     // walk slot words, [B][2][G], zeroed by the stats launch
+  float* zc;       // each child's logits under its parent's rows, [2][B][N] (target, draft)
+  void* slots;     // walk slot words, [B][G][4], zeroed by the stats launch
   int32_t nch;
   int32_t G;       // walk blocks per sequence
   bool held;       // slices of at most kSliceTiles tiles, held in registers

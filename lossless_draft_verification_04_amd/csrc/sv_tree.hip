@@ -11,13 +11,20 @@
 // residual; a node without children gives the bonus draw from its target row.
 //
 // Two launches per call:
-//  1. stats: a block per (node, target|draft, row part) of every node that
-//     has children (leaf rows are skipped), streaming each row once.
-//  2. walk: G blocks per sequence replay the walk in lockstep: merge the
-//     parts of the node they stand on, decide its children in order, and
-//     make one pass over their held slices of the node's row pair per
-//     rejection; the pass totals are exchanged, and the final draw searches
-//     one held slice.
+//  1. stats: a block per (node, target|draft, row part), laid out node-major
+//     so that the low-numbered nodes (parents precede their children, so in a
+//     breadth-first numbering these are the ones with children) are
+//     dispatched first and spread evenly over the compute units; blocks of
+//     nodes without children exit at once.  A working block streams its part
+//     of the row once; the first part of a row also gathers the row's logits
+//     at the node's children's tokens.
+//  2. walk: G blocks per sequence replay the walk in lockstep.  Each stages
+//     the tree, every node's row statistics and every child's logits in LDS
+//     once; at a node it computes all children's p, q and uniforms in
+//     parallel and, at the first rejection, loads its slice of the node's
+//     row pair into registers; each rejection is one pass over that slice,
+//     the pass totals are exchanged, and the final draw searches one held
+//     slice.
 #include "sv_device.hpp"
 #include "sv_internal.h"
 #include "sv_walk.hpp"
@@ -26,42 +33,62 @@ namespace sv {
 
 constexpr int kTNT = 256;
 constexpr int kTU = 4;
+constexpr int kGather = SV_MAX_N / kTNT;  // candidate children per stats thread
 
 template <int DT>
 __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
-  const int64_t per_node = 2 * (int64_t)a.nch;
-  const int64_t per_seq = (int64_t)a.N * per_node;
   const int64_t bid = blockIdx.x;
-  const int b = (int)(bid / per_seq);
-  int64_t rem = bid - (int64_t)b * per_seq;
-  const int u = (int)(rem / per_node);
-  rem -= (int64_t)u * per_node;
-  const int which = (int)(rem / a.nch);
-  const int ch = (int)(rem - (int64_t)which * a.nch);
-  zero_slots(a.slots, (int64_t)a.B * 2 * a.G, bid, kTNT);  // for the walk launch
+  const int ch = (int)(bid % a.nch);
+  int64_t rest = bid / a.nch;
+  const int which = (int)(rest & 1);
+  rest >>= 1;
+  const int b = (int)(rest % a.B);
+  const int u = (int)(rest / a.B);
+  zero_slots(a.slots, (int64_t)a.B * kSlotWords * a.G, bid, kTNT);  // for the walk launch
+  const int64_t rowbase = (int64_t)b * a.N;
+  const void* row = which ? row_ptr(a.drf, rowbase + u, a.drf_sb) : row_ptr(a.tgt, rowbase + u, a.tgt_sb);
+  // children of u; the first part of the row gathers its logits at their
+  // tokens (NaN for a token outside the vocabulary), issued before the stream
   int has_kids = 0;
-  for (int i = u + 1 + threadIdx.x; i < a.N; i += kTNT) has_kids |= (a.parent[(int64_t)b * a.N + i] == u);
+  int gi[kGather];
+  float zg[kGather];
+#pragma unroll
+  for (int k = 0; k < kGather; ++k) {
+    const int i = u + 1 + (int)threadIdx.x + k * kTNT;
+    gi[k] = -1;
+    zg[k] = 0.f;
+    if (i < a.N) {
+      const int32_t pi = a.parent[rowbase + i];
+      const int32_t x = a.tok[rowbase + i];
+      if (pi == u) {
+        has_kids = 1;
+        if (ch == 0) {
+          gi[k] = i;
+          zg[k] = (x >= 0 && x < a.V) ? load_elem<DT>(row, x) : __builtin_nanf("");
+        }
+      }
+    }
+  }
   if (!__syncthreads_or(has_kids)) return;
-  const void* row = which ? row_ptr(a.drf, (int64_t)b * a.N + u, a.drf_sb) : row_ptr(a.tgt, (int64_t)b * a.N + u, a.tgt_sb);
   const int64_t v0 = (int64_t)ch * a.vpc;
   const int64_t v1 = v0 + a.vpc < a.nvec ? v0 + a.vpc : a.nvec;
   const Partial part = range_stats<DT, kTNT, kTU>(row, a.V, v0, v1, a.c);
-  if (threadIdx.x == 0) put_partial(static_cast<Partial*>(a.part) + (((int64_t)b * a.N + u) * 2 + which) * a.nch + ch, part);
+  if (threadIdx.x == 0) put_partial(static_cast<Partial*>(a.part) + ((rowbase + u) * 2 + which) * a.nch + ch, part);
+  float* zc = a.zc + (int64_t)which * a.B * a.N + rowbase;
+#pragma unroll
+  for (int k = 0; k < kGather; ++k)
+    if (gi[k] >= 0) zc[gi[k]] = zg[k];
 }
 
 // ---------------------------------------------------------------------------
 // Walk.  The G blocks of a sequence each own one slice of every row the walk
-// draws from (sv_walk.hpp) and replay the walk in lockstep.  At each node a
-// block loads its slice of the node's target and draft rows into registers
-// once, together with the node's statistics parts and its children's
-// logits; every rejection is then one pass over the held slice and one
-// exchange of the slice sums.  Every decision is a deterministic function of
-// global data and of the exchanged totals (the same bit pattern in every
-// block), so every block walks the identical path.  Block 0 writes the
-// per-child outputs; the owner of the slice holding the draw searches it.
+// draws from (sv_walk.hpp) and replay the walk in lockstep.  Every decision
+// is a deterministic function of global data and of the exchanged totals
+// (the same bits in every block), so every block walks the identical path.
+// Block 0 writes the per-child outputs; the owner of the slice holding the
+// draw searches it.
 // ---------------------------------------------------------------------------
-constexpr int kWNT = 256;      // walk block
-constexpr int kMaxParts = 64;  // stats parts per row staged by the walk
+constexpr int kWNT = 256;  // walk block
 
 template <int DT, bool HELD>
 __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
@@ -75,26 +102,52 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   const int64_t rowbase = (int64_t)b * a.N;
   const Partial* parts = static_cast<const Partial*>(a.part);
   __shared__ int32_t s_par[SV_MAX_N];
-  __shared__ int32_t s_tok[SV_MAX_N];
   __shared__ int s_kids[SV_MAX_N];
   __shared__ int32_t s_path[SV_MAX_N];
-  __shared__ float s_zp[SV_MAX_N], s_zq[SV_MAX_N];
-  __shared__ float s_pm[2 * kMaxParts];
-  __shared__ double s_ps[2 * kMaxParts];
-  __shared__ RowStat s_P, s_Q;
-  __shared__ uint64_t s_words[kMaxG];
+  __shared__ float s_zp[SV_MAX_N], s_zq[SV_MAX_N];  // each child's logits under its parent's rows
+  __shared__ float s_cm[2][SV_MAX_N];                // row statistics of the nodes with children
+  __shared__ double s_S[2][SV_MAX_N];
+  __shared__ double s_pt[SV_MAX_N], s_qt[SV_MAX_N];  // the current node's children, in order
+  __shared__ float s_r[SV_MAX_N];
+  __shared__ uint64_t s_w0[kMaxG], s_w1[kMaxG];
   __shared__ double s_val[kMaxG];
   __shared__ int s_cnt;
   const double us = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
 
-  // the tree's shape and tokens, once
+  // the tree, the gathered logits and every node's row statistic, in one
+  // round of loads (parts and logits of nodes without children were not
+  // written and are never used)
+  const float* zc = a.zc + rowbase;
   for (int i = threadIdx.x; i < a.N; i += kWNT) {
-    const int32_t pi = a.parent[rowbase + i];
-    s_par[i] = pi;
-    s_tok[i] = a.tok[rowbase + i];
-    if (writer && i > 0 && (pi < 0 || pi >= i)) set_error(a.err, SV_DERR_TREE);
+    s_par[i] = a.parent[rowbase + i];
+    s_zp[i] = zc[i];
+    s_zq[i] = zc[(int64_t)a.B * a.N + i];
   }
-  __syncthreads();
+  for (int r = threadIdx.x; r < 2 * (a.N - 1); r += kWNT) {
+    const int u = r >> 1, which = r & 1;
+    const Partial* pr = parts + ((rowbase + u) * 2 + which) * a.nch;  // written by the previous launch
+    float M = kNegInf;
+    for (int i = 0; i < a.nch; ++i) M = fmaxf(M, pr[i].m);
+    float cm = 0.f;
+    double S = 0.0;
+    if (M != kNegInf) {
+      cm = a.c * M;
+      if (a.nch == 1) {
+        S = pr[0].s;
+      } else {
+        for (int i = 0; i < a.nch; ++i) {
+          const Partial pi = pr[i];
+          if (pi.m != kNegInf) S += pi.s * exp2((double)(a.c * pi.m) - (double)cm);
+        }
+      }
+    }
+    s_cm[which][u] = cm;
+    s_S[which][u] = S;
+  }
+  lds_sync();
+  if (writer)
+    for (int i = 1 + threadIdx.x; i < a.N; i += kWNT)
+      if (s_par[i] < 0 || s_par[i] >= i) set_error(a.err, SV_DERR_TREE);
 
   int node = 0, depth = 0;
   int64_t t = -1;
@@ -102,25 +155,26 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   for (;;) {
     // children of `node` in increasing index (from LDS)
     if (threadIdx.x == 0) s_cnt = 0;
-    __syncthreads();
+    lds_sync();
     for (int base = node + 1; base < a.N; base += kWNT) {
       const int i = base + (int)threadIdx.x;
       const int flag = (i < a.N) && s_par[i] == node;
       double excl;
       const double tot = block_exclusive_scan<kWNT>((double)flag, &excl);
       if (flag) s_kids[s_cnt + (int)excl] = i;
-      __syncthreads();
+      lds_sync();
       if (threadIdx.x == 0) s_cnt += (int)tot;
-      __syncthreads();
+      lds_sync();
     }
     const int nk = s_cnt;
     const void* rowP = row_ptr(a.tgt, rowbase + node, a.tgt_sb);
     if (nk == 0 || depth >= a.max_depth) {
       if (nk > 0 && writer) set_error(a.err, SV_DERR_TREE);
-      // bonus draw from P_node (not streamed by the stats pass): the row's
-      // maximum from the slices, then a plain draw with that shift
+      // bonus draw from P_node (not streamed by the stats pass): slice
+      // statistics in one exchange, then a plain draw with the row's shift
       sl.load(rowP, nullptr, v0, v1);
-      const float M = exchange_max(x, sl.max_logit(a.c, a.V), s_words);
+      float M;
+      const double total = exchange_stats(x, sl.row_stats(a.c, a.V), a.c, s_w0, s_w1, s_val, &M);
       if (M == kNegInf && writer && threadIdx.x == 0) set_error(a.err, SV_DERR_ROW);
       DrawSpec sp;
       sp.rowP = rowP;
@@ -131,53 +185,39 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       sp.cmQ = 0.f;
       sp.invSQ = 1.f;
       sp.coef = 0.f;
-      const double total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
       int pick;
       double loc;
       slice_scan(s_val, x.G, us * total, &pick, &loc);
-      if (pick == g) t = sl.search(sp, a.V, loc);
+      if (pick == g) {
+        sl.prepare(sp, a.V);
+        t = sl.search(sp, a.V, loc);
+      }
       break;
     }
     const void* rowQ = row_ptr(a.drf, rowbase + node, a.drf_sb);
-    // one round of loads: the held slice of the node's rows, its stats parts
-    // and every child's logits
-    sl.load(rowP, rowQ, v0, v1);
-    const int np = a.nch <= kMaxParts ? a.nch : kMaxParts;
-    const Partial* pn = parts + (rowbase + node) * 2 * a.nch;
-    for (int i = threadIdx.x; i < 2 * np; i += kWNT) {
-      const Partial pi = get_partial(pn + (i < np ? i : a.nch + (i - np)));
-      s_pm[i] = pi.m;
-      s_ps[i] = pi.s;
-    }
-    for (int k = threadIdx.x; k < nk; k += kWNT) {
-      const int32_t tk = s_tok[s_kids[k]];
-      float zp = 0.f, zq = 0.f;
-      if (tk >= 0 && tk < a.V) {
-        zp = load_elem<DT>(rowP, tk);
-        zq = load_elem<DT>(rowQ, tk);
-      }
-      s_zp[k] = zp;
-      s_zq[k] = zq;
-    }
-    __syncthreads();
-    if (threadIdx.x < 2) {
-      const float* pm = s_pm + threadIdx.x * np;
-      const double* ps = s_ps + threadIdx.x * np;
-      float M = kNegInf;
-      for (int i = 0; i < np; ++i) M = fmaxf(M, pm[i]);
-      RowStat r;
-      r.pad = 0.f;
-      r.cm = M == kNegInf ? 0.f : a.c * M;
-      double S = 0.0;
-      if (M != kNegInf)
-        for (int i = 0; i < np; ++i)
-          if (pm[i] != kNegInf) S += ps[i] * exp2((double)(a.c * pm[i]) - (double)r.cm);
-      r.S = S;
-      if (threadIdx.x == 0) s_P = r; else s_Q = r;
-    }
-    __syncthreads();
-    const RowStat P = s_P, Q = s_Q;
+    // every child's p, q and uniform in parallel; the held slice of the
+    // node's row pair is loaded at the first rejection
+    bool loaded = false;
+    RowStat P, Q;
+    P.cm = s_cm[0][node];
+    P.S = s_S[0][node];
+    Q.cm = s_cm[1][node];
+    Q.S = s_S[1][node];
+    P.pad = Q.pad = 0.f;
     if (writer && threadIdx.x == 0 && (!(P.S > 0.0) || !(Q.S > 0.0))) set_error(a.err, SV_DERR_ROW);
+    for (int k = threadIdx.x; k < nk; k += kWNT) {
+      const int cn = s_kids[k];
+      const float zp = s_zp[cn], zq = s_zq[cn];
+      double pt = 0.0, qt = 0.0;
+      if (!__builtin_isnan(zp)) {
+        pt = prob_of(zp, a.c, P);
+        qt = prob_of(zq, a.c, Q);
+      }
+      s_pt[k] = pt;
+      s_qt[k] = qt;
+      s_r[k] = (float)uniform24(a.seed, (uint32_t)cn, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
+    }
+    lds_sync();
     DrawSpec sp;
     sp.rowP = rowP;
     sp.rowQ = rowQ;
@@ -187,33 +227,30 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     sp.cmQ = Q.cm;
     sp.invSQ = Q.S > 0.0 ? (float)(1.0 / Q.S) : 0.f;
     double c = 0.0, D = 1.0;
-    bool sums_current = false;  // s_val holds the slice sums of the current residual
+    bool sums_current = false;  // the slice holds the sums of the current residual
     int accepted = -1;
     for (int kk = 0; kk < nk; ++kk) {
-      const int ch = s_kids[kk];
-      const int32_t tk = s_tok[ch];
-      double pt = 0.0, qt = 0.0;
-      if (tk >= 0 && tk < a.V) {
-        pt = prob_of(s_zp[kk], a.c, P);
-        qt = prob_of(s_zq[kk], a.c, Q);
-      } else if (writer && threadIdx.x == 0) {
-        set_error(a.err, SV_DERR_TOKEN);
-      }
+      const int cn = s_kids[kk];
+      const double pt = s_pt[kk], qt = s_qt[kk];
       if (writer && threadIdx.x == 0) {
-        if (a.out_p) a.out_p[rowbase + ch] = (float)pt;
-        if (a.out_q) a.out_q[rowbase + ch] = (float)qt;
+        if (__builtin_isnan(s_zp[cn])) set_error(a.err, SV_DERR_TOKEN);
+        if (a.out_p) a.out_p[rowbase + cn] = (float)pt;
+        if (a.out_q) a.out_q[rowbase + cn] = (float)qt;
       }
       const double pcur = fmax(0.0, pt - c * qt) / D;
-      const double r = uniform24(a.seed, (uint32_t)ch, (uint32_t)b, 0, a.round, 0);
-      if (r < accept_ratio(pcur, qt)) {
-        accepted = ch;
+      if ((double)s_r[kk] < accept_ratio(pcur, qt)) {
+        accepted = cn;
         break;
       }
-      const double cn = c + D;
-      sp.coef = (float)cn;
-      const double Dn = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
+      const double cnext = c + D;
+      sp.coef = (float)cnext;
+      if (!loaded) {
+        sl.load(rowP, rowQ, v0, v1);
+        loaded = true;
+      }
+      const double Dn = exchange_sum(x, sl.prepare(sp, a.V), s_w0, s_val);
       if (Dn > 0.0) {
-        c = cn;
+        c = cnext;
         D = Dn;
         sums_current = true;
       } else {
@@ -224,19 +261,20 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       if (threadIdx.x == 0) s_path[depth] = accepted;
       ++depth;
       node = accepted;
-      __syncthreads();
+      lds_sync();
       continue;
     }
     // every child rejected: draw from (p - c q)^+
     sp.coef = (float)c;
-    if (!sums_current) D = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
+    if (!loaded) sl.load(rowP, rowQ, v0, v1);  // (not reached: the last child was rejected)
+    if (!sums_current) D = exchange_sum(x, sl.prepare(sp, a.V), s_w0, s_val);
     int pick;
     double loc;
     slice_scan(s_val, x.G, us * D, &pick, &loc);
     if (pick == g) t = sl.search(sp, a.V, loc);
     break;
   }
-  __syncthreads();
+  lds_sync();
   if (writer) {
     for (int d = threadIdx.x; d < a.max_depth; d += kWNT)
       a.out_path[(int64_t)b * a.max_depth + d] = d < depth ? s_path[d] : -1;

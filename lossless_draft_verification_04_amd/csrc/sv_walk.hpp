@@ -10,17 +10,16 @@
 // and the blocks exchange the slice sums; the block whose slice holds u * S
 // searches it.
 //
-// Exchange: one 64-bit slot word per (sequence, pass parity, block), zeroed
-// by the call's first launch.  After a pass each block
-// stores its value with the pass's tag in the low byte (a double with its
-// 8 lowest mantissa bits replaced, or a float in the high half) and its
-// first wave polls the G slots of the pass until every tag matches: one
-// device-scope store per block and no separate arrival counter.  Two pass
-// parities keep a slow block's slot from being overwritten while it is still
-// read.  The G
-// blocks of a sequence must be resident together (the host sizes G so that
-// the whole launch fits on the device); waits are bounded and a block that
-// waits too long sets SV_DERR_TIMEOUT and stops waiting.
+// Exchange: two 64-bit slot words per (sequence, pass parity, block), zeroed
+// by the call's first launch.  After a pass each block stores its value(s)
+// with the pass's tag in the low byte (a double with its 8 lowest mantissa
+// bits replaced, or a float in the high half) and its first wave polls the G
+// slots of the pass until every tag matches: one or two device-scope stores
+// per block and no separate arrival counter.  Two pass parities keep a slow
+// block's slot from being overwritten while it is still read.  The G blocks
+// of a sequence must be resident together (the host sizes G so that the
+// whole launch fits on the device); waits are bounded and a block that waits
+// too long sets SV_DERR_TIMEOUT and stops waiting.
 #pragma once
 
 #include "sv_device.hpp"
@@ -40,11 +39,11 @@ __device__ void block_sum_vec(const double* v, double* out) {
 #pragma unroll
   for (int i = 0; i < N; ++i) x[i] = wave_sum(v[i]);
   const int w = threadIdx.x / kWave;
-  __syncthreads();
+  lds_sync();
   if ((threadIdx.x & (kWave - 1)) == 0)
 #pragma unroll
     for (int i = 0; i < N; ++i) red[w][i] = x[i];
-  __syncthreads();
+  lds_sync();
 #pragma unroll
   for (int i = 0; i < N; ++i) {
     double r = red[0][i];
@@ -119,6 +118,34 @@ struct Slice {
 #pragma unroll
     for (int u = 0; u < kT; ++u) total += tot[u];
     return total;
+  }
+
+  // (max, sum 2^(z c - c max)) of row P over the slice.
+  __device__ __forceinline__ Partial row_stats(float c, int V) const {
+    if constexpr (!HELD) return range_stats<DT, NT, 4>(rowP, V, v0, v1, c);
+    const float M = max_logit(c, V);
+    double s = 0.0;
+    if (M != kNegInf) {
+      const float cm = c * M;
+#pragma unroll
+      for (int u = 0; u < kT; ++u) {
+        int64_t v;
+        if (valid(u, &v)) {
+          float x[E];
+          unpack<DT>(p[u], x);
+          float acc = 0.f;
+#pragma unroll
+          for (int e = 0; e < E; ++e)
+            if (v * E + e < V) acc += fast_exp2(__builtin_fmaf(x[e], c, -cm));
+          s += (double)acc;
+        }
+      }
+    }
+    Partial r;
+    r.m = M;
+    r.pad = 0.f;
+    r.s = block_sum<NT>(s);
+    return r;
   }
 
   // Largest logit of row P over the slice (-inf if none).
@@ -209,16 +236,18 @@ struct Slice {
 
 // Exchange state of one block.
 struct Exchange {
-  uint64_t* slots;  // [2][G] slot words of this sequence, zero at launch
+  uint64_t* slots;  // [2 parities][G][2 words] of this sequence, zero at launch
   int32_t* err;
   int G, g;
   int pass;   // exchanges so far
   bool late;  // a wait ran out: later exchanges do not wait (first wave only)
 };
 
+constexpr int kSlotWords = 4;  // slot words per block of a launch (2 parities x 2 words)
+
 __device__ __forceinline__ Exchange make_exchange(void* slots, int32_t* err, int b, int G, int g) {
   Exchange x;
-  x.slots = static_cast<uint64_t*>(slots) + (int64_t)b * 2 * G;
+  x.slots = static_cast<uint64_t*>(slots) + (int64_t)b * kSlotWords * G;
   x.err = err;
   x.G = G;
   x.g = g;
@@ -234,23 +263,29 @@ __device__ __forceinline__ double unpack_sum(uint64_t w) { return __longlong_as_
 __device__ __forceinline__ uint64_t pack_max(float m) { return (uint64_t)__float_as_uint(m) << 32; }
 __device__ __forceinline__ float unpack_max(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
 
-// Publish this block's payload (low byte zero) for the current pass and
-// wait for the G payloads of the pass, left (without tags) in s_words[0..G).
-__device__ __forceinline__ void exchange(Exchange& x, uint64_t payload, uint64_t* s_words) {
+// Publish this block's payload(s) (low byte zero; NW = 1 or 2 words) for the
+// current pass and wait for the G blocks' payloads of the pass, left
+// (without tags) in s_w0[0..G) (and s_w1[0..G)).
+template <int NW>
+__device__ __forceinline__ void exchange_n(Exchange& x, uint64_t p0, uint64_t p1, uint64_t* s_w0, uint64_t* s_w1) {
   const uint64_t tag = (uint64_t)(x.pass % 254) + 1;
-  __syncthreads();  // every wave is done with the previous exchange's s_words
+  lds_sync();  // every wave is done with the previous exchange's words
   if (threadIdx.x < kWave) {
     const int l = threadIdx.x;
-    uint64_t* set = x.slots + (x.pass & 1) * x.G;
-    uint64_t w = payload;
+    uint64_t* set = x.slots + (int64_t)(x.pass & 1) * 2 * x.G;
+    uint64_t w0 = p0, w1 = p1;
     bool ok = (l >= x.G) || (l == x.g);
     if (x.G > 1) {
-      if (l == x.g) st_dev(set + l, payload | tag);
+      if (l == x.g) {
+        st_dev(set + 2 * l, p0 | tag);
+        if (NW == 2) st_dev(set + 2 * l + 1, p1 | tag);
+      }
       uint32_t spins = 0;
       for (;;) {
         if (!ok) {
-          w = ld_dev(set + l);
-          ok = (w & kTagMask) == tag;
+          w0 = ld_dev(set + 2 * l);
+          if (NW == 2) w1 = ld_dev(set + 2 * l + 1);
+          ok = (w0 & kTagMask) == tag && (NW == 1 || (w1 & kTagMask) == tag);
         }
         if (__all(ok) || x.late) break;
         if (++spins > kSpinLimit) {
@@ -261,10 +296,17 @@ __device__ __forceinline__ void exchange(Exchange& x, uint64_t payload, uint64_t
         __builtin_amdgcn_s_sleep(1);
       }
     }
-    if (l < x.G) s_words[l] = w & ~kTagMask;
+    if (l < x.G) {
+      s_w0[l] = w0 & ~kTagMask;
+      if (NW == 2) s_w1[l] = w1 & ~kTagMask;
+    }
   }
-  __syncthreads();
+  lds_sync();
   ++x.pass;
+}
+
+__device__ __forceinline__ void exchange(Exchange& x, uint64_t payload, uint64_t* s_words) {
+  exchange_n<1>(x, payload, 0ull, s_words, nullptr);
 }
 
 // Slice values v_l = s_val[l] (l < G, in slice order): every wave computes
@@ -300,7 +342,7 @@ __device__ __forceinline__ double slice_scan(const double* s_val, int G, double 
 __device__ __forceinline__ double exchange_sum(Exchange& x, double mine, uint64_t* s_words, double* s_val) {
   exchange(x, pack_sum(mine), s_words);
   if ((int)threadIdx.x < x.G) s_val[threadIdx.x] = unpack_sum(s_words[threadIdx.x]);
-  __syncthreads();
+  lds_sync();
   int pick;
   double loc;
   return slice_scan(s_val, x.G, 0.0, &pick, &loc);
@@ -312,6 +354,26 @@ __device__ __forceinline__ float exchange_max(Exchange& x, float mine, uint64_t*
   const int l = threadIdx.x & (kWave - 1);
   float m = l < x.G ? unpack_max(s_words[l]) : kNegInf;
   return wave_fmax(m);
+}
+
+// Exchange slice statistics (max m_l, sum s_l of 2^(z c - c m_l)): every
+// thread gets the row maximum M; s_val[0..G) holds the slice weights
+// s_l 2^(c m_l - c M) (for a later slice_scan) and the total is returned.
+__device__ __forceinline__ double exchange_stats(Exchange& x, const Partial& mine, float c, uint64_t* s_w0,
+                                                 uint64_t* s_w1, double* s_val, float* M_out) {
+  exchange_n<2>(x, pack_max(mine.m), pack_sum(mine.s), s_w0, s_w1);
+  const int l = threadIdx.x & (kWave - 1);
+  const float m = l < x.G ? unpack_max(s_w0[l]) : kNegInf;
+  const float M = wave_fmax(m);
+  *M_out = M;
+  if ((int)threadIdx.x < x.G)
+    s_val[threadIdx.x] = (m == kNegInf || M == kNegInf)
+                             ? 0.0
+                             : unpack_sum(s_w1[threadIdx.x]) * exp2((double)(c * m) - (double)(c * M));
+  lds_sync();
+  int pick;
+  double loc;
+  return slice_scan(s_val, x.G, 0.0, &pick, &loc);
 }
 
 // Zero n slot words, spread over the blocks of a launch that precedes the
