@@ -7,9 +7,10 @@ Inputs are resident in HBM before the timed region; distinct copies of the
 inputs (>= 2 GB in total) are rotated so the 256 MB last-level cache cannot
 serve a repeat.
 
-One HIP graph holds one call per input copy and the timed loop replays it
-(plus a tail graph) so that exactly `steps` calls run; host launch cost is
-then not in the step time (the eager rate is reported beside it).
+One HIP graph holds one call per input copy, repeated over the copies up to
+at least 32 calls, and the timed loop replays it (plus a tail graph) so that
+exactly `steps` calls run; host launch cost is then not in the step time
+(the eager rate is reported beside it).
 
 Prints ONE JSON line.  `value` is verified draft positions per second (B *
 gamma per call).  `roofline` reports the call's algorithmic bytes (rows
@@ -80,22 +81,24 @@ def time_calls(fn, copies, steps, warmup):
 
 
 def time_graphs(fn, copies, steps, warmup):
-    """Capture one HIP graph holding one call per input copy (and a tail graph
-    for steps % copies), replay them so that exactly `steps` calls run, and
-    bracket every replay with HIP events on the launch stream.
+    """Capture one HIP graph holding one call per input copy, repeated over the
+    copies until it holds at least 32 calls (and a tail graph for the
+    remainder), replay them so that exactly `steps` calls run, and bracket
+    every replay with HIP events on the launch stream.
 
     Returns (ms_per_step wall, mean event ms per call)."""
     if not USE_GRAPHS:
         return time_calls(fn, copies, steps, warmup)
     fn(copies[0])  # workspace and code objects exist before capture
     torch.cuda.synchronize()
-    L = len(copies)
+    L = len(copies) * max(1, -(-32 // len(copies)))
+    L = min(L, max(steps, 1))
 
     def capture(n):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
-            for c in copies[:n]:
-                fn(c)
+            for i in range(n):
+                fn(copies[i % len(copies)])
         return g
 
     full = capture(L)
@@ -384,8 +387,8 @@ def main():
                                "Zipf(1.1)+Gumbel target rows, draft noise sigma 0.5..2.5",
                    "B": 32, "gamma": 16, "V": 152064, "logits": "bf16", "device": dev_name,
                    "input_copies_rotated": r["copies"], "mean_accepted": round(r["mean_accepted"], 3),
-                   "launch": ("one HIP graph holds one call per input copy; the timed loop replays it so that "
-                              "exactly `steps` calls run" if USE_GRAPHS else "eager calls"),
+                   "launch": ("one HIP graph holds >= 32 calls rotating over the input copies; the timed loop "
+                              "replays it so that exactly `steps` calls run" if USE_GRAPHS else "eager calls"),
                    "eager_ms_per_step": round(r["eager_ms_per_step"], 5)},
         "roofline": rl,
         "cpu_baseline": cpu,

@@ -96,7 +96,7 @@ enum { SV_OP_CHAIN = 0, SV_OP_GREEDY = 1, SV_OP_MULTI = 2, SV_OP_TREE = 3, SV_OP
 #define SV_DERR_TREE 2         /* parent array invalid, or a path longer than max_depth */
 #define SV_DERR_FANOUT 4       /* F[r] outside [0, F_max] */
 #define SV_DERR_ROW 8          /* a needed row has no finite logit */
-#define SV_DERR_TIMEOUT 16     /* a tree walk block waited too long for its partners (results invalid) */
+#define SV_DERR_TIMEOUT 16     /* a draw or tree-walk block waited too long for its partners (results invalid) */
 
 int32_t sv_version(void);
 const char* sv_status_string(sv_status s);
