@@ -267,30 +267,46 @@ __device__ Partial range_stats(const void* row, int V, int64_t v0, int64_t v1, f
   float m = kNegInf;
   float s = 0.f;
   int64_t v = v0 + tid;
-  for (; v + (int64_t)(U - 1) * NT < vf; v += (int64_t)U * NT) {
-    u32x4 d[U];
+  if (v + (int64_t)(U - 1) * NT < vf) {
+    // software pipelined: the next U vectors are in flight while these are
+    // reduced (the prefetch past the end is clamped to the last full vector)
+    u32x4 cur[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) d[u] = load_vec(row, v + (int64_t)u * NT);
-    float x[U * E];
+    for (int u = 0; u < U; ++u) cur[u] = load_vec(row, v + (int64_t)u * NT);
+    for (;;) {
+      const int64_t vn = v + (int64_t)U * NT;
+      const bool more = vn + (int64_t)(U - 1) * NT < vf;
+      u32x4 nxt[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) unpack<DT>(d[u], x + u * E);
-    float gm = x[0];
+      for (int u = 0; u < U; ++u) {
+        const int64_t a = vn + (int64_t)u * NT;
+        nxt[u] = load_vec(row, a < vf ? a : vf - 1);
+      }
+      float x[U * E];
 #pragma unroll
-    for (int e = 1; e < U * E; ++e) gm = fmaxf(gm, x[e]);
-    if (gm > m) {
-      s *= fast_exp2(c * m - c * gm);
-      m = gm;
-    }
-    if (m != kNegInf) {
-      const float cm = c * m;
-      float t[U * E];
+      for (int u = 0; u < U; ++u) unpack<DT>(cur[u], x + u * E);
+      float gm = x[0];
 #pragma unroll
-      for (int e = 0; e < U * E; ++e) t[e] = fast_exp2(__builtin_fmaf(x[e], c, -cm));
+      for (int e = 1; e < U * E; ++e) gm = fmaxf(gm, x[e]);
+      if (gm > m) {
+        s *= fast_exp2(c * m - c * gm);
+        m = gm;
+      }
+      if (m != kNegInf) {
+        const float cm = c * m;
+        float t[U * E];
 #pragma unroll
-      for (int w = U * E / 2; w > 0; w >>= 1)
+        for (int e = 0; e < U * E; ++e) t[e] = fast_exp2(__builtin_fmaf(x[e], c, -cm));
 #pragma unroll
-        for (int e = 0; e < w; ++e) t[e] += t[e + w];
-      s += t[0];
+        for (int w = U * E / 2; w > 0; w >>= 1)
+#pragma unroll
+          for (int e = 0; e < w; ++e) t[e] += t[e + w];
+        s += t[0];
+      }
+      v = vn;
+      if (!more) break;
+#pragma unroll
+      for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     }
   }
   for (; v < v1; v += NT) {

@@ -7,7 +7,8 @@
 // One launch: a block per (row part).  Each wave keeps its current top-F in
 // registers, one entry per lane (lane i = i-th best), and streams its share of
 // the part in increasing index order.  The list starts as the top-F of the
-// wave's first 64-vector window (F rounds of a wave-wide selection).  After
+// wave's first 64-vector window (F rounds of a wave-wide selection, each a
+// DPP reduction).  After
 // that a lane's 16-byte vector is a candidate only if its largest element
 // beats the wave's F-th best so far (elements are seen in index order, so an
 // equal value can never displace an earlier entry); a candidate lane flags
@@ -44,6 +45,45 @@ __device__ __forceinline__ bool top_better(float va, int32_t ia, float vb, int32
   return va > vb || (va == vb && ia < ib);
 }
 
+// DPP data movement within a wave (one VALU instruction each; a lane whose
+// source is outside the pattern keeps `old`).
+template <int CTRL, int ROWS>
+__device__ __forceinline__ int32_t dpp_i(int32_t old, int32_t v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROWS, 0xF, false);
+}
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_f(float old, float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWS, 0xF, false));
+}
+constexpr int kWaveShr1 = 0x138;  // lane l takes lane l - 1
+constexpr int kRowShr = 0x110;    // + n: lane l takes lane l - n within its row of 16
+constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
+
+// (v, i) <- the better of itself and the pair DPP pattern CTRL brings in.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void best_step(float& v, int32_t& i) {
+  const float ov = dpp_f<CTRL, ROWS>(v, v);
+  const int32_t oi = dpp_i<CTRL, ROWS>(i, i);
+  if (oi != kNoIdx && (i == kNoIdx || top_better(ov, oi, v, i))) {
+    v = ov;
+    i = oi;
+  }
+}
+
+// The wave's best pair (value desc, index asc; kNoIdx never wins), in
+// every lane: a reduction within rows of 16, then across rows, ending in
+// lane 63.
+__device__ __forceinline__ void wave_best(float& v, int32_t& i) {
+  best_step<kRowShr + 1, 0xF>(v, i);
+  best_step<kRowShr + 2, 0xF>(v, i);
+  best_step<kRowShr + 4, 0xF>(v, i);
+  best_step<kRowShr + 8, 0xF>(v, i);
+  best_step<kRowBcast15, 0xA>(v, i);
+  best_step<kRowBcast31, 0xC>(v, i);
+  v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
+  i = __builtin_amdgcn_readlane(i, kWave - 1);
+}
+
 // Insert (v, i) into the wave's sorted list (lane l holds entry l; lanes
 // >= F hold the empty entry).  Wave-uniform arguments.
 __device__ __forceinline__ void wave_insert(float& lv, int32_t& li, float v, int32_t i, int F, int lane) {
@@ -51,8 +91,8 @@ __device__ __forceinline__ void wave_insert(float& lv, int32_t& li, float v, int
   const uint64_t m = __ballot(here);
   if (!m) return;
   const int pos = __builtin_ctzll(m);
-  const float up_v = __shfl_up(lv, 1, kWave);
-  const int32_t up_i = __shfl_up(li, 1, kWave);
+  const float up_v = dpp_f<kWaveShr1, 0xF>(lv, lv);
+  const int32_t up_i = dpp_i<kWaveShr1, 0xF>(li, li);
   if (lane < F) {
     if (lane > pos) {
       lv = up_v;
@@ -132,15 +172,7 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
             }
             float wv = bv;
             int32_t wi = bi;
-#pragma unroll
-            for (int o = 32; o > 0; o >>= 1) {
-              const float ov = __shfl_xor(wv, o, kWave);
-              const int32_t oi = __shfl_xor(wi, o, kWave);
-              if (oi != kNoIdx && (wi == kNoIdx || top_better(ov, oi, wv, wi))) {
-                wv = ov;
-                wi = oi;
-              }
-            }
+            wave_best(wv, wi);
             if (wi == kNoIdx) break;  // the window has fewer than F elements
             if (lane == k) {
               lv = wv;
@@ -193,10 +225,15 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
   __syncthreads();
   TopEntry* parts = static_cast<TopEntry*>(a.part) + (int64_t)r * a.nch * a.F_max;
   if (wave == 0 && F > 0) {
+    // each list is sorted: stop at its first entry that does not beat the
+    // current F-th best
     for (int w = 1; w < kFNT / kWave; ++w)
       for (int e = 0; e < F; ++e) {
         const TopEntry t = s_list[w][e];
-        if (t.idx != kNoIdx) wave_insert(lv, li, t.val, t.idx, F, lane);
+        const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), F - 1));
+        const int32_t ti = __builtin_amdgcn_readlane(li, F - 1);
+        if (t.idx == kNoIdx || (ti != kNoIdx && !top_better(t.val, t.idx, tv, ti))) break;
+        wave_insert(lv, li, t.val, t.idx, F, lane);
       }
   }
   if (wave == 0 && lane < a.F_max) put_entry(parts + (int64_t)ch * a.F_max + lane, lane < F ? lv : kNegInf,
@@ -208,7 +245,10 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
     for (int c = 0; c < a.nch; ++c)
       for (int e = 0; e < F; ++e) {
         const TopEntry t = get_entry(parts + (int64_t)c * a.F_max + e);
-        if (t.idx != kNoIdx) wave_insert(fv, fi, t.val, t.idx, F, lane);
+        const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fv), F - 1));
+        const int32_t ti = __builtin_amdgcn_readlane(fi, F - 1);
+        if (t.idx == kNoIdx || (ti != kNoIdx && !top_better(t.val, t.idx, tv, ti))) break;
+        wave_insert(fv, fi, t.val, t.idx, F, lane);
       }
     if (lane < a.F_max) {
       const bool keep = lane < F && fi != kNoIdx;
