@@ -128,12 +128,24 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
     // the loads of kWin windows in flight at once
     constexpr int kWin = 4;
     const int64_t stride = (int64_t)(kFNT / kWave) * kWave;
-    for (int64_t base0 = v0 + (int64_t)wave * kWave; base0 < v1; base0 += stride * kWin) {
-      u32x4 d[kWin];
+    const int64_t step = stride * kWin;
+    int64_t base0 = v0 + (int64_t)wave * kWave;
+    u32x4 d[kWin];
+    if (base0 < v1) {
 #pragma unroll
       for (int u = 0; u < kWin; ++u) {
         const int64_t v = base0 + u * stride + lane;
         d[u] = load_vec(row, v < v1 ? v : v1 - 1);  // unconditional (clamped) so the loads overlap
+      }
+    }
+    for (; base0 < v1; base0 += step) {
+      // software pipelined: the next kWin windows are in flight while these
+      // are scanned (past the end the prefetch is clamped to the last vector)
+      u32x4 nx[kWin];
+#pragma unroll
+      for (int u = 0; u < kWin; ++u) {
+        const int64_t v = base0 + step + u * stride + lane;
+        nx[u] = load_vec(row, v < v1 ? v : v1 - 1);
       }
 #pragma unroll
       for (int u = 0; u < kWin; ++u) {
@@ -213,6 +225,8 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
           }
         }
       }
+#pragma unroll
+      for (int u = 0; u < kWin; ++u) d[u] = nx[u];
     }
   }
   // merge the block's waves into wave 0's list
