@@ -56,6 +56,12 @@ def _load(path):
     L.svo_verify_tree.argtypes = [P, P, i32, i64, i64, P, P, i32, i32, i32, i32, f64, u64, u32, P, P,
                                   P, P, P, P, P, P, P, P, P, P]
     L.svo_verify_tree.restype = i32
+    L.svo_verify_chain_pm.argtypes = [P, i32, i64, P, i32, i32, i32, f64, u64, u32, P, P, P, P, P, P, P, P, P,
+                                      P]
+    L.svo_verify_chain_pm.restype = i32
+    L.svo_verify_tree_pm.argtypes = [P, i32, i64, P, P, i32, i32, i32, i32, f64, u64, u32, P, P, P, P, P, P, P, P,
+                                     P, P, P]
+    L.svo_verify_tree_pm.restype = i32
     L.svo_fanout_topk.argtypes = [P, i32, i64, i32, i32, P, i32, P, P]
     L.svo_fanout_topk.restype = i32
     L.svo_geometric_fanout.argtypes = [i32, f64, f64, i32, i32, P]
@@ -238,6 +244,44 @@ def verify_tree(tgt, drf, node_tok, parent, max_depth, T, seed, round_, dtype, r
                                _ptr(out["q"]), _ptr(out["a"]), _ptr(out["w"]), _ptr(out["mdec"]), _ptr(out["mcdf"]),
                                _ptr(out["passes"]))
     _check(rc, "verify_tree")
+    return out
+
+
+def verify_chain_pm(tgt, tok, T, seed, round_, dtype, r=None, u=None, want_w=False):
+    """Point-mass chain verification.  tgt [B, gamma+1, V], tok [B, gamma]; no draft rows."""
+    tgt, code = _logits(tgt, dtype)
+    B, g1, V = tgt.shape
+    gamma = g1 - 1
+    tok = _i32(tok)
+    rr = None if r is None else np.ascontiguousarray(r, dtype=np.float64)
+    uu = None if u is None else np.ascontiguousarray(u, dtype=np.float64)
+    out = dict(n=np.zeros(B, np.int32), t=np.zeros(B, np.int32), p=np.zeros((B, gamma)), a=np.zeros((B, gamma)),
+               w=np.zeros((B, V)) if want_w else None, mdec=np.zeros(B), mcdf=np.zeros(B),
+               rows=np.zeros(B, np.int32))
+    rc = lib().svo_verify_chain_pm(_ptr(tgt), code, _row_stride(tgt), _ptr(tok), B, gamma, V, float(T), int(seed),
+                                   int(round_), _ptr(rr), _ptr(uu), _ptr(out["n"]), _ptr(out["t"]), _ptr(out["p"]),
+                                   _ptr(out["a"]), _ptr(out["w"]), _ptr(out["mdec"]), _ptr(out["mcdf"]),
+                                   _ptr(out["rows"]))
+    _check(rc, "verify_chain_pm")
+    return out
+
+
+def verify_tree_pm(tgt, node_tok, parent, max_depth, T, seed, round_, dtype, r=None, u=None, want_w=False):
+    """Point-mass tree verification.  tgt [B, N, V], node_tok/parent [B, N]; no draft rows."""
+    tgt, code = _logits(tgt, dtype)
+    B, N, V = tgt.shape
+    node_tok = _i32(node_tok)
+    parent = _i32(parent)
+    rr = None if r is None else np.ascontiguousarray(r, dtype=np.float64)
+    uu = None if u is None else np.ascontiguousarray(u, dtype=np.float64)
+    out = dict(len=np.zeros(B, np.int32), path=np.zeros((B, max_depth), np.int32), t=np.zeros(B, np.int32),
+               p=np.full((B, N), np.nan), a=np.zeros((B, N)), w=np.zeros((B, V)) if want_w else None,
+               mdec=np.zeros(B), mcdf=np.zeros(B), passes=np.zeros(B, np.int32))
+    rc = lib().svo_verify_tree_pm(_ptr(tgt), code, _row_stride(tgt), _ptr(node_tok), _ptr(parent), B, N,
+                                  int(max_depth), V, float(T), int(seed), int(round_), _ptr(rr), _ptr(uu),
+                                  _ptr(out["len"]), _ptr(out["path"]), _ptr(out["t"]), _ptr(out["p"]), _ptr(out["a"]),
+                                  _ptr(out["w"]), _ptr(out["mdec"]), _ptr(out["mcdf"]), _ptr(out["passes"]))
+    _check(rc, "verify_tree_pm")
     return out
 
 

@@ -15,7 +15,9 @@
 //         round).
 //   [SD2] "SpecDiff-2: Scaling Diffusion Drafter Alignment ..." wiki summary,
 //         "Core method": K candidates drawn from shared position-wise
-//         marginals, the verifier keeps the best one.
+//         marginals, the verifier keeps the best one; greedy acceptance (the
+//         chosen token accepted by a Bernoulli of the verifier probability,
+//         the residual resampled on rejection, no drafter probability).
 //   [PR]  "PRESTO: prefix-aligned tree drafting ...", §2.1 (token tree,
 //         sequential acceptance from the root until a mismatch).
 //   [SSD] "Speculative Speculative Decoding (SSD) / Saguaro" review, §3
@@ -332,6 +334,122 @@ TreeResult tree_round(const TreeInputs& in, const double* r /*[N], r[i] for chil
   }
 }
 
+// ---------------------------------------------------------------------------
+// Point-mass ("greedy") acceptance, [SD2] "Core method": the chosen draft
+// token is accepted with a Bernoulli of the verifier's probability and the
+// residual is resampled on a rejection; no drafter probability is used.
+// Reading: this is [DV] §2.1's single step with the draft replaced by a point
+// mass at the chosen token, q = delta_x.  The acceptance ratio is p(x)/1 and
+// the residual max(0, p - delta_x) is p with x removed (mass 1 - p(x)); [DV]
+// §2.1's invariance argument holds for any q, so every step returns the
+// target law.  Chain: x_j is accepted iff r_j < p_j(x_j); at the first
+// rejection (0-based row n) the correction is drawn from p_{n+1} with x_{n+1}
+// removed (from p_{n+1} itself if that mass is 0, by rounding only); with
+// every draft accepted the bonus is drawn from p_{gamma+1}.  Draft rows are
+// not used.  sample_rows = 1 either way.
+// ---------------------------------------------------------------------------
+ChainResult chain_round_pm(const std::vector<std::vector<double>>& P, const int32_t* x, int gamma, const double* r,
+                           double u, double* out_p, double* a_trace, std::vector<double>* w_out) {
+  ChainResult res;
+  for (int j = 0; j < gamma; ++j)
+    if (out_p) out_p[j] = P[j][x[j]];
+  if (a_trace)
+    for (int j = 0; j < gamma; ++j) a_trace[j] = std::nan("");
+  int n = 0;
+  for (int j = 0; j < gamma; ++j) {
+    const double a = accept_ratio(P[j][x[j]], 1.0);  // q = delta_x: a = p(x)
+    if (a_trace) a_trace[j] = a;
+    res.mdec = std::min(res.mdec, std::fabs(r[j] - a));
+    const bool accept = r[j] < a;
+    if (!accept) break;
+    ++n;
+  }
+  res.n = n;
+  std::vector<double> w;
+  if (n < gamma) {
+    w = P[n];
+    w[x[n]] = 0.0;  // the rejected token leaves the residual
+    double mass = 0.0;
+    for (double v : w) mass += v;
+    if (!(mass > 0.0)) w = P[n];
+  } else {
+    w = P[gamma];  // every draft accepted: the bonus row
+  }
+  res.sample_rows = 1;
+  res.t = sample_inverse_cdf(w, u, &res.mcdf);
+  if (w_out) *w_out = w;
+  return res;
+}
+
+// ---------------------------------------------------------------------------
+// Tree with point-mass siblings ([PR] §2.1 sequential acceptance from the
+// root; the point-mass step above at every child).  At node u the children
+// (increasing index) are tried against a running residual w that starts as
+// P_u, with mass D = 1: child i is accepted iff r_i < w(x_i) / D; on a
+// rejection x_i is removed (D <- D - w(x_i), then w(x_i) <- 0), so a repeated
+// sibling token is rejected for sure and removes nothing.  An accepted child
+// becomes the current node.  When every child is rejected the correction is
+// drawn from w (from P_u if its mass is 0, by rounding only); a node without
+// children, or at max_depth, gives the bonus draw from P_u.  Every step is
+// exactly lossless whatever the sibling tokens, deterministic top-F ones
+// included.  Draft rows are not used; row_passes = 1 (the final draw).
+// ---------------------------------------------------------------------------
+TreeResult tree_round_pm(const TreeInputs& in, const double* r, double u, double* out_p, double* a_trace,
+                         std::vector<double>* w_out) {
+  TreeResult res;
+  if (a_trace)
+    for (int i = 0; i < in.N; ++i) a_trace[i] = std::nan("");
+  std::vector<double> p, w;
+  int node = 0;
+  for (;;) {
+    std::vector<int> kids;
+    for (int i = node + 1; i < in.N; ++i)
+      if (in.parent[i] == node) kids.push_back(i);
+    if (!softmax_row(in.tgt, in.dtype, (in.row0 + node) * in.tgt_stride, in.V, in.T, p)) {
+      res.ok = false;
+      return res;
+    }
+    res.row_passes = 1;
+    if (kids.empty() || (int)res.path.size() >= in.max_depth) {
+      if (!kids.empty()) res.ok = false;
+      res.t = sample_inverse_cdf(p, u, &res.mcdf);
+      if (w_out) *w_out = p;
+      return res;
+    }
+    w = p;
+    double D = 1.0;
+    int accepted = -1;
+    for (int ch : kids) {
+      const int tok = in.node_tok[ch];
+      if (tok < 0 || tok >= in.V) {
+        res.ok = false;
+        return res;
+      }
+      if (out_p) out_p[ch] = p[tok];
+      const double a = D > 0.0 ? accept_ratio(w[tok] / D, 1.0) : 0.0;
+      if (a_trace) a_trace[ch] = a;
+      res.mdec = std::min(res.mdec, std::fabs(r[ch] - a));
+      if (r[ch] < a) {
+        accepted = ch;
+        break;
+      }
+      D -= w[tok];
+      w[tok] = 0.0;
+    }
+    if (accepted >= 0) {
+      res.path.push_back(accepted);
+      node = accepted;
+      continue;
+    }
+    double mass = 0.0;
+    for (double v : w) mass += v;
+    if (!(mass > 0.0)) w = p;
+    res.t = sample_inverse_cdf(w, u, &res.mcdf);
+    if (w_out) *w_out = w;
+    return res;
+  }
+}
+
 }  // namespace
 
 // ===========================================================================
@@ -515,6 +633,80 @@ int svo_verify_tree(const void* tgt, const void* drf, int dtype, int64_t tgt_str
     if (w_out) {
       double S = 0.0;
       for (double x : w) S += x;
+      for (int v = 0; v < V; ++v) w_out[(int64_t)b * V + v] = w[v] / S;
+    }
+    if (out_mdec) out_mdec[b] = res.mdec;
+    if (out_mcdf) out_mcdf[b] = res.mcdf;
+    if (out_passes) out_passes[b] = res.row_passes;
+  }
+  return 0;
+}
+
+// Point-mass chain verification (chain_round_pm): target rows only, laid out
+// as for svo_verify_chain.  r_in ([B*gamma]) and u_in ([B]) optionally replace
+// the Philox uniforms; a_trace [B*gamma] (NaN where no decision) and w_out
+// [B*V] (normalised weights of the final draw) may be null.
+int svo_verify_chain_pm(const void* tgt, int dtype, int64_t tgt_stride, const int32_t* tok, int B, int gamma, int V,
+                        double T, uint64_t seed, uint32_t round, const double* r_in, const double* u_in,
+                        int32_t* out_n, int32_t* out_tok, double* out_p, double* a_trace, double* w_out,
+                        double* out_mdec, double* out_mcdf, int32_t* out_rows) {
+  if (B < 0 || gamma < 1 || V < 1 || !(T > 0.0)) return 1;
+  std::vector<std::vector<double>> P(gamma + 1);
+  std::vector<double> r(gamma), w;
+  for (int b = 0; b < B; ++b) {
+    for (int j = 0; j <= gamma; ++j)
+      if (!softmax_row(tgt, dtype, ((int64_t)b * (gamma + 1) + j) * tgt_stride, V, T, P[j])) return 2;
+    const int32_t* x = tok + (int64_t)b * gamma;
+    for (int j = 0; j < gamma; ++j)
+      if (x[j] < 0 || x[j] >= V) return 3;
+    for (int j = 0; j < gamma; ++j) {
+      const uint32_t pos = (uint32_t)j + 1u;  // 1-based position, as in svo_verify_chain
+      r[j] = r_in ? r_in[(int64_t)b * gamma + j] : draw_uniform(seed, pos, (uint32_t)b, 0, round, 0);
+    }
+    const double u = u_in ? u_in[b] : draw_uniform(seed, 0, (uint32_t)b, 0, round, 1);
+    ChainResult res = chain_round_pm(P, x, gamma, r.data(), u, out_p ? out_p + (int64_t)b * gamma : nullptr,
+                                     a_trace ? a_trace + (int64_t)b * gamma : nullptr, w_out ? &w : nullptr);
+    out_n[b] = res.n;
+    out_tok[b] = res.t;
+    if (w_out) {
+      double S = 0.0;
+      for (double v : w) S += v;
+      for (int v = 0; v < V; ++v) w_out[(int64_t)b * V + v] = w[v] / S;
+    }
+    if (out_mdec) out_mdec[b] = res.mdec;
+    if (out_mcdf) out_mcdf[b] = res.mcdf;
+    if (out_rows) out_rows[b] = res.sample_rows;
+  }
+  return 0;
+}
+
+// Point-mass tree verification (tree_round_pm), same layout and optional
+// arguments as svo_verify_tree, without draft rows.
+int svo_verify_tree_pm(const void* tgt, int dtype, int64_t tgt_stride, const int32_t* node_tok, const int32_t* parent,
+                       int B, int N, int max_depth, int V, double T, uint64_t seed, uint32_t round, const double* r_in,
+                       const double* u_in, int32_t* out_len, int32_t* out_path, int32_t* out_tok, double* out_p,
+                       double* a_trace, double* w_out, double* out_mdec, double* out_mcdf, int32_t* out_passes) {
+  if (B < 0 || N < 1 || max_depth < 1 || V < 1 || !(T > 0.0)) return 1;
+  std::vector<double> r(N), w;
+  for (int b = 0; b < B; ++b) {
+    const int32_t* par = parent + (int64_t)b * N;
+    for (int i = 1; i < N; ++i)
+      if (par[i] < 0 || par[i] >= i) return 4;
+    for (int i = 0; i < N; ++i)
+      r[i] = r_in ? r_in[(int64_t)b * N + i] : draw_uniform(seed, (uint32_t)i, (uint32_t)b, 0, round, 0);
+    const double u = u_in ? u_in[b] : draw_uniform(seed, 0, (uint32_t)b, 0, round, 1);
+    TreeInputs in{tgt, nullptr, dtype, tgt_stride, 0, node_tok + (int64_t)b * N, par, (int64_t)b * N,
+                  N, V, max_depth, T};
+    TreeResult res = tree_round_pm(in, r.data(), u, out_p ? out_p + (int64_t)b * N : nullptr,
+                                   a_trace ? a_trace + (int64_t)b * N : nullptr, w_out ? &w : nullptr);
+    if (!res.ok) return 5;
+    out_len[b] = (int32_t)res.path.size();
+    for (int d = 0; d < max_depth; ++d)
+      out_path[(int64_t)b * max_depth + d] = d < (int)res.path.size() ? res.path[d] : -1;
+    out_tok[b] = res.t;
+    if (w_out) {
+      double S = 0.0;
+      for (double v : w) S += v;
       for (int v = 0; v < V; ++v) w_out[(int64_t)b * V + v] = w[v] / S;
     }
     if (out_mdec) out_mdec[b] = res.mdec;

@@ -197,6 +197,88 @@ def tree_sequence_distribution(tab: Tables, parent, m, T=1.0):
     return dist(())
 
 
+def _recurse(round_outcomes, m):
+    memo = {}
+
+    def dist(prefix):
+        if len(prefix) >= m:
+            return {prefix[:m]: 1.0}
+        if prefix in memo:
+            return memo[prefix]
+        acc = defaultdict(float)
+        for e, pr in round_outcomes(prefix).items():
+            for s, pr2 in dist(prefix + e).items():
+                acc[s] += pr * pr2
+        memo[prefix] = acc
+        return acc
+
+    return dist(())
+
+
+def chain_pm_sequence_distribution(tab: Tables, gamma, m, choose, T=1.0, verify=None):
+    """Distribution of the first m tokens from repeated point-mass chain rounds
+    whose drafts are chosen deterministically: x_j = choose(context)."""
+    V = tab.V
+    verify = verify or oracle.verify_chain_pm
+
+    def round_outcomes(prefix):
+        xs = []
+        for _ in range(gamma):
+            xs.append(int(choose(prefix + tuple(xs))))
+        tgt = np.stack([logits_of(tab.p(prefix + tuple(xs[:j])), T) for j in range(gamma + 1)])[None]
+        tok = np.array(xs, np.int32)[None]
+
+        def run(r, u):
+            o = verify(tgt, tok, T, 0, 0, "f64", r=r[None], u=np.array([u]), want_w=True)
+            n = int(o["n"][0])
+            return tuple(xs[:n]) + (int(o["t"][0]),), o["a"][0], o["w"][0]
+
+        return enumerate_cells(run, gamma, V)
+
+    return _recurse(round_outcomes, m)
+
+
+def tree_pm_sequence_distribution(tab: Tables, parent, m, rank_source="q", T=1.0, pm=True):
+    """Distribution of the first m tokens from repeated tree rounds whose
+    siblings are deterministic: the k-th child (in index order) of a node is
+    the k-th most likely token of the node's draft distribution (top-F
+    siblings).  pm selects the point-mass rule, else the standard sibling
+    rule with the node's draft q held fixed."""
+    V = tab.V
+    N = len(parent)
+    max_depth = N
+
+    def round_outcomes(prefix):
+        ctx = {0: prefix}
+        tok = [0] * N
+        seen = defaultdict(int)
+        for i in range(1, N):
+            pu = parent[i]
+            order = np.argsort(-(tab.q(ctx[pu]) if rank_source == "q" else tab.p(ctx[pu])), kind="stable")
+            tok[i] = int(order[seen[pu]])
+            seen[pu] += 1
+            ctx[i] = ctx[pu] + (tok[i],)
+        tgt = np.stack([logits_of(tab.p(ctx[i]), T) for i in range(N)])[None]
+        drf = np.stack([logits_of(tab.q(ctx[i]), T) for i in range(N)])[None]
+        tok_a = np.array(tok, np.int32)[None]
+        par_a = np.array(parent, np.int32)[None]
+
+        def run(r, u):
+            if pm:
+                o = oracle.verify_tree_pm(tgt, tok_a, par_a, max_depth, T, 0, 0, "f64", r=r[None],
+                                          u=np.array([u]), want_w=True)
+            else:
+                o = oracle.verify_tree(tgt, drf, tok_a, par_a, max_depth, T, 0, 0, "f64", r=r[None],
+                                       u=np.array([u]), want_w=True)
+            L = int(o["len"][0])
+            emitted = tuple(tok[i] for i in o["path"][0][:L]) + (int(o["t"][0]),)
+            return emitted, o["a"][0], o["w"][0]
+
+        return enumerate_cells(run, N, V)
+
+    return _recurse(round_outcomes, m)
+
+
 def max_marginal_error(tab: Tables, distr, m):
     err = 0.0
     total = 0.0

@@ -28,6 +28,16 @@ TREE_PINS = [
     pins.test_chain_shaped_tree_is_chain,
 ]
 
+PM_CHAIN_PINS = [
+    pins.test_pm_chain_equals_chain_with_point_mass_drafts,
+    lambda: pins.test_pm_chain_round_is_lossless_for_any_drafter(2, 3, 1.0, 0.0, 41, "p_argmin"),
+]
+PM_TREE_PINS = [
+    lambda: pins.test_pm_tree_with_top_f_siblings_is_lossless([-1, 0, 0, 1, 1], 2, 52, 0.8),
+    pins.test_pm_repeated_sibling_token_is_rejected_and_removes_nothing,
+    pins.test_pm_chain_shaped_tree_is_pm_chain,
+]
+
 MUTANTS = [
     # (name, original text, planted text, pins expected to catch it)
     ("decision inverted", "if (!(r[j] < a)) break;", "if (!(r[j] > a)) break;", CHAIN_PINS),
@@ -57,6 +67,12 @@ MUTANTS = [
     ("fan-out unstable order", "std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return z[a] > z[b]; });",
      "std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return z[a] >= z[b] && a != b && z[a] == z[b] ? a > b : z[a] > z[b]; });",
      [pins.test_fanout_is_stable_sort]),
+    ("point-mass residual keeps the rejected token", "    w[x[n]] = 0.0;  // the rejected token leaves the residual\n",
+     "\n", PM_CHAIN_PINS),
+    ("point-mass tree mass not reduced", "      D -= w[tok];\n", "\n", PM_TREE_PINS),
+    ("point-mass tree ratio not renormalised", "accept_ratio(w[tok] / D, 1.0)", "accept_ratio(w[tok], 1.0)",
+     PM_TREE_PINS),
+    ("point-mass tree draw ignores removals", "    if (!(mass > 0.0)) w = p;\n", "    w = p;\n", PM_TREE_PINS),
     ("geometric fan-out floor", "F_out[k] = (int32_t)std::ceil(f);", "F_out[k] = (int32_t)std::floor(f);",
      [pins.test_geometric_fanout_closed_form]),
 ]

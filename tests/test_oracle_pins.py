@@ -358,3 +358,101 @@ def test_fanout_is_stable_sort():
         assert list(ids[r][:F[r]]) == list(order[:F[r]])
         assert (ids[r][F[r]:] == -1).all()
         assert np.array_equal(got_vals[r][:F[r]], vals[r][order[:F[r]]])
+
+
+# ---------------------------------------------------------------- point-mass mode
+# SpecDiff-2 page, Core method ("greedy acceptance": accept the chosen token
+# with a Bernoulli of the verifier probability, resample the residual on a
+# rejection, no drafter probability), read as the draft-then-verify page's
+# §2.1 step with a point-mass draft q = delta_x.
+
+def test_pm_chain_equals_chain_with_point_mass_drafts():
+    """The point-mass chain is the standard chain fed one-hot draft rows at
+    the drafted tokens: same decisions, same residual, same draws."""
+    rng = np.random.default_rng(31)
+    for V, gamma, T in ((7, 3, 1.0), (40, 6, 0.7), (300, 5, 1.4)):
+        B = 40
+        tgt = rng.normal(scale=2.0, size=(B, gamma + 1, V))
+        tgt[rng.random(tgt.shape) < 0.2] = -np.inf
+        tgt[..., 0] = 0.0  # every row keeps a finite logit
+        tok = rng.integers(0, V, size=(B, gamma)).astype(np.int32)
+        drf = np.full((B, gamma, V), -np.inf)
+        for b in range(B):
+            for j in range(gamma):
+                drf[b, j, tok[b, j]] = 0.0
+        for seed, rnd in ((0, 0), (7, 3)):
+            a = oracle.verify_chain_pm(tgt, tok, T, seed, rnd, "f64")
+            c = oracle.verify_chain(tgt, drf, tok, T, seed, rnd, "f64")
+            assert np.array_equal(a["n"], c["n"]) and np.array_equal(a["t"], c["t"])
+            assert np.array_equal(a["p"], c["p"])
+            assert (a["rows"] == 1).all()
+
+
+@pytest.mark.parametrize("gamma,m,T,pz,seed,chooser", [
+    (2, 3, 1.0, 0.0, 41, "p_argmin"),
+    (3, 3, 0.7, 0.3, 42, "q_argmax"),
+    (2, 4, 1.3, 0.2, 43, "hash"),
+])
+def test_pm_chain_round_is_lossless_for_any_drafter(gamma, m, T, pz, seed, chooser):
+    """Exact enumeration: with deterministic drafts (even the least likely
+    token under the target), the emitted sequence's law is the target chain
+    rule."""
+    tab = E.Tables(V=4, seed=seed, p_zero=pz)
+    choose = {
+        "p_argmin": lambda ctx: int(np.argmin(tab.p(ctx))),
+        "q_argmax": lambda ctx: int(np.argmax(tab.q(ctx))),
+        "hash": lambda ctx: (sum(ctx) * 7 + len(ctx) * 3 + 1) % tab.V,
+    }[chooser]
+    d = E.chain_pm_sequence_distribution(tab, gamma, m, choose, T)
+    assert E.max_marginal_error(tab, d, m) < 1e-12
+
+
+@pytest.mark.parametrize("parent,m,seed,T", [
+    ([-1, 0, 0, 0], 2, 51, 1.0),
+    ([-1, 0, 0, 1, 1], 2, 52, 0.8),
+    ([-1, 0, 1, 0, 2], 3, 53, 1.2),
+])
+def test_pm_tree_with_top_f_siblings_is_lossless(parent, m, seed, T):
+    """Exact enumeration with deterministic top-F siblings (the k-th child is
+    the draft's k-th most likely token): the point-mass rule keeps the target
+    law, while the standard sibling rule with q held fixed does not."""
+    tab = E.Tables(V=4, seed=seed, p_zero=0.2)
+    d = E.tree_pm_sequence_distribution(tab, parent, m, T=T, pm=True)
+    assert E.max_marginal_error(tab, d, m) < 1e-12
+    if len(parent) > 2:
+        d_std = E.tree_pm_sequence_distribution(tab, parent, m, T=T, pm=False)
+        assert E.max_marginal_error(tab, d_std, m) > 1e-3
+
+
+def test_pm_chain_shaped_tree_is_pm_chain():
+    """A tree that is a single path gives exactly the point-mass chain."""
+    rng = np.random.default_rng(61)
+    B, gamma, V, T = 12, 5, 50, 0.9
+    tgt = rng.normal(scale=2.0, size=(B, gamma + 1, V))
+    tok = rng.integers(0, V, size=(B, gamma)).astype(np.int32)
+    node_tok = np.concatenate([np.zeros((B, 1), np.int32), tok], axis=1)
+    parent = np.tile(np.arange(-1, gamma, dtype=np.int32), (B, 1))
+    # the uniforms the chain uses for x_j (counter idx j) are the tree's for node j
+    for seed, rnd in ((0, 0), (3, 2)):
+        c = oracle.verify_chain_pm(tgt, tok, T, seed, rnd, "f64")
+        t = oracle.verify_tree_pm(tgt, node_tok, parent, gamma, T, seed, rnd, "f64")
+        assert np.array_equal(c["n"], t["len"]) and np.array_equal(c["t"], t["t"])
+        for b in range(B):
+            assert np.array_equal(c["p"][b, :c["n"][b] + (c["n"][b] < gamma)],
+                                  t["p"][b, 1:1 + c["n"][b] + (c["n"][b] < gamma)])
+
+
+def test_pm_repeated_sibling_token_is_rejected_and_removes_nothing():
+    """A sibling whose token was already rejected has residual probability 0:
+    it is rejected for sure, and the final draw never returns that token."""
+    V, T = 6, 1.0
+    tgt = np.log(np.array([[0.30, 0.25, 0.20, 0.15, 0.05, 0.05]]))[None].repeat(3, axis=1)
+    node_tok = np.array([[0, 2, 2]], np.int32)
+    parent = np.array([[-1, 0, 0]], np.int32)
+    # reject the first sibling (r >= p = 0.2), then the repeat has ratio 0
+    o = oracle.verify_tree_pm(tgt, node_tok, parent, 2, T, 0, 0, "f64", r=np.array([[0.0, 0.5, 0.0]]),
+                              u=np.array([0.999]), want_w=True)
+    assert o["len"][0] == 0 and o["a"][0, 2] == 0.0 and o["t"][0] != 2
+    w = o["w"][0]
+    assert w[2] == 0.0 and np.isclose(w.sum(), 1.0)
+    assert np.allclose(w, np.array([0.30, 0.25, 0.0, 0.15, 0.05, 0.05]) / 0.8)
