@@ -19,6 +19,9 @@
  *   - "PRESTO: prefix-aligned tree drafting for diffusion speculative
  *     decoding", §2.1 (token tree, accept sequentially from the root until a
  *     mismatch).
+ *   - SpecDiff-2 page, Core method, greedy acceptance (the point-mass entry
+ *     points: a drafted token is accepted with the verifier's probability of
+ *     it, the residual resampled on a rejection, no drafter probabilities).
  *   - "Speculative Speculative Decoding (SSD) / Saguaro" review, §3 (fan-out:
  *     top-F_k tokens of the draft logits per lookahead position k) and
  *     Theorem 12 (geometric F_k).
@@ -81,7 +84,15 @@ typedef int32_t sv_dtype;
 enum { SV_F32 = 0, SV_BF16 = 1 };
 
 typedef int32_t sv_op;
-enum { SV_OP_CHAIN = 0, SV_OP_GREEDY = 1, SV_OP_MULTI = 2, SV_OP_TREE = 3, SV_OP_FANOUT = 4 };
+enum {
+  SV_OP_CHAIN = 0,
+  SV_OP_GREEDY = 1,
+  SV_OP_MULTI = 2,
+  SV_OP_TREE = 3,
+  SV_OP_FANOUT = 4,
+  SV_OP_CHAIN_PM = 5,
+  SV_OP_TREE_PM = 6
+};
 
 /* Limits of this build. */
 #define SV_MAX_GAMMA 64        /* draft positions per chain */
@@ -103,7 +114,7 @@ const char* sv_status_string(sv_status s);
 
 /*
  * Workspace bytes for one call of `op` with the given shape.  gamma_or_N is
- * gamma (chain, greedy, multi) or N (tree); B is the number of sequences (or
+ * gamma (chain, greedy, multi, chain_pm) or N (tree, tree_pm); B is the number of sequences (or
  * R, the number of rows, for fan-out); K is used by multi only; F_max by
  * fan-out only.  Returns SV_EINVAL / SV_EUNSUPPORTED for shapes the
  * corresponding call would reject.
@@ -190,6 +201,48 @@ sv_status sv_verify_tree(const void* tgt, const void* drf, sv_dtype dt, int64_t 
                          const int32_t* node_tok, const int32_t* parent, int32_t B, int32_t N, int32_t max_depth,
                          int32_t V, float T, uint64_t seed, uint32_t round, int32_t* out_len, int32_t* out_path,
                          int32_t* out_tok, float* out_p, float* out_q, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Point-mass ("greedy acceptance") chain verification: SpecDiff-2 page, Core
+ * method, read as the draft-then-verify page's §2.1 step with the draft
+ * distribution a point mass at the drafted token (q = delta_x).  Lossless for
+ * any drafter, and no draft logits are read.
+ *   tgt [B, gamma+1, V] rows p_1..p_{gamma+1} as in sv_verify_chain;
+ *   draft_tok [B, gamma] int32 (any tokens in [0, V): sampled, argmax, ...)
+ * Decision: accept x_j iff U_j < p_j(x_j) (U_j as for sv_verify_chain).
+ * Outputs (device):
+ *   out_n   [B] accepted drafts n (0..gamma)
+ *   out_tok [B] correction drawn from p_{n+1} with x_{n+1} removed (from
+ *           p_{n+1} itself if what is left rounds to 0), or the bonus from
+ *           p_{gamma+1}
+ *   out_p   [B, gamma] float p_j(x_j) for every j; may be NULL
+ * Reads target rows 1..gamma once, then one row per sequence.  Workspace:
+ * SV_OP_CHAIN_PM.
+ */
+sv_status sv_verify_chain_pm(const void* tgt, sv_dtype dt, int64_t tgt_stride, const int32_t* draft_tok, int32_t B,
+                             int32_t gamma, int32_t V, float T, uint64_t seed, uint32_t round, int32_t* out_n,
+                             int32_t* out_tok, float* out_p, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Point-mass tree verification (PRESTO page §2.1, sequential acceptance from
+ * the root, with the point-mass step of sv_verify_chain_pm at every child).
+ * Tree layout, max_depth, uniforms and outputs as for sv_verify_tree, without
+ * draft rows.  At a node the children are tried in increasing index against a
+ * running residual w (initially p_node, mass D = 1): child i is accepted iff
+ * U_i < w(x_i) / D; a rejection removes x_i from w (D -= w(x_i), w(x_i) = 0),
+ * so a sibling repeating a rejected token is rejected.  When every child is
+ * rejected the correction is drawn from w (from p_node if w rounds to 0);
+ * a node without children (or at max_depth) gives the bonus draw from its
+ * row.  Lossless for any sibling tokens, deterministic top-F ones included.
+ *   out_p [B, N] float: p_parent(x_i) of every child tried (untouched
+ *         otherwise); may be NULL
+ * Reads the target rows of nodes with children once, then one row per
+ * sequence.  Workspace: SV_OP_TREE_PM.
+ */
+sv_status sv_verify_tree_pm(const void* tgt, sv_dtype dt, int64_t tgt_stride, const int32_t* node_tok,
+                            const int32_t* parent, int32_t B, int32_t N, int32_t max_depth, int32_t V, float T,
+                            uint64_t seed, uint32_t round, int32_t* out_len, int32_t* out_path, int32_t* out_tok,
+                            float* out_p, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Top-F fan-out (SSD / Saguaro review §3): for each row r the F[r] largest

@@ -102,12 +102,13 @@ void pick_slices(int32_t B, int64_t nvec, int cap_held, int cap_stream, int32_t*
   }
 }
 
-sv_status plan_chain(sv_dtype dt, int32_t B, int32_t K, int32_t gamma, int32_t V, Plan* pl) {
+// pm: point-mass acceptance (target rows only).
+sv_status plan_chain(sv_dtype dt, int32_t B, int32_t K, int32_t gamma, int32_t V, bool pm, Plan* pl) {
   if (bad_dtype(dt)) return SV_EDTYPE;
   if (B < 0 || K < 1 || gamma < 1 || V < 1) return SV_EINVAL;
   if (B > SV_MAX_SEQ || K > SV_MAX_K || gamma > SV_MAX_GAMMA || V > SV_MAX_V) return SV_EUNSUPPORTED;
   pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
-  const int64_t rows = (int64_t)B * (K + 1) * gamma;
+  const int64_t rows = (int64_t)B * (K + (pm ? 0 : 1)) * gamma;
   split(rows, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
   pl->grid1 = rows * pl->nch1;
   if (pl->grid1 > INT32_MAX || (int64_t)B * kMaxG > INT32_MAX) return SV_EUNSUPPORTED;
@@ -140,12 +141,12 @@ sv_status plan_greedy(sv_dtype dt, int32_t B, int32_t gamma, int32_t V, Plan* pl
 
 constexpr int kWalkMaxParts = 64; // stats parts per row the walk stages
 
-sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, Plan* pl) {
+sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, bool pm, Plan* pl) {
   if (bad_dtype(dt)) return SV_EDTYPE;
   if (B < 0 || N < 1 || V < 1) return SV_EINVAL;
   if (B > SV_MAX_SEQ || N > SV_MAX_N || V > SV_MAX_V) return SV_EUNSUPPORTED;
   pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
-  const int64_t rows = (int64_t)B * N * 2;
+  const int64_t rows = (int64_t)B * N * (pm ? 1 : 2);
   // only rows of nodes with children are streamed (about half of them in a
   // bushy tree): aim the part count at twice the usual block target
   split(rows, pl->nvec, 2 * stats_blocks(), &pl->nch1, &pl->vpc1);
@@ -231,10 +232,12 @@ sv_status sv_workspace_size(sv_op op, sv_dtype dt, int32_t B, int32_t K, int32_t
   Plan pl;
   sv_status st;
   switch (op) {
-    case SV_OP_CHAIN: st = plan_chain(dt, B, 1, gamma_or_N, V, &pl); break;
-    case SV_OP_MULTI: st = plan_chain(dt, B, K, gamma_or_N, V, &pl); break;
+    case SV_OP_CHAIN: st = plan_chain(dt, B, 1, gamma_or_N, V, false, &pl); break;
+    case SV_OP_MULTI: st = plan_chain(dt, B, K, gamma_or_N, V, false, &pl); break;
     case SV_OP_GREEDY: st = plan_greedy(dt, B, gamma_or_N, V, &pl); break;
-    case SV_OP_TREE: st = plan_tree(dt, B, gamma_or_N, V, &pl); break;
+    case SV_OP_TREE: st = plan_tree(dt, B, gamma_or_N, V, false, &pl); break;
+    case SV_OP_CHAIN_PM: st = plan_chain(dt, B, 1, gamma_or_N, V, true, &pl); break;
+    case SV_OP_TREE_PM: st = plan_tree(dt, B, gamma_or_N, V, true, &pl); break;
     case SV_OP_FANOUT: st = plan_fanout(dt, B, V, F_max, &pl); break;
     default: return SV_EINVAL;
   }
@@ -263,15 +266,15 @@ sv_status sv_get_device_error(void* ws, int32_t* flags, void* stream) {
 static sv_status verify_chain_like(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride,
                                    int64_t drf_stride, const int32_t* tok, int32_t B, int32_t K, int32_t gamma,
                                    int32_t V, float T, uint64_t seed, uint32_t round, int32_t* out_k, int32_t* out_n,
-                                   int32_t* out_tok, int32_t* out_n_cand, float* out_p, float* out_q, void* ws,
-                                   size_t ws_bytes, void* stream) {
+                                   int32_t* out_tok, int32_t* out_n_cand, float* out_p, float* out_q, bool pm,
+                                   void* ws, size_t ws_bytes, void* stream) {
   Plan pl;
-  sv_status st = plan_chain(dt, B, K, gamma, V, &pl);
+  sv_status st = plan_chain(dt, B, K, gamma, V, pm, &pl);
   if (st != SV_OK) return st;
   if (bad_temperature(T) || round >= (1u << 30)) return SV_EINVAL;
   if (B == 0) return SV_OK;
   if ((st = check_rows(tgt, tgt_stride, V, dt)) != SV_OK) return st;
-  if ((st = check_rows(drf, drf_stride, V, dt)) != SV_OK) return st;
+  if (!pm && (st = check_rows(drf, drf_stride, V, dt)) != SV_OK) return st;
   if (!tok || !out_n || !out_tok) return SV_EINVAL;
   if ((st = check_ws(ws, ws_bytes, pl)) != SV_OK) return st;
   char* w = static_cast<char*>(ws);
@@ -300,7 +303,8 @@ static sv_status verify_chain_like(const void* tgt, const void* drf, sv_dtype dt
   p.zq = p.zg + (int64_t)B * K * gamma;
   p.slots = w + pl.off_jobs;
   p.nch1 = pl.nch1;
-  pick_slices(B, pl.nvec, chain_draw_capacity(dt, true), chain_draw_capacity(dt, false), &p.G, &p.held);
+  p.pm = pm;
+  pick_slices(B, pl.nvec, chain_draw_capacity(dt, true, pm), chain_draw_capacity(dt, false, pm), &p.G, &p.held);
   p.vpc1 = pl.vpc1;
   p.nvec = pl.nvec;
   return launch_chain(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
@@ -311,7 +315,14 @@ sv_status sv_verify_chain(const void* tgt, const void* drf, sv_dtype dt, int64_t
                           uint32_t round, int32_t* out_n, int32_t* out_tok, float* out_p, float* out_q, void* ws,
                           size_t ws_bytes, void* stream) {
   return verify_chain_like(tgt, drf, dt, tgt_stride, drf_stride, draft_tok, B, 1, gamma, V, T, seed, round, nullptr,
-                           out_n, out_tok, nullptr, out_p, out_q, ws, ws_bytes, stream);
+                           out_n, out_tok, nullptr, out_p, out_q, false, ws, ws_bytes, stream);
+}
+
+sv_status sv_verify_chain_pm(const void* tgt, sv_dtype dt, int64_t tgt_stride, const int32_t* draft_tok, int32_t B,
+                             int32_t gamma, int32_t V, float T, uint64_t seed, uint32_t round, int32_t* out_n,
+                             int32_t* out_tok, float* out_p, void* ws, size_t ws_bytes, void* stream) {
+  return verify_chain_like(tgt, nullptr, dt, tgt_stride, 0, draft_tok, B, 1, gamma, V, T, seed, round, nullptr, out_n,
+                           out_tok, nullptr, out_p, nullptr, true, ws, ws_bytes, stream);
 }
 
 sv_status sv_verify_multi(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride, int64_t drf_stride,
@@ -320,7 +331,7 @@ sv_status sv_verify_multi(const void* tgt, const void* drf, sv_dtype dt, int64_t
                           int32_t* out_n_cand, float* out_p, float* out_q, void* ws, size_t ws_bytes, void* stream) {
   if (!out_k) return SV_EINVAL;
   return verify_chain_like(tgt, drf, dt, tgt_stride, drf_stride, draft_tok, B, K, gamma, V, T, seed, round, out_k,
-                           out_n, out_tok, out_n_cand, out_p, out_q, ws, ws_bytes, stream);
+                           out_n, out_tok, out_n_cand, out_p, out_q, false, ws, ws_bytes, stream);
 }
 
 sv_status sv_verify_greedy(const void* tgt, sv_dtype dt, int64_t stride, const int32_t* draft_tok, int32_t B,
@@ -353,18 +364,19 @@ sv_status sv_verify_greedy(const void* tgt, sv_dtype dt, int64_t stride, const i
   return launch_greedy(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
 }
 
-sv_status sv_verify_tree(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride, int64_t drf_stride,
-                         const int32_t* node_tok, const int32_t* parent, int32_t B, int32_t N, int32_t max_depth,
-                         int32_t V, float T, uint64_t seed, uint32_t round, int32_t* out_len, int32_t* out_path,
-                         int32_t* out_tok, float* out_p, float* out_q, void* ws, size_t ws_bytes, void* stream) {
+static sv_status verify_tree_like(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride,
+                                  int64_t drf_stride, const int32_t* node_tok, const int32_t* parent, int32_t B,
+                                  int32_t N, int32_t max_depth, int32_t V, float T, uint64_t seed, uint32_t round,
+                                  int32_t* out_len, int32_t* out_path, int32_t* out_tok, float* out_p, float* out_q,
+                                  bool pm, void* ws, size_t ws_bytes, void* stream) {
   Plan pl;
-  sv_status st = plan_tree(dt, B, N, V, &pl);
+  sv_status st = plan_tree(dt, B, N, V, pm, &pl);
   if (st != SV_OK) return st;
   if (max_depth < 1 || max_depth > SV_MAX_N) return SV_EINVAL;
   if (bad_temperature(T) || round >= (1u << 30)) return SV_EINVAL;
   if (B == 0) return SV_OK;
   if ((st = check_rows(tgt, tgt_stride, V, dt)) != SV_OK) return st;
-  if ((st = check_rows(drf, drf_stride, V, dt)) != SV_OK) return st;
+  if (!pm && (st = check_rows(drf, drf_stride, V, dt)) != SV_OK) return st;
   if (!node_tok || !parent || !out_len || !out_path || !out_tok) return SV_EINVAL;
   if ((st = check_ws(ws, ws_bytes, pl)) != SV_OK) return st;
   char* w = static_cast<char*>(ws);
@@ -392,10 +404,27 @@ sv_status sv_verify_tree(const void* tgt, const void* drf, sv_dtype dt, int64_t 
   p.zc = reinterpret_cast<float*>(w + pl.off_part2);
   p.part = w + pl.off_part1;
   p.nch = pl.nch1;
-  pick_slices(B, pl.nvec, tree_walk_capacity(dt, true), tree_walk_capacity(dt, false), &p.G, &p.held);
+  p.pm = pm;
+  pick_slices(B, pl.nvec, tree_walk_capacity(dt, true, pm), tree_walk_capacity(dt, false, pm), &p.G, &p.held);
   p.vpc = pl.vpc1;
   p.nvec = pl.nvec;
   return launch_tree(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+sv_status sv_verify_tree(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride, int64_t drf_stride,
+                         const int32_t* node_tok, const int32_t* parent, int32_t B, int32_t N, int32_t max_depth,
+                         int32_t V, float T, uint64_t seed, uint32_t round, int32_t* out_len, int32_t* out_path,
+                         int32_t* out_tok, float* out_p, float* out_q, void* ws, size_t ws_bytes, void* stream) {
+  return verify_tree_like(tgt, drf, dt, tgt_stride, drf_stride, node_tok, parent, B, N, max_depth, V, T, seed, round,
+                          out_len, out_path, out_tok, out_p, out_q, false, ws, ws_bytes, stream);
+}
+
+sv_status sv_verify_tree_pm(const void* tgt, sv_dtype dt, int64_t tgt_stride, const int32_t* node_tok,
+                            const int32_t* parent, int32_t B, int32_t N, int32_t max_depth, int32_t V, float T,
+                            uint64_t seed, uint32_t round, int32_t* out_len, int32_t* out_path, int32_t* out_tok,
+                            float* out_p, void* ws, size_t ws_bytes, void* stream) {
+  return verify_tree_like(tgt, nullptr, dt, tgt_stride, 0, node_tok, parent, B, N, max_depth, V, T, seed, round,
+                          out_len, out_path, out_tok, out_p, nullptr, true, ws, ws_bytes, stream);
 }
 
 sv_status sv_fanout_topk(const void* logits, sv_dtype dt, int64_t stride, int32_t R, int32_t V, const int32_t* F,

@@ -18,6 +18,14 @@
 //     holds u * S searches it (sv_walk.hpp).
 // The bonus row p_{gamma+1} is only read when every draft of the kept
 // candidate is accepted.
+//
+// Point-mass mode (SpecDiff-2 page, Core method: the chosen draft token is
+// accepted with the verifier's own probability, the residual is resampled on
+// a rejection; no drafter probabilities).  Read as the draft-then-verify
+// page's §2.1 step with q a point mass at the drafted token: accept x_j iff
+// r_j < p_j(x_j); the residual at a rejection is p_{n+1} with x_{n+1}
+// removed.  Only target rows are streamed (no draft rows at all), and the
+// draw is a plain draw from one row with one excluded token.
 #include "sv_device.hpp"
 #include "sv_internal.h"
 #include "sv_walk.hpp"
@@ -33,6 +41,7 @@ struct Job {
   float cmP, cmQ;
   double SP, SQ;
   double u;
+  int32_t ex;  // point-mass residual: the rejected token (-1: none)
 };
 
 // Parts of one sequence staged in LDS by the deciding block (all loads in
@@ -76,13 +85,13 @@ __device__ __forceinline__ RowStat merge_staged(const StagedParts& st, bool stag
 
 // Decisions of sequence b (identical in every block that makes them); the
 // draw job goes to *s_job, and the writer block stores the outputs.
-template <int DT>
+template <int DT, bool PM>
 __device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_job) {
   __shared__ StagedParts st;
   __shared__ RowStat sQ[SV_MAX_GAMMA];
   __shared__ int sN[SV_MAX_K];
-  const int rows = (a.K + 1) * a.gamma;
   const int Kg = a.K * a.gamma;
+  const int rows = PM ? Kg : Kg + a.gamma;
   const int nparts = rows * a.nch1;
   const bool staged = nparts <= kStage;
   const Partial* pb = static_cast<const Partial*>(a.part1) + (int64_t)b * nparts;
@@ -97,7 +106,7 @@ __device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_jo
     const int64_t o = ((int64_t)b * a.K + wave) * a.gamma + lane;
     x0 = a.tok[o];
     zp0 = a.zg[o];
-    zq0 = a.zq[o];
+    if (!PM) zq0 = a.zq[o];
   }
   if (staged) {
     for (int i = threadIdx.x; i < nparts; i += kNT) {
@@ -107,15 +116,23 @@ __device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_jo
     }
   }
   lds_sync();
-  for (int j = threadIdx.x; j < a.gamma; j += kNT)
-    sQ[j] = merge_staged(st, staged, pb, (Kg + j) * a.nch1, a.nch1, a.c);
-  lds_sync();
+  if (!PM) {
+    for (int j = threadIdx.x; j < a.gamma; j += kNT)
+      sQ[j] = merge_staged(st, staged, pb, (Kg + j) * a.nch1, a.nch1, a.c);
+    lds_sync();
+  }
   for (int k = wave; k < a.K; k += kNT / kWave) {
     bool acc = false;
     if (lane < a.gamma) {
       const int j = lane;
       const RowStat sp = merge_staged(st, staged, pb, (k * a.gamma + j) * a.nch1, a.nch1, a.c);
-      const RowStat sq = sQ[j];
+      RowStat sq;
+      if (PM) {
+        sq.cm = 0.f;
+        sq.S = 1.0;
+      } else {
+        sq = sQ[j];
+      }
       const int64_t o = ((int64_t)b * a.K + k) * a.gamma + j;
       int32_t x;
       float zp, zq;
@@ -126,12 +143,12 @@ __device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_jo
       } else {
         x = a.tok[o];
         zp = a.zg[o];
-        zq = a.zq[o];
+        zq = PM ? 0.f : a.zq[o];
       }
-      double p = 0.0, q = 0.0;
+      double p = 0.0, q = PM ? 1.0 : 0.0;  // point mass: q(x) = 1
       if (x >= 0 && x < a.V) {
         p = prob_of(zp, a.c, sp);
-        q = prob_of(zq, a.c, sq);
+        if (!PM) q = prob_of(zq, a.c, sq);
       } else if (writer) {
         set_error(a.err, SV_DERR_TOKEN);
       }
@@ -139,7 +156,7 @@ __device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_jo
       const double r = uniform24(a.seed, (uint32_t)(j + 1), (uint32_t)b, (uint32_t)k, a.round, 0);
       acc = r < accept_ratio(p, q);
       if (writer && a.out_p) a.out_p[o] = (float)p;
-      if (writer && a.out_q) a.out_q[o] = (float)q;
+      if (!PM && writer && a.out_q) a.out_q[o] = (float)q;
     }
     const uint64_t rejected = ~(uint64_t)__ballot(acc);
     int n = rejected ? __builtin_ctzll(rejected) : kWave;
@@ -161,13 +178,22 @@ __device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_jo
     }
     Job jb;
     jb.rowP = ((int64_t)b * a.K + best) * (a.gamma + 1) + n;
+    jb.ex = -1;
     if (n < a.gamma) {
       const RowStat sp = merge_staged(st, staged, pb, (best * a.gamma + n) * a.nch1, a.nch1, a.c);
-      jb.rowQ = (int64_t)b * a.gamma + n;
       jb.cmP = sp.cm;
       jb.SP = sp.S;
-      jb.cmQ = sQ[n].cm;
-      jb.SQ = sQ[n].S;
+      if (PM) {
+        const int32_t xn = a.tok[((int64_t)b * a.K + best) * a.gamma + n];
+        jb.ex = xn >= 0 && xn < a.V ? xn : -1;
+        jb.rowQ = -1;
+        jb.cmQ = 0.f;
+        jb.SQ = 0.0;
+      } else {
+        jb.rowQ = (int64_t)b * a.gamma + n;
+        jb.cmQ = sQ[n].cm;
+        jb.SQ = sQ[n].S;
+      }
     } else {
       jb.rowQ = -1;
       jb.cmP = jb.cmQ = 0.f;
@@ -181,7 +207,7 @@ __device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_jo
 
 template <int DT>
 __global__ __launch_bounds__(kNT) void chain_stats_kernel(ChainParams a) {
-  const int rows = (a.K + 1) * a.gamma;
+  const int rows = a.pm ? a.K * a.gamma : (a.K + 1) * a.gamma;
   const int64_t per_seq = (int64_t)rows * a.nch1;
   const int64_t bid = blockIdx.x;
   const int b = (int)(bid / per_seq);
@@ -225,6 +251,8 @@ __device__ DrawSpec job_spec(const ChainParams& a, const Job& jb, float cm_plain
   sp.rowP = row_ptr(a.tgt, jb.rowP, a.tgt_sb);
   sp.c = a.c;
   sp.coef = 1.f;
+  sp.ex = nullptr;
+  sp.nex = 0;
   if (jb.rowQ >= 0) {
     sp.rowQ = row_ptr(a.drf, jb.rowQ, a.drf_sb);
     sp.cmP = jb.cmP;
@@ -243,26 +271,40 @@ __device__ DrawSpec job_spec(const ChainParams& a, const Job& jb, float cm_plain
 
 // Draw: G blocks per sequence, each deciding the sequence and owning one
 // slice of the draw row(s).
-template <int DT, bool HELD>
+template <int DT, bool HELD, bool PM>
 __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
   const int b = blockIdx.x / a.G;
   const int g = blockIdx.x - b * a.G;
   __shared__ Job s_job;
   __shared__ uint64_t s_words[kMaxG], s_w1[kMaxG];
   __shared__ double s_val[kMaxG];
-  chain_decide<DT>(a, b, g == 0, &s_job);
+  chain_decide<DT, PM>(a, b, g == 0, &s_job);
   const Job jb = s_job;
   const int64_t spv = (a.nvec + a.G - 1) / a.G;
   const int64_t v0 = (int64_t)g * spv < a.nvec ? (int64_t)g * spv : a.nvec;
   const int64_t v1 = v0 + spv < a.nvec ? v0 + spv : a.nvec;
   Exchange x = make_exchange(a.slots, a.err, b, a.G, g);
-  const bool resid = jb.rowQ >= 0 && jb.SP > 0.0 && jb.SQ > 0.0;
+  const bool resid = !PM && jb.rowQ >= 0 && jb.SP > 0.0 && jb.SQ > 0.0;
+  const bool pm_resid = PM && jb.SP > 0.0;  // a rejection, in a row with mass
   DrawSpec sp = job_spec<DT>(a, jb, 0.f);
   Slice<DT, kNT, HELD> sl;
   sl.load(sp.rowP, resid ? sp.rowQ : nullptr, v0, v1);
   double total;
   bool plain = false;
-  if (resid) {
+  if (pm_resid) {
+    // p_{n+1} without the rejected token, under the row's own shift
+    sp.rowQ = nullptr;
+    sp.cmP = jb.cmP;
+    sp.invSP = 1.f;
+    sp.ex = &s_job.ex;
+    sp.nex = jb.ex >= 0 ? 1 : 0;
+    total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
+    if (!(total > 0.0)) {
+      // the row is a point mass at the rejected token (by rounding): draw from it
+      sp.nex = 0;
+      total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
+    }
+  } else if (resid) {
     total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
     if (!(total > 0.0)) {
       // residual mass rounded to 0: draw from p_{n+1} itself
@@ -298,10 +340,18 @@ hipError_t launch_chain_t(const ChainParams& p, const Plan& plan, hipStream_t s)
   // B * G <= the blocks the device holds at once (chosen by the caller): a
   // sequence's blocks are resident together on an otherwise idle device,
   // and their waits are bounded either way
-  if (p.held)
-    chain_draw_kernel<DT, true><<<dim3((unsigned)p.B * p.G), dim3(kNT), 0, s>>>(p);
-  else
-    chain_draw_kernel<DT, false><<<dim3((unsigned)p.B * p.G), dim3(kNT), 0, s>>>(p);
+  const dim3 grid((unsigned)p.B * p.G);
+  if (p.pm) {
+    if (p.held)
+      chain_draw_kernel<DT, true, true><<<grid, dim3(kNT), 0, s>>>(p);
+    else
+      chain_draw_kernel<DT, false, true><<<grid, dim3(kNT), 0, s>>>(p);
+  } else {
+    if (p.held)
+      chain_draw_kernel<DT, true, false><<<grid, dim3(kNT), 0, s>>>(p);
+    else
+      chain_draw_kernel<DT, false, false><<<grid, dim3(kNT), 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 
@@ -309,20 +359,24 @@ hipError_t launch_chain(const ChainParams& p, sv_dtype dt, const Plan& plan, hip
   return dt == SV_BF16 ? launch_chain_t<SV_BF16>(p, plan, s) : launch_chain_t<SV_F32>(p, plan, s);
 }
 
+template <int DT, bool PM>
+const void* draw_fn(bool held) {
+  return held ? reinterpret_cast<const void*>(&chain_draw_kernel<DT, true, PM>)
+              : reinterpret_cast<const void*>(&chain_draw_kernel<DT, false, PM>);
+}
+
 // Blocks of the draw kernel the device holds at once.
-int chain_draw_capacity(sv_dtype dt, bool held) {
-  static int cache[2][2][64];
+int chain_draw_capacity(sv_dtype dt, bool held, bool pm) {
+  static int cache[2][2][2][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int& c = cache[dt == SV_BF16][held][dev];
+  int& c = cache[dt == SV_BF16][held][pm][dev];
   if (c == 0) {
     const void* fn;
     if (dt == SV_BF16)
-      fn = held ? reinterpret_cast<const void*>(&chain_draw_kernel<SV_BF16, true>)
-                : reinterpret_cast<const void*>(&chain_draw_kernel<SV_BF16, false>);
+      fn = pm ? draw_fn<SV_BF16, true>(held) : draw_fn<SV_BF16, false>(held);
     else
-      fn = held ? reinterpret_cast<const void*>(&chain_draw_kernel<SV_F32, true>)
-                : reinterpret_cast<const void*>(&chain_draw_kernel<SV_F32, false>);
+      fn = pm ? draw_fn<SV_F32, true>(held) : draw_fn<SV_F32, false>(held);
     c = device_capacity(fn, kNT, dev);
   }
   return c;

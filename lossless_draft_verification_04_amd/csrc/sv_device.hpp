@@ -355,6 +355,8 @@ __device__ __forceinline__ double prob_of(float z, float c, const RowStat& st) {
 //   residual: w = max(0, p - coef * q), p and q normalised by their row
 //             statistics (coef = 1 for a chain, c_i for a tree node);
 //   plain:    w = 2^(z c - cm) (bonus draw / fallback, unnormalised).
+// Either form may exclude a short list of token ids (weight 0): the
+// point-mass rule's rejected tokens.
 // ---------------------------------------------------------------------------
 struct DrawSpec {
   const void* rowP;
@@ -363,6 +365,8 @@ struct DrawSpec {
   float cmP, invSP;  // residual: p = 2^(zP c - cmP) * invSP; plain: shift cmP, invSP unused
   float cmQ, invSQ;
   float coef;
+  const int32_t* ex;  // excluded token ids (LDS, same in every thread)
+  int32_t nex;        // their count (0: none)
 };
 
 template <int DT>
@@ -388,6 +392,12 @@ __device__ __forceinline__ void draw_weights_from(const DrawSpec& sp, int V, int
 #pragma unroll
     for (int e = 0; e < E; ++e)
       if (vi * E + e >= V) w[e] = 0.f;
+  }
+  for (int i = 0; i < sp.nex; ++i) {
+    const int64_t d = (int64_t)sp.ex[i] - vi * E;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (d == e) w[e] = 0.f;
   }
 }
 

@@ -38,6 +38,7 @@ struct ChainParams {
   int32_t nch1;
   int32_t G;       // draw blocks per sequence
   bool held;       // slices of at most kSliceTiles tiles, held in registers
+  bool pm;         // point-mass acceptance: target rows only
   int64_t vpc1, nvec;
 };
 
@@ -78,6 +79,7 @@ struct TreeParams {
   int32_t nch;
   int32_t G;       // walk blocks per sequence
   bool held;       // slices of at most kSliceTiles tiles, held in registers
+  bool pm;         // point-mass acceptance: target rows only
   int64_t vpc, nvec;
 };
 
@@ -114,8 +116,8 @@ hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s);
 
 // Blocks of one launch of the draw / walk kernel (held or streamed slices)
 // the current device holds at once (0 if unknown).
-int chain_draw_capacity(sv_dtype dt, bool held);
-int tree_walk_capacity(sv_dtype dt, bool held);
+int chain_draw_capacity(sv_dtype dt, bool held, bool pm);
+int tree_walk_capacity(sv_dtype dt, bool held, bool pm);
 
 // Blocks of kernel fn (block of nt threads) device dev holds at once.
 inline int device_capacity(const void* fn, int nt, int dev) {

@@ -25,6 +25,18 @@
 //     row pair into registers; each rejection is one pass over that slice,
 //     the pass totals are exchanged, and the final draw searches one held
 //     slice.
+//
+// Point-mass mode (SpecDiff-2 page, Core method: accept a drafted token with
+// the verifier's probability, resample the residual on a rejection; read as
+// the draft-then-verify page's §2.1 step with q a point mass at the child's
+// token).  At a node the children are tried in index order against a running
+// residual w = P_node with mass D = 1: child i is accepted iff
+// r_i < w(x_i) / D; a rejection removes x_i (D -= w(x_i), w(x_i) = 0), so a
+// repeated sibling token is rejected for sure.  Every decision is scalar
+// arithmetic on the gathered p(x_i): no pass over V until the one final draw
+// (P_node without the rejected tokens, or the bonus row).  Only target rows
+// are streamed.  Exactly lossless for any sibling tokens, deterministic top-F
+// ones included.
 #include "sv_device.hpp"
 #include "sv_internal.h"
 #include "sv_walk.hpp"
@@ -40,8 +52,9 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
   const int64_t bid = blockIdx.x;
   const int ch = (int)(bid % a.nch);
   int64_t rest = bid / a.nch;
-  const int which = (int)(rest & 1);
-  rest >>= 1;
+  const int nw = a.pm ? 1 : 2;  // rows per node: target (and draft)
+  const int which = a.pm ? 0 : (int)(rest & 1);
+  if (!a.pm) rest >>= 1;
   const int b = (int)(rest % a.B);
   const int u = (int)(rest / a.B);
   zero_slots(a.slots, (int64_t)a.B * kSlotWords * a.G, bid, kTNT);  // for the walk launch
@@ -73,7 +86,7 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
   const int64_t v0 = (int64_t)ch * a.vpc;
   const int64_t v1 = v0 + a.vpc < a.nvec ? v0 + a.vpc : a.nvec;
   const Partial part = range_stats<DT, kTNT, kTU>(row, a.V, v0, v1, a.c);
-  if (threadIdx.x == 0) put_partial(static_cast<Partial*>(a.part) + ((rowbase + u) * 2 + which) * a.nch + ch, part);
+  if (threadIdx.x == 0) put_partial(static_cast<Partial*>(a.part) + ((rowbase + u) * nw + which) * a.nch + ch, part);
   float* zc = a.zc + (int64_t)which * a.B * a.N + rowbase;
 #pragma unroll
   for (int k = 0; k < kGather; ++k)
@@ -89,6 +102,55 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
 // draw searches it.
 // ---------------------------------------------------------------------------
 constexpr int kWNT = 256;  // walk block
+
+// Children of `node` in increasing index (from the staged parent array) into
+// s_kids; returns their count (the same in every thread).
+__device__ int node_children(int node, int N, const int32_t* s_par, int* s_kids, int* s_cnt) {
+  if (threadIdx.x == 0) *s_cnt = 0;
+  lds_sync();
+  for (int base = node + 1; base < N; base += kWNT) {
+    const int i = base + (int)threadIdx.x;
+    const int flag = (i < N) && s_par[i] == node;
+    double excl;
+    const double tot = block_exclusive_scan<kWNT>((double)flag, &excl);
+    if (flag) s_kids[*s_cnt + (int)excl] = i;
+    lds_sync();
+    if (threadIdx.x == 0) *s_cnt += (int)tot;
+    lds_sync();
+  }
+  return *s_cnt;
+}
+
+// Bonus draw from the row at rowP (a node without children, or at the depth
+// limit; the row was not streamed by the stats pass): the slices' statistics
+// in one exchange, then a plain draw under the row's shift.  Returns the
+// token in the block whose slice holds the draw, -1 in the others.
+template <int DT, bool HELD>
+__device__ int64_t bonus_draw(const TreeParams& a, Exchange& x, Slice<DT, kWNT, HELD>& sl, const void* rowP,
+                              int64_t v0, int64_t v1, double us, bool writer, uint64_t* s_w0, uint64_t* s_w1,
+                              double* s_val) {
+  sl.load(rowP, nullptr, v0, v1);
+  float M;
+  const double total = exchange_stats(x, sl.row_stats(a.c, a.V), a.c, s_w0, s_w1, s_val, &M);
+  if (M == kNegInf && writer && threadIdx.x == 0) set_error(a.err, SV_DERR_ROW);
+  DrawSpec sp;
+  sp.rowP = rowP;
+  sp.rowQ = nullptr;
+  sp.c = a.c;
+  sp.cmP = M == kNegInf ? 0.f : a.c * M;
+  sp.invSP = 1.f;
+  sp.cmQ = 0.f;
+  sp.invSQ = 1.f;
+  sp.coef = 0.f;
+  sp.ex = nullptr;
+  sp.nex = 0;
+  int pick;
+  double loc;
+  slice_scan(s_val, x.G, us * total, &pick, &loc);
+  if (pick != x.g) return -1;
+  sl.prepare(sp, a.V);
+  return sl.search(sp, a.V, loc);
+}
 
 template <int DT, bool HELD>
 __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
@@ -153,45 +215,11 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   int64_t t = -1;
   Slice<DT, kWNT, HELD> sl;
   for (;;) {
-    // children of `node` in increasing index (from LDS)
-    if (threadIdx.x == 0) s_cnt = 0;
-    lds_sync();
-    for (int base = node + 1; base < a.N; base += kWNT) {
-      const int i = base + (int)threadIdx.x;
-      const int flag = (i < a.N) && s_par[i] == node;
-      double excl;
-      const double tot = block_exclusive_scan<kWNT>((double)flag, &excl);
-      if (flag) s_kids[s_cnt + (int)excl] = i;
-      lds_sync();
-      if (threadIdx.x == 0) s_cnt += (int)tot;
-      lds_sync();
-    }
-    const int nk = s_cnt;
+    const int nk = node_children(node, a.N, s_par, s_kids, &s_cnt);
     const void* rowP = row_ptr(a.tgt, rowbase + node, a.tgt_sb);
     if (nk == 0 || depth >= a.max_depth) {
       if (nk > 0 && writer) set_error(a.err, SV_DERR_TREE);
-      // bonus draw from P_node (not streamed by the stats pass): slice
-      // statistics in one exchange, then a plain draw with the row's shift
-      sl.load(rowP, nullptr, v0, v1);
-      float M;
-      const double total = exchange_stats(x, sl.row_stats(a.c, a.V), a.c, s_w0, s_w1, s_val, &M);
-      if (M == kNegInf && writer && threadIdx.x == 0) set_error(a.err, SV_DERR_ROW);
-      DrawSpec sp;
-      sp.rowP = rowP;
-      sp.rowQ = nullptr;
-      sp.c = a.c;
-      sp.cmP = M == kNegInf ? 0.f : a.c * M;
-      sp.invSP = 1.f;
-      sp.cmQ = 0.f;
-      sp.invSQ = 1.f;
-      sp.coef = 0.f;
-      int pick;
-      double loc;
-      slice_scan(s_val, x.G, us * total, &pick, &loc);
-      if (pick == g) {
-        sl.prepare(sp, a.V);
-        t = sl.search(sp, a.V, loc);
-      }
+      t = bonus_draw<DT, HELD>(a, x, sl, rowP, v0, v1, us, writer, s_w0, s_w1, s_val);
       break;
     }
     const void* rowQ = row_ptr(a.drf, rowbase + node, a.drf_sb);
@@ -226,6 +254,8 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     sp.invSP = P.S > 0.0 ? (float)(1.0 / P.S) : 0.f;
     sp.cmQ = Q.cm;
     sp.invSQ = Q.S > 0.0 ? (float)(1.0 / Q.S) : 0.f;
+    sp.ex = nullptr;
+    sp.nex = 0;
     double c = 0.0, D = 1.0;
     bool sums_current = false;  // the slice holds the sums of the current residual
     int accepted = -1;
@@ -283,6 +313,172 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   if (t >= 0 && threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
 }
 
+// Point-mass walk.  The G blocks of a sequence replay the same scalar
+// decisions; only the final draw touches the logits (one row, one exchange).
+template <int DT, bool HELD>
+__global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
+  const int b = blockIdx.x / a.G;
+  const int g = blockIdx.x - b * a.G;
+  Exchange x = make_exchange(a.slots, a.err, b, a.G, g);
+  const int64_t spv = (a.nvec + a.G - 1) / a.G;
+  const int64_t v0 = (int64_t)g * spv < a.nvec ? (int64_t)g * spv : a.nvec;
+  const int64_t v1 = v0 + spv < a.nvec ? v0 + spv : a.nvec;
+  constexpr int E = Fmt<DT>::kPerVec;
+  const int64_t e0 = v0 * E, e1 = v1 * E;  // this block's token range
+  const bool writer = (g == 0);
+  const int64_t rowbase = (int64_t)b * a.N;
+  const Partial* parts = static_cast<const Partial*>(a.part);
+  __shared__ int32_t s_par[SV_MAX_N];
+  __shared__ int32_t s_tok[SV_MAX_N];
+  __shared__ int s_kids[SV_MAX_N];
+  __shared__ int32_t s_path[SV_MAX_N];
+  __shared__ float s_zp[SV_MAX_N];   // each child's logit under its parent's target row
+  __shared__ float s_cm[SV_MAX_N];   // target row statistics of the nodes with children
+  __shared__ double s_S[SV_MAX_N];
+  __shared__ double s_pt[SV_MAX_N];  // the current node's children, in order: p(x_i)
+  __shared__ double s_w[SV_MAX_N];   // w(x_i) when child i is tried (0 for a repeated token)
+  __shared__ float s_r[SV_MAX_N];
+  __shared__ int32_t s_ex[SV_MAX_N];  // rejected tokens inside this block's slice
+  __shared__ uint64_t s_w0[kMaxG], s_w1[kMaxG];
+  __shared__ double s_val[kMaxG];
+  __shared__ int s_cnt;
+  const double us = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
+
+  const float* zc = a.zc + rowbase;
+  for (int i = threadIdx.x; i < a.N; i += kWNT) {
+    s_par[i] = a.parent[rowbase + i];
+    s_tok[i] = a.tok[rowbase + i];
+    s_zp[i] = zc[i];
+  }
+  for (int u = threadIdx.x; u < a.N - 1; u += kWNT) {
+    const Partial* pr = parts + (rowbase + u) * a.nch;  // written by the previous launch
+    float M = kNegInf;
+    for (int i = 0; i < a.nch; ++i) M = fmaxf(M, pr[i].m);
+    float cm = 0.f;
+    double S = 0.0;
+    if (M != kNegInf) {
+      cm = a.c * M;
+      if (a.nch == 1) {
+        S = pr[0].s;
+      } else {
+        for (int i = 0; i < a.nch; ++i) {
+          const Partial pi = pr[i];
+          if (pi.m != kNegInf) S += pi.s * exp2((double)(a.c * pi.m) - (double)cm);
+        }
+      }
+    }
+    s_cm[u] = cm;
+    s_S[u] = S;
+  }
+  lds_sync();
+  if (writer)
+    for (int i = 1 + threadIdx.x; i < a.N; i += kWNT)
+      if (s_par[i] < 0 || s_par[i] >= i) set_error(a.err, SV_DERR_TREE);
+
+  int node = 0, depth = 0;
+  int64_t t = -1;
+  Slice<DT, kWNT, HELD> sl;
+  for (;;) {
+    const int nk = node_children(node, a.N, s_par, s_kids, &s_cnt);
+    const void* rowP = row_ptr(a.tgt, rowbase + node, a.tgt_sb);
+    if (nk == 0 || depth >= a.max_depth) {
+      if (nk > 0 && writer) set_error(a.err, SV_DERR_TREE);
+      t = bonus_draw<DT, HELD>(a, x, sl, rowP, v0, v1, us, writer, s_w0, s_w1, s_val);
+      break;
+    }
+    RowStat P;
+    P.cm = s_cm[node];
+    P.S = s_S[node];
+    P.pad = 0.f;
+    if (writer && threadIdx.x == 0 && !(P.S > 0.0)) set_error(a.err, SV_DERR_ROW);
+    // every child's p, uniform and residual weight in parallel: all earlier
+    // siblings are rejected when child i is tried, so w(x_i) is p(x_i) unless
+    // an earlier sibling carries the same token
+    for (int k = threadIdx.x; k < nk; k += kWNT) {
+      const int cn = s_kids[k];
+      const float zp = s_zp[cn];
+      const double pt = __builtin_isnan(zp) ? 0.0 : prob_of(zp, a.c, P);
+      const int32_t tk = s_tok[cn];
+      bool repeated = false;
+      for (int j = 0; j < k && !repeated; ++j) repeated = s_tok[s_kids[j]] == tk;
+      s_pt[k] = pt;
+      s_w[k] = repeated ? 0.0 : pt;
+      s_r[k] = (float)uniform24(a.seed, (uint32_t)cn, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
+    }
+    lds_sync();
+    double D = 1.0;
+    int accepted = -1, tried = nk;
+    for (int kk = 0; kk < nk; ++kk) {
+      const double w = s_w[kk];
+      const double ar = D > 0.0 ? accept_ratio(w / D, 1.0) : 0.0;
+      if ((double)s_r[kk] < ar) {
+        accepted = s_kids[kk];
+        tried = kk + 1;
+        break;
+      }
+      D -= w;
+    }
+    if (writer)
+      for (int k = threadIdx.x; k < tried; k += kWNT) {
+        const int cn = s_kids[k];
+        if (__builtin_isnan(s_zp[cn])) set_error(a.err, SV_DERR_TOKEN);
+        if (a.out_p) a.out_p[rowbase + cn] = (float)s_pt[k];
+      }
+    if (accepted >= 0) {
+      if (threadIdx.x == 0) s_path[depth] = accepted;
+      ++depth;
+      node = accepted;
+      lds_sync();
+      continue;
+    }
+    // every child rejected: P_node without the children's tokens; this
+    // block's list holds those inside its slice
+    if (threadIdx.x == 0) s_cnt = 0;
+    lds_sync();
+    for (int base = 0; base < nk; base += kWNT) {
+      const int k = base + (int)threadIdx.x;
+      const int32_t tk = k < nk ? s_tok[s_kids[k]] : -1;
+      const int flag = tk >= 0 && tk < a.V && tk >= e0 && tk < e1;
+      double excl;
+      const double tot = block_exclusive_scan<kWNT>((double)flag, &excl);
+      if (flag) s_ex[s_cnt + (int)excl] = tk;
+      lds_sync();
+      if (threadIdx.x == 0) s_cnt += (int)tot;
+      lds_sync();
+    }
+    DrawSpec sp;
+    sp.rowP = rowP;
+    sp.rowQ = nullptr;
+    sp.c = a.c;
+    sp.cmP = P.cm;
+    sp.invSP = 1.f;
+    sp.cmQ = 0.f;
+    sp.invSQ = 1.f;
+    sp.coef = 0.f;
+    sp.ex = s_ex;
+    sp.nex = s_cnt;
+    sl.load(rowP, nullptr, v0, v1);
+    double total = exchange_sum(x, sl.prepare(sp, a.V), s_w0, s_val);
+    if (!(total > 0.0)) {
+      // the row's mass sits on the rejected tokens (by rounding): draw from P_node
+      sp.nex = 0;
+      total = exchange_sum(x, sl.prepare(sp, a.V), s_w0, s_val);
+    }
+    int pick;
+    double loc;
+    slice_scan(s_val, x.G, us * total, &pick, &loc);
+    if (pick == g) t = sl.search(sp, a.V, loc);
+    break;
+  }
+  lds_sync();
+  if (writer) {
+    for (int d = threadIdx.x; d < a.max_depth; d += kWNT)
+      a.out_path[(int64_t)b * a.max_depth + d] = d < depth ? s_path[d] : -1;
+    if (threadIdx.x == 0) a.out_len[b] = depth;
+  }
+  if (t >= 0 && threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
+}
+
 template <int DT>
 hipError_t launch_tree_t(const TreeParams& p, const Plan& plan, hipStream_t s) {
   tree_stats_kernel<DT><<<dim3((unsigned)plan.grid1), dim3(kTNT), 0, s>>>(p);
@@ -291,10 +487,18 @@ hipError_t launch_tree_t(const TreeParams& p, const Plan& plan, hipStream_t s) {
   // B * G <= the blocks the device holds at once (chosen by the caller): a
   // sequence's blocks are resident together on an otherwise idle device,
   // and their waits are bounded either way
-  if (p.held)
-    tree_walk_kernel<DT, true><<<dim3((unsigned)p.B * p.G), dim3(kWNT), 0, s>>>(p);
-  else
-    tree_walk_kernel<DT, false><<<dim3((unsigned)p.B * p.G), dim3(kWNT), 0, s>>>(p);
+  const dim3 grid((unsigned)p.B * p.G);
+  if (p.pm) {
+    if (p.held)
+      tree_pm_walk_kernel<DT, true><<<grid, dim3(kWNT), 0, s>>>(p);
+    else
+      tree_pm_walk_kernel<DT, false><<<grid, dim3(kWNT), 0, s>>>(p);
+  } else {
+    if (p.held)
+      tree_walk_kernel<DT, true><<<grid, dim3(kWNT), 0, s>>>(p);
+    else
+      tree_walk_kernel<DT, false><<<grid, dim3(kWNT), 0, s>>>(p);
+  }
   return hipGetLastError();
 }
 
@@ -302,20 +506,23 @@ hipError_t launch_tree(const TreeParams& p, sv_dtype dt, const Plan& plan, hipSt
   return dt == SV_BF16 ? launch_tree_t<SV_BF16>(p, plan, s) : launch_tree_t<SV_F32>(p, plan, s);
 }
 
+template <int DT>
+const void* walk_fn(bool held, bool pm) {
+  if (pm)
+    return held ? reinterpret_cast<const void*>(&tree_pm_walk_kernel<DT, true>)
+                : reinterpret_cast<const void*>(&tree_pm_walk_kernel<DT, false>);
+  return held ? reinterpret_cast<const void*>(&tree_walk_kernel<DT, true>)
+              : reinterpret_cast<const void*>(&tree_walk_kernel<DT, false>);
+}
+
 // Blocks of the walk kernel the device holds at once.
-int tree_walk_capacity(sv_dtype dt, bool held) {
-  static int cache[2][2][64];
+int tree_walk_capacity(sv_dtype dt, bool held, bool pm) {
+  static int cache[2][2][2][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int& c = cache[dt == SV_BF16][held][dev];
+  int& c = cache[dt == SV_BF16][held][pm][dev];
   if (c == 0) {
-    const void* fn;
-    if (dt == SV_BF16)
-      fn = held ? reinterpret_cast<const void*>(&tree_walk_kernel<SV_BF16, true>)
-                : reinterpret_cast<const void*>(&tree_walk_kernel<SV_BF16, false>);
-    else
-      fn = held ? reinterpret_cast<const void*>(&tree_walk_kernel<SV_F32, true>)
-                : reinterpret_cast<const void*>(&tree_walk_kernel<SV_F32, false>);
+    const void* fn = dt == SV_BF16 ? walk_fn<SV_BF16>(held, pm) : walk_fn<SV_F32>(held, pm);
     c = device_capacity(fn, kWNT, dev);
   }
   return c;

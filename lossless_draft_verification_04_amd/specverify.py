@@ -30,7 +30,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 SV_OK, SV_EINVAL, SV_EDTYPE, SV_EALIGN, SV_EWORKSPACE, SV_EUNSUPPORTED, SV_EHIP = range(7)
 SV_F32, SV_BF16 = 0, 1
-SV_OP_CHAIN, SV_OP_GREEDY, SV_OP_MULTI, SV_OP_TREE, SV_OP_FANOUT = range(5)
+SV_OP_CHAIN, SV_OP_GREEDY, SV_OP_MULTI, SV_OP_TREE, SV_OP_FANOUT, SV_OP_CHAIN_PM, SV_OP_TREE_PM = range(7)
 DERR_TOKEN, DERR_TREE, DERR_FANOUT, DERR_ROW = 1, 2, 4, 8
 
 _P = ctypes.c_void_p
@@ -50,6 +50,9 @@ _SIGS = {
                          _P, _P, _P, _sz, _P], _i32),
     "sv_verify_tree": ([_P, _P, _i32, _i64, _i64, _P, _P, _i32, _i32, _i32, _i32, _f32, _u64, _u32, _P, _P, _P,
                         _P, _P, _P, _sz, _P], _i32),
+    "sv_verify_chain_pm": ([_P, _i32, _i64, _P, _i32, _i32, _i32, _f32, _u64, _u32, _P, _P, _P, _P, _sz, _P], _i32),
+    "sv_verify_tree_pm": ([_P, _i32, _i64, _P, _P, _i32, _i32, _i32, _i32, _f32, _u64, _u32, _P, _P, _P, _P, _P,
+                           _sz, _P], _i32),
     "sv_fanout_topk": ([_P, _i32, _i64, _i32, _i32, _P, _i32, _P, _P, _P, _sz, _P], _i32),
     "sv_geometric_fanout": ([_i32, _f64, _f64, _i32, _i32, ctypes.POINTER(_i32)], _i32),
 }
@@ -164,6 +167,24 @@ def sv_verify_chain(tgt, drf, tok, T, seed=0, round_=0, want_pq=True, workspace=
     return dict(n=out_n, tok=out_tok, p=p, q=q)
 
 
+def sv_verify_chain_pm(tgt, tok, T, seed=0, round_=0, want_p=True, workspace=None):
+    """Point-mass acceptance. tgt [B, gamma+1, V], tok [B, gamma] int32 -> dict(n, tok, p)."""
+    B, g1, V = tgt.shape
+    gamma = g1 - 1
+    _i32_tensor(tok, (B, gamma), "tok")
+    dt = _dtype_code(tgt)
+    dev = tgt.device
+    ws = workspace if workspace is not None else Workspace.get(
+        dev, workspace_size(SV_OP_CHAIN_PM, dt, B, 1, gamma, V))
+    out_n = torch.empty(B, dtype=torch.int32, device=dev)
+    out_tok = torch.empty(B, dtype=torch.int32, device=dev)
+    p = torch.empty(B, gamma, dtype=torch.float32, device=dev) if want_p else None
+    _check(_lib.sv_verify_chain_pm(_ptr(tgt), dt, _row_stride(tgt, "tgt"), _ptr(tok), B, gamma, V, float(T),
+                                   int(seed), int(round_), _ptr(out_n), _ptr(out_tok), _ptr(p), _ptr(ws),
+                                   ws.numel(), _stream(dev)), "sv_verify_chain_pm")
+    return dict(n=out_n, tok=out_tok, p=p)
+
+
 def sv_verify_greedy(tgt, tok, want_argmax=True, workspace=None):
     """tgt [B, gamma+1, V], tok [B, gamma] -> dict(n, tok, argmax [B, gamma+1])."""
     B, g1, V = tgt.shape
@@ -221,6 +242,25 @@ def sv_verify_tree(tgt, drf, node_tok, parent, max_depth, T, seed=0, round_=0, w
                                _ptr(node_tok), _ptr(parent), B, N, int(max_depth), V, float(T), int(seed),
                                int(round_), _ptr(out["len"]), _ptr(out["path"]), _ptr(out["tok"]), _ptr(out["p"]),
                                _ptr(out["q"]), _ptr(ws), ws.numel(), _stream(dev)), "sv_verify_tree")
+    return out
+
+
+def sv_verify_tree_pm(tgt, node_tok, parent, max_depth, T, seed=0, round_=0, want_p=True, workspace=None):
+    """Point-mass acceptance. tgt [B, N, V]; node_tok, parent [B, N] -> dict(len, path, tok, p)."""
+    B, N, V = tgt.shape
+    _i32_tensor(node_tok, (B, N), "node_tok")
+    _i32_tensor(parent, (B, N), "parent")
+    dt = _dtype_code(tgt)
+    dev = tgt.device
+    ws = workspace if workspace is not None else Workspace.get(dev, workspace_size(SV_OP_TREE_PM, dt, B, 1, N, V))
+    out = dict(len=torch.empty(B, dtype=torch.int32, device=dev),
+               path=torch.empty(B, max_depth, dtype=torch.int32, device=dev),
+               tok=torch.empty(B, dtype=torch.int32, device=dev),
+               p=torch.full((B, N), float("nan"), dtype=torch.float32, device=dev) if want_p else None)
+    _check(_lib.sv_verify_tree_pm(_ptr(tgt), dt, _row_stride(tgt, "tgt"), _ptr(node_tok), _ptr(parent), B, N,
+                                  int(max_depth), V, float(T), int(seed), int(round_), _ptr(out["len"]),
+                                  _ptr(out["path"]), _ptr(out["tok"]), _ptr(out["p"]), _ptr(ws), ws.numel(),
+                                  _stream(dev)), "sv_verify_tree_pm")
     return out
 
 

@@ -137,6 +137,45 @@ def tree(wl, seed=0, round_=0):
     return out, ref
 
 
+def chain_pm(wl, seed=0, round_=0, T=None):
+    T = f32(wl.params["T"] if T is None else T)
+    g = wl.to(DEV)
+    say(f"  chain_pm B={wl.params['B']} gamma={wl.params['gamma']} V={wl.params['V']} {wl.params['dtype']} "
+        f"T={T} seed={seed} round={round_}")
+    out = svx.sv_verify_chain_pm(g["tgt"], g["tok"], T, seed=seed, round_=round_)
+    torch.cuda.synchronize()
+    ref = oracle.verify_chain_pm(np_logits(wl.tensors["tgt"]), wl.tensors["tok"].numpy(), T, seed, round_,
+                                 wl.params["dtype"])
+    n, t = out["n"].cpu().numpy(), out["tok"].cpu().numpy()
+    exc = (ref["mdec"] < MARGIN) | (ref["mcdf"] < MARGIN)
+    check_excepted("chain_pm n/tok", exc, (n != ref["n"]) | (t != ref["t"]))
+    check_probs("chain_pm p", out["p"].cpu().numpy(), ref["p"])
+    return out, ref
+
+
+def tree_pm(wl, seed=0, round_=0):
+    T = f32(wl.params["T"])
+    g = wl.to(DEV)
+    p = wl.params
+    md = p["max_depth"]
+    say(f"  tree_pm B={p['B']} N={p['N']} depth<={md} V={p['V']} {p['dtype']} seed={seed} round={round_}")
+    out = svx.sv_verify_tree_pm(g["tgt"], g["tok"], g["parent"], md, T, seed=seed, round_=round_)
+    torch.cuda.synchronize()
+    ref = oracle.verify_tree_pm(np_logits(wl.tensors["tgt"]), wl.tensors["tok"].numpy(),
+                                wl.tensors["parent"].numpy(), md, T, seed, round_, p["dtype"])
+    L, path, t = out["len"].cpu().numpy(), out["path"].cpu().numpy(), out["tok"].cpu().numpy()
+    exc = (ref["mdec"] < MARGIN) | (ref["mcdf"] < MARGIN)
+    mism = (L != ref["len"]) | (t != ref["t"]) | (path != ref["path"]).any(1)
+    check_excepted("tree_pm len/path/tok", exc, mism)
+    tried = ~np.isnan(ref["p"])
+    got_p = out["p"].cpu().numpy()
+    mask = tried & (~mism)[:, None]
+    check_probs("tree_pm p", got_p, ref["p"], mask)
+    # children the oracle did not try stay untouched where both walked the same path
+    assert np.isnan(got_p[~tried & (~mism)[:, None]]).all()
+    return out, ref
+
+
 def fanout(logits_cpu, F_cpu, F_max):
     dt = dtype_name(logits_cpu)
     say(f"  fanout R={logits_cpu.shape[0]} V={logits_cpu.shape[1]} F_max={F_max} {dt}")

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 11
+    assert len(names) == 13
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(svx.EXPORTED)
@@ -59,9 +59,16 @@ def test_workspace_size():
     assert st == svx.SV_OK and n > 65536 * 4
     st2, n2 = ws_size(svx.SV_OP_MULTI, svx.SV_BF16, 32, 1, 16, 152064)
     assert st2 == svx.SV_OK and n2 == n  # multi with K = 1 is the chain
-    for op in range(5):
+    for op in range(7):
         st, n = ws_size(op, svx.SV_BF16, 8, 2, 16, 1000, 8)
         assert st == svx.SV_OK and n % 256 == 0
+    # point-mass calls stream no draft rows: never more scratch than the standard ones
+    for std, pm, g in ((svx.SV_OP_CHAIN, svx.SV_OP_CHAIN_PM, 16), (svx.SV_OP_TREE, svx.SV_OP_TREE_PM, 64)):
+        n_std = ws_size(std, svx.SV_BF16, 32, 1, g, 152064)[1]
+        n_pm = ws_size(pm, svx.SV_BF16, 32, 1, g, 152064)[1]
+        assert 0 < n_pm <= n_std
+    assert ws_size(svx.SV_OP_CHAIN_PM, 0, 1, 1, 65, 100)[0] == svx.SV_EUNSUPPORTED
+    assert ws_size(svx.SV_OP_TREE_PM, 0, 1, 1, 1025, 100)[0] == svx.SV_EUNSUPPORTED
     assert ws_size(svx.SV_OP_CHAIN, 7, 1, 1, 4, 100)[0] == svx.SV_EDTYPE
     assert ws_size(svx.SV_OP_CHAIN, 0, 1, 1, 0, 100)[0] == svx.SV_EINVAL
     assert ws_size(svx.SV_OP_CHAIN, 0, 1, 1, 65, 100)[0] == svx.SV_EUNSUPPORTED
@@ -70,6 +77,7 @@ def test_workspace_size():
     assert ws_size(svx.SV_OP_FANOUT, 0, 4, 1, 1, 100, 65)[0] == svx.SV_EUNSUPPORTED
     assert ws_size(svx.SV_OP_CHAIN, 0, 1, 1, 4, (1 << 24) + 1)[0] == svx.SV_EUNSUPPORTED
     assert ws_size(9, 0, 1, 1, 4, 100)[0] == svx.SV_EINVAL
+    assert ws_size(-1, 0, 1, 1, 4, 100)[0] == svx.SV_EINVAL
 
 
 def chain(tgt=A, drf=A2, dt=svx.SV_BF16, ts=1024, ds=1024, tok=A, B=2, g=4, V=1000, T=1.0, rnd=0,
@@ -119,6 +127,26 @@ def test_multi_greedy_tree_fanout_argument_checks():
                                       1 << 30, None)
     assert f(Fm=0) == svx.SV_EINVAL and f(Fm=65) == svx.SV_EUNSUPPORTED and f(F=None) == svx.SV_EINVAL
     assert f(R=0) == svx.SV_OK
+
+
+def test_point_mass_argument_checks():
+    c = lambda **kw: L.sv_verify_chain_pm(kw.get("tgt", A), kw.get("dt", 1), kw.get("ts", 1024), kw.get("tok", A),
+                                          kw.get("B", 2), kw.get("g", 4), 1000, kw.get("T", 1.0), 0,
+                                          kw.get("rnd", 0), kw.get("n", A), A, None, kw.get("ws", WS),
+                                          kw.get("wsb", 1 << 30), None)
+    assert c(dt=5) == svx.SV_EDTYPE and c(g=0) == svx.SV_EINVAL and c(g=65) == svx.SV_EUNSUPPORTED
+    assert c(T=0.0) == svx.SV_EINVAL and c(T=float("nan")) == svx.SV_EINVAL and c(rnd=1 << 30) == svx.SV_EINVAL
+    assert c(tgt=None) == svx.SV_EINVAL and c(tok=None) == svx.SV_EINVAL and c(n=None) == svx.SV_EINVAL
+    assert c(tgt=MIS) == svx.SV_EALIGN and c(ts=1004) == svx.SV_EALIGN and c(ts=999) == svx.SV_EINVAL
+    assert c(ws=None) == svx.SV_EWORKSPACE and c(wsb=1024) == svx.SV_EWORKSPACE
+    assert c(B=0) == svx.SV_OK
+    tr = lambda **kw: L.sv_verify_tree_pm(kw.get("tgt", A), 1, 1024, A, kw.get("par", A), kw.get("B", 2),
+                                          kw.get("N", 8), kw.get("md", 4), 1000, kw.get("T", 1.0), 0, 0,
+                                          kw.get("len", A), A, A, None, WS, kw.get("wsb", 1 << 30), None)
+    assert tr(N=0) == svx.SV_EINVAL and tr(N=1025) == svx.SV_EUNSUPPORTED and tr(md=0) == svx.SV_EINVAL
+    assert tr(md=1025) == svx.SV_EINVAL and tr(par=None) == svx.SV_EINVAL and tr(len=None) == svx.SV_EINVAL
+    assert tr(tgt=MIS) == svx.SV_EALIGN and tr(T=-2.0) == svx.SV_EINVAL and tr(wsb=64) == svx.SV_EWORKSPACE
+    assert tr(B=0) == svx.SV_OK
 
 
 def test_workspace_helpers_reject_bad_arguments():
