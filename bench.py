@@ -19,7 +19,8 @@ bonus row, per sequence) over its mean duration from HIP events recorded on
 the launch stream, against the 8 TB/s HBM peak.  `cpu_baseline` times the
 CPU oracle (single-threaded fp64) on the same workload.  `variants` holds the
 same measurements for the other rows of the hot path (greedy window,
-multi-candidate, tree, fan-out, and the small fp32 chain).
+multi-candidate, tree, fan-out, the small fp32 chain, and the point-mass
+chain and tree, which read no draft rows).
 """
 from __future__ import annotations
 
@@ -184,6 +185,29 @@ def bench_chain(wl, steps, warmup, seed=0):
                 alg_bytes=alg, mean_accepted=float(n.mean()), copies=len(copies), eager_ms_per_step=e_wall), out
 
 
+def device_copy(wl, keys):
+    """The named tensors of a workload on the GPU (padded row strides kept)."""
+    return W.Workload(wl.kind, wl.params, {k: wl.tensors[k] for k in keys}).to("cuda")
+
+
+def bench_chain_pm(wl, steps, warmup, seed=0):
+    """Point-mass chain on the chain workload: target rows 1..gamma per sequence, then one row."""
+    p = wl.params
+    T = float(np.float32(p["T"]))
+    per_copy = wl.tensors["tgt"].numel() * esize(p["dtype"])
+    copies = [device_copy(wl, ("tgt", "tok")) for _ in range(n_copies(per_copy))]
+    fn = lambda g: svx.sv_verify_chain_pm(g["tgt"], g["tok"], T, seed=seed, round_=0, want_p=False)
+    out = fn(copies[0])
+    torch.cuda.synchronize()
+    n = out["n"].cpu().numpy()
+    wall, ev_ms = time_graphs(fn, copies, steps, warmup)
+    B, g = p["B"], p["gamma"]
+    pos = B * g
+    alg = (g * B + B) * p["V"] * esize(p["dtype"])
+    return dict(positions_per_call=pos, positions_per_s=pos / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
+                alg_bytes=alg, mean_accepted=float(n.mean()), copies=len(copies))
+
+
 def bench_greedy(wl, steps, warmup):
     p = wl.params
     per_copy = wl.tensors["tgt"].numel() * esize(p["dtype"])
@@ -257,6 +281,26 @@ def bench_tree(wl, steps, warmup):
     fn = lambda g: svx.sv_verify_tree(g["tgt"], g["drf"], g["tok"], g["parent"], p["max_depth"], T, want_pq=False)
     wall, ev_ms = time_graphs(fn, copies, steps, warmup)
     pos = p["B"] * (p["N"] - 1)
+    return dict(positions_per_call=pos, positions_per_s=pos / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
+                alg_bytes=alg, mean_accepted=float(out["len"].float().mean().item()), copies=len(copies))
+
+
+def bench_tree_pm(wl, steps, warmup):
+    """Point-mass tree: the target row of every node with children, then one row per sequence (the
+    final node's row for the draw without the rejected tokens, or the bonus row)."""
+    p = wl.params
+    T = float(np.float32(p["T"]))
+    per_copy = wl.tensors["tgt"].numel() * esize(p["dtype"])
+    copies = [device_copy(wl, ("tgt", "tok", "parent")) for _ in range(n_copies(per_copy))]
+    fn = lambda g: svx.sv_verify_tree_pm(g["tgt"], g["tok"], g["parent"], p["max_depth"], T, want_p=False)
+    out = fn(copies[0])
+    torch.cuda.synchronize()
+    wall, ev_ms = time_graphs(fn, copies, steps, warmup)
+    parent = wl.tensors["parent"]
+    B, N = parent.shape
+    internal = sum(len(set(x for x in parent[b].tolist() if x >= 0)) for b in range(B))
+    alg = (internal + B) * p["V"] * esize(p["dtype"])
+    pos = B * (N - 1)
     return dict(positions_per_call=pos, positions_per_s=pos / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
                 alg_bytes=alg, mean_accepted=float(out["len"].float().mean().item()), copies=len(copies))
 
@@ -343,6 +387,7 @@ def main():
         warm_v = max(3, args.warmup // 2)
         for name, mk, fn in [
             ("chain_small_f32", lambda: W.chain_normal(**W.CHAIN_SMALL), lambda w: bench_chain(w, steps_v, warm_v)[0]),
+            ("chain_pm_batched", lambda: wl, lambda w: bench_chain_pm(w, steps_v, warm_v)),
             ("greedy_window", lambda: W.greedy_zipf(**W.GREEDY_WINDOW), lambda w: bench_greedy(w, steps_v, warm_v)),
             ("multi_candidate", lambda: W.multi_zipf(**W.MULTI_CAND), lambda w: bench_multi(w, steps_v, warm_v)),
             ("tree", lambda: W.tree_zipf(**W.TREE_FANOUT), lambda w: bench_tree(w, steps_v, warm_v)),
@@ -352,6 +397,8 @@ def main():
             variants[name] = summarize(fn(w))
             log(f"{name}: {variants[name]}")
             if name == "tree":
+                variants["tree_pm"] = summarize(bench_tree_pm(w, steps_v, warm_v))
+                log(f"tree_pm: {variants['tree_pm']}")
                 variants["fanout_tree_draft_rows"] = summarize(bench_fanout(w, steps_v, warm_v))
                 log(f"fanout: {variants['fanout_tree_draft_rows']}")
             del w

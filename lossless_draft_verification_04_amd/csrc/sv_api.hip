@@ -33,10 +33,14 @@ int stats_blocks() {
   static const int v = env_int("SV_STATS_BLOCKS", 1024);
   return v;
 }
-// Upper bound on the draw / walk blocks per sequence (SV_DRAW_G caps it for
-// tuning sweeps).
+// Upper bound on the draw / walk blocks per sequence (SV_DRAW_G overrides it
+// for tuning sweeps, up to kMaxG).  Measured on MI355X: at 48-64 blocks per
+// sequence the exchange costs more than the shorter slices save (point-mass
+// chain call on the 32 x 16 x 152064 batch: 46.4 us at 48, 41.5-42.0 us at
+// 24-32, 46.7 us at 16; the other paths change by under 2% from 24 to 64).
+constexpr int kDefaultDrawG = 32;
 int draw_g_limit() {
-  static const int v = env_int("SV_DRAW_G", kMaxG);
+  static const int v = env_int("SV_DRAW_G", kDefaultDrawG);
   return v < kMaxG ? v : kMaxG;
 }
 
