@@ -64,6 +64,8 @@ def _load(path):
     L.svo_verify_tree_pm.restype = i32
     L.svo_fanout_topk.argtypes = [P, i32, i64, i32, i32, P, i32, P, P]
     L.svo_fanout_topk.restype = i32
+    L.svo_cache_hit_test.argtypes = [P, i32, i64, i32, i32, i32, P, P, P, P, P]
+    L.svo_cache_hit_test.restype = i32
     L.svo_geometric_fanout.argtypes = [i32, f64, f64, i32, i32, P]
     L.svo_geometric_fanout.restype = i32
     return L
@@ -296,6 +298,20 @@ def fanout_topk(logits, F, F_max, dtype):
                                _ptr(vals))
     _check(rc, "fanout_topk")
     return ids, vals
+
+
+def cache_hit_test(drf, n, t, F, dtype):
+    """Speculation-cache hit test.  drf [B, K+1, V] draft rows per lookahead position, outcome (n, t) [B],
+    F [K+1] or None -> dict(rank [B], hit [B] or None)."""
+    drf, code = _logits(drf, dtype)
+    B, K1, V = drf.shape
+    n, t = _i32(n), _i32(t)
+    Fa = None if F is None else _i32(F)
+    out = dict(rank=np.zeros(B, np.int32), hit=None if F is None else np.zeros(B, np.int32))
+    rc = lib().svo_cache_hit_test(_ptr(drf), code, _row_stride(drf), B, K1 - 1, V, _ptr(n), _ptr(t), _ptr(Fa),
+                                  _ptr(out["rank"]), _ptr(out["hit"]))
+    _check(rc, "cache_hit_test")
+    return out
 
 
 def geometric_fanout(F0, a_p, r, K, capped_last=False):

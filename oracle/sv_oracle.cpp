@@ -741,6 +741,36 @@ int svo_fanout_topk(const void* logits, int dtype, int64_t stride, int R, int V,
   return 0;
 }
 
+// Speculation-cache hit test ([SSD] §3, cache strategy: for every lookahead
+// position k = 0..K the cache holds the top-F_k tokens of the draft logits at
+// k; a verification outcome (k', t*) is served from the cache iff t* is among
+// the tokens cached for k' = the hit event of Definition 11).  Draft row
+// (b, k) = b*(K+1) + k.  For sequence b with outcome (n[b], t[b]):
+// out_rank[b] = the 0-based position of t[b] in draft row (b, n[b]) under the
+// fan-out's order (value descending, index ascending on equal values), so the
+// outcome is cached iff out_rank[b] < F[n[b]]; out_hit[b] is that test (F and
+// out_hit may be null).  The row is sorted in full by that total order.
+int svo_cache_hit_test(const void* drf, int dtype, int64_t stride, int B, int K, int V, const int32_t* n,
+                       const int32_t* t, const int32_t* F, int32_t* out_rank, int32_t* out_hit) {
+  if (B < 0 || K < 0 || V < 1) return 1;
+  std::vector<int> order(V);
+  std::vector<double> z(V);
+  for (int b = 0; b < B; ++b) {
+    if (n[b] < 0 || n[b] > K || t[b] < 0 || t[b] >= V) return 3;
+    const int64_t row = (int64_t)b * (K + 1) + n[b];
+    for (int v = 0; v < V; ++v) {
+      order[v] = v;
+      z[v] = load_logit(drf, dtype, row * stride + v);
+    }
+    std::sort(order.begin(), order.end(), [&](int a, int c) { return z[a] > z[c] || (z[a] == z[c] && a < c); });
+    int pos = 0;
+    while (order[pos] != t[b]) ++pos;
+    out_rank[b] = pos;
+    if (F && out_hit) out_hit[b] = pos < F[n[b]] ? 1 : 0;
+  }
+  return 0;
+}
+
 // Geometric fan-out of [SSD] Theorem 12: F_k = F_0 * a_p^{k/(1+r)} for k < K
 // and, when capped_last, F_K = F_0 * a_p^{K/(1+r)} * (1 - a_p)^{-1/(1+r)};
 // rounded up to integers.  Writes K+1 values; returns their sum.

@@ -37,6 +37,12 @@ PM_TREE_PINS = [
     pins.test_pm_repeated_sibling_token_is_rejected_and_removes_nothing,
     pins.test_pm_chain_shaped_tree_is_pm_chain,
 ]
+CACHE_PINS = [
+    pins.test_cache_rank_is_position_in_numpy_stable_order,
+    pins.test_cache_rank_brute_force_count,
+    pins.test_cache_hit_is_membership_in_the_fanout_cache,
+]
+
 
 MUTANTS = [
     # (name, original text, planted text, pins expected to catch it)
@@ -73,6 +79,11 @@ MUTANTS = [
     ("point-mass tree ratio not renormalised", "accept_ratio(w[tok] / D, 1.0)", "accept_ratio(w[tok], 1.0)",
      PM_TREE_PINS),
     ("point-mass tree draw ignores removals", "    if (!(mass > 0.0)) w = p;\n", "    w = p;\n", PM_TREE_PINS),
+    ("cache rank ties to the highest index", "(z[a] == z[c] && a < c)", "(z[a] == z[c] && a > c)", CACHE_PINS),
+    ("cache hit counts the F-th token in", "out_hit[b] = pos < F[n[b]] ? 1 : 0;",
+     "out_hit[b] = pos <= F[n[b]] ? 1 : 0;", CACHE_PINS),
+    ("cache row of the next position", "const int64_t row = (int64_t)b * (K + 1) + n[b];",
+     "const int64_t row = (int64_t)b * (K + 1) + (n[b] < K ? n[b] + 1 : n[b]);", CACHE_PINS),
     ("geometric fan-out floor", "F_out[k] = (int32_t)std::ceil(f);", "F_out[k] = (int32_t)std::floor(f);",
      [pins.test_geometric_fanout_closed_form]),
 ]

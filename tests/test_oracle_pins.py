@@ -456,3 +456,82 @@ def test_pm_repeated_sibling_token_is_rejected_and_removes_nothing():
     w = o["w"][0]
     assert w[2] == 0.0 and np.isclose(w.sum(), 1.0)
     assert np.allclose(w, np.array([0.30, 0.25, 0.0, 0.15, 0.05, 0.05]) / 0.8)
+
+
+# ---------------------------------------------------------------- speculation-cache hit test
+# SSD / Saguaro review §3 (cache strategy): the cache holds the top-F_k draft
+# tokens of every lookahead position k; an outcome (n, t) is a hit iff t is
+# among the tokens cached for position n.
+
+def _tie_heavy_rows(rng, B, K1, V):
+    bits = rng.integers(0x3F00, 0x3F06, size=(B, K1, V)).astype(np.uint16)  # bf16 with many ties
+    bits[:, ::2] = rng.integers(0, 0xFFFF, size=bits[:, ::2].shape).astype(np.uint16) & 0x7F7F
+    bits[rng.random(bits.shape) < 0.05] = 0x8000  # -0.0, equal to +0.0 as a number
+    bits[rng.random(bits.shape) < 0.05] = 0x0000
+    bits[rng.random(bits.shape) < 0.05] = 0xFF80  # -inf (masked token)
+    return bits, (bits.astype(np.uint32) << 16).view(np.float32)
+
+
+def test_cache_rank_is_position_in_numpy_stable_order():
+    rng = np.random.default_rng(61)
+    B, K, V = 50, 4, 257
+    bits, vals = _tie_heavy_rows(rng, B, K + 1, V)
+    n = rng.integers(0, K + 1, B).astype(np.int32)
+    t = rng.integers(0, V, B).astype(np.int32)
+    out = oracle.cache_hit_test(bits, n, t, None, "bf16")
+    for b in range(B):
+        order = np.argsort(-vals[b, n[b]].astype(np.float64), kind="stable")
+        assert out["rank"][b] == int(np.nonzero(order == t[b])[0][0])
+    assert out["hit"] is None
+
+
+def test_cache_rank_brute_force_count():
+    """rank = #{v : z_v > z_t, or z_v == z_t and v < t}, counted by hand (f32 and f64 rows)."""
+    rng = np.random.default_rng(62)
+    for dtype, npdt in (("f32", np.float32), ("f64", np.float64)):
+        B, K, V = 12, 2, 23
+        z = rng.integers(-3, 3, size=(B, K + 1, V)).astype(npdt)
+        z[rng.random(z.shape) < 0.1] = -np.inf
+        n = rng.integers(0, K + 1, B).astype(np.int32)
+        t = rng.integers(0, V, B).astype(np.int32)
+        out = oracle.cache_hit_test(z, n, t, None, dtype)
+        for b in range(B):
+            row, tb = z[b, n[b]], int(t[b])
+            want = sum(1 for v in range(V) if row[v] > row[tb] or (row[v] == row[tb] and v < tb))
+            assert out["rank"][b] == want
+
+
+def test_cache_hit_is_membership_in_the_fanout_cache():
+    """hit(n, t) == t among the top-F_n ids the fan-out caches for position n (F = 0, ties, F >= V)."""
+    rng = np.random.default_rng(63)
+    S, K, V = 6, 3, 40
+    bits, _ = _tie_heavy_rows(rng, S, K + 1, V)
+    F = np.array([0, 3, 17, 45], np.int32)
+    ids, _ = oracle.fanout_topk(bits.reshape(S * (K + 1), V), np.tile(F, S), 64, "bf16")
+    ids = ids.reshape(S, K + 1, 64)
+    # every outcome (n, t) of every sequence: the batch repeats each sequence's rows
+    seq, n, t = np.meshgrid(np.arange(S), np.arange(K + 1), np.arange(V), indexing="ij")
+    seq, n, t = seq.ravel(), n.ravel().astype(np.int32), t.ravel().astype(np.int32)
+    out = oracle.cache_hit_test(np.ascontiguousarray(bits[seq]), n, t, F, "bf16")
+    for i in range(len(seq)):
+        cached = set(ids[seq[i], n[i]][:F[n[i]]].tolist()) - {-1}
+        assert bool(out["hit"][i]) == (int(t[i]) in cached)
+    assert out["hit"].sum() == S * (0 + 3 + 17 + 40)
+
+
+def test_cache_rank_uniform_over_random_tokens():
+    """A row of distinct values ranks every token exactly once: over all t, the ranks are 0..V-1."""
+    rng = np.random.default_rng(64)
+    V = 97
+    z = rng.permutation(V).astype(np.float32)[None, None, :]
+    ranks = [oracle.cache_hit_test(z, np.array([0], np.int32), np.array([v], np.int32), None, "f32")["rank"][0]
+             for v in range(V)]
+    assert sorted(ranks) == list(range(V))
+    assert all(ranks[v] == V - 1 - int(z[0, 0, v]) for v in range(V))
+
+
+def test_cache_rejects_outcomes_outside_the_window():
+    z = np.zeros((2, 3, 5), np.float32)
+    for n, t in (([0, 3], [0, 0]), ([0, -1], [0, 0]), ([0, 0], [0, 5]), ([0, 0], [-1, 0])):
+        with pytest.raises(oracle.OracleError):
+            oracle.cache_hit_test(z, np.array(n, np.int32), np.array(t, np.int32), None, "f32")
