@@ -19,8 +19,9 @@ bonus row, per sequence) over its mean duration from HIP events recorded on
 the launch stream, against the 8 TB/s HBM peak.  `cpu_baseline` times the
 CPU oracle (single-threaded fp64) on the same workload.  `variants` holds the
 same measurements for the other rows of the hot path (greedy window,
-multi-candidate, tree, fan-out, the small fp32 chain, and the point-mass
-chain and tree, which read no draft rows).
+multi-candidate, tree, fan-out, the small fp32 chain, the point-mass chain
+and tree, which read no draft rows, and the speculation-cache hit test with
+its hit rate against temperature for geometric and uniform fan-out).
 """
 from __future__ import annotations
 
@@ -305,6 +306,67 @@ def bench_tree_pm(wl, steps, warmup):
                 alg_bytes=alg, mean_accepted=float(out["len"].float().mean().item()), copies=len(copies))
 
 
+def uniform_fanout(total, K):
+    """K+1 positions sharing `total` cache slots evenly (the first positions take the remainder)."""
+    return [total // (K + 1) + (1 if k < total % (K + 1) else 0) for k in range(K + 1)]
+
+
+def bench_cache(wl, steps, warmup, temps=(0.0, 0.5, 1.0), rounds=32, F0=8, r_exp=1.0):
+    """Speculation-cache hit test on the chain workload with the drafter's lookahead row: the kernel's time on
+    the realised outcomes of one verification call, and the hit rate against temperature for the geometric
+    fan-out (Theorem 12 with the acceptance rate measured at that temperature, capped last term) and a uniform
+    fan-out with the same number of cache slots."""
+    p = wl.params
+    B, K, V = p["B"], p["gamma"], p["V"]
+    rows_cpu = W.lookahead_rows(wl)
+    g = wl.to("cuda")
+    store = torch.empty(B, K + 1, rows_cpu.stride(1), dtype=rows_cpu.dtype, device="cuda")
+    rows = store[..., :V]
+    rows.copy_(rows_cpu)
+    table = {}
+    for T in temps:
+        tok = W.redraw_tokens(wl, T, seed=int(1000 * T) + 7).cuda()
+        ns, ts = [], []
+        for rnd in range(1 if T == 0 else rounds):
+            if T == 0:
+                out = svx.sv_verify_greedy(g["tgt"], tok, want_argmax=False)
+            else:
+                out = svx.sv_verify_chain(g["tgt"], g["drf"], tok, float(np.float32(T)), seed=11, round_=rnd,
+                                          want_pq=False)
+            ns.append(out["n"].clone())
+            ts.append(out["tok"].clone())
+        n, t = torch.cat(ns), torch.cat(ts)
+        nn = n.double()
+        # acceptance rate per position: accepted over tried (a rejection ends the window)
+        a_p = float(nn.sum() / (nn.sum() + (n < K).double().sum()))
+        a_p = min(max(a_p, 0.01), 0.99)
+        F_geo = svx.sv_geometric_fanout(F0, a_p, r_exp, K, capped_last=True)
+        F_uni = uniform_fanout(sum(F_geo), K)
+        res = {}
+        for name, F in (("geometric", F_geo), ("uniform", F_uni)):
+            Fd = torch.tensor(F, dtype=torch.int32, device="cuda")
+            hits = [svx.sv_cache_hit_test(rows, nr, tr, Fd)["hit"] for nr, tr in zip(ns, ts)]
+            res[name] = round(float(torch.cat(hits).double().mean()), 4)
+        table[str(T)] = dict(outcomes=int(n.numel()), a_p=round(a_p, 4), slots=sum(F_geo), F_geometric=F_geo,
+                             F_uniform=F_uni, hit_geometric=res["geometric"], hit_uniform=res["uniform"],
+                             mean_accepted=round(float(nn.mean()), 3))
+    # kernel time on one call's outcomes (T of the workload), rows rotated over copies
+    out = svx.sv_verify_chain(g["tgt"], g["drf"], g["tok"], float(np.float32(p["T"])), want_pq=False)
+    F = torch.tensor(svx.sv_geometric_fanout(F0, 0.7, r_exp, K, capped_last=True), dtype=torch.int32, device="cuda")
+    per_copy = B * V * esize(p["dtype"])  # one row per sequence is read
+    copies = []
+    for _ in range(n_copies(per_copy * (K + 1))):
+        c = torch.empty_like(store)[..., :V]
+        c.copy_(rows)
+        copies.append(dict(rows=c, n=out["n"].clone(), t=out["tok"].clone(), F=F))
+    fn = lambda c: svx.sv_cache_hit_test(c["rows"], c["n"], c["t"], c["F"])
+    fn(copies[0])
+    torch.cuda.synchronize()
+    wall, ev_ms = time_graphs(fn, copies, steps, warmup)
+    return dict(sequences_per_call=B, sequences_per_s=B / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
+                alg_bytes=per_copy, copies=len(copies), hit_rate_vs_T=table)
+
+
 def bench_fanout(wl, steps, warmup):
     p = wl.params
     B, N, V = wl.tensors["drf"].shape
@@ -396,6 +458,12 @@ def main():
             w = mk()
             variants[name] = summarize(fn(w))
             log(f"{name}: {variants[name]}")
+            if name == "chain_pm_batched":
+                log("generating the lookahead row for the cache hit test")
+                wc = W.chain_zipf(**W.CHAIN_BATCHED, lookahead_row=True)
+                variants["cache_hit_test"] = summarize(bench_cache(wc, steps_v, warm_v))
+                log(f"cache_hit_test: {variants['cache_hit_test']}")
+                del wc
             if name == "tree":
                 variants["tree_pm"] = summarize(bench_tree_pm(w, steps_v, warm_v))
                 log(f"tree_pm: {variants['tree_pm']}")

@@ -91,7 +91,8 @@ enum {
   SV_OP_TREE = 3,
   SV_OP_FANOUT = 4,
   SV_OP_CHAIN_PM = 5,
-  SV_OP_TREE_PM = 6
+  SV_OP_TREE_PM = 6,
+  SV_OP_CACHE = 7
 };
 
 /* Limits of this build. */
@@ -114,7 +115,7 @@ const char* sv_status_string(sv_status s);
 
 /*
  * Workspace bytes for one call of `op` with the given shape.  gamma_or_N is
- * gamma (chain, greedy, multi, chain_pm) or N (tree, tree_pm); B is the number of sequences (or
+ * gamma (chain, greedy, multi, chain_pm), N (tree, tree_pm) or K (cache); B is the number of sequences (or
  * R, the number of rows, for fan-out); K is used by multi only; F_max by
  * fan-out only.  Returns SV_EINVAL / SV_EUNSUPPORTED for shapes the
  * corresponding call would reject.
@@ -253,6 +254,32 @@ sv_status sv_verify_tree_pm(const void* tgt, sv_dtype dt, int64_t tgt_stride, co
  */
 sv_status sv_fanout_topk(const void* logits, sv_dtype dt, int64_t stride, int32_t R, int32_t V, const int32_t* F,
                          int32_t F_max, int32_t* out_ids, float* out_vals, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Speculation-cache hit test (SSD / Saguaro review §3, cache strategy: the
+ * cache holds the top-F_k draft tokens of every lookahead position k = 0..K;
+ * an outcome (n, t) -- n drafts accepted, then token t -- is served iff t is
+ * among the tokens cached for position n, the hit event of Definition 11).
+ *   drf [B, K+1, V] draft logits per lookahead position; row (b, k) at
+ *       b*(K+1) + k (0 <= K <= SV_MAX_GAMMA)
+ *   n, t [B] device int32: the realised outcome (e.g. out_n / out_tok of a
+ *       verification call)
+ *   F [K+1] device int32 fan-out per position (e.g. sv_geometric_fanout), or
+ *       NULL together with out_hit
+ * Outputs (device):
+ *   out_rank [B] the 0-based position of t in draft row (b, n) under the
+ *            fan-out's order (value descending, index ascending on equal
+ *            values): #{v : z_v > z_t, or z_v == z_t and v < t}; so t is
+ *            cached iff out_rank < F[n], and out_rank + 1 is the smallest
+ *            fan-out that would have cached it
+ *   out_hit  [B] 1 iff out_rank[b] < F[n[b]], else 0 (may be NULL with F)
+ * n outside [0, K] or t outside [0, V) sets SV_DERR_TOKEN and gives rank -1,
+ * hit 0.  Reads one draft row per sequence.  Workspace: SV_OP_CACHE (the
+ * fixed part only).
+ */
+sv_status sv_cache_hit_test(const void* drf, sv_dtype dt, int64_t stride, int32_t B, int32_t K, int32_t V,
+                            const int32_t* n, const int32_t* t, const int32_t* F, int32_t* out_rank, int32_t* out_hit,
+                            void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Host helper, SSD / Saguaro review Theorem 12: F_k = ceil(F0 * a_p^(k/(1+r)))

@@ -186,6 +186,21 @@ sv_status plan_fanout(sv_dtype dt, int32_t R, int32_t V, int32_t F_max, Plan* pl
   return SV_OK;
 }
 
+// Cache hit test: one row per sequence, split so the launch has about the
+// usual block count; the per-sequence words live in the counter region.
+sv_status plan_cache(sv_dtype dt, int32_t B, int32_t K, int32_t V, Plan* pl) {
+  if (bad_dtype(dt)) return SV_EDTYPE;
+  if (B < 0 || K < 0 || V < 1) return SV_EINVAL;
+  if (B > SV_MAX_SEQ || K > SV_MAX_GAMMA || V > SV_MAX_V) return SV_EUNSUPPORTED;
+  static_assert((size_t)SV_MAX_SEQ * sizeof(uint64_t) <= kWsCounters * sizeof(uint32_t), "cache words");
+  pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
+  split(B, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
+  pl->grid1 = (int64_t)B * pl->nch1;
+  if (pl->grid1 > INT32_MAX) return SV_EUNSUPPORTED;
+  pl->bytes = kWsFixed;
+  return SV_OK;
+}
+
 sv_status check_ws(const void* ws, size_t ws_bytes, const Plan& pl) {
   if (!ws || ws_bytes < pl.bytes) return SV_EWORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return SV_EALIGN;
@@ -242,6 +257,7 @@ sv_status sv_workspace_size(sv_op op, sv_dtype dt, int32_t B, int32_t K, int32_t
     case SV_OP_TREE: st = plan_tree(dt, B, gamma_or_N, V, false, &pl); break;
     case SV_OP_CHAIN_PM: st = plan_chain(dt, B, 1, gamma_or_N, V, true, &pl); break;
     case SV_OP_TREE_PM: st = plan_tree(dt, B, gamma_or_N, V, true, &pl); break;
+    case SV_OP_CACHE: st = plan_cache(dt, B, gamma_or_N, V, &pl); break;
     case SV_OP_FANOUT: st = plan_fanout(dt, B, V, F_max, &pl); break;
     default: return SV_EINVAL;
   }
@@ -457,6 +473,36 @@ sv_status sv_fanout_topk(const void* logits, sv_dtype dt, int64_t stride, int32_
   p.vpc = pl.vpc1;
   p.nvec = pl.nvec;
   return launch_fanout(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+sv_status sv_cache_hit_test(const void* drf, sv_dtype dt, int64_t stride, int32_t B, int32_t K, int32_t V,
+                            const int32_t* n, const int32_t* t, const int32_t* F, int32_t* out_rank, int32_t* out_hit,
+                            void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  sv_status st = plan_cache(dt, B, K, V, &pl);
+  if (st != SV_OK) return st;
+  if (B == 0) return SV_OK;
+  if ((st = check_rows(drf, stride, V, dt)) != SV_OK) return st;
+  if (!n || !t || !out_rank || (!F) != (!out_hit)) return SV_EINVAL;
+  if ((st = check_ws(ws, ws_bytes, pl)) != SV_OK) return st;
+  char* w = static_cast<char*>(ws);
+  CacheParams p;
+  p.drf = drf;
+  p.sb = stride * elem_bytes(dt);
+  p.B = B;
+  p.K = K;
+  p.V = V;
+  p.n = n;
+  p.t = t;
+  p.F = F;
+  p.out_rank = out_rank;
+  p.out_hit = out_hit;
+  p.err = reinterpret_cast<int32_t*>(w);
+  p.words = reinterpret_cast<uint64_t*>(w + kWsHeader);
+  p.nch = pl.nch1;
+  p.vpc = pl.vpc1;
+  p.nvec = pl.nvec;
+  return launch_cache(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 int32_t sv_geometric_fanout(int32_t F0, double a_p, double r, int32_t K, int32_t capped_last, int32_t* F_out) {

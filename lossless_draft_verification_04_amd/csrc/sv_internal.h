@@ -98,6 +98,21 @@ struct FanoutParams {
   int64_t vpc, nvec;
 };
 
+struct CacheParams {
+  const void* drf;
+  int64_t sb;
+  int32_t B, K, V;
+  const int32_t* n;
+  const int32_t* t;
+  const int32_t* F;
+  int32_t* out_rank;
+  int32_t* out_hit;
+  int32_t* err;
+  uint64_t* words;  // one per sequence in the counter region: arrivals (high) | count (low)
+  int32_t nch;
+  int64_t vpc, nvec;
+};
+
 // Workspace plans (chunking + scratch sizes), computed identically by
 // sv_workspace_size and the entry points.
 struct Plan {
@@ -112,6 +127,7 @@ hipError_t launch_chain(const ChainParams& p, sv_dtype dt, const Plan& plan, hip
 hipError_t launch_greedy(const GreedyParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
 hipError_t launch_tree(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
 hipError_t launch_fanout(const FanoutParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
+hipError_t launch_cache(const CacheParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
 hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s);
 
 // Blocks of one launch of the draw / walk kernel (held or streamed slices)

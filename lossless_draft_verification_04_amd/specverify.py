@@ -30,7 +30,8 @@ _lib = ctypes.CDLL(_LIB_PATH)
 
 SV_OK, SV_EINVAL, SV_EDTYPE, SV_EALIGN, SV_EWORKSPACE, SV_EUNSUPPORTED, SV_EHIP = range(7)
 SV_F32, SV_BF16 = 0, 1
-SV_OP_CHAIN, SV_OP_GREEDY, SV_OP_MULTI, SV_OP_TREE, SV_OP_FANOUT, SV_OP_CHAIN_PM, SV_OP_TREE_PM = range(7)
+(SV_OP_CHAIN, SV_OP_GREEDY, SV_OP_MULTI, SV_OP_TREE, SV_OP_FANOUT, SV_OP_CHAIN_PM, SV_OP_TREE_PM,
+ SV_OP_CACHE) = range(8)
 DERR_TOKEN, DERR_TREE, DERR_FANOUT, DERR_ROW = 1, 2, 4, 8
 
 _P = ctypes.c_void_p
@@ -54,6 +55,7 @@ _SIGS = {
     "sv_verify_tree_pm": ([_P, _i32, _i64, _P, _P, _i32, _i32, _i32, _i32, _f32, _u64, _u32, _P, _P, _P, _P, _P,
                            _sz, _P], _i32),
     "sv_fanout_topk": ([_P, _i32, _i64, _i32, _i32, _P, _i32, _P, _P, _P, _sz, _P], _i32),
+    "sv_cache_hit_test": ([_P, _i32, _i64, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _sz, _P], _i32),
     "sv_geometric_fanout": ([_i32, _f64, _f64, _i32, _i32, ctypes.POINTER(_i32)], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -277,6 +279,24 @@ def sv_fanout_topk(logits, F, F_max, want_vals=True, workspace=None):
     _check(_lib.sv_fanout_topk(_ptr(logits), dt, _row_stride(logits, "logits"), R, V, _ptr(F), int(F_max), _ptr(ids),
                                _ptr(vals), _ptr(ws), ws.numel(), _stream(dev)), "sv_fanout_topk")
     return ids, vals
+
+
+def sv_cache_hit_test(drf, n, t, F=None, workspace=None):
+    """drf [B, K+1, V]; outcome n, t [B] int32 (device); F [K+1] int32 (device) or None
+    -> dict(rank [B], hit [B] or None)."""
+    B, K1, V = drf.shape
+    _i32_tensor(n, (B,), "n")
+    _i32_tensor(t, (B,), "t")
+    if F is not None:
+        _i32_tensor(F, (K1,), "F")
+    dt = _dtype_code(drf)
+    dev = drf.device
+    ws = workspace if workspace is not None else Workspace.get(dev, workspace_size(SV_OP_CACHE, dt, B, 1, K1 - 1, V))
+    rank = torch.empty(B, dtype=torch.int32, device=dev)
+    hit = torch.empty(B, dtype=torch.int32, device=dev) if F is not None else None
+    _check(_lib.sv_cache_hit_test(_ptr(drf), dt, _row_stride(drf, "drf"), B, K1 - 1, V, _ptr(n), _ptr(t), _ptr(F),
+                                  _ptr(rank), _ptr(hit), _ptr(ws), ws.numel(), _stream(dev)), "sv_cache_hit_test")
+    return dict(rank=rank, hit=hit)
 
 
 def sv_geometric_fanout(F0, a_p, r, K, capped_last=False):

@@ -158,8 +158,12 @@ def chain_normal(B=1, gamma=4, V=32000, T=1.0, dtype="f32", seed=1001) -> Worklo
                     dict(tgt=tgt, drf=drf, tok=tok))
 
 
-def chain_zipf(B=32, gamma=16, V=152064, T=0.8, dtype="bf16", seed=1002, sig_lo=0.5, sig_hi=2.5) -> Workload:
-    """Chain inputs with Gumbel-perturbed Zipf target rows and rising draft noise."""
+def chain_zipf(B=32, gamma=16, V=152064, T=0.8, dtype="bf16", seed=1002, sig_lo=0.5, sig_hi=2.5,
+               lookahead_row=False) -> Workload:
+    """Chain inputs with Gumbel-perturbed Zipf target rows and rising draft noise.
+
+    lookahead_row: also draw the drafter's row for position gamma+1 (target row gamma+1 plus N(0, sig_hi^2)
+    noise) as ``drf_next`` [B, V], after everything else, so the other tensors do not change."""
     gen = _gen(seed)
     _, tgt = _alloc_rows((B, gamma + 1), V, dtype)
     _, drf = _alloc_rows((B, gamma), V, dtype)
@@ -170,8 +174,36 @@ def chain_zipf(B=32, gamma=16, V=152064, T=0.8, dtype="bf16", seed=1002, sig_lo=
         tgt[b].copy_(t32)
         drf[b].copy_(d32)
     tok = gumbel_max_tokens(drf.reshape(B * gamma, V), T, gen).reshape(B, gamma)
-    return Workload("chain", dict(B=B, gamma=gamma, V=V, T=T, dtype=dtype, seed=seed),
-                    dict(tgt=tgt, drf=drf, tok=tok))
+    tensors = dict(tgt=tgt, drf=drf, tok=tok)
+    if lookahead_row:
+        _, nxt = _alloc_rows((B,), V, dtype)
+        for b in range(B):
+            nxt[b].copy_(tgt[b, gamma].to(torch.float32) + torch.randn(V, generator=gen) * sig_hi)
+        tensors["drf_next"] = nxt
+    return Workload("chain", dict(B=B, gamma=gamma, V=V, T=T, dtype=dtype, seed=seed), tensors)
+
+
+def redraw_tokens(wl: Workload, T: float, seed: int) -> torch.Tensor:
+    """Draft tokens of a chain workload drawn afresh from q_j at temperature T (Gumbel-max); T = 0 takes the
+    draft rows' first maximal index (the greedy drafter)."""
+    p = wl.params
+    rows = wl.tensors["drf"].reshape(p["B"] * p["gamma"], p["V"])
+    if T == 0:
+        tok = torch.argmax(rows.to(torch.float32), dim=1).to(torch.int32)[:, None]
+    else:
+        tok = gumbel_max_tokens(rows, T, _gen(seed))
+    return tok.reshape(p["B"], p["gamma"]).contiguous()
+
+
+def lookahead_rows(wl: Workload) -> torch.Tensor:
+    """The drafter's rows for lookahead positions k = 0..gamma as one [B, gamma+1, V] tensor (padded rows):
+    draft rows q_1..q_gamma, then ``drf_next``."""
+    p = wl.params
+    B, gamma, V = p["B"], p["gamma"], p["V"]
+    _, out = _alloc_rows((B, gamma + 1), V, p["dtype"])
+    out[:, :gamma].copy_(wl.tensors["drf"])
+    out[:, gamma].copy_(wl.tensors["drf_next"])
+    return out
 
 
 def greedy_zipf(B=64, gamma=32, V=151936, dtype="bf16", seed=1003, match0=0.9, decay=0.95) -> Workload:

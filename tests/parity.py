@@ -176,6 +176,26 @@ def tree_pm(wl, seed=0, round_=0):
     return out, ref
 
 
+def cache(rows_cpu, n_cpu, t_cpu, F_cpu=None):
+    """Cache hit test of outcomes (n, t) against lookahead rows [B, K+1, V] (padded CPU view): exact ranks."""
+    B, K1, V = rows_cpu.shape
+    say(f"  cache B={B} K={K1 - 1} V={V} {dtype_name(rows_cpu)} F={'yes' if F_cpu is not None else 'no'}")
+    Vs = rows_cpu.stride(1)
+    store = torch.empty(B, K1, Vs, dtype=rows_cpu.dtype, device=DEV)
+    rows = store[..., :V]
+    rows.copy_(rows_cpu)
+    out = svx.sv_cache_hit_test(rows, n_cpu.to(DEV), t_cpu.to(DEV), None if F_cpu is None else F_cpu.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.cache_hit_test(np_logits(rows_cpu), n_cpu.numpy(), t_cpu.numpy(),
+                                None if F_cpu is None else F_cpu.numpy(), dtype_name(rows_cpu))
+    got = out["rank"].cpu().numpy()
+    bad = np.nonzero(got != ref["rank"])[0]
+    assert len(bad) == 0, f"cache ranks differ at {bad[:10].tolist()}: gpu {got[bad[:5]]} oracle {ref['rank'][bad[:5]]}"
+    if F_cpu is not None:
+        assert np.array_equal(out["hit"].cpu().numpy(), ref["hit"])
+    return out, ref
+
+
 def fanout(logits_cpu, F_cpu, F_max):
     dt = dtype_name(logits_cpu)
     say(f"  fanout R={logits_cpu.shape[0]} V={logits_cpu.shape[1]} F_max={F_max} {dt}")

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 13
+    assert len(names) == 14
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(svx.EXPORTED)
@@ -59,7 +59,7 @@ def test_workspace_size():
     assert st == svx.SV_OK and n > 65536 * 4
     st2, n2 = ws_size(svx.SV_OP_MULTI, svx.SV_BF16, 32, 1, 16, 152064)
     assert st2 == svx.SV_OK and n2 == n  # multi with K = 1 is the chain
-    for op in range(7):
+    for op in range(8):
         st, n = ws_size(op, svx.SV_BF16, 8, 2, 16, 1000, 8)
         assert st == svx.SV_OK and n % 256 == 0
     # point-mass calls stream no draft rows: never more scratch than the standard ones
@@ -69,6 +69,10 @@ def test_workspace_size():
         assert 0 < n_pm <= n_std
     assert ws_size(svx.SV_OP_CHAIN_PM, 0, 1, 1, 65, 100)[0] == svx.SV_EUNSUPPORTED
     assert ws_size(svx.SV_OP_TREE_PM, 0, 1, 1, 1025, 100)[0] == svx.SV_EUNSUPPORTED
+    assert ws_size(svx.SV_OP_CACHE, 0, 1, 1, 65, 100)[0] == svx.SV_EUNSUPPORTED
+    assert ws_size(svx.SV_OP_CACHE, 0, 32769, 1, 4, 100)[0] == svx.SV_EUNSUPPORTED
+    assert ws_size(svx.SV_OP_CACHE, 0, 1, 1, -1, 100)[0] == svx.SV_EINVAL
+    assert ws_size(svx.SV_OP_CACHE, 1, 32, 1, 16, 152064) == (svx.SV_OK, 256 + 65536 * 4)  # fixed part only
     assert ws_size(svx.SV_OP_CHAIN, 7, 1, 1, 4, 100)[0] == svx.SV_EDTYPE
     assert ws_size(svx.SV_OP_CHAIN, 0, 1, 1, 0, 100)[0] == svx.SV_EINVAL
     assert ws_size(svx.SV_OP_CHAIN, 0, 1, 1, 65, 100)[0] == svx.SV_EUNSUPPORTED
@@ -147,6 +151,20 @@ def test_point_mass_argument_checks():
     assert tr(md=1025) == svx.SV_EINVAL and tr(par=None) == svx.SV_EINVAL and tr(len=None) == svx.SV_EINVAL
     assert tr(tgt=MIS) == svx.SV_EALIGN and tr(T=-2.0) == svx.SV_EINVAL and tr(wsb=64) == svx.SV_EWORKSPACE
     assert tr(B=0) == svx.SV_OK
+
+
+def test_cache_hit_test_argument_checks():
+    c = lambda **kw: L.sv_cache_hit_test(kw.get("drf", A), kw.get("dt", 1), kw.get("s", 1024), kw.get("B", 2),
+                                         kw.get("K", 4), kw.get("V", 1000), kw.get("n", A), kw.get("t", A),
+                                         kw.get("F", A), kw.get("rank", A), kw.get("hit", A), kw.get("ws", WS),
+                                         kw.get("wsb", 1 << 30), None)
+    assert c(dt=5) == svx.SV_EDTYPE and c(K=-1) == svx.SV_EINVAL and c(K=65) == svx.SV_EUNSUPPORTED
+    assert c(V=0) == svx.SV_EINVAL and c(drf=None) == svx.SV_EINVAL and c(drf=MIS) == svx.SV_EALIGN
+    assert c(s=999) == svx.SV_EINVAL and c(s=1004) == svx.SV_EALIGN
+    assert c(n=None) == svx.SV_EINVAL and c(t=None) == svx.SV_EINVAL and c(rank=None) == svx.SV_EINVAL
+    assert c(F=None) == svx.SV_EINVAL and c(hit=None) == svx.SV_EINVAL  # F and out_hit come together
+    assert c(ws=None) == svx.SV_EWORKSPACE and c(wsb=1024) == svx.SV_EWORKSPACE
+    assert c(B=0) == svx.SV_OK and c(B=0, F=None, hit=None) == svx.SV_OK
 
 
 def test_workspace_helpers_reject_bad_arguments():
