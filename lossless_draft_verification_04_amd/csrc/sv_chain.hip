@@ -216,7 +216,6 @@ __global__ __launch_bounds__(kNT) void chain_stats_kernel(ChainParams a) {
   const int ch = (int)(rem - (int64_t)lr * a.nch1);
   const int Kg = a.K * a.gamma;
   const bool is_tgt = lr < Kg;
-  zero_slots(a.slots, (int64_t)a.B * kSlotWords * a.G, bid, kNT);  // for the draw launch
   const void* row;
   int j;
   if (is_tgt) {
@@ -228,21 +227,22 @@ __global__ __launch_bounds__(kNT) void chain_stats_kernel(ChainParams a) {
     row = row_ptr(a.drf, (int64_t)b * a.gamma + j, a.drf_sb);
   }
   // the first part of a row also gathers the drafted tokens' logits in it
-  // (target row (k, j): x_{k,j}; draft row j: x_{k,j} of every candidate k),
-  // issued before the stream so their latency is hidden
+  // (target row (k, j): x_{k,j}; draft row j: x_{k,j} of every candidate k);
+  // the token is loaded here and the logit inside the stream
   int64_t zo = -1;
-  float zx = 0.f;
+  int32_t x = 0;
   if (ch == 0 && (int)threadIdx.x < (is_tgt ? 1 : a.K)) {
     const int k = is_tgt ? lr / a.gamma : (int)threadIdx.x;
     zo = ((int64_t)b * a.K + k) * a.gamma + j;
-    const int32_t x = a.tok[zo];
-    if (x >= 0 && x < a.V) zx = load_elem<DT>(row, x);
+    x = a.tok[zo];
   }
   const int64_t v0 = (int64_t)ch * a.vpc1;
   const int64_t v1 = v0 + a.vpc1 < a.nvec ? v0 + a.vpc1 : a.nvec;
-  const Partial part = range_stats<DT, kNT, kU>(row, a.V, v0, v1, a.c);
+  uint32_t zbits = 0;
+  const Partial part = range_stats<DT, kNT, kU>(row, a.V, v0, v1, a.c, zo >= 0, x, &zbits);
   if (threadIdx.x == 0) put_partial(static_cast<Partial*>(a.part1) + (int64_t)b * per_seq + (int64_t)lr * a.nch1 + ch, part);
-  if (zo >= 0) (is_tgt ? a.zg : a.zq)[zo] = zx;
+  if (zo >= 0) (is_tgt ? a.zg : a.zq)[zo] = (x >= 0 && x < a.V) ? bits_value<DT>(zbits) : 0.f;
+  zero_slots(a.slots, (int64_t)a.B * kSlotWords * a.G, bid, kNT);  // for the draw launch
 }
 
 template <int DT>

@@ -71,6 +71,23 @@ __device__ __forceinline__ float load_elem(const void* row, int64_t i) {
   }
 }
 
+// One logit's bits (a gather whose value is used much later: keeping the
+// raw bits lets the conversion wait until the use) and their fp32 value.
+template <int DT>
+__device__ __forceinline__ uint32_t load_bits(const void* row, int64_t i) {
+  if constexpr (DT == SV_BF16)
+    return reinterpret_cast<const uint16_t*>(row)[i];
+  else
+    return reinterpret_cast<const uint32_t*>(row)[i];
+}
+template <int DT>
+__device__ __forceinline__ float bits_value(uint32_t w) {
+  if constexpr (DT == SV_BF16)
+    return __uint_as_float(w << 16);
+  else
+    return __uint_as_float(w);
+}
+
 // 2^x on the hardware exp unit (no denormal fix-up; terms that small are
 // below 2^-126 of the row maximum and do not matter to any sum here).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
@@ -257,9 +274,14 @@ struct RowStat {
 
 // Online (max, sum) over vectors [v0, v1) of one row by a block of NT
 // threads; U vectors in flight per thread.  Every thread returns the
-// block's partial.
+// block's partial.  A thread with `gather` set also loads the bits of
+// element gx of the row (clamped into [0, V)) into *gbits; the load is
+// issued after the first vectors of the stream, so waiting for gx (loaded by
+// the caller) does not hold back the stream, and nothing waits for the
+// gathered bits before the caller uses them.
 template <int DT, int NT, int U>
-__device__ Partial range_stats(const void* row, int V, int64_t v0, int64_t v1, float c) {
+__device__ Partial range_stats(const void* row, int V, int64_t v0, int64_t v1, float c, bool gather = false,
+                               int32_t gx = 0, uint32_t* gbits = nullptr) {
   constexpr int E = Fmt<DT>::kPerVec;
   const int tid = threadIdx.x;
   const int64_t nfull = V / E;
@@ -267,12 +289,17 @@ __device__ Partial range_stats(const void* row, int V, int64_t v0, int64_t v1, f
   float m = kNegInf;
   float s = 0.f;
   int64_t v = v0 + tid;
+  bool gathered = !gather;
   if (v + (int64_t)(U - 1) * NT < vf) {
     // software pipelined: the next U vectors are in flight while these are
     // reduced (the prefetch past the end is clamped to the last full vector)
     u32x4 cur[U];
 #pragma unroll
     for (int u = 0; u < U; ++u) cur[u] = load_vec(row, v + (int64_t)u * NT);
+    if (!gathered) {
+      *gbits = load_bits<DT>(row, gx >= 0 && gx < V ? gx : 0);
+      gathered = true;
+    }
     for (;;) {
       const int64_t vn = v + (int64_t)U * NT;
       const bool more = vn + (int64_t)(U - 1) * NT < vf;
@@ -309,6 +336,7 @@ __device__ Partial range_stats(const void* row, int V, int64_t v0, int64_t v1, f
       for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     }
   }
+  if (!gathered) *gbits = load_bits<DT>(row, gx >= 0 && gx < V ? gx : 0);
   for (; v < v1; v += NT) {
     float x[E];
     unpack<DT>(load_vec(row, v), x);

@@ -57,40 +57,55 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
   if (!a.pm) rest >>= 1;
   const int b = (int)(rest % a.B);
   const int u = (int)(rest / a.B);
-  zero_slots(a.slots, (int64_t)a.B * kSlotWords * a.G, bid, kTNT);  // for the walk launch
   const int64_t rowbase = (int64_t)b * a.N;
   const void* row = which ? row_ptr(a.drf, rowbase + u, a.drf_sb) : row_ptr(a.tgt, rowbase + u, a.tgt_sb);
-  // children of u; the first part of the row gathers its logits at their
-  // tokens (NaN for a token outside the vocabulary), issued before the stream
-  int has_kids = 0;
-  int gi[kGather];
-  float zg[kGather];
+  // children of u among the candidates i = u + 1 + tid + k * kTNT: every
+  // parent and token is loaded in one round (clamped indexes), so the block
+  // waits for one round trip before it knows whether it streams
+  int32_t pk[kGather], xk[kGather];
 #pragma unroll
   for (int k = 0; k < kGather; ++k) {
     const int i = u + 1 + (int)threadIdx.x + k * kTNT;
-    gi[k] = -1;
-    zg[k] = 0.f;
-    if (i < a.N) {
-      const int32_t pi = a.parent[rowbase + i];
-      const int32_t x = a.tok[rowbase + i];
-      if (pi == u) {
-        has_kids = 1;
-        if (ch == 0) {
-          gi[k] = i;
-          zg[k] = (x >= 0 && x < a.V) ? load_elem<DT>(row, x) : __builtin_nanf("");
-        }
-      }
+    const int ic = i < a.N ? i : a.N - 1;
+    pk[k] = a.parent[rowbase + ic];
+    xk[k] = a.tok[rowbase + ic];
+  }
+  int has_kids = 0;
+#pragma unroll
+  for (int k = 0; k < kGather; ++k) {
+    const int i = u + 1 + (int)threadIdx.x + k * kTNT;
+    if (i < a.N && pk[k] == u) has_kids = 1;
+    else pk[k] = -1;  // not a child of u
+  }
+  if (!__syncthreads_or(has_kids)) {
+    zero_slots(a.slots, (int64_t)a.B * kSlotWords * a.G, bid, kTNT);  // for the walk launch
+    return;
+  }
+  // the first part of the row gathers its logits at the children's tokens
+  // (NaN for a token outside the vocabulary); the loads are issued before the
+  // stream and their bits used after it, so no wait precedes the stream
+  uint32_t zg[kGather];
+  if (ch == 0) {  // block-uniform; the loads are unconditional (clamped token) so none waits for another
+#pragma unroll
+    for (int k = 0; k < kGather; ++k) {
+      const int32_t x = xk[k];
+      zg[k] = load_bits<DT>(row, x >= 0 && x < a.V ? x : 0);
     }
   }
-  if (!__syncthreads_or(has_kids)) return;
   const int64_t v0 = (int64_t)ch * a.vpc;
   const int64_t v1 = v0 + a.vpc < a.nvec ? v0 + a.vpc : a.nvec;
   const Partial part = range_stats<DT, kTNT, kTU>(row, a.V, v0, v1, a.c);
   if (threadIdx.x == 0) put_partial(static_cast<Partial*>(a.part) + ((rowbase + u) * nw + which) * a.nch + ch, part);
   float* zc = a.zc + (int64_t)which * a.B * a.N + rowbase;
+  if (ch == 0) {
 #pragma unroll
-  for (int k = 0; k < kGather; ++k)
-    if (gi[k] >= 0) zc[gi[k]] = zg[k];
+    for (int k = 0; k < kGather; ++k) {
+      const int32_t x = xk[k];
+      if (pk[k] >= 0)
+        zc[u + 1 + (int)threadIdx.x + k * kTNT] = (x >= 0 && x < a.V) ? bits_value<DT>(zg[k]) : __builtin_nanf("");
+    }
+  }
+  zero_slots(a.slots, (int64_t)a.B * kSlotWords * a.G, bid, kTNT);  // for the walk launch
 }
 
 // ---------------------------------------------------------------------------
