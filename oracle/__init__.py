@@ -66,6 +66,8 @@ def _load(path):
     L.svo_fanout_topk.restype = i32
     L.svo_cache_hit_test.argtypes = [P, i32, i64, i32, i32, i32, P, P, P, P, P]
     L.svo_cache_hit_test.restype = i32
+    L.svo_presto_score.argtypes = [P, P, i32, i64, i64, P, P, i32, i32, i32, f64, P, i32, i32, i32, P, P, P, P, P]
+    L.svo_presto_score.restype = i32
     L.svo_geometric_fanout.argtypes = [i32, f64, f64, i32, i32, P]
     L.svo_geometric_fanout.restype = i32
     return L
@@ -311,6 +313,24 @@ def cache_hit_test(drf, n, t, F, dtype):
     rc = lib().svo_cache_hit_test(_ptr(drf), code, _row_stride(drf), B, K1 - 1, V, _ptr(n), _ptr(t), _ptr(Fa),
                                   _ptr(out["rank"]), _ptr(out["hit"]))
     _check(rc, "cache_hit_test")
+    return out
+
+
+def presto_score(tgt, drf, node_tok, parent, T, lam, k, b_top, dtype):
+    """PRESTO scoring and one expansion step.  tgt, drf [B, N, V]; node_tok, parent [B, N]; lam [D] (lambda of
+    depth d at lam[min(d, D) - 1]) -> dict(s, S [B, N], node, tok, score [B, b_top])."""
+    tgt, code = _logits(tgt, dtype)
+    drf, code2 = _logits(drf, dtype)
+    B, N, V = tgt.shape
+    node_tok, parent = _i32(node_tok), _i32(parent)
+    lam = np.ascontiguousarray(lam, dtype=np.float32)
+    out = dict(s=np.zeros((B, N)), S=np.zeros((B, N)), node=np.zeros((B, b_top), np.int32),
+               tok=np.zeros((B, b_top), np.int32), score=np.zeros((B, b_top)))
+    rc = lib().svo_presto_score(_ptr(tgt), _ptr(drf), code, _row_stride(tgt), _row_stride(drf), _ptr(node_tok),
+                                _ptr(parent), B, N, V, float(T), _ptr(lam), len(lam), int(k), int(b_top),
+                                _ptr(out["s"]), _ptr(out["S"]), _ptr(out["node"]), _ptr(out["tok"]),
+                                _ptr(out["score"]))
+    _check(rc, "presto_score")
     return out
 
 

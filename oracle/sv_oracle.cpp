@@ -450,6 +450,32 @@ TreeResult tree_round_pm(const TreeInputs& in, const double* r, double u, double
   }
 }
 
+// ---------------------------------------------------------------------------
+// PRESTO prefix-aligned scoring ([PR] §4.1, eq. 9-10; §4.3 self-speculative
+// form: the target's conditional rows are available, so the acceptance
+// probability rho = min(1, p/q) is exact rather than predicted).  Token score
+// s = log q(t) + lambda * log rho(t): the log of the KL-regularised proxy
+// p* ~ q * rho^lambda up to its normaliser ([PR] §4.4).  lambda = 0 gives
+// log q (its rho term is taken as 0 even where rho = 0).  A token with
+// q(t) = 0, or with p(t) = 0 while lambda > 0, scores -inf.
+// ---------------------------------------------------------------------------
+double presto_token_score(double p, double q, double lambda) {
+  if (!(q > 0.0)) return -kInf;
+  const double logq = std::log(q);
+  if (lambda == 0.0) return logq;
+  if (!(p > 0.0)) return -kInf;
+  const double rho = std::min(1.0, p / q);
+  return logq + lambda * std::log(rho);
+}
+
+// lambda of a node at depth d >= 1: lam[min(d, D) - 1].
+double presto_lambda(const float* lam, int D, int d) { return (double)lam[std::min(d, D) - 1]; }
+
+struct PrestoCand {
+  double score;
+  int node, tok;
+};
+
 }  // namespace
 
 // ===========================================================================
@@ -767,6 +793,79 @@ int svo_cache_hit_test(const void* drf, int dtype, int64_t stride, int B, int K,
     while (order[pos] != t[b]) ++pos;
     out_rank[b] = pos;
     if (F && out_hit) out_hit[b] = pos < F[n[b]] ? 1 : 0;
+  }
+  return 0;
+}
+
+// PRESTO scoring and one priority expansion step ([PR] §4.1-4.2), tree layout
+// as for svo_verify_tree (node u's rows are the target / draft distributions
+// of u's children; depth(0) = 0, depth(i) = depth(parent(i)) + 1).
+//   out_s [B*N]: s_i = presto_token_score(P_u(x_i), Q_u(x_i), lambda_{depth(i)})
+//                for i >= 1, u = parent(i); 0 for the root.
+//   out_S [B*N]: path score S_i = sum of s along the root-to-i path (eq. 10).
+//   Expansion (Algorithm 1, one step from the frontier = the leaves, nodes
+//   without children): every leaf u proposes its k best tokens t by
+//   presto_token_score(P_u(t), Q_u(t), lambda_{depth(u)+1}) (score
+//   descending, token ascending; -inf scores are not proposed); a proposal's
+//   priority is S_u + its score; the b_top best proposals of the sequence
+//   (priority descending, then node ascending, then token ascending) go to
+//   out_node / out_tok / out_score [B*b_top], padded with -1 / -1 / -inf.
+int svo_presto_score(const void* tgt, const void* drf, int dtype, int64_t tgt_stride, int64_t drf_stride,
+                     const int32_t* node_tok, const int32_t* parent, int B, int N, int V, double T, const float* lam,
+                     int D, int k, int b_top, double* out_s, double* out_S, int32_t* out_node, int32_t* out_tok,
+                     double* out_score) {
+  if (B < 0 || N < 1 || V < 1 || !(T > 0.0) || D < 1 || k < 0 || b_top < 0) return 1;
+  std::vector<double> P, Q;
+  std::vector<int> depth(N), nkids(N);
+  for (int b = 0; b < B; ++b) {
+    const int32_t* par = parent + (int64_t)b * N;
+    const int32_t* tok = node_tok + (int64_t)b * N;
+    double* s_b = out_s + (int64_t)b * N;
+    double* S_b = out_S + (int64_t)b * N;
+    std::fill(nkids.begin(), nkids.end(), 0);
+    depth[0] = 0;
+    for (int i = 1; i < N; ++i) {
+      if (par[i] < 0 || par[i] >= i) return 4;
+      if (tok[i] < 0 || tok[i] >= V) return 3;
+      depth[i] = depth[par[i]] + 1;
+      nkids[par[i]] += 1;
+    }
+    s_b[0] = 0.0;
+    std::vector<PrestoCand> cands;
+    for (int u = 0; u < N; ++u) {
+      const int64_t row = (int64_t)b * N + u;
+      if (!softmax_row(tgt, dtype, row * tgt_stride, V, T, P)) return 2;
+      if (!softmax_row(drf, dtype, row * drf_stride, V, T, Q)) return 2;
+      for (int i = u + 1; i < N; ++i)
+        if (par[i] == u) s_b[i] = presto_token_score(P[tok[i]], Q[tok[i]], presto_lambda(lam, D, depth[i]));
+      if (nkids[u] == 0) {
+        const double lam_child = presto_lambda(lam, D, depth[u] + 1);
+        std::vector<PrestoCand> mine;
+        for (int t = 0; t < V; ++t) {
+          const double sc = presto_token_score(P[t], Q[t], lam_child);
+          if (sc > -kInf) mine.push_back({sc, u, t});
+        }
+        std::sort(mine.begin(), mine.end(), [](const PrestoCand& a, const PrestoCand& c) {
+          return a.score > c.score || (a.score == c.score && a.tok < c.tok);
+        });
+        for (int j = 0; j < k && j < (int)mine.size(); ++j) cands.push_back(mine[j]);
+      }
+    }
+    // path scores: parents precede children
+    S_b[0] = 0.0;
+    for (int i = 1; i < N; ++i) S_b[i] = S_b[par[i]] + s_b[i];
+    for (PrestoCand& c : cands) c.score += S_b[c.node];
+    std::sort(cands.begin(), cands.end(), [](const PrestoCand& a, const PrestoCand& c) {
+      if (a.score != c.score) return a.score > c.score;
+      if (a.node != c.node) return a.node < c.node;
+      return a.tok < c.tok;
+    });
+    for (int j = 0; j < b_top; ++j) {
+      const bool has = j < (int)cands.size();
+      out_node[(int64_t)b * b_top + j] = has ? cands[j].node : -1;
+      out_tok[(int64_t)b * b_top + j] = has ? cands[j].tok : -1;
+      out_score[(int64_t)b * b_top + j] = has ? cands[j].score : -kInf;
+    }
   }
   return 0;
 }

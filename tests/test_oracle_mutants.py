@@ -43,6 +43,13 @@ CACHE_PINS = [
     pins.test_cache_hit_is_membership_in_the_fanout_cache,
 ]
 
+PRESTO_PINS = [
+    pins.test_presto_scores_match_log_softmax_and_ancestor_sums,
+    lambda: pins.test_presto_proxy_minimises_the_kl_objective(1.0),
+    pins.test_presto_lambda_zero_expands_the_draft_top_k,
+    pins.test_presto_expansion_brute_force,
+]
+
 
 MUTANTS = [
     # (name, original text, planted text, pins expected to catch it)
@@ -84,6 +91,15 @@ MUTANTS = [
      "out_hit[b] = pos <= F[n[b]] ? 1 : 0;", CACHE_PINS),
     ("cache row of the next position", "const int64_t row = (int64_t)b * (K + 1) + n[b];",
      "const int64_t row = (int64_t)b * (K + 1) + (n[b] < K ? n[b] + 1 : n[b]);", CACHE_PINS),
+    ("presto ratio not clipped at 1", "const double rho = std::min(1.0, p / q);", "const double rho = p / q;",
+     PRESTO_PINS),
+    ("presto lambda on the draft term", "return logq + lambda * std::log(rho);",
+     "return lambda * logq + std::log(rho);", PRESTO_PINS),
+    ("presto path score drops the parent", "S_b[i] = S_b[par[i]] + s_b[i];", "S_b[i] = s_b[i];", PRESTO_PINS),
+    ("presto expands internal nodes too", "      if (nkids[u] == 0) {\n", "      if (nkids[u] >= 0) {\n",
+     PRESTO_PINS),
+    ("presto expansion uses the leaf's own depth", "presto_lambda(lam, D, depth[u] + 1)",
+     "presto_lambda(lam, D, depth[u] > 0 ? depth[u] : 1)", PRESTO_PINS),
     ("geometric fan-out floor", "F_out[k] = (int32_t)std::ceil(f);", "F_out[k] = (int32_t)std::floor(f);",
      [pins.test_geometric_fanout_closed_form]),
 ]

@@ -535,3 +535,146 @@ def test_cache_rejects_outcomes_outside_the_window():
     for n, t in (([0, 3], [0, 0]), ([0, -1], [0, 0]), ([0, 0], [0, 5]), ([0, 0], [-1, 0])):
         with pytest.raises(oracle.OracleError):
             oracle.cache_hit_test(z, np.array(n, np.int32), np.array(t, np.int32), None, "f32")
+
+
+# ---------------------------------------------------------------- PRESTO scoring
+# PRESTO page §4.1 (token score s = log q + lambda log rho, rho = min(1, p/q);
+# path score = sum of token scores, eq. 10), §4.2 (priority expansion), §4.4
+# (the proxy p* ~ q rho^lambda minimises KL(p || q) - lambda E_p[log rho]).
+
+def _presto_tree(rng, B, N, V, masked=0.0):
+    tgt = rng.normal(scale=2.0, size=(B, N, V))
+    drf = tgt + rng.normal(scale=1.0, size=(B, N, V))
+    if masked:
+        tgt[rng.random(tgt.shape) < masked] = -np.inf
+        drf[rng.random(drf.shape) < masked] = -np.inf
+        tgt[..., 0] = 0.0
+        drf[..., 0] = 0.0
+    parent = np.full((B, N), -1, np.int32)
+    tok = np.zeros((B, N), np.int32)
+    for b in range(B):
+        for i in range(1, N):
+            parent[b, i] = rng.integers(0, i)
+            tok[b, i] = rng.integers(0, V)
+    return tgt, drf, tok, parent
+
+
+def _log_softmax_rows(z, T):
+    with np.errstate(invalid="ignore"):
+        return scipy.special.log_softmax(z / T, axis=-1)
+
+
+def test_presto_scores_match_log_softmax_and_ancestor_sums():
+    rng = np.random.default_rng(71)
+    B, N, V, T = 5, 14, 30, 0.8
+    tgt, drf, tok, parent = _presto_tree(rng, B, N, V, masked=0.15)
+    lam = np.array([0.5, 1.0, 0.0, 2.0], np.float32)
+    out = oracle.presto_score(tgt, drf, tok, parent, T, lam, 2, 3, "f64")
+    lp, lq = _log_softmax_rows(tgt, T), _log_softmax_rows(drf, T)
+    for b in range(B):
+        depth = [0] * N
+        for i in range(1, N):
+            depth[i] = depth[parent[b, i]] + 1
+        for i in range(1, N):
+            u, x = parent[b, i], tok[b, i]
+            la = float(lam[min(depth[i], len(lam)) - 1])
+            a, c = lp[b, u, x], lq[b, u, x]
+            if c == -np.inf or (la > 0 and a == -np.inf):
+                want = -np.inf
+            else:
+                want = c + (la * min(0.0, a - c) if la > 0 else 0.0)
+            got = out["s"][b, i]
+            assert (got == want) if want == -np.inf else abs(got - want) < 1e-12
+            # ancestor sum, walked by hand
+            S, j = 0.0, i
+            while j > 0:
+                S += out["s"][b, j]
+                j = parent[b, j]
+            assert (out["S"][b, i] == S) if S == -np.inf else abs(out["S"][b, i] - S) < 1e-12
+        assert out["s"][b, 0] == 0.0 and out["S"][b, 0] == 0.0
+
+
+@pytest.mark.parametrize("lam_val", [0.3, 1.0, 2.5])
+def test_presto_proxy_minimises_the_kl_objective(lam_val):
+    """With the root as the only node, the expansion proposes every token with
+    its score s(t); softmax(s) must be the minimiser of KL(p || q) - lambda
+    E_p[log rho], whose minimum is -log sum_t q(t) rho(t)^lambda."""
+    rng = np.random.default_rng(72)
+    V, T = 40, 1.1
+    tgt = rng.normal(scale=2.0, size=(1, 1, V))
+    drf = tgt + rng.normal(scale=1.5, size=(1, 1, V))
+    out = oracle.presto_score(tgt, drf, np.zeros((1, 1), np.int32), np.full((1, 1), -1, np.int32), T,
+                              np.array([lam_val], np.float32), V, V, "f64")
+    assert sorted(out["tok"][0].tolist()) == list(range(V))
+    s = np.empty(V)
+    s[out["tok"][0]] = out["score"][0]
+    p = scipy.special.softmax(tgt[0, 0] / T)
+    q = scipy.special.softmax(drf[0, 0] / T)
+    log_rho = np.minimum(0.0, np.log(p) - np.log(q))
+    pstar = scipy.special.softmax(s)
+
+    def objective(r):
+        return float(np.sum(r * (np.log(r) - np.log(q))) - lam_val * np.sum(r * log_rho))
+
+    closed = -math.log(float(np.sum(q * np.exp(lam_val * log_rho))))
+    assert abs(objective(pstar) - closed) < 1e-10
+    for _ in range(20):
+        r = pstar * np.exp(rng.normal(scale=0.05, size=V))
+        r /= r.sum()
+        assert objective(r) > objective(pstar)
+
+
+def test_presto_lambda_zero_expands_the_draft_top_k():
+    """lambda = 0: the proxy is q itself, so a leaf proposes the fan-out's top-k of its draft row."""
+    rng = np.random.default_rng(73)
+    V, k = 200, 9
+    bits = rng.integers(0x3F00, 0x3F20, size=(1, 1, V)).astype(np.uint16)  # bf16 with ties
+    tgt_bits = rng.integers(0x3F00, 0x4000, size=(1, 1, V)).astype(np.uint16)
+    out = oracle.presto_score(tgt_bits, bits, np.zeros((1, 1), np.int32), np.full((1, 1), -1, np.int32), 0.7,
+                              np.array([0.0], np.float32), k, k, "bf16")
+    ids, _ = oracle.fanout_topk(bits.reshape(1, V), np.array([k], np.int32), k, "bf16")
+    assert out["tok"][0].tolist() == ids[0].tolist()
+    assert (out["node"][0] == 0).all()
+
+
+def test_presto_expansion_brute_force():
+    rng = np.random.default_rng(74)
+    B, N, V, T, k, b_top = 4, 11, 17, 0.9, 3, 7
+    tgt, drf, tok, parent = _presto_tree(rng, B, N, V, masked=0.2)
+    lam = np.array([0.7, 1.3, 0.4], np.float32)
+    out = oracle.presto_score(tgt, drf, tok, parent, T, lam, k, b_top, "f64")
+    lp, lq = _log_softmax_rows(tgt, T), _log_softmax_rows(drf, T)
+    for b in range(B):
+        depth = [0] * N
+        for i in range(1, N):
+            depth[i] = depth[parent[b, i]] + 1
+        leaves = [u for u in range(N) if not (parent[b] == u).any()]
+        cands = []
+        for u in leaves:
+            la = float(lam[min(depth[u] + 1, len(lam)) - 1])
+            mine = []
+            for t in range(V):
+                a, c = lp[b, u, t], lq[b, u, t]
+                if c == -np.inf or a == -np.inf:
+                    continue
+                mine.append((c + la * min(0.0, a - c), t))
+            mine.sort(key=lambda e: (-e[0], e[1]))
+            cands += [(out["S"][b, u] + sc, u, t) for sc, t in mine[:k]]
+        cands.sort(key=lambda e: (-e[0], e[1], e[2]))
+        for j in range(b_top):
+            if j < len(cands):
+                assert (out["node"][b, j], out["tok"][b, j]) == (cands[j][1], cands[j][2])
+                want = cands[j][0]
+                assert out["score"][b, j] == want if want == -np.inf else abs(out["score"][b, j] - want) < 1e-12
+            else:
+                assert out["node"][b, j] == -1 and out["score"][b, j] == -np.inf
+
+
+def test_presto_rejects_bad_trees():
+    z = np.zeros((1, 3, 5))
+    with pytest.raises(oracle.OracleError):
+        oracle.presto_score(z, z, np.zeros((1, 3), np.int32), np.array([[-1, 0, 2]], np.int32), 1.0,
+                            np.array([1.0], np.float32), 2, 2, "f64")
+    with pytest.raises(oracle.OracleError):
+        oracle.presto_score(z, z, np.array([[0, 0, 5]], np.int32), np.array([[-1, 0, 0]], np.int32), 1.0,
+                            np.array([1.0], np.float32), 2, 2, "f64")
