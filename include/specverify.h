@@ -92,7 +92,8 @@ enum {
   SV_OP_FANOUT = 4,
   SV_OP_CHAIN_PM = 5,
   SV_OP_TREE_PM = 6,
-  SV_OP_CACHE = 7
+  SV_OP_CACHE = 7,
+  SV_OP_PRESTO = 8
 };
 
 /* Limits of this build. */
@@ -115,10 +116,11 @@ const char* sv_status_string(sv_status s);
 
 /*
  * Workspace bytes for one call of `op` with the given shape.  gamma_or_N is
- * gamma (chain, greedy, multi, chain_pm), N (tree, tree_pm) or K (cache); B is the number of sequences (or
- * R, the number of rows, for fan-out); K is used by multi only; F_max by
- * fan-out only.  Returns SV_EINVAL / SV_EUNSUPPORTED for shapes the
- * corresponding call would reject.
+ * gamma (chain, greedy, multi, chain_pm), N (tree, tree_pm, presto) or K
+ * (cache); B is the number of sequences (or R, the number of rows, for
+ * fan-out); K is used by multi only; F_max by fan-out, and as k by presto.
+ * Returns SV_EINVAL / SV_EUNSUPPORTED for shapes the corresponding call would
+ * reject.
  */
 sv_status sv_workspace_size(sv_op op, sv_dtype dt, int32_t B, int32_t K, int32_t gamma_or_N, int32_t V,
                             int32_t F_max, size_t* bytes);
@@ -280,6 +282,42 @@ sv_status sv_fanout_topk(const void* logits, sv_dtype dt, int64_t stride, int32_
 sv_status sv_cache_hit_test(const void* drf, sv_dtype dt, int64_t stride, int32_t B, int32_t K, int32_t V,
                             const int32_t* n, const int32_t* t, const int32_t* F, int32_t* out_rank, int32_t* out_hit,
                             void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * PRESTO prefix-aligned scoring and one priority expansion step ("PRESTO:
+ * prefix-aligned tree drafting for diffusion speculative decoding", §4.1
+ * eq. 9-10, §4.2, §4.3 self-speculative form: the tree's target rows give
+ * the acceptance probability exactly).  Tree layout as for sv_verify_tree:
+ * node u's rows P_u (tgt) and Q_u (drf) are the distributions of u's
+ * children; depth(0) = 0, depth(i) = depth(parent(i)) + 1; lambda of depth
+ * d >= 1 is lambda[min(d, D) - 1] (device float array of D >= 1 values).
+ * Token score of a token t under node u at child depth d (natural log):
+ *   s_u(t) = log Q_u(t) + lambda_d * log min(1, P_u(t) / Q_u(t))
+ * (-inf where Q_u(t) = 0, or where P_u(t) = 0 and lambda_d > 0; lambda_d = 0
+ * gives log Q_u(t)), i.e. the log of the proxy q * rho^lambda of §4.4 up to
+ * its normaliser.
+ * Outputs (device):
+ *   out_s [B, N] s_i = s_{parent(i)}(tok_i) for i >= 1, 0 for the root
+ *   out_S [B, N] path score, the sum of s along the root-to-i path (eq. 10)
+ *   (out_s / out_S may be NULL)
+ *   out_node, out_tok [B, b_top], out_score [B, b_top] (may be NULL): one
+ *     expansion step from the leaves (nodes without children): each leaf u
+ *     proposes its k best tokens by s_u(t) (score descending, token
+ *     ascending; -inf scores are not proposed), a proposal's priority is
+ *     S_u + s_u(t), and the b_top best proposals of the sequence are listed
+ *     by priority descending, then node ascending, then token ascending;
+ *     padded with node -1, token -1, score -inf.
+ * 1 <= k, b_top <= SV_MAX_FANOUT.  Reads every node's row pair twice at most
+ * (statistics, then the leaves' rows for the proposals).  Device errors: a
+ * token outside [0, V) (its s is -inf), an invalid parent array, a row
+ * without a finite logit.  Workspace: SV_OP_PRESTO with gamma_or_N = N and
+ * F_max = k.
+ */
+sv_status sv_presto_score(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride, int64_t drf_stride,
+                          const int32_t* node_tok, const int32_t* parent, int32_t B, int32_t N, int32_t V, float T,
+                          const float* lambda, int32_t D, int32_t k, int32_t b_top, float* out_s, float* out_S,
+                          int32_t* out_node, int32_t* out_tok, float* out_score, void* ws, size_t ws_bytes,
+                          void* stream);
 
 /*
  * Host helper, SSD / Saguaro review Theorem 12: F_k = ceil(F0 * a_p^(k/(1+r)))

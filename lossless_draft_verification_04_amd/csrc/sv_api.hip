@@ -201,6 +201,30 @@ sv_status plan_cache(sv_dtype dt, int32_t B, int32_t K, int32_t V, Plan* pl) {
   return SV_OK;
 }
 
+// PRESTO scoring: statistics of every node's row pair (all rows stream), then
+// the expansion over the same rows (only leaves work); k proposals per part.
+sv_status plan_presto(sv_dtype dt, int32_t B, int32_t N, int32_t V, int32_t k, Plan* pl) {
+  if (bad_dtype(dt)) return SV_EDTYPE;
+  if (B < 0 || N < 1 || V < 1 || k < 1) return SV_EINVAL;
+  if (B > SV_MAX_SEQ || N > SV_MAX_N || V > SV_MAX_V || k > SV_MAX_FANOUT) return SV_EUNSUPPORTED;
+  pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
+  const int64_t rows = (int64_t)B * N * 2;
+  split(rows, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
+  split((int64_t)B * N, pl->nvec, stats_blocks(), &pl->nch2, &pl->vpc2);
+  pl->grid1 = rows * pl->nch1;
+  pl->grid2 = (int64_t)B * N * pl->nch2;
+  if (pl->grid1 > INT32_MAX || pl->grid2 > INT32_MAX) return SV_EUNSUPPORTED;
+  size_t off = kWsFixed;
+  pl->off_part1 = off;
+  off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
+  pl->off_part2 = off;  // gathered child logits
+  off = align_up(off + (size_t)2 * B * N * sizeof(float), 256);
+  pl->off_lists = off;  // expansion part lists (8-byte entries)
+  off = align_up(off + (size_t)B * N * pl->nch2 * k * 8, 256);
+  pl->bytes = off;
+  return SV_OK;
+}
+
 sv_status check_ws(const void* ws, size_t ws_bytes, const Plan& pl) {
   if (!ws || ws_bytes < pl.bytes) return SV_EWORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return SV_EALIGN;
@@ -258,6 +282,7 @@ sv_status sv_workspace_size(sv_op op, sv_dtype dt, int32_t B, int32_t K, int32_t
     case SV_OP_CHAIN_PM: st = plan_chain(dt, B, 1, gamma_or_N, V, true, &pl); break;
     case SV_OP_TREE_PM: st = plan_tree(dt, B, gamma_or_N, V, true, &pl); break;
     case SV_OP_CACHE: st = plan_cache(dt, B, gamma_or_N, V, &pl); break;
+    case SV_OP_PRESTO: st = plan_presto(dt, B, gamma_or_N, V, F_max, &pl); break;
     case SV_OP_FANOUT: st = plan_fanout(dt, B, V, F_max, &pl); break;
     default: return SV_EINVAL;
   }
@@ -425,6 +450,7 @@ static sv_status verify_tree_like(const void* tgt, const void* drf, sv_dtype dt,
   p.part = w + pl.off_part1;
   p.nch = pl.nch1;
   p.pm = pm;
+  p.all_rows = false;
   pick_slices(B, pl.nvec, tree_walk_capacity(dt, true, pm), tree_walk_capacity(dt, false, pm), &p.G, &p.held);
   p.vpc = pl.vpc1;
   p.nvec = pl.nvec;
@@ -503,6 +529,78 @@ sv_status sv_cache_hit_test(const void* drf, sv_dtype dt, int64_t stride, int32_
   p.vpc = pl.vpc1;
   p.nvec = pl.nvec;
   return launch_cache(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+sv_status sv_presto_score(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride, int64_t drf_stride,
+                          const int32_t* node_tok, const int32_t* parent, int32_t B, int32_t N, int32_t V, float T,
+                          const float* lambda, int32_t D, int32_t k, int32_t b_top, float* out_s, float* out_S,
+                          int32_t* out_node, int32_t* out_tok, float* out_score, void* ws, size_t ws_bytes,
+                          void* stream) {
+  Plan pl;
+  sv_status st = plan_presto(dt, B, N, V, k, &pl);
+  if (st != SV_OK) return st;
+  if (bad_temperature(T) || D < 1 || b_top < 1) return SV_EINVAL;
+  if (b_top > SV_MAX_FANOUT) return SV_EUNSUPPORTED;
+  if (B == 0) return SV_OK;
+  if ((st = check_rows(tgt, tgt_stride, V, dt)) != SV_OK) return st;
+  if ((st = check_rows(drf, drf_stride, V, dt)) != SV_OK) return st;
+  if (!node_tok || !parent || !lambda || !out_node || !out_tok) return SV_EINVAL;
+  if ((st = check_ws(ws, ws_bytes, pl)) != SV_OK) return st;
+  char* w = static_cast<char*>(ws);
+  TreeParams t;
+  std::memset(&t, 0, sizeof t);
+  t.tgt = tgt;
+  t.drf = drf;
+  t.tgt_sb = tgt_stride * elem_bytes(dt);
+  t.drf_sb = drf_stride * elem_bytes(dt);
+  t.tok = node_tok;
+  t.parent = parent;
+  t.B = B;
+  t.N = N;
+  t.max_depth = N;
+  t.V = V;
+  t.c = log2e_over(T);
+  t.err = reinterpret_cast<int32_t*>(w);
+  t.part = w + pl.off_part1;
+  t.zc = reinterpret_cast<float*>(w + pl.off_part2);
+  t.slots = nullptr;
+  t.nch = pl.nch1;
+  t.G = 0;  // no walk: nothing to zero
+  t.held = true;
+  t.pm = false;
+  t.all_rows = true;
+  t.vpc = pl.vpc1;
+  t.nvec = pl.nvec;
+  PrestoParams p;
+  p.tgt = tgt;
+  p.drf = drf;
+  p.tgt_sb = t.tgt_sb;
+  p.drf_sb = t.drf_sb;
+  p.tok = node_tok;
+  p.parent = parent;
+  p.B = B;
+  p.N = N;
+  p.V = V;
+  p.c = t.c;
+  p.lam = lambda;
+  p.D = D;
+  p.k = k;
+  p.b_top = b_top;
+  p.out_s = out_s;
+  p.out_S = out_S;
+  p.out_node = out_node;
+  p.out_tok = out_tok;
+  p.out_score = out_score;
+  p.err = t.err;
+  p.cnt = reinterpret_cast<uint32_t*>(w + kWsHeader);
+  p.part = t.part;
+  p.zc = t.zc;
+  p.lists = w + pl.off_lists;
+  p.nch1 = pl.nch1;
+  p.nch2 = pl.nch2;
+  p.vpc2 = pl.vpc2;
+  p.nvec = pl.nvec;
+  return launch_presto(p, t, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 int32_t sv_geometric_fanout(int32_t F0, double a_p, double r, int32_t K, int32_t capped_last, int32_t* F_out) {

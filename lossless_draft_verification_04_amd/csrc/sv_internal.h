@@ -80,7 +80,32 @@ struct TreeParams {
   int32_t G;       // walk blocks per sequence
   bool held;       // slices of at most kSliceTiles tiles, held in registers
   bool pm;         // point-mass acceptance: target rows only
+  bool all_rows;   // stream every node's rows (leaves too), not only those with children
   int64_t vpc, nvec;
+};
+
+struct PrestoParams {
+  const void* tgt;
+  const void* drf;
+  int64_t tgt_sb, drf_sb;
+  const int32_t* tok;
+  const int32_t* parent;
+  int32_t B, N, V;
+  float c;           // log2(e) / T
+  const float* lam;  // lambda per depth, [D]
+  int32_t D, k, b_top;
+  float* out_s;
+  float* out_S;
+  int32_t* out_node;
+  int32_t* out_tok;
+  float* out_score;
+  int32_t* err;
+  uint32_t* cnt;     // per-sequence arrival counters
+  void* part;        // row statistics parts, [B][N][2][nch1] (tree statistics launch)
+  float* zc;         // each child's logits under its parent's rows, [2][B][N]
+  void* lists;       // expansion part lists, [B][N][nch2][k]
+  int32_t nch1, nch2;
+  int64_t vpc2, nvec;
 };
 
 struct FanoutParams {
@@ -118,7 +143,7 @@ struct CacheParams {
 struct Plan {
   int32_t nch1 = 1, nch2 = 1;
   int64_t vpc1 = 0, vpc2 = 0, nvec = 0;
-  size_t off_part1 = 0, off_jobs = 0, off_part2 = 0;
+  size_t off_part1 = 0, off_jobs = 0, off_part2 = 0, off_lists = 0;
   size_t bytes = 0;
   int64_t grid1 = 0, grid2 = 0;
 };
@@ -128,6 +153,8 @@ hipError_t launch_greedy(const GreedyParams& p, sv_dtype dt, const Plan& plan, h
 hipError_t launch_tree(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
 hipError_t launch_fanout(const FanoutParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
 hipError_t launch_cache(const CacheParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
+hipError_t launch_presto(const PrestoParams& p, const TreeParams& stats, sv_dtype dt, const Plan& plan,
+                         hipStream_t s);
 hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s);
 
 // Blocks of one launch of the draw / walk kernel (held or streamed slices)

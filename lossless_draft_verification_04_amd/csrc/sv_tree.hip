@@ -77,7 +77,7 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
     if (i < a.N && pk[k] == u) has_kids = 1;
     else pk[k] = -1;  // not a child of u
   }
-  if (!__syncthreads_or(has_kids)) {
+  if (!a.all_rows && !__syncthreads_or(has_kids)) {
     zero_slots(a.slots, (int64_t)a.B * kSlotWords * a.G, bid, kTNT);  // for the walk launch
     return;
   }
@@ -492,6 +492,15 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
     if (threadIdx.x == 0) a.out_len[b] = depth;
   }
   if (t >= 0 && threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
+}
+
+// The statistics launch alone (also used by the PRESTO scoring call).
+hipError_t launch_tree_stats(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s) {
+  if (dt == SV_BF16)
+    tree_stats_kernel<SV_BF16><<<dim3((unsigned)plan.grid1), dim3(kTNT), 0, s>>>(p);
+  else
+    tree_stats_kernel<SV_F32><<<dim3((unsigned)plan.grid1), dim3(kTNT), 0, s>>>(p);
+  return hipGetLastError();
 }
 
 template <int DT>

@@ -31,7 +31,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 SV_OK, SV_EINVAL, SV_EDTYPE, SV_EALIGN, SV_EWORKSPACE, SV_EUNSUPPORTED, SV_EHIP = range(7)
 SV_F32, SV_BF16 = 0, 1
 (SV_OP_CHAIN, SV_OP_GREEDY, SV_OP_MULTI, SV_OP_TREE, SV_OP_FANOUT, SV_OP_CHAIN_PM, SV_OP_TREE_PM,
- SV_OP_CACHE) = range(8)
+ SV_OP_CACHE, SV_OP_PRESTO) = range(9)
 DERR_TOKEN, DERR_TREE, DERR_FANOUT, DERR_ROW = 1, 2, 4, 8
 
 _P = ctypes.c_void_p
@@ -56,6 +56,8 @@ _SIGS = {
                            _sz, _P], _i32),
     "sv_fanout_topk": ([_P, _i32, _i64, _i32, _i32, _P, _i32, _P, _P, _P, _sz, _P], _i32),
     "sv_cache_hit_test": ([_P, _i32, _i64, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _sz, _P], _i32),
+    "sv_presto_score": ([_P, _P, _i32, _i64, _i64, _P, _P, _i32, _i32, _i32, _f32, _P, _i32, _i32, _i32, _P, _P,
+                         _P, _P, _P, _P, _sz, _P], _i32),
     "sv_geometric_fanout": ([_i32, _f64, _f64, _i32, _i32, ctypes.POINTER(_i32)], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -297,6 +299,31 @@ def sv_cache_hit_test(drf, n, t, F=None, workspace=None):
     _check(_lib.sv_cache_hit_test(_ptr(drf), dt, _row_stride(drf, "drf"), B, K1 - 1, V, _ptr(n), _ptr(t), _ptr(F),
                                   _ptr(rank), _ptr(hit), _ptr(ws), ws.numel(), _stream(dev)), "sv_cache_hit_test")
     return dict(rank=rank, hit=hit)
+
+
+def sv_presto_score(tgt, drf, node_tok, parent, T, lam, k, b_top, want_scores=True, workspace=None):
+    """tgt, drf [B, N, V]; node_tok, parent [B, N] int32; lam [D] float32 (device)
+    -> dict(s, S [B, N] float or None, node, tok [B, b_top] int32, score [B, b_top] float)."""
+    B, N, V = tgt.shape
+    if tuple(drf.shape) != (B, N, V) or drf.dtype != tgt.dtype:
+        raise SpecVerifyError(SV_EINVAL, f"drf shape {tuple(drf.shape)} / dtype does not match tgt")
+    _i32_tensor(node_tok, (B, N), "node_tok")
+    _i32_tensor(parent, (B, N), "parent")
+    if lam.dtype != torch.float32 or lam.dim() != 1 or not lam.is_contiguous():
+        raise SpecVerifyError(SV_EINVAL, "lam: want a contiguous float32 vector")
+    dt = _dtype_code(tgt)
+    dev = tgt.device
+    ws = workspace if workspace is not None else Workspace.get(
+        dev, workspace_size(SV_OP_PRESTO, dt, B, 1, N, V, int(k)))
+    f = lambda *shape: torch.empty(*shape, dtype=torch.float32, device=dev)
+    out = dict(s=f(B, N) if want_scores else None, S=f(B, N) if want_scores else None,
+               node=torch.empty(B, b_top, dtype=torch.int32, device=dev),
+               tok=torch.empty(B, b_top, dtype=torch.int32, device=dev), score=f(B, b_top))
+    _check(_lib.sv_presto_score(_ptr(tgt), _ptr(drf), dt, _row_stride(tgt, "tgt"), _row_stride(drf, "drf"),
+                                _ptr(node_tok), _ptr(parent), B, N, V, float(T), _ptr(lam), lam.numel(), int(k),
+                                int(b_top), _ptr(out["s"]), _ptr(out["S"]), _ptr(out["node"]), _ptr(out["tok"]),
+                                _ptr(out["score"]), _ptr(ws), ws.numel(), _stream(dev)), "sv_presto_score")
+    return out
 
 
 def sv_geometric_fanout(F0, a_p, r, K, capped_last=False):

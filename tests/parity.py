@@ -196,6 +196,52 @@ def cache(rows_cpu, n_cpu, t_cpu, F_cpu=None):
     return out, ref
 
 
+SCORE_TOL = 1e-4  # natural-log scores: fp32 on the GPU against fp64 in the oracle
+
+
+def _close_scores(got, want):
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    inf = np.isinf(want)
+    diff = np.abs(np.where(inf, 0.0, got) - np.where(inf, 0.0, want))
+    return np.where(inf, got == want, diff <= SCORE_TOL * np.maximum(1.0, np.abs(np.where(inf, 0.0, want))))
+
+
+def presto(wl, lam, k, b_top, T=None):
+    """PRESTO scoring: s and S within SCORE_TOL; the expansion list position by position, where a position
+    whose oracle priority lies within SCORE_TOL of a neighbour's may hold any of the tied proposals."""
+    p = wl.params
+    T = f32(p["T"] if T is None else T)
+    g = wl.to(DEV)
+    lam = np.asarray(lam, dtype=np.float32)
+    say(f"  presto B={p['B']} N={p['N']} V={p['V']} {p['dtype']} T={T} lam={lam.tolist()} k={k} b={b_top}")
+    out = svx.sv_presto_score(g["tgt"], g["drf"], g["tok"], g["parent"], T, torch.from_numpy(lam).to(DEV), k, b_top)
+    torch.cuda.synchronize()
+    extra = 16
+    ref = oracle.presto_score(np_logits(wl.tensors["tgt"]), np_logits(wl.tensors["drf"]), wl.tensors["tok"].numpy(),
+                              wl.tensors["parent"].numpy(), T, lam, k, b_top + extra, p["dtype"])
+    for name in ("s", "S"):
+        ok = _close_scores(out[name].cpu().numpy(), ref[name])
+        assert ok.all(), f"presto {name}: {int((~ok).sum())} off, first at {np.argwhere(~ok)[0].tolist()}"
+    gn, gt, gs = (out[x].cpu().numpy() for x in ("node", "tok", "score"))
+    rn, rt, rs = ref["node"], ref["tok"], ref["score"]
+    ok = _close_scores(gs, rs[:, :b_top])
+    assert ok.all(), f"presto priorities: {int((~ok).sum())} off, first at {np.argwhere(~ok)[0].tolist()}"
+    tied = 0
+    for b in range(p["B"]):
+        for j in range(b_top):
+            if (gn[b, j], gt[b, j]) == (rn[b, j], rt[b, j]):
+                continue
+            # a near tie: the GPU's proposal must be one of the oracle's proposals at that priority
+            near = [(rn[b, i], rt[b, i]) for i in range(b_top + extra)
+                    if rn[b, i] >= 0 and abs(rs[b, i] - rs[b, j]) <= SCORE_TOL * max(1.0, abs(rs[b, j]))]
+            assert (gn[b, j], gt[b, j]) in near, \
+                f"presto proposal {b},{j}: gpu {(gn[b, j], gt[b, j])} oracle {(rn[b, j], rt[b, j])}"
+            tied += 1
+    say(f"  presto proposals: {p['B'] * b_top} compared, {tied} inside near ties")
+    return out, ref
+
+
 def fanout(logits_cpu, F_cpu, F_max):
     dt = dtype_name(logits_cpu)
     say(f"  fanout R={logits_cpu.shape[0]} V={logits_cpu.shape[1]} F_max={F_max} {dt}")

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 14
+    assert len(names) == 15
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(svx.EXPORTED)
@@ -59,7 +59,7 @@ def test_workspace_size():
     assert st == svx.SV_OK and n > 65536 * 4
     st2, n2 = ws_size(svx.SV_OP_MULTI, svx.SV_BF16, 32, 1, 16, 152064)
     assert st2 == svx.SV_OK and n2 == n  # multi with K = 1 is the chain
-    for op in range(8):
+    for op in range(9):
         st, n = ws_size(op, svx.SV_BF16, 8, 2, 16, 1000, 8)
         assert st == svx.SV_OK and n % 256 == 0
     # point-mass calls stream no draft rows: never more scratch than the standard ones
@@ -73,6 +73,9 @@ def test_workspace_size():
     assert ws_size(svx.SV_OP_CACHE, 0, 32769, 1, 4, 100)[0] == svx.SV_EUNSUPPORTED
     assert ws_size(svx.SV_OP_CACHE, 0, 1, 1, -1, 100)[0] == svx.SV_EINVAL
     assert ws_size(svx.SV_OP_CACHE, 1, 32, 1, 16, 152064) == (svx.SV_OK, 256 + 65536 * 4)  # fixed part only
+    assert ws_size(svx.SV_OP_PRESTO, 1, 8, 1, 64, 128256, 65)[0] == svx.SV_EUNSUPPORTED  # k > 64
+    assert ws_size(svx.SV_OP_PRESTO, 1, 8, 1, 64, 128256, 0)[0] == svx.SV_EINVAL
+    assert ws_size(svx.SV_OP_PRESTO, 1, 8, 1, 1025, 128256, 8)[0] == svx.SV_EUNSUPPORTED
     assert ws_size(svx.SV_OP_CHAIN, 7, 1, 1, 4, 100)[0] == svx.SV_EDTYPE
     assert ws_size(svx.SV_OP_CHAIN, 0, 1, 1, 0, 100)[0] == svx.SV_EINVAL
     assert ws_size(svx.SV_OP_CHAIN, 0, 1, 1, 65, 100)[0] == svx.SV_EUNSUPPORTED
@@ -165,6 +168,20 @@ def test_cache_hit_test_argument_checks():
     assert c(F=None) == svx.SV_EINVAL and c(hit=None) == svx.SV_EINVAL  # F and out_hit come together
     assert c(ws=None) == svx.SV_EWORKSPACE and c(wsb=1024) == svx.SV_EWORKSPACE
     assert c(B=0) == svx.SV_OK and c(B=0, F=None, hit=None) == svx.SV_OK
+
+
+def test_presto_argument_checks():
+    c = lambda **kw: L.sv_presto_score(kw.get("tgt", A), kw.get("drf", A2), kw.get("dt", 1), 1024, 1024,
+                                       kw.get("tok", A), kw.get("par", A), kw.get("B", 2), kw.get("N", 8), 1000,
+                                       kw.get("T", 1.0), kw.get("lam", A), kw.get("D", 2), kw.get("k", 4),
+                                       kw.get("b", 8), None, None, kw.get("node", A), kw.get("tk", A), None, WS,
+                                       kw.get("wsb", 1 << 30), None)
+    assert c(dt=5) == svx.SV_EDTYPE and c(N=0) == svx.SV_EINVAL and c(N=1025) == svx.SV_EUNSUPPORTED
+    assert c(k=0) == svx.SV_EINVAL and c(k=65) == svx.SV_EUNSUPPORTED and c(b=0) == svx.SV_EINVAL
+    assert c(b=65) == svx.SV_EUNSUPPORTED and c(D=0) == svx.SV_EINVAL and c(T=0.0) == svx.SV_EINVAL
+    assert c(tgt=MIS) == svx.SV_EALIGN and c(drf=None) == svx.SV_EINVAL and c(lam=None) == svx.SV_EINVAL
+    assert c(tok=None) == svx.SV_EINVAL and c(par=None) == svx.SV_EINVAL and c(node=None) == svx.SV_EINVAL
+    assert c(tk=None) == svx.SV_EINVAL and c(wsb=4096) == svx.SV_EWORKSPACE and c(B=0) == svx.SV_OK
 
 
 def test_workspace_helpers_reject_bad_arguments():
