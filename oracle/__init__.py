@@ -68,6 +68,8 @@ def _load(path):
     L.svo_cache_hit_test.restype = i32
     L.svo_presto_score.argtypes = [P, P, i32, i64, i64, P, P, i32, i32, i32, f64, P, i32, i32, i32, P, P, P, P, P]
     L.svo_presto_score.restype = i32
+    L.svo_branch_fork.argtypes = [P, i32, i64, P, P, i32, i32, i32, f64, f64, i32, P, P, P, P, P]
+    L.svo_branch_fork.restype = i32
     L.svo_geometric_fanout.argtypes = [i32, f64, f64, i32, i32, P]
     L.svo_geometric_fanout.restype = i32
     return L
@@ -331,6 +333,22 @@ def presto_score(tgt, drf, node_tok, parent, T, lam, k, b_top, dtype):
                                 _ptr(out["s"]), _ptr(out["S"]), _ptr(out["node"]), _ptr(out["tok"]),
                                 _ptr(out["score"]))
     _check(rc, "presto_score")
+    return out
+
+
+def branch_fork(drf, tok, cls, T, eps, k_max, dtype):
+    """SpecBranch fork.  drf [B, gamma+1, V] draft rows q_1..q_{gamma+1}; tok [B, gamma]; cls [B] or None
+    -> dict(pos, qb, k [B], ids [B, k_max], margin [B])."""
+    drf, code = _logits(drf, dtype)
+    B, g1, V = drf.shape
+    tok = _i32(tok)
+    cl = None if cls is None else _i32(cls)
+    out = dict(pos=np.zeros(B, np.int32), qb=np.zeros(B), k=np.zeros(B, np.int32),
+               ids=np.zeros((B, k_max), np.int32), margin=np.zeros(B))
+    rc = lib().svo_branch_fork(_ptr(drf), code, _row_stride(drf), _ptr(tok), _ptr(cl), B, g1 - 1, V, float(T),
+                               float(eps), int(k_max), _ptr(out["pos"]), _ptr(out["qb"]), _ptr(out["k"]),
+                               _ptr(out["ids"]), _ptr(out["margin"]))
+    _check(rc, "branch_fork")
     return out
 
 

@@ -870,6 +870,78 @@ int svo_presto_score(const void* tgt, const void* drf, int dtype, int64_t tgt_st
   return 0;
 }
 
+// SpecBranch branch resampling ([SB] "Key designs" 2-3): the hybrid
+// predictor's class s in {0, 1, 2} (an input: the predictor itself is a
+// trained network) places the branch point b on the window's positions
+// 1..gamma+1 -- s = 0: the round's first token (b = 1); s = 1: the first
+// drafted token whose draft probability falls below eps (b = gamma + 1 when
+// none does); s = 2: the next round's first token (b = gamma + 1).  Then
+// k = max(1, floor(k_max * (1 - q(x_b)))) branches are forked with the top-k
+// tokens of the draft distribution at b (value descending, index ascending).
+// At b = gamma + 1 no token is drafted yet: x_b is taken as the draft's most
+// likely token there (the first maximal index), so q(x_b) = max q_{gamma+1}.
+// Draft rows q_1..q_{gamma+1} at (b, j) = b*(gamma+1) + (j-1); tokens
+// x_1..x_gamma at b*gamma + (j-1); s may be null (every class 1).  Outputs:
+// out_pos [B] the 1-based branch position, out_qb [B] q(x_b), out_k [B],
+// out_ids [B*k_max] the branch tokens (-1 padded); out_margin [B] (may be
+// null) the distance of the two decisions to their edges: min over the
+// tested positions of |q_j(x_j) - eps|, and of k_max * (1 - q(x_b)) to the
+// nearest integer.
+int svo_branch_fork(const void* drf, int dtype, int64_t stride, const int32_t* tok, const int32_t* cls, int B,
+                    int gamma, int V, double T, double eps, int k_max, int32_t* out_pos, double* out_qb,
+                    int32_t* out_k, int32_t* out_ids, double* out_margin) {
+  if (B < 0 || gamma < 1 || V < 1 || !(T > 0.0) || k_max < 1) return 1;
+  std::vector<double> q;
+  std::vector<int> order(V);
+  for (int b = 0; b < B; ++b) {
+    const int s = cls ? cls[b] : 1;
+    if (s < 0 || s > 2) return 5;
+    const int32_t* x = tok + (int64_t)b * gamma;
+    for (int j = 0; j < gamma; ++j)
+      if (x[j] < 0 || x[j] >= V) return 3;
+    const int64_t row0 = (int64_t)b * (gamma + 1);
+    double margin = kInf;
+    int pos = gamma + 1;
+    if (s == 0) {
+      pos = 1;
+    } else if (s == 1) {
+      for (int j = 1; j <= gamma; ++j) {
+        if (!softmax_row(drf, dtype, (row0 + j - 1) * stride, V, T, q)) return 2;
+        const double qx = q[x[j - 1]];
+        margin = std::min(margin, std::fabs(qx - eps));
+        if (qx < eps) {
+          pos = j;
+          break;
+        }
+      }
+    }
+    if (!softmax_row(drf, dtype, (row0 + pos - 1) * stride, V, T, q)) return 2;
+    double qb;
+    if (pos <= gamma) {
+      qb = q[x[pos - 1]];
+    } else {
+      int best = 0;
+      for (int v = 1; v < V; ++v)
+        if (q[v] > q[best]) best = v;
+      qb = q[best];
+    }
+    const double kf = (double)k_max * (1.0 - qb);
+    const int k = std::max(1, (int)std::floor(kf));
+    margin = std::min(margin, std::fabs(kf - std::round(kf)));
+    // top-k of the draft row at b: a stable sort of the logits, descending
+    for (int v = 0; v < V; ++v) order[v] = v;
+    std::vector<double> z(V);
+    for (int v = 0; v < V; ++v) z[v] = load_logit(drf, dtype, (row0 + pos - 1) * stride + v);
+    std::stable_sort(order.begin(), order.end(), [&](int a, int c) { return z[a] > z[c]; });
+    out_pos[b] = pos;
+    out_qb[b] = qb;
+    out_k[b] = k;
+    for (int i = 0; i < k_max; ++i) out_ids[(int64_t)b * k_max + i] = (i < k && i < V) ? order[i] : -1;
+    if (out_margin) out_margin[b] = margin;
+  }
+  return 0;
+}
+
 // Geometric fan-out of [SSD] Theorem 12: F_k = F_0 * a_p^{k/(1+r)} for k < K
 // and, when capped_last, F_K = F_0 * a_p^{K/(1+r)} * (1 - a_p)^{-1/(1+r)};
 // rounded up to integers.  Writes K+1 values; returns their sum.

@@ -50,6 +50,8 @@ PRESTO_PINS = [
     pins.test_presto_expansion_brute_force,
 ]
 
+BRANCH_PINS = [pins.test_branch_fork_brute_force, pins.test_branch_fork_special_cases]
+
 
 MUTANTS = [
     # (name, original text, planted text, pins expected to catch it)
@@ -100,6 +102,13 @@ MUTANTS = [
      PRESTO_PINS),
     ("presto expansion uses the leaf's own depth", "presto_lambda(lam, D, depth[u] + 1)",
      "presto_lambda(lam, D, depth[u] > 0 ? depth[u] : 1)", PRESTO_PINS),
+    ("branch point at the first confident token", "        if (qx < eps) {", "        if (qx > eps) {",
+     BRANCH_PINS),
+    ("branch count rounded up", "std::max(1, (int)std::floor(kf));", "std::max(1, (int)std::ceil(kf));", BRANCH_PINS),
+    ("branch count ignores confidence", "const double kf = (double)k_max * (1.0 - qb);",
+     "const double kf = (double)k_max * qb;", BRANCH_PINS),
+    ("class 0 branches at the next round", "    if (s == 0) {\n      pos = 1;", "    if (s == 0) {\n      pos = gamma + 1;",
+     BRANCH_PINS),
     ("geometric fan-out floor", "F_out[k] = (int32_t)std::ceil(f);", "F_out[k] = (int32_t)std::floor(f);",
      [pins.test_geometric_fanout_closed_form]),
 ]

@@ -678,3 +678,73 @@ def test_presto_rejects_bad_trees():
     with pytest.raises(oracle.OracleError):
         oracle.presto_score(z, z, np.array([[0, 0, 5]], np.int32), np.array([[-1, 0, 0]], np.int32), 1.0,
                             np.array([1.0], np.float32), 2, 2, "f64")
+
+
+# ---------------------------------------------------------------- SpecBranch fork
+# SpecBranch notes, key designs 2-3: branch point by the hybrid predictor's class
+# (0: the round's first token; 1: the first drafted token with q(x) < eps; 2:
+# the next round's first token), k = max(1, floor(k_max (1 - q(x_b)))) branches
+# forked with the top-k of the draft distribution at the branch point.
+
+def _branch_brute(z, tok, cls, T, eps, k_max):
+    B, g1, V = z.shape
+    gamma = g1 - 1
+    q = scipy.special.softmax(z / T, axis=-1)
+    out = []
+    for b in range(B):
+        s = 1 if cls is None else int(cls[b])
+        pos = 1 if s == 0 else gamma + 1
+        if s == 1:
+            for j in range(1, gamma + 1):
+                if q[b, j - 1, tok[b, j - 1]] < eps:
+                    pos = j
+                    break
+        row = q[b, pos - 1]
+        qb = row[tok[b, pos - 1]] if pos <= gamma else row[int(np.argmax(row))]
+        k = max(1, int(math.floor(k_max * (1.0 - qb))))
+        order = np.argsort(-z[b, pos - 1], kind="stable")
+        out.append((pos, qb, k, [int(order[i]) if i < k and i < V else -1 for i in range(k_max)]))
+    return out
+
+
+def test_branch_fork_brute_force():
+    rng = np.random.default_rng(91)
+    B, gamma, V, T, k_max = 60, 5, 23, 0.9, 6
+    z = rng.integers(-3, 4, size=(B, gamma + 1, V)).astype(np.float64) * 0.7  # ties
+    z[rng.random(z.shape) < 0.1] = -np.inf
+    z[..., 0] = 0.0
+    q = scipy.special.softmax(z / T, axis=-1)
+    tok = np.array([[rng.choice(V, p=q[b, j]) for j in range(gamma)] for b in range(B)], np.int32)
+    cls = rng.integers(0, 3, B).astype(np.int32)
+    for eps in (0.05, 0.2, 0.6):
+        got = oracle.branch_fork(z, tok, cls, T, eps, k_max, "f64")
+        for b, (pos, qb, k, ids) in enumerate(_branch_brute(z, tok, cls, T, eps, k_max)):
+            assert got["pos"][b] == pos and got["k"][b] == k and abs(got["qb"][b] - qb) < 1e-12
+            assert got["ids"][b].tolist() == ids
+        assert set(got["pos"].tolist()) > {1}  # several branch points occur
+
+
+def test_branch_fork_special_cases():
+    rng = np.random.default_rng(92)
+    B, gamma, V, T = 30, 4, 40, 1.0
+    z = rng.normal(scale=2.0, size=(B, gamma + 1, V))
+    tok = rng.integers(0, V, size=(B, gamma)).astype(np.int32)
+    never = oracle.branch_fork(z, tok, None, T, 0.0, 8, "f64")  # q(x) < 0 never holds
+    assert (never["pos"] == gamma + 1).all()
+    always = oracle.branch_fork(z, tok, None, T, 1.5, 8, "f64")  # q(x) <= 1 < eps
+    assert (always["pos"] == 1).all()
+    first = oracle.branch_fork(z, tok, np.zeros(B, np.int32), T, 0.5, 8, "f64")
+    last = oracle.branch_fork(z, tok, np.full(B, 2, np.int32), T, 0.5, 8, "f64")
+    assert (first["pos"] == 1).all() and (last["pos"] == gamma + 1).all()
+    one = oracle.branch_fork(z, tok, None, T, 0.3, 1, "f64")
+    assert (one["k"] == 1).all()
+    # more branches where the branch point is less confident, never outside [1, k_max]
+    r = oracle.branch_fork(z, tok, None, T, 0.3, 16, "f64")
+    order = np.argsort(r["qb"])
+    assert (np.diff(r["k"][order]) <= 0).all() and r["k"].min() >= 1 and r["k"].max() <= 16
+    # the branches are the fan-out's top-k of the branch row
+    z32 = z.astype(np.float32)
+    r32 = oracle.branch_fork(z32, tok, None, T, 0.3, 16, "f32")
+    rows = np.stack([z32[b, r32["pos"][b] - 1] for b in range(B)])
+    ids, _ = oracle.fanout_topk(rows, r32["k"], 16, "f32")
+    assert np.array_equal(ids, r32["ids"])
