@@ -20,8 +20,9 @@ the launch stream, against the 8 TB/s HBM peak.  `cpu_baseline` times the
 CPU oracle (single-threaded fp64) on the same workload.  `variants` holds the
 same measurements for the other rows of the hot path (greedy window,
 multi-candidate, tree, fan-out, the small fp32 chain, the point-mass chain
-and tree, which read no draft rows, and the speculation-cache hit test with
-its hit rate against temperature for geometric and uniform fan-out).
+and tree, which read no draft rows, the speculation-cache hit test with
+its hit rate against temperature for geometric and uniform fan-out, and
+PRESTO scoring with one priority expansion step on the tree workload).
 """
 from __future__ import annotations
 
@@ -367,6 +368,29 @@ def bench_cache(wl, steps, warmup, temps=(0.0, 0.5, 1.0), rounds=32, F0=8, r_exp
                 alg_bytes=per_copy, copies=len(copies), hit_rate_vs_T=table)
 
 
+PRESTO_LAMBDA = [0.5, 1.0, 1.5, 2.0]
+
+
+def bench_presto(wl, steps, warmup, k=8, b_top=32):
+    """PRESTO scoring and one expansion step on the tree workload: every node's row pair is read for its
+    statistics, and each leaf's row pair once more for its proposals."""
+    p = wl.params
+    T = float(np.float32(p["T"]))
+    per_copy = (wl.tensors["tgt"].numel() + wl.tensors["drf"].numel()) * esize(p["dtype"])
+    copies = [wl.to("cuda") for _ in range(n_copies(per_copy))]
+    lam = torch.tensor(PRESTO_LAMBDA, dtype=torch.float32, device="cuda")
+    fn = lambda g: svx.sv_presto_score(g["tgt"], g["drf"], g["tok"], g["parent"], T, lam, k, b_top)
+    fn(copies[0])
+    torch.cuda.synchronize()
+    wall, ev_ms = time_graphs(fn, copies, steps, warmup)
+    parent = wl.tensors["parent"]
+    B, N = parent.shape
+    leaves = sum(N - len(set(x for x in parent[b].tolist() if x >= 0)) for b in range(B))
+    alg = (2 * B * N + 2 * leaves) * p["V"] * esize(p["dtype"])
+    return dict(nodes_per_call=B * N, nodes_per_s=B * N / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
+                alg_bytes=alg, leaves=leaves, k=k, b_top=b_top, lam=PRESTO_LAMBDA, copies=len(copies))
+
+
 def bench_fanout(wl, steps, warmup):
     p = wl.params
     B, N, V = wl.tensors["drf"].shape
@@ -469,6 +493,8 @@ def main():
                 log(f"tree_pm: {variants['tree_pm']}")
                 variants["fanout_tree_draft_rows"] = summarize(bench_fanout(w, steps_v, warm_v))
                 log(f"fanout: {variants['fanout_tree_draft_rows']}")
+                variants["presto_tree"] = summarize(bench_presto(w, steps_v, warm_v))
+                log(f"presto: {variants['presto_tree']}")
             del w
             torch.cuda.empty_cache()
 

@@ -210,17 +210,32 @@ sv_status plan_presto(sv_dtype dt, int32_t B, int32_t N, int32_t V, int32_t k, P
   pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
   const int64_t rows = (int64_t)B * N * 2;
   split(rows, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
-  split((int64_t)B * N, pl->nvec, stats_blocks(), &pl->nch2, &pl->vpc2);
+  if (pl->nch1 > kWalkMaxParts) {  // the expansion stages a row's parts in LDS
+    pl->vpc1 = (pl->nvec + kWalkMaxParts - 1) / kWalkMaxParts;
+    pl->nch1 = (int32_t)((pl->nvec + pl->vpc1 - 1) / pl->vpc1);
+  }
+  // the proposal scan costs a few operations per token and only leaves
+  // (about half the nodes) work: twice the usual block count, with at most
+  // 1024 / k parts per row (a leaf's last part merges the parts' lists)
+  split((int64_t)B * N, pl->nvec, 2 * stats_blocks(), &pl->nch2, &pl->vpc2);
+  const int32_t max_parts = 1024 / k;
+  if (pl->nch2 > max_parts) {
+    pl->vpc2 = (pl->nvec + max_parts - 1) / max_parts;
+    pl->nch2 = (int32_t)((pl->nvec + pl->vpc2 - 1) / pl->vpc2);
+  }
   pl->grid1 = rows * pl->nch1;
   pl->grid2 = (int64_t)B * N * pl->nch2;
   if (pl->grid1 > INT32_MAX || pl->grid2 > INT32_MAX) return SV_EUNSUPPORTED;
   size_t off = kWsFixed;
   pl->off_part1 = off;
   off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
-  pl->off_part2 = off;  // gathered child logits
+  pl->off_part2 = off;  // gathered child logits, then each leaf's merged list (8-byte entries)
   off = align_up(off + (size_t)2 * B * N * sizeof(float), 256);
+  off = align_up(off + (size_t)B * N * k * 8, 256);
   pl->off_lists = off;  // expansion part lists (8-byte entries)
   off = align_up(off + (size_t)B * N * pl->nch2 * k * 8, 256);
+  pl->off_jobs = off;   // per-node arrival counters, zeroed by the statistics launch
+  off = align_up(off + (size_t)B * N * sizeof(uint32_t) + 8, 256);
   pl->bytes = off;
   return SV_OK;
 }
@@ -452,6 +467,7 @@ static sv_status verify_tree_like(const void* tgt, const void* drf, sv_dtype dt,
   p.pm = pm;
   p.all_rows = false;
   pick_slices(B, pl.nvec, tree_walk_capacity(dt, true, pm), tree_walk_capacity(dt, false, pm), &p.G, &p.held);
+  p.nzero = (int64_t)B * kSlotWords * p.G;
   p.vpc = pl.vpc1;
   p.nvec = pl.nvec;
   return launch_tree(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
@@ -563,9 +579,10 @@ sv_status sv_presto_score(const void* tgt, const void* drf, sv_dtype dt, int64_t
   t.err = reinterpret_cast<int32_t*>(w);
   t.part = w + pl.off_part1;
   t.zc = reinterpret_cast<float*>(w + pl.off_part2);
-  t.slots = nullptr;
+  t.slots = w + pl.off_jobs;  // the expansion's per-node arrival counters
+  t.nzero = ((int64_t)B * N + 1) / 2;
   t.nch = pl.nch1;
-  t.G = 0;  // no walk: nothing to zero
+  t.G = 0;
   t.held = true;
   t.pm = false;
   t.all_rows = true;
@@ -592,10 +609,11 @@ sv_status sv_presto_score(const void* tgt, const void* drf, sv_dtype dt, int64_t
   p.out_tok = out_tok;
   p.out_score = out_score;
   p.err = t.err;
-  p.cnt = reinterpret_cast<uint32_t*>(w + kWsHeader);
   p.part = t.part;
   p.zc = t.zc;
   p.lists = w + pl.off_lists;
+  p.leaf_lists = w + pl.off_part2 + align_up((size_t)2 * B * N * sizeof(float), 256);
+  p.leaf_cnt = reinterpret_cast<uint32_t*>(w + pl.off_jobs);
   p.nch1 = pl.nch1;
   p.nch2 = pl.nch2;
   p.vpc2 = pl.vpc2;

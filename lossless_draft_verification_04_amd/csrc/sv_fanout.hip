@@ -81,14 +81,7 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
   if (wave == 0) {
     float fv = kNegInf;
     int32_t fi = kNoIdx;
-    for (int c = 0; c < a.nch; ++c)
-      for (int e = 0; e < F; ++e) {
-        const TopEntry t = get_entry(parts + (int64_t)c * a.F_max + e);
-        const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(fv), F - 1));
-        const int32_t ti = __builtin_amdgcn_readlane(fi, F - 1);
-        if (t.idx == kNoIdx || (ti != kNoIdx && !top_better(t.val, t.idx, tv, ti))) break;
-        wave_insert(fv, fi, t.val, t.idx, F, lane);
-      }
+    if (F > 0) wave_merge_entries(parts, a.nch * a.F_max, F, fv, fi, lane);
     if (lane < a.F_max) {
       const bool keep = lane < F && fi != kNoIdx;
       a.out_ids[(int64_t)r * a.F_max + lane] = keep ? fi : -1;

@@ -76,6 +76,7 @@ struct TreeParams {
   void* part;
   float* zc;       // each child's logits under its parent's rows, [2][B][N] (target, draft)
   void* slots;     // walk slot words, [B][G][4], zeroed by the stats launch
+  int64_t nzero;   // 64-bit words of `slots` the stats launch zeroes
   int32_t nch;
   int32_t G;       // walk blocks per sequence
   bool held;       // slices of at most kSliceTiles tiles, held in registers
@@ -100,10 +101,11 @@ struct PrestoParams {
   int32_t* out_tok;
   float* out_score;
   int32_t* err;
-  uint32_t* cnt;     // per-sequence arrival counters
   void* part;        // row statistics parts, [B][N][2][nch1] (tree statistics launch)
   float* zc;         // each child's logits under its parent's rows, [2][B][N]
   void* lists;       // expansion part lists, [B][N][nch2][k]
+  void* leaf_lists;  // each leaf's merged list, [B][N][k]
+  uint32_t* leaf_cnt;  // arrivals per node, [B][N], zeroed by the statistics launch
   int32_t nch1, nch2;
   int64_t vpc2, nvec;
 };

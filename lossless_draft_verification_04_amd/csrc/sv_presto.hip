@@ -11,18 +11,19 @@
 // under the proxy and keeps the sequence's b best proposals by priority
 // S_u + s_u(t).
 //
-// Two launches per call:
+// Three launches per call:
 //  1. statistics: tree_stats_kernel over every node's row pair (leaves
 //     included), which also gathers each child's logits under its parent's
 //     rows.
-//  2. expansion: a block per (node, row part).  Blocks of nodes with children
-//     only arrive.  A leaf's block merges the node's row statistics, turns its
-//     part of the row pair into proxy scores (base 2, in registers) and keeps
-//     each wave's k best (sv_topk.hpp); the waves' lists merge into the
-//     part's list.  The last block of a sequence to arrive computes every
-//     node's s and S (level by level from the root, so each S is summed in
-//     root-to-node order), merges each leaf's part lists into its top k, and
-//     those into the sequence's top b.
+//  2. expansion: a block per (node, row part); blocks of nodes with children
+//     exit.  A leaf's block merges the node's row statistics, turns its part
+//     of the row pair into proxy scores (in registers) and keeps each wave's
+//     k best (sv_topk.hpp); the waves' lists merge into the part's list, and
+//     the leaf's last part to finish merges the parts' lists into the leaf's
+//     top k.
+//  3. final: a block per sequence computes every node's s and S (level by
+//     level from the root, so each S is summed in root-to-node order) and
+//     ranks the leaves' proposals into the sequence's top b.
 #include <cmath>
 
 #include "sv_device.hpp"
@@ -32,6 +33,8 @@
 namespace sv {
 
 constexpr int kPNT = 256;
+constexpr int kStageE = 1024;  // proposal entries the final launch stages at once
+constexpr int kMaxParts = 64;  // statistics parts per row (the plan caps it)
 constexpr float kLn2 = 0.69314718055994531f;
 
 hipError_t launch_tree_stats(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
@@ -47,25 +50,36 @@ __device__ __forceinline__ float proxy_log2(float zp, float zq, float c, float o
   return lq + lam * fminf(0.f, lp - lq);
 }
 
-// A leaf's row pair as a value source for the wave top-k scan.
-template <int DT>
+// A leaf's row pair as a value source for the wave top-k scan.  It lists
+// the proxy in logit units, y = z_q + lambda * min(0, z_p - z_q - delta)
+// with delta = (offP - offQ) / c: log2 of the proxy weight is c * y - offQ,
+// an increasing affine map, so the order (and every tie) is the same, and
+// each token costs four operations after unpacking.  lambda = 0 lists z_q
+// (LAM0: no 0 * -inf where p = 0).
+template <int DT, bool LAM0>
 struct ProxyValues {
   const void* rowP;
   const void* rowQ;
   int V;
-  float c, offP, offQ, lam;
+  float delta, lam;
   struct Data {
     u32x4 p, q;
   };
   static constexpr bool kSkipNegInf = true;
-  __device__ __forceinline__ Data load(int64_t v) const { return Data{load_vec(rowP, v), load_vec(rowQ, v)}; }
+  __device__ __forceinline__ Data load(int64_t v) const {
+    if constexpr (LAM0) return Data{d_zero(), load_vec(rowQ, v)};
+    return Data{load_vec(rowP, v), load_vec(rowQ, v)};
+  }
+  static __device__ __forceinline__ u32x4 d_zero() { return u32x4{0u, 0u, 0u, 0u}; }
   __device__ __forceinline__ void values(const Data& d, int64_t v, float* x) const {
     constexpr int E = Fmt<DT>::kPerVec;
-    float zp[E];
-    unpack<DT>(d.p, zp);
     unpack<DT>(d.q, x);
+    if constexpr (!LAM0) {
+      float zp[E];
+      unpack<DT>(d.p, zp);
 #pragma unroll
-    for (int e = 0; e < E; ++e) x[e] = proxy_log2(zp[e], x[e], c, offP, offQ, lam);
+      for (int e = 0; e < E; ++e) x[e] = __builtin_fmaf(lam, fminf(0.f, (zp[e] - x[e]) - delta), x[e]);
+    }
     if ((v + 1) * E > V) {
 #pragma unroll
       for (int e = 0; e < E; ++e)
@@ -86,8 +100,8 @@ __device__ float row_offset(const PrestoParams& a, int64_t node_row, int which) 
 // Lambda of a node at depth d >= 1.
 __device__ __forceinline__ float lambda_at(const PrestoParams& a, int d) { return a.lam[(d < a.D ? d : a.D) - 1]; }
 
-// Insert (v, n, t) into a wave's sorted list of (priority desc, node asc,
-// token asc); lane l holds entry l, lanes >= F the empty entry (node kNoIdx).
+// Candidate order: priority descending, then node ascending, then token
+// ascending; an empty entry (node kNoIdx) beats nothing.
 __device__ __forceinline__ bool cand_better(float va, int32_t na, int32_t ta, float vb, int32_t nb, int32_t tb) {
   if (na == kNoIdx) return false;
   if (nb == kNoIdx) return true;
@@ -95,28 +109,6 @@ __device__ __forceinline__ bool cand_better(float va, int32_t na, int32_t ta, fl
   if (na != nb) return na < nb;
   return ta < tb;
 }
-__device__ __forceinline__ void wave_insert3(float& lv, int32_t& ln, int32_t& lt, float v, int32_t n, int32_t t,
-                                             int F, int lane) {
-  const bool here = lane < F && cand_better(v, n, t, lv, ln, lt);
-  const uint64_t m = __ballot(here);
-  if (!m) return;
-  const int pos = __builtin_ctzll(m);
-  const float up_v = dpp_f<kWaveShr1, 0xF>(lv, lv);
-  const int32_t up_n = dpp_i<kWaveShr1, 0xF>(ln, ln);
-  const int32_t up_t = dpp_i<kWaveShr1, 0xF>(lt, lt);
-  if (lane < F) {
-    if (lane > pos) {
-      lv = up_v;
-      ln = up_n;
-      lt = up_t;
-    } else if (lane == pos) {
-      lv = v;
-      ln = n;
-      lt = t;
-    }
-  }
-}
-
 template <int DT>
 __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
   constexpr int E = Fmt<DT>::kPerVec;
@@ -130,15 +122,38 @@ __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
   const int64_t rowbase = (int64_t)b * a.N;
   __shared__ int32_t s_par[SV_MAX_N];  // parents, each clamped below its node
   __shared__ int s_flag, s_depth;
+  __shared__ Partial s_parts[2][kMaxParts];  // the node's row statistics parts (target, draft)
+  __shared__ float s_offs[2];
+  __shared__ float s_lamv[SV_MAX_N];  // lambda of depths 1..N
+  // one round of loads: the parents, the node's parts of both rows, lambda
   for (int i = threadIdx.x; i < a.N; i += kPNT) {
     const int32_t p = a.parent[rowbase + i];
     s_par[i] = (i > 0 && p >= 0 && p < i) ? p : 0;
   }
+  for (int i = threadIdx.x; i < a.N; i += kPNT) s_lamv[i] = a.lam[(i + 1 < a.D ? i + 1 : a.D) - 1];
+  for (int i = threadIdx.x; i < 2 * a.nch1; i += kPNT)
+    s_parts[i / a.nch1][i % a.nch1] =
+        static_cast<const Partial*>(a.part)[((rowbase + u) * 2 + i / a.nch1) * a.nch1 + i % a.nch1];
   if (threadIdx.x == 0) s_flag = 0;
   lds_sync();
   for (int i = u + 1 + (int)threadIdx.x; i < a.N; i += kPNT)
     if (s_par[i] == u) s_flag = 1;
-  if (threadIdx.x == 0) {
+  if (threadIdx.x < 2) {
+    // offset c * max + log2 S of row `which` (+inf for a row without a finite logit)
+    const Partial* pp = s_parts[threadIdx.x];
+    float M = kNegInf;
+    for (int i = 0; i < a.nch1; ++i) M = fmaxf(M, pp[i].m);
+    float off = __builtin_huge_valf();
+    if (M != kNegInf) {
+      const float cm = a.c * M;
+      double S = 0.0;
+      for (int i = 0; i < a.nch1; ++i)
+        if (pp[i].m != kNegInf) S += pp[i].s * exp2((double)(a.c * pp[i].m) - (double)cm);
+      if (S > 0.0) off = (float)((double)cm + log2(S));
+    }
+    s_offs[threadIdx.x] = off;
+  }
+  if (threadIdx.x == kWave) {
     int d = 0;
     for (int j = u; j > 0; j = s_par[j]) ++d;
     s_depth = d;
@@ -147,17 +162,26 @@ __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
   TopEntry* lists = static_cast<TopEntry*>(a.lists) + ((rowbase + u) * a.nch2 + ch) * a.k;
   if (!s_flag) {
     // a leaf: its k best proposals in this part of its row pair
-    const float offP = row_offset(a, rowbase + u, 0);
-    const float offQ = row_offset(a, rowbase + u, 1);
-    const ProxyValues<DT> src{row_ptr(a.tgt, rowbase + u, a.tgt_sb), row_ptr(a.drf, rowbase + u, a.drf_sb), a.V,
-                              a.c, offP, offQ, lambda_at(a, s_depth + 1)};
-    if (ch == 0 && threadIdx.x == 0 && (offP == __builtin_huge_valf() || offQ == __builtin_huge_valf()))
-      set_error(a.err, SV_DERR_ROW);
+    const float offP = s_offs[0];
+    const float offQ = s_offs[1];
+    const bool empty = offP == __builtin_huge_valf() || offQ == __builtin_huge_valf();
+    if (ch == 0 && threadIdx.x == 0 && empty) set_error(a.err, SV_DERR_ROW);
     float lv = kNegInf;
     int32_t li = kNoIdx;
     const int64_t v0 = (int64_t)ch * a.vpc2;
     const int64_t v1 = v0 + a.vpc2 < a.nvec ? v0 + a.vpc2 : a.nvec;
-    wave_topk_scan<kPNT, E>(src, v0, v1, a.V, a.k, lv, li);
+    const float lam = s_lamv[s_depth];  // the proposals' depth is the leaf's + 1
+    const void* rowP = row_ptr(a.tgt, rowbase + u, a.tgt_sb);
+    const void* rowQ = row_ptr(a.drf, rowbase + u, a.drf_sb);
+    if (!empty) {
+      if (lam == 0.f)
+        wave_topk_scan<kPNT, E>(ProxyValues<DT, true>{rowP, rowQ, a.V, 0.f, 0.f}, v0, v1, a.V, a.k, lv, li);
+      else
+        wave_topk_scan<kPNT, E>(ProxyValues<DT, false>{rowP, rowQ, a.V, (offP - offQ) / a.c, lam}, v0, v1, a.V,
+                                a.k, lv, li);
+    }
+    // logit units -> log2 of the proxy weight
+    if (li != kNoIdx) lv = __builtin_fmaf(lv, a.c, -offQ);
     __shared__ TopEntry s_list[kPNT / kWave][SV_MAX_FANOUT];
     lds_sync();
     if (lane < SV_MAX_FANOUT) {
@@ -174,12 +198,37 @@ __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
           if (t.idx == kNoIdx || (ti != kNoIdx && !top_better(t.val, t.idx, tv, ti))) break;
           wave_insert(lv, li, t.val, t.idx, a.k, lane);
         }
-      if (lane < a.k) put_entry(lists + lane, lv, li);
+      if (a.nch2 == 1 && lane < a.k) put_entry(static_cast<TopEntry*>(a.leaf_lists) + (rowbase + u) * a.k + lane, lv, li);
+      if (a.nch2 > 1 && lane < a.k) put_entry(lists + lane, lv, li);
+    }
+    // the leaf's last part to finish merges the parts' lists into the leaf's
+    if (a.nch2 > 1 && arrive_last<kPNT>(&a.leaf_cnt[rowbase + u], (uint32_t)a.nch2) && wave == 0) {
+      lv = kNegInf;
+      li = kNoIdx;
+      wave_merge_entries(static_cast<const TopEntry*>(a.lists) + (rowbase + u) * a.nch2 * a.k, a.nch2 * a.k, a.k, lv,
+                         li, lane);
+      if (lane < a.k) put_entry(static_cast<TopEntry*>(a.leaf_lists) + (rowbase + u) * a.k + lane, lv, li);
+      if (lane == 0) __hip_atomic_store(&a.leaf_cnt[rowbase + u], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
-  if (!arrive_last<kPNT>(&a.cnt[b], (uint32_t)(a.N * a.nch2))) return;
+}
 
-  // ---- the sequence's last block: scores, path scores, top b proposals
+// One block per sequence (after the expansion launch): every node's s and S,
+// each leaf's part lists merged into its top k, and those into the
+// sequence's top b.
+__global__ __launch_bounds__(kPNT) void presto_final_kernel(PrestoParams a) {
+  const int b = blockIdx.x;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int64_t rowbase = (int64_t)b * a.N;
+  __shared__ int32_t s_par[SV_MAX_N];  // parents, each clamped below its node
+  for (int i = threadIdx.x; i < a.N; i += kPNT) {
+    const int32_t p = a.parent[rowbase + i];
+    const bool ok = i == 0 || (p >= 0 && p < i);
+    if (!ok) set_error(a.err, SV_DERR_TREE);
+    s_par[i] = (i > 0 && ok) ? p : 0;
+  }
+  lds_sync();
   __shared__ float s_off[2][SV_MAX_N];  // row offsets of the nodes with children (target, draft)
   __shared__ float s_s[SV_MAX_N], s_S[SV_MAX_N];
   __shared__ int s_dep[SV_MAX_N];
@@ -190,12 +239,6 @@ __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
     s_dep[i] = i == 0 ? 0 : -1;
   }
   lds_sync();
-  if (threadIdx.x == 0) {
-    for (int i = 1; i < a.N; ++i) {
-      const int32_t p = a.parent[rowbase + i];
-      if (p < 0 || p >= i) set_error(a.err, SV_DERR_TREE);
-    }
-  }
   for (int i = 1 + threadIdx.x; i < a.N; i += kPNT) s_leaf[s_par[i]] = 0;
   lds_sync();
   for (int i = threadIdx.x; i < 2 * a.N; i += kPNT) {
@@ -203,8 +246,15 @@ __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
     if (!s_leaf[node]) s_off[which][node] = row_offset(a, rowbase + node, which);
   }
   lds_sync();
-  const float* zt = a.zc + rowbase;
-  const float* zd = a.zc + (int64_t)a.B * a.N + rowbase;
+  // the children's gathered logits and lambda per level, in LDS for the
+  // level loop
+  __shared__ float s_zt[SV_MAX_N], s_zd[SV_MAX_N], s_lam[SV_MAX_N];
+  for (int i = threadIdx.x; i < a.N; i += kPNT) {
+    s_zt[i] = a.zc[rowbase + i];
+    s_zd[i] = a.zc[(int64_t)a.B * a.N + rowbase + i];
+    s_lam[i] = a.lam[(i + 1 < a.D ? i + 1 : a.D) - 1];  // depth i + 1
+  }
+  lds_sync();
   // depth and path score, level by level (parents precede children)
   if (threadIdx.x == 0) {
     s_s[0] = 0.f;
@@ -216,13 +266,13 @@ __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
     for (int i = 1 + threadIdx.x; i < a.N; i += kPNT) {
       const int p = s_par[i];
       if (s_dep[i] < 0 && s_dep[p] == level - 1) {
-        const float zp = zt[i], zq = zd[i];
+        const float zp = s_zt[i], zq = s_zd[i];
         float sc;
         if (__builtin_isnan(zp) || __builtin_isnan(zq)) {
           set_error(a.err, SV_DERR_TOKEN);
           sc = kNegInf;
         } else {
-          sc = proxy_log2(zp, zq, a.c, s_off[0][p], s_off[1][p], lambda_at(a, level)) * kLn2;
+          sc = proxy_log2(zp, zq, a.c, s_off[0][p], s_off[1][p], s_lam[level - 1]) * kLn2;
         }
         s_s[i] = sc;
         s_S[i] = s_S[p] + sc;
@@ -237,63 +287,96 @@ __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
     if (a.out_s) a.out_s[rowbase + i] = s_s[i];
     if (a.out_S) a.out_S[rowbase + i] = s_S[i];
   }
-  // every leaf's part lists -> its top k -> the wave's top b; waves take
-  // leaves in turn
-  float gv = kNegInf;
-  int32_t gn = kNoIdx, gt = kNoIdx;
-  const TopEntry* all = static_cast<const TopEntry*>(a.lists) + rowbase * a.nch2 * a.k;
-  for (int leaf = wave; leaf < a.N; leaf += kPNT / kWave) {
-    if (!s_leaf[leaf]) continue;
-    float lv = kNegInf;
-    int32_t li = kNoIdx;
-    for (int c = 0; c < a.nch2; ++c)
-      for (int e = 0; e < a.k; ++e) {
-        const TopEntry t = get_entry(all + ((int64_t)leaf * a.nch2 + c) * a.k + e);
-        const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), a.k - 1));
-        const int32_t ti = __builtin_amdgcn_readlane(li, a.k - 1);
-        if (t.idx == kNoIdx || (ti != kNoIdx && !top_better(t.val, t.idx, tv, ti))) break;
-        wave_insert(lv, li, t.val, t.idx, a.k, lane);
-      }
-    // the leaf's list is sorted by score, so by priority: stop at the first
-    // entry that does not enter the top b
-    const float Su = s_S[leaf];
-    for (int e = 0; e < a.k; ++e) {
-      const int32_t t = __builtin_amdgcn_readlane(li, e);
-      if (t == kNoIdx) break;
-      const float pr = Su + __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), e)) * kLn2;
-      const float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), a.b_top - 1));
-      const int32_t bn = __builtin_amdgcn_readlane(gn, a.b_top - 1);
-      const int32_t bt = __builtin_amdgcn_readlane(gt, a.b_top - 1);
-      if (!cand_better(pr, leaf, t, bv, bn, bt)) break;
-      wave_insert3(gv, gn, gt, pr, leaf, t, a.b_top, lane);
-    }
+  // Proposals: every leaf's list of k (merged by the expansion launch),
+  // staged in LDS in chunks of whole leaves with all loads in flight
+  // together.  The valid entries of a chunk, compacted, and the current top b
+  // are ranked against each other: each counts the candidates that beat it,
+  // eight at a time, with (node, token) packed into one 64-bit key so that
+  // the order is (priority descending, key ascending); every key is
+  // distinct, so the ranks are too, and those below b form the new top b.
+  const TopEntry* all = static_cast<const TopEntry*>(a.leaf_lists) + rowbase * a.k;
+  const int per_leaf = a.k;
+  const int leaves_per_chunk = kStageE / per_leaf;
+  __shared__ float c_v[kStageE];
+  __shared__ int32_t c_t[kStageE];
+  // candidates: the chunk's kept entries, then the top b, padded to a multiple of 8
+  __shared__ float k_v[kStageE + SV_MAX_FANOUT + 8];
+  __shared__ int64_t k_key[kStageE + SV_MAX_FANOUT + 8];
+  __shared__ float top_v[SV_MAX_FANOUT];
+  __shared__ int32_t top_n[SV_MAX_FANOUT], top_t[SV_MAX_FANOUT];
+  __shared__ int s_nk;
+  for (int j = threadIdx.x; j < a.b_top; j += kPNT) {
+    top_v[j] = kNegInf;
+    top_n[j] = kNoIdx;
+    top_t[j] = kNoIdx;
   }
-  __shared__ float m_v[kPNT / kWave][SV_MAX_FANOUT];
-  __shared__ int32_t m_n[kPNT / kWave][SV_MAX_FANOUT], m_t[kPNT / kWave][SV_MAX_FANOUT];
-  if (lane < SV_MAX_FANOUT) {
-    m_v[wave][lane] = gv;
-    m_n[wave][lane] = gn;
-    m_t[wave][lane] = gt;
+  for (int n0 = 0; n0 < a.N; n0 += leaves_per_chunk) {
+    const int n1 = n0 + leaves_per_chunk < a.N ? n0 + leaves_per_chunk : a.N;
+    const int ne = (n1 - n0) * per_leaf;
+    lds_sync();  // the previous chunk is consumed
+    for (int e = threadIdx.x; e < ne; e += kPNT) {
+      TopEntry t;
+      t.val = kNegInf;
+      t.idx = kNoIdx;
+      if (s_leaf[n0 + e / per_leaf]) t = get_entry(all + (int64_t)n0 * per_leaf + e);
+      c_v[e] = t.val;
+      c_t[e] = t.idx;
+    }
+    if (threadIdx.x == 0) s_nk = 0;
+    lds_sync();
+    // compact the valid entries in index order
+    for (int e0 = 0; e0 < ne; e0 += kPNT) {
+      const int e = e0 + (int)threadIdx.x;
+      const int keep = (e < ne && c_t[e] != kNoIdx) ? 1 : 0;
+      double before;
+      const int total = (int)block_exclusive_scan<kPNT>((double)keep, &before);
+      if (keep) {
+        const int at = s_nk + (int)before;
+        const int node = n0 + e / per_leaf;
+        k_v[at] = s_S[node] + c_v[e] * kLn2;
+        k_key[at] = ((int64_t)node << 32) | (uint32_t)c_t[e];
+      }
+      lds_sync();
+      if (threadIdx.x == 0) s_nk += total;
+      lds_sync();
+    }
+    const int nk = s_nk;
+    const int nc = (nk + a.b_top + 7) & ~7;
+    for (int j = threadIdx.x; j < nc - nk; j += kPNT) {
+      const bool top = j < a.b_top && top_n[j] != kNoIdx;
+      k_v[nk + j] = top ? top_v[j] : kNegInf;
+      k_key[nk + j] = top ? (((int64_t)top_n[j] << 32) | (uint32_t)top_t[j]) : INT64_MAX;
+    }
+    lds_sync();
+    for (int i = threadIdx.x; i < nc; i += kPNT) {
+      const float vi = k_v[i];
+      const int64_t ki = k_key[i];
+      if (ki == INT64_MAX) continue;
+      int rank = 0;
+      for (int j0 = 0; j0 < nc; j0 += 8) {
+        float vj[8];
+        int64_t kj[8];
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+          vj[q] = k_v[j0 + q];
+          kj[q] = k_key[j0 + q];
+        }
+#pragma unroll
+        for (int q = 0; q < 8; ++q) rank += (vj[q] > vi || (vj[q] == vi && kj[q] < ki)) ? 1 : 0;
+      }
+      if (rank < a.b_top) {
+        top_v[rank] = vi;
+        top_n[rank] = (int32_t)(ki >> 32);
+        top_t[rank] = (int32_t)(ki & 0xffffffff);
+      }
+    }
   }
   lds_sync();
-  if (wave == 0) {
-    for (int w = 1; w < kPNT / kWave; ++w)
-      for (int e = 0; e < a.b_top; ++e) {
-        const float v = m_v[w][e];
-        const int32_t n = m_n[w][e], t = m_t[w][e];
-        const float bv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(gv), a.b_top - 1));
-        const int32_t bn = __builtin_amdgcn_readlane(gn, a.b_top - 1);
-        const int32_t bt = __builtin_amdgcn_readlane(gt, a.b_top - 1);
-        if (!cand_better(v, n, t, bv, bn, bt)) break;
-        wave_insert3(gv, gn, gt, v, n, t, a.b_top, lane);
-      }
-    if (lane < a.b_top) {
-      const bool has = gn != kNoIdx;
-      a.out_node[(int64_t)b * a.b_top + lane] = has ? gn : -1;
-      a.out_tok[(int64_t)b * a.b_top + lane] = has ? gt : -1;
-      if (a.out_score) a.out_score[(int64_t)b * a.b_top + lane] = has ? gv : kNegInf;
-    }
-    if (lane == 0) __hip_atomic_store(&a.cnt[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int j = threadIdx.x; j < a.b_top; j += kPNT) {
+    const bool has = top_n[j] != kNoIdx;
+    a.out_node[(int64_t)b * a.b_top + j] = has ? top_n[j] : -1;
+    a.out_tok[(int64_t)b * a.b_top + j] = has ? top_t[j] : -1;
+    if (a.out_score) a.out_score[(int64_t)b * a.b_top + j] = has ? top_v[j] : kNegInf;
   }
 }
 
@@ -305,6 +388,9 @@ hipError_t launch_presto(const PrestoParams& p, const TreeParams& stats, sv_dtyp
     presto_expand_kernel<SV_BF16><<<dim3((unsigned)plan.grid2), dim3(kPNT), 0, s>>>(p);
   else
     presto_expand_kernel<SV_F32><<<dim3((unsigned)plan.grid2), dim3(kPNT), 0, s>>>(p);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  presto_final_kernel<<<dim3((unsigned)p.B), dim3(kPNT), 0, s>>>(p);
   return hipGetLastError();
 }
 

@@ -99,6 +99,30 @@ __device__ __forceinline__ void wave_insert(float& lv, int32_t& li, float v, int
   }
 }
 
+// Merge n sorted-or-not entries (src[0..n), written by other blocks of the
+// launch) into the wave's list (lv, li) of F entries: 64 device-scope loads
+// at a time, one per lane, then the entries are taken from the lanes in
+// turn; an entry that does not beat the current F-th best is skipped.
+__device__ __forceinline__ void wave_merge_entries(const TopEntry* src, int n, int F, float& lv, int32_t& li,
+                                                   int lane) {
+  for (int e0 = 0; e0 < n; e0 += kWave) {
+    TopEntry mine;
+    mine.val = kNegInf;
+    mine.idx = kNoIdx;
+    if (e0 + lane < n) mine = get_entry(src + e0 + lane);
+    const int cnt = n - e0 < kWave ? n - e0 : kWave;
+    for (int i = 0; i < cnt; ++i) {
+      const int32_t ti = __builtin_amdgcn_readlane(mine.idx, i);
+      if (ti == kNoIdx) continue;
+      const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mine.val), i));
+      const float fv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), F - 1));
+      const int32_t fi = __builtin_amdgcn_readlane(li, F - 1);
+      if (fi != kNoIdx && !top_better(tv, ti, fv, fi)) continue;
+      wave_insert(lv, li, tv, ti, F, lane);
+    }
+  }
+}
+
 // Scan vectors [v0, v1) of a value source into the wave's list (lv, li) of
 // at most F entries (F <= 64).  Src provides
 //   using Data = ...;                        one vector's raw data

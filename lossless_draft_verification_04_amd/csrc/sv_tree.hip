@@ -78,7 +78,7 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
     else pk[k] = -1;  // not a child of u
   }
   if (!a.all_rows && !__syncthreads_or(has_kids)) {
-    zero_slots(a.slots, (int64_t)a.B * kSlotWords * a.G, bid, kTNT);  // for the walk launch
+    zero_slots(a.slots, a.nzero, bid, kTNT);  // for the walk launch
     return;
   }
   // the first part of the row gathers its logits at the children's tokens
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
         zc[u + 1 + (int)threadIdx.x + k * kTNT] = (x >= 0 && x < a.V) ? bits_value<DT>(zg[k]) : __builtin_nanf("");
     }
   }
-  zero_slots(a.slots, (int64_t)a.B * kSlotWords * a.G, bid, kTNT);  // for the walk launch
+  zero_slots(a.slots, a.nzero, bid, kTNT);  // for the walk launch
 }
 
 // ---------------------------------------------------------------------------
