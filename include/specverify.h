@@ -93,7 +93,8 @@ enum {
   SV_OP_CHAIN_PM = 5,
   SV_OP_TREE_PM = 6,
   SV_OP_CACHE = 7,
-  SV_OP_PRESTO = 8
+  SV_OP_PRESTO = 8,
+  SV_OP_BRANCH = 9
 };
 
 /* Limits of this build. */
@@ -116,9 +117,10 @@ const char* sv_status_string(sv_status s);
 
 /*
  * Workspace bytes for one call of `op` with the given shape.  gamma_or_N is
- * gamma (chain, greedy, multi, chain_pm), N (tree, tree_pm, presto) or K
- * (cache); B is the number of sequences (or R, the number of rows, for
- * fan-out); K is used by multi only; F_max by fan-out, and as k by presto.
+ * gamma (chain, greedy, multi, chain_pm, branch), N (tree, tree_pm, presto)
+ * or K (cache); B is the number of sequences (or R, the number of rows, for
+ * fan-out); K is used by multi only; F_max by fan-out, as k by presto and as
+ * k_max by branch.
  * Returns SV_EINVAL / SV_EUNSUPPORTED for shapes the corresponding call would
  * reject.
  */
@@ -318,6 +320,32 @@ sv_status sv_presto_score(const void* tgt, const void* drf, sv_dtype dt, int64_t
                           const float* lambda, int32_t D, int32_t k, int32_t b_top, float* out_s, float* out_S,
                           int32_t* out_node, int32_t* out_tok, float* out_score, void* ws, size_t ws_bytes,
                           void* stream);
+
+/*
+ * SpecBranch branch resampling ("SpecBranch: Speculative Decoding via Hybrid
+ * Drafting and Rollback-Aware Branch Parallelism" notes, key designs 2-3).
+ * The hybrid predictor's class per sequence (a trained network's output,
+ * passed in) places the branch point b on the window's positions 1..gamma+1:
+ *   cls 0: b = 1 (the round's first token);
+ *   cls 1: b = the first j with q_j(x_j) < eps (b = gamma + 1 if none);
+ *   cls 2: b = gamma + 1 (the next round's first token);
+ * then k = max(1, floor(k_max * (1 - q(x_b)))) branches are the k largest
+ * logits of draft row b (value descending, index ascending).  At
+ * b = gamma + 1 no token is drafted: x_b is the row's most likely token, so
+ * q(x_b) = max_v q_{gamma+1}(v).  q = softmax(z / T).
+ *   drf [B, gamma+1, V] draft rows q_1..q_{gamma+1}; row (b, j) at
+ *       b*(gamma+1) + (j-1)
+ *   draft_tok [B, gamma] x_1..x_gamma; cls [B] device int32 or NULL (every
+ *       class 1; a class outside {0, 1, 2} sets SV_DERR_TOKEN and reads as 1)
+ * Outputs (device): out_pos [B] b (1-based); out_qb [B] q(x_b) (may be NULL);
+ *   out_k [B] (may be NULL); out_ids [B, k_max] the branches (-1 padded).
+ * 1 <= k_max <= SV_MAX_FANOUT.  Reads the gamma + 1 draft rows once, then
+ * the branch row.  Workspace: SV_OP_BRANCH with gamma_or_N = gamma and
+ * F_max = k_max.
+ */
+sv_status sv_branch_fork(const void* drf, sv_dtype dt, int64_t stride, const int32_t* draft_tok, const int32_t* cls,
+                         int32_t B, int32_t gamma, int32_t V, float T, float eps, int32_t k_max, int32_t* out_pos,
+                         float* out_qb, int32_t* out_k, int32_t* out_ids, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Host helper, SSD / Saguaro review Theorem 12: F_k = ceil(F0 * a_p^(k/(1+r)))

@@ -240,6 +240,30 @@ sv_status plan_presto(sv_dtype dt, int32_t B, int32_t N, int32_t V, int32_t k, P
   return SV_OK;
 }
 
+// SpecBranch fork: statistics of the gamma + 1 draft rows of every sequence,
+// then one row per sequence scanned by several blocks.
+sv_status plan_branch(sv_dtype dt, int32_t B, int32_t gamma, int32_t V, int32_t k_max, Plan* pl) {
+  if (bad_dtype(dt)) return SV_EDTYPE;
+  if (B < 0 || gamma < 1 || V < 1 || k_max < 1) return SV_EINVAL;
+  if (B > SV_MAX_SEQ || gamma > SV_MAX_GAMMA || V > SV_MAX_V || k_max > SV_MAX_FANOUT) return SV_EUNSUPPORTED;
+  pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
+  const int64_t rows = (int64_t)B * (gamma + 1);
+  split(rows, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
+  split(B, pl->nvec, stats_blocks(), &pl->nch2, &pl->vpc2);
+  pl->grid1 = rows * pl->nch1;
+  pl->grid2 = (int64_t)B * pl->nch2;
+  if (pl->grid1 > INT32_MAX || pl->grid2 > INT32_MAX) return SV_EUNSUPPORTED;
+  size_t off = kWsFixed;
+  pl->off_part1 = off;
+  off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
+  pl->off_part2 = off;  // gathered draft logits
+  off = align_up(off + (size_t)B * gamma * sizeof(float), 256);
+  pl->off_lists = off;  // fork part lists (8-byte entries)
+  off = align_up(off + (size_t)B * pl->nch2 * k_max * 8, 256);
+  pl->bytes = off;
+  return SV_OK;
+}
+
 sv_status check_ws(const void* ws, size_t ws_bytes, const Plan& pl) {
   if (!ws || ws_bytes < pl.bytes) return SV_EWORKSPACE;
   if (reinterpret_cast<uintptr_t>(ws) % 256 != 0) return SV_EALIGN;
@@ -298,6 +322,7 @@ sv_status sv_workspace_size(sv_op op, sv_dtype dt, int32_t B, int32_t K, int32_t
     case SV_OP_TREE_PM: st = plan_tree(dt, B, gamma_or_N, V, true, &pl); break;
     case SV_OP_CACHE: st = plan_cache(dt, B, gamma_or_N, V, &pl); break;
     case SV_OP_PRESTO: st = plan_presto(dt, B, gamma_or_N, V, F_max, &pl); break;
+    case SV_OP_BRANCH: st = plan_branch(dt, B, gamma_or_N, V, F_max, &pl); break;
     case SV_OP_FANOUT: st = plan_fanout(dt, B, V, F_max, &pl); break;
     default: return SV_EINVAL;
   }
@@ -619,6 +644,47 @@ sv_status sv_presto_score(const void* tgt, const void* drf, sv_dtype dt, int64_t
   p.vpc2 = pl.vpc2;
   p.nvec = pl.nvec;
   return launch_presto(p, t, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
+}
+
+sv_status sv_branch_fork(const void* drf, sv_dtype dt, int64_t stride, const int32_t* draft_tok, const int32_t* cls,
+                         int32_t B, int32_t gamma, int32_t V, float T, float eps, int32_t k_max, int32_t* out_pos,
+                         float* out_qb, int32_t* out_k, int32_t* out_ids, void* ws, size_t ws_bytes, void* stream) {
+  Plan pl;
+  sv_status st = plan_branch(dt, B, gamma, V, k_max, &pl);
+  if (st != SV_OK) return st;
+  if (bad_temperature(T) || !std::isfinite(eps)) return SV_EINVAL;
+  if (B == 0) return SV_OK;
+  if ((st = check_rows(drf, stride, V, dt)) != SV_OK) return st;
+  if (!draft_tok || !out_pos || !out_ids) return SV_EINVAL;
+  if ((st = check_ws(ws, ws_bytes, pl)) != SV_OK) return st;
+  if (B > (int32_t)kWsCounters) return SV_EUNSUPPORTED;
+  char* w = static_cast<char*>(ws);
+  BranchParams p;
+  p.drf = drf;
+  p.sb = stride * elem_bytes(dt);
+  p.tok = draft_tok;
+  p.cls = cls;
+  p.B = B;
+  p.gamma = gamma;
+  p.V = V;
+  p.c = log2e_over(T);
+  p.eps = (double)eps;
+  p.k_max = k_max;
+  p.out_pos = out_pos;
+  p.out_qb = out_qb;
+  p.out_k = out_k;
+  p.out_ids = out_ids;
+  p.err = reinterpret_cast<int32_t*>(w);
+  p.cnt = reinterpret_cast<uint32_t*>(w + kWsHeader);
+  p.part = w + pl.off_part1;
+  p.zq = reinterpret_cast<float*>(w + pl.off_part2);
+  p.lists = w + pl.off_lists;
+  p.nch1 = pl.nch1;
+  p.nch2 = pl.nch2;
+  p.vpc1 = pl.vpc1;
+  p.vpc2 = pl.vpc2;
+  p.nvec = pl.nvec;
+  return launch_branch(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
 }
 
 int32_t sv_geometric_fanout(int32_t F0, double a_p, double r, int32_t K, int32_t capped_last, int32_t* F_out) {

@@ -16,26 +16,6 @@ namespace sv {
 
 constexpr int kFNT = 256;
 
-// One logit row as a value source (elements past V read as -inf; -inf
-// logits are listed like any other value).
-template <int DT>
-struct RowValues {
-  const void* row;
-  int V;
-  using Data = u32x4;
-  static constexpr bool kSkipNegInf = false;
-  __device__ __forceinline__ Data load(int64_t v) const { return load_vec(row, v); }
-  __device__ __forceinline__ void values(const Data& d, int64_t v, float* x) const {
-    constexpr int E = Fmt<DT>::kPerVec;
-    unpack<DT>(d, x);
-    if ((v + 1) * E > V) {
-#pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (v * E + e >= V) x[e] = kNegInf;
-    }
-  }
-};
-
 template <int DT>
 __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
   constexpr int E = Fmt<DT>::kPerVec;

@@ -110,6 +110,28 @@ struct PrestoParams {
   int64_t vpc2, nvec;
 };
 
+struct BranchParams {
+  const void* drf;  // draft rows q_1..q_{gamma+1} per sequence
+  int64_t sb;
+  const int32_t* tok;
+  const int32_t* cls;  // predictor class per sequence, or null (every class 1)
+  int32_t B, gamma, V;
+  float c;  // log2(e) / T
+  double eps;
+  int32_t k_max;
+  int32_t* out_pos;
+  float* out_qb;
+  int32_t* out_k;
+  int32_t* out_ids;
+  int32_t* err;
+  uint32_t* cnt;   // per-sequence arrival counters
+  void* part;      // statistics parts, [B][gamma+1][nch1]
+  float* zq;       // draft logits of the drafted tokens, [B][gamma] (NaN: token out of range)
+  void* lists;     // fork part lists, [B][nch2][k_max]
+  int32_t nch1, nch2;
+  int64_t vpc1, vpc2, nvec;
+};
+
 struct FanoutParams {
   const void* logits;
   int64_t sb;
@@ -155,6 +177,7 @@ hipError_t launch_greedy(const GreedyParams& p, sv_dtype dt, const Plan& plan, h
 hipError_t launch_tree(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
 hipError_t launch_fanout(const FanoutParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
 hipError_t launch_cache(const CacheParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
+hipError_t launch_branch(const BranchParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
 hipError_t launch_presto(const PrestoParams& p, const TreeParams& stats, sv_dtype dt, const Plan& plan,
                          hipStream_t s);
 hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s);

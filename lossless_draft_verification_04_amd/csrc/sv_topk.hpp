@@ -99,6 +99,26 @@ __device__ __forceinline__ void wave_insert(float& lv, int32_t& li, float v, int
   }
 }
 
+// One logit row as a value source (elements past V read as -inf; -inf
+// logits are listed like any other value).
+template <int DT>
+struct RowValues {
+  const void* row;
+  int V;
+  using Data = u32x4;
+  static constexpr bool kSkipNegInf = false;
+  __device__ __forceinline__ Data load(int64_t v) const { return load_vec(row, v); }
+  __device__ __forceinline__ void values(const Data& d, int64_t v, float* x) const {
+    constexpr int E = Fmt<DT>::kPerVec;
+    unpack<DT>(d, x);
+    if ((v + 1) * E > V) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (v * E + e >= V) x[e] = kNegInf;
+    }
+  }
+};
+
 // Merge n sorted-or-not entries (src[0..n), written by other blocks of the
 // launch) into the wave's list (lv, li) of F entries: 64 device-scope loads
 // at a time, one per lane, then the entries are taken from the lanes in

@@ -31,7 +31,7 @@ _lib = ctypes.CDLL(_LIB_PATH)
 SV_OK, SV_EINVAL, SV_EDTYPE, SV_EALIGN, SV_EWORKSPACE, SV_EUNSUPPORTED, SV_EHIP = range(7)
 SV_F32, SV_BF16 = 0, 1
 (SV_OP_CHAIN, SV_OP_GREEDY, SV_OP_MULTI, SV_OP_TREE, SV_OP_FANOUT, SV_OP_CHAIN_PM, SV_OP_TREE_PM,
- SV_OP_CACHE, SV_OP_PRESTO) = range(9)
+ SV_OP_CACHE, SV_OP_PRESTO, SV_OP_BRANCH) = range(10)
 DERR_TOKEN, DERR_TREE, DERR_FANOUT, DERR_ROW = 1, 2, 4, 8
 
 _P = ctypes.c_void_p
@@ -58,6 +58,8 @@ _SIGS = {
     "sv_cache_hit_test": ([_P, _i32, _i64, _i32, _i32, _i32, _P, _P, _P, _P, _P, _P, _sz, _P], _i32),
     "sv_presto_score": ([_P, _P, _i32, _i64, _i64, _P, _P, _i32, _i32, _i32, _f32, _P, _i32, _i32, _i32, _P, _P,
                          _P, _P, _P, _P, _sz, _P], _i32),
+    "sv_branch_fork": ([_P, _i32, _i64, _P, _P, _i32, _i32, _i32, _f32, _f32, _i32, _P, _P, _P, _P, _P, _sz, _P],
+                       _i32),
     "sv_geometric_fanout": ([_i32, _f64, _f64, _i32, _i32, ctypes.POINTER(_i32)], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
@@ -323,6 +325,27 @@ def sv_presto_score(tgt, drf, node_tok, parent, T, lam, k, b_top, want_scores=Tr
                                 _ptr(node_tok), _ptr(parent), B, N, V, float(T), _ptr(lam), lam.numel(), int(k),
                                 int(b_top), _ptr(out["s"]), _ptr(out["S"]), _ptr(out["node"]), _ptr(out["tok"]),
                                 _ptr(out["score"]), _ptr(ws), ws.numel(), _stream(dev)), "sv_presto_score")
+    return out
+
+
+def sv_branch_fork(drf, tok, T, eps, k_max, cls=None, workspace=None):
+    """drf [B, gamma+1, V] draft rows q_1..q_{gamma+1}; tok [B, gamma]; cls [B] int32 or None
+    -> dict(pos, qb, k [B], ids [B, k_max])."""
+    B, g1, V = drf.shape
+    gamma = g1 - 1
+    _i32_tensor(tok, (B, gamma), "tok")
+    if cls is not None:
+        _i32_tensor(cls, (B,), "cls")
+    dt = _dtype_code(drf)
+    dev = drf.device
+    ws = workspace if workspace is not None else Workspace.get(
+        dev, workspace_size(SV_OP_BRANCH, dt, B, 1, gamma, V, int(k_max)))
+    out = dict(pos=torch.empty(B, dtype=torch.int32, device=dev), qb=torch.empty(B, dtype=torch.float32, device=dev),
+               k=torch.empty(B, dtype=torch.int32, device=dev),
+               ids=torch.empty(B, k_max, dtype=torch.int32, device=dev))
+    _check(_lib.sv_branch_fork(_ptr(drf), dt, _row_stride(drf, "drf"), _ptr(tok), _ptr(cls), B, gamma, V, float(T),
+                               float(eps), int(k_max), _ptr(out["pos"]), _ptr(out["qb"]), _ptr(out["k"]),
+                               _ptr(out["ids"]), _ptr(ws), ws.numel(), _stream(dev)), "sv_branch_fork")
     return out
 
 

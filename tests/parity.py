@@ -242,6 +242,28 @@ def presto(wl, lam, k, b_top, T=None):
     return out, ref
 
 
+def branch(rows_cpu, tok_cpu, cls_cpu, T, eps, k_max):
+    """SpecBranch fork: positions, branch counts and branches exact outside the margin; q(x_b) within 1e-5."""
+    B, g1, V = rows_cpu.shape
+    T, eps = f32(T), f32(eps)
+    say(f"  branch B={B} gamma={g1 - 1} V={V} {dtype_name(rows_cpu)} T={T} eps={eps} k_max={k_max} "
+        f"cls={'none' if cls_cpu is None else 'given'}")
+    Vs = rows_cpu.stride(1)
+    store = torch.empty(B, g1, Vs, dtype=rows_cpu.dtype, device=DEV)
+    rows = store[..., :V]
+    rows.copy_(rows_cpu)
+    out = svx.sv_branch_fork(rows, tok_cpu.to(DEV), T, eps, k_max, None if cls_cpu is None else cls_cpu.to(DEV))
+    torch.cuda.synchronize()
+    ref = oracle.branch_fork(np_logits(rows_cpu), tok_cpu.numpy(), None if cls_cpu is None else cls_cpu.numpy(), T,
+                             eps, k_max, dtype_name(rows_cpu))
+    pos, k, ids = out["pos"].cpu().numpy(), out["k"].cpu().numpy(), out["ids"].cpu().numpy()
+    exc = ref["margin"] < MARGIN
+    mism = (pos != ref["pos"]) | (k != ref["k"]) | (ids != ref["ids"]).any(1)
+    check_excepted("branch pos/k/ids", exc, mism)
+    check_probs("branch q(x_b)", out["qb"].cpu().numpy(), ref["qb"], ~mism)
+    return out, ref
+
+
 def fanout(logits_cpu, F_cpu, F_max):
     dt = dtype_name(logits_cpu)
     say(f"  fanout R={logits_cpu.shape[0]} V={logits_cpu.shape[1]} F_max={F_max} {dt}")

@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 15
+    assert len(names) == 16
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(svx.EXPORTED)
@@ -59,7 +59,7 @@ def test_workspace_size():
     assert st == svx.SV_OK and n > 65536 * 4
     st2, n2 = ws_size(svx.SV_OP_MULTI, svx.SV_BF16, 32, 1, 16, 152064)
     assert st2 == svx.SV_OK and n2 == n  # multi with K = 1 is the chain
-    for op in range(9):
+    for op in range(10):
         st, n = ws_size(op, svx.SV_BF16, 8, 2, 16, 1000, 8)
         assert st == svx.SV_OK and n % 256 == 0
     # point-mass calls stream no draft rows: never more scratch than the standard ones
@@ -83,7 +83,7 @@ def test_workspace_size():
     assert ws_size(svx.SV_OP_TREE, 0, 1, 1, 1025, 100)[0] == svx.SV_EUNSUPPORTED
     assert ws_size(svx.SV_OP_FANOUT, 0, 4, 1, 1, 100, 65)[0] == svx.SV_EUNSUPPORTED
     assert ws_size(svx.SV_OP_CHAIN, 0, 1, 1, 4, (1 << 24) + 1)[0] == svx.SV_EUNSUPPORTED
-    assert ws_size(9, 0, 1, 1, 4, 100)[0] == svx.SV_EINVAL
+    assert ws_size(99, 0, 1, 1, 4, 100)[0] == svx.SV_EINVAL
     assert ws_size(-1, 0, 1, 1, 4, 100)[0] == svx.SV_EINVAL
 
 
@@ -182,6 +182,20 @@ def test_presto_argument_checks():
     assert c(tgt=MIS) == svx.SV_EALIGN and c(drf=None) == svx.SV_EINVAL and c(lam=None) == svx.SV_EINVAL
     assert c(tok=None) == svx.SV_EINVAL and c(par=None) == svx.SV_EINVAL and c(node=None) == svx.SV_EINVAL
     assert c(tk=None) == svx.SV_EINVAL and c(wsb=4096) == svx.SV_EWORKSPACE and c(B=0) == svx.SV_OK
+
+
+def test_branch_fork_argument_checks():
+    c = lambda **kw: L.sv_branch_fork(kw.get("drf", A), kw.get("dt", 1), kw.get("s", 1024), kw.get("tok", A), None,
+                                      kw.get("B", 2), kw.get("g", 4), 1000, kw.get("T", 1.0), kw.get("eps", 0.3),
+                                      kw.get("km", 8), kw.get("pos", A), None, None, kw.get("ids", A), WS,
+                                      kw.get("wsb", 1 << 30), None)
+    assert c(dt=5) == svx.SV_EDTYPE and c(g=0) == svx.SV_EINVAL and c(g=65) == svx.SV_EUNSUPPORTED
+    assert c(km=0) == svx.SV_EINVAL and c(km=65) == svx.SV_EUNSUPPORTED and c(T=0.0) == svx.SV_EINVAL
+    assert c(eps=float("nan")) == svx.SV_EINVAL and c(drf=MIS) == svx.SV_EALIGN and c(s=999) == svx.SV_EINVAL
+    assert c(tok=None) == svx.SV_EINVAL and c(pos=None) == svx.SV_EINVAL and c(ids=None) == svx.SV_EINVAL
+    assert c(wsb=4096) == svx.SV_EWORKSPACE and c(B=0) == svx.SV_OK
+    assert ws_size(svx.SV_OP_BRANCH, 1, 32, 1, 16, 152064, 8)[0] == svx.SV_OK
+    assert ws_size(svx.SV_OP_BRANCH, 1, 32, 1, 16, 152064, 0)[0] == svx.SV_EINVAL
 
 
 def test_workspace_helpers_reject_bad_arguments():
