@@ -21,8 +21,9 @@ CPU oracle (single-threaded fp64) on the same workload.  `variants` holds the
 same measurements for the other rows of the hot path (greedy window,
 multi-candidate, tree, fan-out, the small fp32 chain, the point-mass chain
 and tree, which read no draft rows, the speculation-cache hit test with
-its hit rate against temperature for geometric and uniform fan-out, and
-PRESTO scoring with one priority expansion step on the tree workload).
+its hit rate against temperature for geometric and uniform fan-out, the
+SpecBranch fork, and PRESTO scoring with one priority expansion step on the
+tree workload).
 """
 from __future__ import annotations
 
@@ -368,6 +369,31 @@ def bench_cache(wl, steps, warmup, temps=(0.0, 0.5, 1.0), rounds=32, F0=8, r_exp
                 alg_bytes=per_copy, copies=len(copies), hit_rate_vs_T=table)
 
 
+def bench_branch(wl, steps, warmup, eps=0.3, k_max=8):
+    """SpecBranch fork on the chain workload with the lookahead row: the gamma + 1 draft rows of every sequence
+    read for their statistics, then the branch row once more for its top-k."""
+    p = wl.params
+    B, g, V = p["B"], p["gamma"], p["V"]
+    T = float(np.float32(p["T"]))
+    rows_cpu = W.lookahead_rows(wl)
+    per_copy = rows_cpu.numel() * esize(p["dtype"])
+    cls = torch.randint(0, 3, (B,), generator=torch.Generator().manual_seed(5), dtype=torch.int32).cuda()
+    copies = []
+    for _ in range(n_copies(per_copy)):
+        store = torch.empty(B, g + 1, rows_cpu.stride(1), dtype=rows_cpu.dtype, device="cuda")
+        r = store[..., :V]
+        r.copy_(rows_cpu)
+        copies.append(dict(rows=r, tok=wl.tensors["tok"].cuda()))
+    fn = lambda c: svx.sv_branch_fork(c["rows"], c["tok"], T, eps, k_max, cls)
+    out = fn(copies[0])
+    torch.cuda.synchronize()
+    wall, ev_ms = time_graphs(fn, copies, steps, warmup)
+    alg = (g + 2) * B * V * esize(p["dtype"])
+    return dict(sequences_per_call=B, sequences_per_s=B / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
+                alg_bytes=alg, mean_branch_pos=float(out["pos"].float().mean().item()),
+                mean_branches=float(out["k"].float().mean().item()), eps=eps, k_max=k_max, copies=len(copies))
+
+
 PRESTO_LAMBDA = [0.5, 1.0, 1.5, 2.0]
 
 
@@ -487,6 +513,8 @@ def main():
                 wc = W.chain_zipf(**W.CHAIN_BATCHED, lookahead_row=True)
                 variants["cache_hit_test"] = summarize(bench_cache(wc, steps_v, warm_v))
                 log(f"cache_hit_test: {variants['cache_hit_test']}")
+                variants["branch_fork"] = summarize(bench_branch(wc, steps_v, warm_v))
+                log(f"branch_fork: {variants['branch_fork']}")
                 del wc
             if name == "tree":
                 variants["tree_pm"] = summarize(bench_tree_pm(w, steps_v, warm_v))
