@@ -136,7 +136,11 @@ __global__ __launch_bounds__(kBNT) void branch_fork_kernel(BranchParams a) {
   int32_t li = kNoIdx;
   const int64_t v0 = (int64_t)ch * a.vpc2;
   const int64_t v1 = v0 + a.vpc2 < a.nvec ? v0 + a.vpc2 : a.nvec;
-  wave_topk_scan<kBNT, E>(RowValues<DT>{row, a.V}, v0, v1, a.V, k, lv, li);
+  {
+    const TopPair t = wave_topk_scan<kBNT, E>(RowValues<DT>{row, a.V}, v0, v1, a.V, k);
+    lv = t.v;
+    li = t.i;
+  }
   __shared__ TopEntry s_list[kBNT / kWave][SV_MAX_FANOUT];
   lds_sync();
   if (lane < SV_MAX_FANOUT) {

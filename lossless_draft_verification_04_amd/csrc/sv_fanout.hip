@@ -33,7 +33,11 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
   int32_t li = kNoIdx;
   const int64_t v0 = (int64_t)ch * a.vpc;
   const int64_t v1 = v0 + a.vpc < a.nvec ? v0 + a.vpc : a.nvec;
-  if (F > 0) wave_topk_scan<kFNT, E>(RowValues<DT>{row, a.V}, v0, v1, a.V, F, lv, li);
+  if (F > 0) {
+    const TopPair t = wave_topk_scan<kFNT, E>(RowValues<DT>{row, a.V}, v0, v1, a.V, F);
+    lv = t.v;
+    li = t.i;
+  }
   // merge the block's waves into wave 0's list
   __shared__ TopEntry s_list[kFNT / kWave][SV_MAX_FANOUT];
   __syncthreads();

@@ -174,11 +174,13 @@ __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
     const void* rowP = row_ptr(a.tgt, rowbase + u, a.tgt_sb);
     const void* rowQ = row_ptr(a.drf, rowbase + u, a.drf_sb);
     if (!empty) {
-      if (lam == 0.f)
-        wave_topk_scan<kPNT, E>(ProxyValues<DT, true>{rowP, rowQ, a.V, 0.f, 0.f}, v0, v1, a.V, a.k, lv, li);
-      else
-        wave_topk_scan<kPNT, E>(ProxyValues<DT, false>{rowP, rowQ, a.V, (offP - offQ) / a.c, lam}, v0, v1, a.V,
-                                a.k, lv, li);
+      const TopPair t =
+          lam == 0.f
+              ? wave_topk_scan<kPNT, E>(ProxyValues<DT, true>{rowP, rowQ, a.V, 0.f, 0.f}, v0, v1, a.V, a.k)
+              : wave_topk_scan<kPNT, E>(ProxyValues<DT, false>{rowP, rowQ, a.V, (offP - offQ) / a.c, lam}, v0, v1,
+                                        a.V, a.k);
+      lv = t.v;
+      li = t.i;
     }
     // logit units -> log2 of the proxy weight
     if (li != kNoIdx) lv = __builtin_fmaf(lv, a.c, -offQ);

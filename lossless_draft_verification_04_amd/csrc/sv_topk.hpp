@@ -150,8 +150,16 @@ __device__ __forceinline__ void wave_merge_entries(const TopEntry* src, int n, i
 //   void values(const Data&, int64_t v, float* x) const;
 //                                            its E values (-inf past V)
 //   static constexpr bool kSkipNegInf;       -inf values are never listed
+// A lane's entry of a wave's list (lane l holds the l-th best).
+struct TopPair {
+  float v;
+  int32_t i;
+};
+
 template <int NT, int E, class Src>
-__device__ void wave_topk_scan(const Src& src, int64_t v0, int64_t v1, int V, int F, float& lv, int32_t& li) {
+__device__ TopPair wave_list_scan(const Src src, int64_t v0, int64_t v1, int V, int F) {
+  float lv = kNegInf;
+  int32_t li = kNoIdx;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   int count = 0;  // entries held (wave-uniform)
@@ -259,6 +267,15 @@ __device__ void wave_topk_scan(const Src& src, int64_t v0, int64_t v1, int V, in
       for (int u = 0; u < kWin; ++u) d[u] = nx[u];
     }
   }
+  return TopPair{lv, li};
+}
+
+// The wave's list of the F best values of [v0, v1).  (Per-lane lists were
+// measured ten times slower on the fan-out rows: some lane of the 64 inserts
+// at nearly every element, so the whole wave runs the insertion.)
+template <int NT, int E, class Src>
+__device__ TopPair wave_topk_scan(const Src src, int64_t v0, int64_t v1, int V, int F) {
+  return wave_list_scan<NT, E>(src, v0, v1, V, F);
 }
 
 }  // namespace sv
