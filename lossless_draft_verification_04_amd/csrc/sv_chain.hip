@@ -83,31 +83,89 @@ __device__ __forceinline__ RowStat merge_staged(const StagedParts& st, bool stag
   return r;
 }
 
-// Decisions of sequence b (identical in every block that makes them); the
-// draw job goes to *s_job, and the writer block stores the outputs.
+// Parts per row that a lane merges straight from memory (more are staged in
+// LDS by the whole block first).
+constexpr int kDirectParts = 4;
+
+// Parts [0, n) at gp, 1 <= n <= kDirectParts, as 16-byte vectors: every
+// load is issued at once and unconditionally (clamped indexes), so the
+// merge waits for one round trip.
+__device__ __forceinline__ void load_parts(const Partial* gp, int n, u32x4 (&v)[kDirectParts]) {
+#pragma unroll
+  for (int i = 0; i < kDirectParts; ++i)
+    v[i] = *reinterpret_cast<const u32x4*>(gp + (i < n ? i : n - 1));  // written by the previous launch
+}
+
+// Row statistic from loaded parts (the arithmetic of merge_staged).
+__device__ __forceinline__ RowStat merge_loaded(const u32x4 (&v)[kDirectParts], int n, float c) {
+  float m[kDirectParts];
+  double sum[kDirectParts];
+#pragma unroll
+  for (int i = 0; i < kDirectParts; ++i) {
+    m[i] = __uint_as_float(v[i][0]);
+    sum[i] = __longlong_as_double((long long)(((uint64_t)v[i][3] << 32) | v[i][2]));
+  }
+  float M = kNegInf;
+#pragma unroll
+  for (int i = 0; i < kDirectParts; ++i)
+    if (i < n) M = fmaxf(M, m[i]);
+  RowStat r;
+  r.pad = 0.f;
+  if (M == kNegInf) {
+    r.cm = 0.f;
+    r.S = 0.0;
+    return r;
+  }
+  r.cm = c * M;
+  if (n == 1) {
+    r.S = sum[0];
+    return r;
+  }
+  double S = 0.0;
+#pragma unroll
+  for (int i = 0; i < kDirectParts; ++i)
+    if (i < n && m[i] != kNegInf) S += sum[i] * exp2((double)(c * m[i]) - (double)r.cm);
+  r.S = S;
+  return r;
+}
+
+// Decisions of one sequence in LDS.  With at most one candidate per wave
+// the per-position outputs wait in pq until after the draw's exchange, so
+// that no block carries stores into the loads and exchange on the critical
+// path (a wait for a load also waits for earlier stores here).
+struct Decided {
+  StagedParts st;
+  int n[SV_MAX_K];  // first rejection (accepted count) per candidate
+  Job job[SV_MAX_K];
+  float2 pq[kNT / kWave][SV_MAX_GAMMA];  // (p, q) per (candidate, position) when deferred
+  int best;
+  bool deferred;
+};
+
+// Decisions of sequence b (identical in every block that makes them).  Wave
+// k takes candidate k: lane j merges the statistics of its target and draft
+// rows j, decides position j + 1, and the lane at the candidate's first
+// rejection (lane 0 when every draft is accepted) writes the candidate's
+// draw job, so the only block barrier is the one before the longest
+// candidate is picked (plus the staging barrier when a row has more than
+// kDirectParts parts).  The writer block reports errors and, unless the
+// outputs are deferred (d.deferred), stores them; chain_outputs stores
+// deferred ones.  Returns the kept candidate's job (in LDS).
 template <int DT, bool PM>
-__device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_job) {
-  __shared__ StagedParts st;
-  __shared__ RowStat sQ[SV_MAX_GAMMA];
-  __shared__ int sN[SV_MAX_K];
+__device__ const Job* chain_decide(const ChainParams& a, int b, bool writer, Decided& d) {
+  StagedParts& st = d.st;
+  int* sN = d.n;
+  Job* sJob = d.job;
+  const bool defer = a.K <= kNT / kWave;
   const int Kg = a.K * a.gamma;
   const int rows = PM ? Kg : Kg + a.gamma;
   const int nparts = rows * a.nch1;
-  const bool staged = nparts <= kStage;
+  const bool direct = a.nch1 <= kDirectParts;
+  const bool staged = !direct && nparts <= kStage;
   const Partial* pb = static_cast<const Partial*>(a.part1) + (int64_t)b * nparts;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
 
-  // the drafted tokens' logits were gathered by the stats pass: one round of
-  // independent loads with the parts
-  float zp0 = 0.f, zq0 = 0.f;
-  int32_t x0 = -1;
-  if (wave < a.K && lane < a.gamma) {
-    const int64_t o = ((int64_t)b * a.K + wave) * a.gamma + lane;
-    x0 = a.tok[o];
-    zp0 = a.zg[o];
-    if (!PM) zq0 = a.zq[o];
-  }
   if (staged) {
     for (int i = threadIdx.x; i < nparts; i += kNT) {
       const Partial pi = pb[i];  // written by the previous launch
@@ -115,37 +173,39 @@ __device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_jo
       st.s[i] = pi.s;
     }
   }
-  lds_sync();
-  if (!PM) {
-    for (int j = threadIdx.x; j < a.gamma; j += kNT)
-      sQ[j] = merge_staged(st, staged, pb, (Kg + j) * a.nch1, a.nch1, a.c);
-    lds_sync();
-  }
+  if (!direct) lds_sync();  // block-uniform
   for (int k = wave; k < a.K; k += kNT / kWave) {
     bool acc = false;
+    RowStat sp, sq;
+    sp.cm = sq.cm = 0.f;
+    sp.pad = sq.pad = 0.f;
+    sp.S = 0.0;
+    sq.S = 1.0;  // point mass: q(x) = 1
+    int32_t x = -1;
+    // the draw uniform (only the job's lane uses it), computed while the
+    // loads below are in flight
+    const double u = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
     if (lane < a.gamma) {
       const int j = lane;
-      const RowStat sp = merge_staged(st, staged, pb, (k * a.gamma + j) * a.nch1, a.nch1, a.c);
-      RowStat sq;
-      if (PM) {
-        sq.cm = 0.f;
-        sq.S = 1.0;
-      } else {
-        sq = sQ[j];
-      }
       const int64_t o = ((int64_t)b * a.K + k) * a.gamma + j;
-      int32_t x;
-      float zp, zq;
-      if (k == wave) {
-        x = x0;
-        zp = zp0;
-        zq = zq0;
+      const int first_p = (k * a.gamma + j) * a.nch1, first_q = (Kg + j) * a.nch1;
+      const double r = uniform24(a.seed, (uint32_t)(j + 1), (uint32_t)b, (uint32_t)k, a.round, 0);
+      // the drafted token, its gathered logits (stats pass) and the rows'
+      // parts: one round of independent loads
+      x = a.tok[o];
+      const float zp = a.zg[o];
+      const float zq = PM ? 0.f : a.zq[o];
+      if (direct) {
+        u32x4 vp[kDirectParts], vq[kDirectParts];
+        load_parts(pb + first_p, a.nch1, vp);
+        if (!PM) load_parts(pb + first_q, a.nch1, vq);
+        sp = merge_loaded(vp, a.nch1, a.c);
+        if (!PM) sq = merge_loaded(vq, a.nch1, a.c);
       } else {
-        x = a.tok[o];
-        zp = a.zg[o];
-        zq = PM ? 0.f : a.zq[o];
+        sp = merge_staged(st, staged, pb, first_p, a.nch1, a.c);
+        if (!PM) sq = merge_staged(st, staged, pb, first_q, a.nch1, a.c);
       }
-      double p = 0.0, q = PM ? 1.0 : 0.0;  // point mass: q(x) = 1
+      double p = 0.0, q = PM ? 1.0 : 0.0;
       if (x >= 0 && x < a.V) {
         p = prob_of(zp, a.c, sp);
         if (!PM) q = prob_of(zq, a.c, sq);
@@ -153,56 +213,76 @@ __device__ void chain_decide(const ChainParams& a, int b, bool writer, Job* s_jo
         set_error(a.err, SV_DERR_TOKEN);
       }
       if (writer && (!(sp.S > 0.0) || !(sq.S > 0.0))) set_error(a.err, SV_DERR_ROW);
-      const double r = uniform24(a.seed, (uint32_t)(j + 1), (uint32_t)b, (uint32_t)k, a.round, 0);
       acc = r < accept_ratio(p, q);
-      if (writer && a.out_p) a.out_p[o] = (float)p;
-      if (!PM && writer && a.out_q) a.out_q[o] = (float)q;
+      if (defer) {
+        d.pq[k][j] = make_float2((float)p, (float)q);
+      } else if (writer) {
+        if (a.out_p) a.out_p[o] = (float)p;
+        if (!PM && a.out_q) a.out_q[o] = (float)q;
+      }
     }
     const uint64_t rejected = ~(uint64_t)__ballot(acc);
     int n = rejected ? __builtin_ctzll(rejected) : kWave;
     if (n > a.gamma) n = a.gamma;
     if (lane == 0) {
       sN[k] = n;
-      if (writer && a.out_n_cand) a.out_n_cand[(int64_t)b * a.K + k] = n;
+      if (!defer && writer && a.out_n_cand) a.out_n_cand[(int64_t)b * a.K + k] = n;
     }
-  }
-  lds_sync();
-  if (threadIdx.x == 0) {
-    int best = 0;
-    for (int k = 1; k < a.K; ++k)
-      if (sN[k] > sN[best]) best = k;
-    const int n = sN[best];
-    if (writer) {
-      a.out_n[b] = n;
-      if (a.out_k) a.out_k[b] = best;
-    }
-    Job jb;
-    jb.rowP = ((int64_t)b * a.K + best) * (a.gamma + 1) + n;
-    jb.ex = -1;
-    if (n < a.gamma) {
-      const RowStat sp = merge_staged(st, staged, pb, (best * a.gamma + n) * a.nch1, a.nch1, a.c);
-      jb.cmP = sp.cm;
-      jb.SP = sp.S;
-      if (PM) {
-        const int32_t xn = a.tok[((int64_t)b * a.K + best) * a.gamma + n];
-        jb.ex = xn >= 0 && xn < a.V ? xn : -1;
-        jb.rowQ = -1;
-        jb.cmQ = 0.f;
-        jb.SQ = 0.0;
+    if (lane == (n < a.gamma ? n : 0)) {
+      Job jb;
+      jb.rowP = ((int64_t)b * a.K + k) * (a.gamma + 1) + n;
+      jb.ex = -1;
+      if (n < a.gamma) {
+        jb.cmP = sp.cm;
+        jb.SP = sp.S;
+        if (PM) {
+          jb.ex = x >= 0 && x < a.V ? x : -1;
+          jb.rowQ = -1;
+          jb.cmQ = 0.f;
+          jb.SQ = 0.0;
+        } else {
+          jb.rowQ = (int64_t)b * a.gamma + n;
+          jb.cmQ = sq.cm;
+          jb.SQ = sq.S;
+        }
       } else {
-        jb.rowQ = (int64_t)b * a.gamma + n;
-        jb.cmQ = sQ[n].cm;
-        jb.SQ = sQ[n].S;
+        jb.rowQ = -1;
+        jb.cmP = jb.cmQ = 0.f;
+        jb.SP = jb.SQ = 0.0;
       }
-    } else {
-      jb.rowQ = -1;
-      jb.cmP = jb.cmQ = 0.f;
-      jb.SP = jb.SQ = 0.0;
+      jb.u = u;
+      sJob[k] = jb;
     }
-    jb.u = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
-    *s_job = jb;
   }
   lds_sync();
+  int best = 0;
+  for (int k = 1; k < a.K; ++k)
+    if (sN[k] > sN[best]) best = k;
+  d.best = best;
+  d.deferred = defer;
+  if (!defer && writer && threadIdx.x == 0) {
+    a.out_n[b] = sN[best];
+    if (a.out_k) a.out_k[b] = best;
+  }
+  return &sJob[best];
+}
+
+// The deferred outputs of sequence b (one block).
+template <bool PM>
+__device__ void chain_outputs(const ChainParams& a, int b, const Decided& d) {
+  if (!d.deferred) return;
+  const int lane = threadIdx.x & (kWave - 1);
+  const int k = threadIdx.x / kWave;
+  if (k < a.K && lane < a.gamma) {
+    const int64_t o = ((int64_t)b * a.K + k) * a.gamma + lane;
+    if (a.out_p) a.out_p[o] = d.pq[k][lane].x;
+    if (!PM && a.out_q) a.out_q[o] = d.pq[k][lane].y;
+  }
+  if (k < a.K && lane == 0 && a.out_n_cand) a.out_n_cand[(int64_t)b * a.K + k] = d.n[k];
+  if (threadIdx.x == 0) {
+    a.out_n[b] = d.n[d.best];
+    if (a.out_k) a.out_k[b] = d.best;
+  }
 }
 
 template <int DT>
@@ -275,11 +355,11 @@ template <int DT, bool HELD, bool PM>
 __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
   const int b = blockIdx.x / a.G;
   const int g = blockIdx.x - b * a.G;
-  __shared__ Job s_job;
   __shared__ uint64_t s_words[kMaxG], s_w1[kMaxG];
   __shared__ double s_val[kMaxG];
-  chain_decide<DT, PM>(a, b, g == 0, &s_job);
-  const Job jb = s_job;
+  __shared__ Decided dec;
+  const Job* pj = chain_decide<DT, PM>(a, b, g == 0, dec);
+  const Job jb = *pj;
   const int64_t spv = (a.nvec + a.G - 1) / a.G;
   const int64_t v0 = (int64_t)g * spv < a.nvec ? (int64_t)g * spv : a.nvec;
   const int64_t v1 = v0 + spv < a.nvec ? v0 + spv : a.nvec;
@@ -296,7 +376,7 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
     sp.rowQ = nullptr;
     sp.cmP = jb.cmP;
     sp.invSP = 1.f;
-    sp.ex = &s_job.ex;
+    sp.ex = &pj->ex;
     sp.nex = jb.ex >= 0 ? 1 : 0;
     total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
     if (!(total > 0.0)) {
@@ -325,6 +405,8 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
   int pick;
   double loc;
   slice_scan(s_val, x.G, jb.u * total, &pick, &loc);
+  // a block other than the searching one stores the deferred outputs
+  if (g == (x.G > 1 && pick == 0 ? 1 : 0)) chain_outputs<PM>(a, b, dec);
   if (pick == g) {
     if (plain) sl.prepare(sp, a.V);  // the owner's weights under the row's shift
     const int64_t t = sl.search(sp, a.V, loc);

@@ -20,11 +20,11 @@
 //     at the node's children's tokens.
 //  2. walk: G blocks per sequence replay the walk in lockstep.  Each stages
 //     the tree, every node's row statistics and every child's logits in LDS
-//     once; at a node it computes all children's p, q and uniforms in
-//     parallel and, at the first rejection, loads its slice of the node's
-//     row pair into registers; each rejection is one pass over that slice,
-//     the pass totals are exchanged, and the final draw searches one held
-//     slice.
+//     once and computes every child's p, q and uniform there; at a node it
+//     tries the children in order and, at the first rejection, loads its
+//     slice of the node's row pair into registers; each rejection is one
+//     pass over that slice, the pass totals are exchanged, and the final
+//     draw searches one held slice.
 //
 // Point-mass mode (SpecDiff-2 page, Core method: accept a drafted token with
 // the verifier's probability, resample the residual on a rejection; read as
@@ -184,7 +184,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   __shared__ float s_zp[SV_MAX_N], s_zq[SV_MAX_N];  // each child's logits under its parent's rows
   __shared__ float s_cm[2][SV_MAX_N];                // row statistics of the nodes with children
   __shared__ double s_S[2][SV_MAX_N];
-  __shared__ double s_pt[SV_MAX_N], s_qt[SV_MAX_N];  // the current node's children, in order
+  __shared__ double s_pt[SV_MAX_N], s_qt[SV_MAX_N];  // each child's p and q under its parent's rows
   __shared__ float s_r[SV_MAX_N];
   __shared__ uint64_t s_w0[kMaxG], s_w1[kMaxG];
   __shared__ double s_val[kMaxG];
@@ -225,6 +225,27 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   if (writer)
     for (int i = 1 + threadIdx.x; i < a.N; i += kWNT)
       if (s_par[i] < 0 || s_par[i] >= i) set_error(a.err, SV_DERR_TREE);
+  // every child's p and q under its parent's rows and its acceptance
+  // uniform, once for the whole tree (indexed by node)
+  for (int i = 1 + threadIdx.x; i < a.N; i += kWNT) {
+    const int u = (s_par[i] >= 0 && s_par[i] < i) ? s_par[i] : 0;
+    RowStat P, Q;
+    P.cm = s_cm[0][u];
+    P.S = s_S[0][u];
+    Q.cm = s_cm[1][u];
+    Q.S = s_S[1][u];
+    P.pad = Q.pad = 0.f;
+    const float zp = s_zp[i], zq = s_zq[i];
+    double pt = 0.0, qt = 0.0;
+    if (!__builtin_isnan(zp)) {
+      pt = prob_of(zp, a.c, P);
+      qt = prob_of(zq, a.c, Q);
+    }
+    s_pt[i] = pt;
+    s_qt[i] = qt;
+    s_r[i] = (float)uniform24(a.seed, (uint32_t)i, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
+  }
+  lds_sync();
 
   int node = 0, depth = 0;
   int64_t t = -1;
@@ -238,8 +259,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       break;
     }
     const void* rowQ = row_ptr(a.drf, rowbase + node, a.drf_sb);
-    // every child's p, q and uniform in parallel; the held slice of the
-    // node's row pair is loaded at the first rejection
+    // the held slice of the node's row pair is loaded at the first rejection
     bool loaded = false;
     RowStat P, Q;
     P.cm = s_cm[0][node];
@@ -248,19 +268,6 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     Q.S = s_S[1][node];
     P.pad = Q.pad = 0.f;
     if (writer && threadIdx.x == 0 && (!(P.S > 0.0) || !(Q.S > 0.0))) set_error(a.err, SV_DERR_ROW);
-    for (int k = threadIdx.x; k < nk; k += kWNT) {
-      const int cn = s_kids[k];
-      const float zp = s_zp[cn], zq = s_zq[cn];
-      double pt = 0.0, qt = 0.0;
-      if (!__builtin_isnan(zp)) {
-        pt = prob_of(zp, a.c, P);
-        qt = prob_of(zq, a.c, Q);
-      }
-      s_pt[k] = pt;
-      s_qt[k] = qt;
-      s_r[k] = (float)uniform24(a.seed, (uint32_t)cn, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
-    }
-    lds_sync();
     DrawSpec sp;
     sp.rowP = rowP;
     sp.rowQ = rowQ;
@@ -276,14 +283,14 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     int accepted = -1;
     for (int kk = 0; kk < nk; ++kk) {
       const int cn = s_kids[kk];
-      const double pt = s_pt[kk], qt = s_qt[kk];
+      const double pt = s_pt[cn], qt = s_qt[cn];
       if (writer && threadIdx.x == 0) {
         if (__builtin_isnan(s_zp[cn])) set_error(a.err, SV_DERR_TOKEN);
         if (a.out_p) a.out_p[rowbase + cn] = (float)pt;
         if (a.out_q) a.out_q[rowbase + cn] = (float)qt;
       }
       const double pcur = fmax(0.0, pt - c * qt) / D;
-      if ((double)s_r[kk] < accept_ratio(pcur, qt)) {
+      if ((double)s_r[cn] < accept_ratio(pcur, qt)) {
         accepted = cn;
         break;
       }

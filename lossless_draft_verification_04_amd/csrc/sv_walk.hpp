@@ -31,25 +31,40 @@ constexpr int kMaxG = 64;        // blocks (slices) per sequence
 constexpr uint32_t kSpinLimit = 1u << 22;
 constexpr uint64_t kTagMask = 0xffull;
 
-// Sum of N per-thread values over the block, each in a fixed order.
+// Exclusive prefix sums in thread order of N per-thread values (excl) and
+// their block totals (out; waves in index order), with one block barrier
+// pair for all N.
 template <int NT, int N>
-__device__ void block_sum_vec(const double* v, double* out) {
+__device__ void block_scan_vec(const double* v, double* excl, double* out) {
   __shared__ double red[NT / kWave][N];
-  double x[N];
-#pragma unroll
-  for (int i = 0; i < N; ++i) x[i] = wave_sum(v[i]);
+  const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
-  lds_sync();
-  if ((threadIdx.x & (kWave - 1)) == 0)
+  double inc[N];
 #pragma unroll
-    for (int i = 0; i < N; ++i) red[w][i] = x[i];
+  for (int i = 0; i < N; ++i) inc[i] = v[i];
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+#pragma unroll
+    for (int i = 0; i < N; ++i) {
+      const double y = __shfl_up(inc[i], o, kWave);
+      if (lane >= o) inc[i] += y;
+    }
+  }
+  lds_sync();
+  if (lane == kWave - 1)
+#pragma unroll
+    for (int i = 0; i < N; ++i) red[w][i] = inc[i];
   lds_sync();
 #pragma unroll
   for (int i = 0; i < N; ++i) {
-    double r = red[0][i];
+    double before = 0.0, total = 0.0;
 #pragma unroll
-    for (int k = 1; k < NT / kWave; ++k) r += red[k][i];
-    out[i] = r;
+    for (int k = 0; k < NT / kWave; ++k) {
+      if (k < w) before += red[k][i];
+      total += red[k][i];
+    }
+    excl[i] = before + (inc[i] - v[i]);
+    out[i] = total;
   }
 }
 
@@ -62,8 +77,9 @@ struct Slice {
   static constexpr int E = Fmt<DT>::kPerVec;
   static constexpr int kT = HELD ? kSliceTiles : 1;
   u32x4 p[kT], q[kT];
-  double own[kT];  // this thread's weight sum per tile (last prepare)
-  double tot[kT];  // the block's weight sum per tile (last prepare)
+  double own[kT];   // this thread's weight sum per tile (last prepare)
+  double excl[kT];  // the weight of the tile's earlier threads (last prepare)
+  double tot[kT];   // the block's weight sum per tile (last prepare)
   const void* rowP;
   const void* rowQ;
   int64_t v0, v1;
@@ -80,14 +96,26 @@ struct Slice {
       q[u] = p[u];
     }
     if constexpr (!HELD) return;
+    // every tile's loads are issued together, with no branch between them
+    // (a branch per tile let the compiler wait for one tile before issuing
+    // the next); positions past the slice load its last vector (index 0 for
+    // an empty slice), which valid() then ignores
+    const int64_t last = v1 > 0 ? v1 - 1 : 0;
+    int64_t vc[kT];
 #pragma unroll
     for (int u = 0; u < kT; ++u) {
-      if (v0 + (int64_t)u * NT < v1) {  // block-uniform
-        const int64_t v = v0 + (int64_t)u * NT + threadIdx.x;
-        const int64_t vc = v < v1 ? v : v1 - 1;  // clamped: the loads are unconditional and overlap
-        p[u] = load_vec(rp, vc);
-        if (rq) q[u] = load_vec(rq, vc);
+      const int64_t v = v0 + (int64_t)u * NT + threadIdx.x;
+      vc[u] = v < v1 ? v : last;
+    }
+    if (rq) {
+#pragma unroll
+      for (int u = 0; u < kT; ++u) {
+        p[u] = load_vec(rp, vc[u]);
+        q[u] = load_vec(rq, vc[u]);
       }
+    } else {
+#pragma unroll
+      for (int u = 0; u < kT; ++u) p[u] = load_vec(rp, vc[u]);
     }
   }
 
@@ -97,8 +125,10 @@ struct Slice {
     return v < v1;
   }
 
-  // Weight sums of sp over the slice: per thread and per tile (kept for a
-  // later search with the same sp) and the block total (fixed order).
+  // Weight sums of sp over the slice: per thread and per tile, with each
+  // tile's exclusive prefix over the threads (kept for a later search with
+  // the same sp, so that the search needs no scan), and the block total
+  // (fixed order).
   // sp.rowQ must be null, or the row pair the slice holds.
   __device__ __forceinline__ double prepare(const DrawSpec& sp, int V) {
     if constexpr (!HELD) return range_weight_sum<DT, NT>(sp, V, v0, v1);
@@ -113,7 +143,7 @@ struct Slice {
         for (int e = 0; e < E; ++e) own[u] += (double)w[e];
       }
     }
-    block_sum_vec<NT, kT>(own, tot);
+    block_scan_vec<NT, kT>(own, excl, tot);
     double total = 0.0;
 #pragma unroll
     for (int u = 0; u < kT; ++u) total += tot[u];
@@ -207,9 +237,7 @@ struct Slice {
 #pragma unroll
     for (int u = 0; u < kT; ++u) {
       if (u == pick) {
-        double excl;
-        block_exclusive_scan<NT>(own[u], &excl);
-        const double t_local = loc - excl;
+        const double t_local = loc - excl[u];
         int64_t found = INT64_MAX;
         int64_t v;
         if (valid(u, &v) && own[u] > 0.0 && t_local >= 0.0 && t_local < own[u]) {
