@@ -356,7 +356,7 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
   const int b = blockIdx.x / a.G;
   const int g = blockIdx.x - b * a.G;
   __shared__ uint64_t s_words[kMaxG], s_w1[kMaxG];
-  __shared__ double s_val[kMaxG];
+  SliceSums ss;  // the slices' values of the last exchange
   __shared__ Decided dec;
   const Job* pj = chain_decide<DT, PM>(a, b, g == 0, dec);
   const Job jb = *pj;
@@ -378,24 +378,24 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
     sp.invSP = 1.f;
     sp.ex = &pj->ex;
     sp.nex = jb.ex >= 0 ? 1 : 0;
-    total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
+    total = exchange_sum(x, sl.prepare(sp, a.V), s_words, &ss);
     if (!(total > 0.0)) {
       // the row is a point mass at the rejected token (by rounding): draw from it
       sp.nex = 0;
-      total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
+      total = exchange_sum(x, sl.prepare(sp, a.V), s_words, &ss);
     }
   } else if (resid) {
-    total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
+    total = exchange_sum(x, sl.prepare(sp, a.V), s_words, &ss);
     if (!(total > 0.0)) {
       // residual mass rounded to 0: draw from p_{n+1} itself
       sp.rowQ = nullptr;
-      total = exchange_sum(x, sl.prepare(sp, a.V), s_words, s_val);
+      total = exchange_sum(x, sl.prepare(sp, a.V), s_words, &ss);
     }
   } else {
     // bonus draw (or a row without mass): the row's statistics from the
     // slices in one exchange, then a plain draw with the row's shift
     float M;
-    total = exchange_stats(x, sl.row_stats(a.c, a.V), a.c, s_words, s_w1, s_val, &M);
+    total = exchange_stats(x, sl.row_stats(a.c, a.V), a.c, s_words, s_w1, &ss, &M);
     if (g == 0 && threadIdx.x == 0 && M == kNegInf) set_error(a.err, SV_DERR_ROW);
     sp.rowQ = nullptr;
     sp.cmP = M == kNegInf ? 0.f : a.c * M;
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
   }
   int pick;
   double loc;
-  slice_scan(s_val, x.G, jb.u * total, &pick, &loc);
+  pick_slice(ss, x.G, jb.u * total, &pick, &loc);
   // a block other than the searching one stores the deferred outputs
   if (g == (x.G > 1 && pick == 0 ? 1 : 0)) chain_outputs<PM>(a, b, dec);
   if (pick == g) {

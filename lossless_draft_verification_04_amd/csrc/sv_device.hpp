@@ -164,6 +164,46 @@ __device__ __forceinline__ float wave_fmax(float v) {
   for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
   return v;
 }
+// Lane movement by DPP (gfx9 encodings): row_shr:n shifts within 16-lane
+// rows, row_bcast:15 / row_bcast:31 broadcast lane 15 of each row to the
+// next row / lane 31 to rows 2 and 3.  Lanes without a source, and rows
+// outside ROWS, read `fill`.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ double dpp_d(double v, double fill) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v), f = (uint64_t)__double_as_longlong(fill);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)f, (int)(uint32_t)b, CTRL, ROWS, 0xF, false);
+  const uint32_t hi =
+      (uint32_t)__builtin_amdgcn_update_dpp((int)(uint32_t)(f >> 32), (int)(uint32_t)(b >> 32), CTRL, ROWS, 0xF, false);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142, kDppRowBcast31 = 0x143;
+
+// Inclusive prefix sum over the wave's lanes in lane order: four row shifts
+// and two row broadcasts, no LDS traffic.
+__device__ __forceinline__ double wave_incl_scan(double v) {
+  v += dpp_d<kDppRowShr1, 0xF>(v, 0.0);
+  v += dpp_d<kDppRowShr2, 0xF>(v, 0.0);
+  v += dpp_d<kDppRowShr4, 0xF>(v, 0.0);
+  v += dpp_d<kDppRowShr8, 0xF>(v, 0.0);
+  v += dpp_d<kDppRowBcast15, 0xA>(v, 0.0);
+  v += dpp_d<kDppRowBcast31, 0xC>(v, 0.0);
+  return v;
+}
+
+// Lane l's value (l wave-uniform).
+__device__ __forceinline__ double readlane_d(double v, int l) {
+  const uint64_t b = (uint64_t)__double_as_longlong(v);
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), l);
+  return __longlong_as_double((long long)(((uint64_t)hi << 32) | lo));
+}
+__device__ __forceinline__ int64_t readlane_i64(int64_t v, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(uint64_t)v, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)((uint64_t)v >> 32), l);
+  return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
@@ -234,12 +274,7 @@ __device__ double block_exclusive_scan(double v, double* excl) {
   __shared__ double wtot[NT / kWave];
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
-  double inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double y = __shfl_up(inc, o, kWave);
-    if (lane >= o) inc += y;
-  }
+  const double inc = wave_incl_scan(v);
   lds_sync();
   if (lane == kWave - 1) wtot[w] = inc;
   lds_sync();

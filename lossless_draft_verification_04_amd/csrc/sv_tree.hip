@@ -143,10 +143,10 @@ __device__ int node_children(int node, int N, const int32_t* s_par, int* s_kids,
 template <int DT, bool HELD>
 __device__ int64_t bonus_draw(const TreeParams& a, Exchange& x, Slice<DT, kWNT, HELD>& sl, const void* rowP,
                               int64_t v0, int64_t v1, double us, bool writer, uint64_t* s_w0, uint64_t* s_w1,
-                              double* s_val) {
+                              SliceSums& ss) {
   sl.load(rowP, nullptr, v0, v1);
   float M;
-  const double total = exchange_stats(x, sl.row_stats(a.c, a.V), a.c, s_w0, s_w1, s_val, &M);
+  const double total = exchange_stats(x, sl.row_stats(a.c, a.V), a.c, s_w0, s_w1, &ss, &M);
   if (M == kNegInf && writer && threadIdx.x == 0) set_error(a.err, SV_DERR_ROW);
   DrawSpec sp;
   sp.rowP = rowP;
@@ -161,7 +161,7 @@ __device__ int64_t bonus_draw(const TreeParams& a, Exchange& x, Slice<DT, kWNT, 
   sp.nex = 0;
   int pick;
   double loc;
-  slice_scan(s_val, x.G, us * total, &pick, &loc);
+  pick_slice(ss, x.G, us * total, &pick, &loc);
   if (pick != x.g) return -1;
   sl.prepare(sp, a.V);
   return sl.search(sp, a.V, loc);
@@ -187,7 +187,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   __shared__ double s_pt[SV_MAX_N], s_qt[SV_MAX_N];  // each child's p and q under its parent's rows
   __shared__ float s_r[SV_MAX_N];
   __shared__ uint64_t s_w0[kMaxG], s_w1[kMaxG];
-  __shared__ double s_val[kMaxG];
+  SliceSums ss;  // the slices' values of the last exchange
   __shared__ int s_cnt;
   const double us = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
 
@@ -255,7 +255,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     const void* rowP = row_ptr(a.tgt, rowbase + node, a.tgt_sb);
     if (nk == 0 || depth >= a.max_depth) {
       if (nk > 0 && writer) set_error(a.err, SV_DERR_TREE);
-      t = bonus_draw<DT, HELD>(a, x, sl, rowP, v0, v1, us, writer, s_w0, s_w1, s_val);
+      t = bonus_draw<DT, HELD>(a, x, sl, rowP, v0, v1, us, writer, s_w0, s_w1, ss);
       break;
     }
     const void* rowQ = row_ptr(a.drf, rowbase + node, a.drf_sb);
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
         sl.load(rowP, rowQ, v0, v1);
         loaded = true;
       }
-      const double Dn = exchange_sum(x, sl.prepare(sp, a.V), s_w0, s_val);
+      const double Dn = exchange_sum(x, sl.prepare(sp, a.V), s_w0, &ss);
       if (Dn > 0.0) {
         c = cnext;
         D = Dn;
@@ -319,10 +319,10 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     // every child rejected: draw from (p - c q)^+
     sp.coef = (float)c;
     if (!loaded) sl.load(rowP, rowQ, v0, v1);  // (not reached: the last child was rejected)
-    if (!sums_current) D = exchange_sum(x, sl.prepare(sp, a.V), s_w0, s_val);
+    if (!sums_current) D = exchange_sum(x, sl.prepare(sp, a.V), s_w0, &ss);
     int pick;
     double loc;
-    slice_scan(s_val, x.G, us * D, &pick, &loc);
+    pick_slice(ss, x.G, us * D, &pick, &loc);
     if (pick == g) t = sl.search(sp, a.V, loc);
     break;
   }
@@ -362,7 +362,7 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
   __shared__ float s_r[SV_MAX_N];
   __shared__ int32_t s_ex[SV_MAX_N];  // rejected tokens inside this block's slice
   __shared__ uint64_t s_w0[kMaxG], s_w1[kMaxG];
-  __shared__ double s_val[kMaxG];
+  SliceSums ss;  // the slices' values of the last exchange
   __shared__ int s_cnt;
   const double us = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
 
@@ -405,7 +405,7 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
     const void* rowP = row_ptr(a.tgt, rowbase + node, a.tgt_sb);
     if (nk == 0 || depth >= a.max_depth) {
       if (nk > 0 && writer) set_error(a.err, SV_DERR_TREE);
-      t = bonus_draw<DT, HELD>(a, x, sl, rowP, v0, v1, us, writer, s_w0, s_w1, s_val);
+      t = bonus_draw<DT, HELD>(a, x, sl, rowP, v0, v1, us, writer, s_w0, s_w1, ss);
       break;
     }
     RowStat P;
@@ -480,15 +480,15 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
     sp.ex = s_ex;
     sp.nex = s_cnt;
     sl.load(rowP, nullptr, v0, v1);
-    double total = exchange_sum(x, sl.prepare(sp, a.V), s_w0, s_val);
+    double total = exchange_sum(x, sl.prepare(sp, a.V), s_w0, &ss);
     if (!(total > 0.0)) {
       // the row's mass sits on the rejected tokens (by rounding): draw from P_node
       sp.nex = 0;
-      total = exchange_sum(x, sl.prepare(sp, a.V), s_w0, s_val);
+      total = exchange_sum(x, sl.prepare(sp, a.V), s_w0, &ss);
     }
     int pick;
     double loc;
-    slice_scan(s_val, x.G, us * total, &pick, &loc);
+    pick_slice(ss, x.G, us * total, &pick, &loc);
     if (pick == g) t = sl.search(sp, a.V, loc);
     break;
   }

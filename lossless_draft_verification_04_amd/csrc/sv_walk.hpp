@@ -41,15 +41,7 @@ __device__ void block_scan_vec(const double* v, double* excl, double* out) {
   const int w = threadIdx.x / kWave;
   double inc[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) inc[i] = v[i];
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-#pragma unroll
-    for (int i = 0; i < N; ++i) {
-      const double y = __shfl_up(inc[i], o, kWave);
-      if (lane >= o) inc[i] += y;
-    }
-  }
+  for (int i = 0; i < N; ++i) inc[i] = wave_incl_scan(v[i]);
   lds_sync();
   if (lane == kWave - 1)
 #pragma unroll
@@ -253,7 +245,17 @@ struct Slice {
           }
           if (found == INT64_MAX) found = last;
         }
-        const int64_t r = block_min_i64<NT>(found);
+        // the first qualifying thread holds the smallest index (rounding can
+        // let neighbouring threads' ranges overlap)
+        __shared__ int64_t s_found[NT / kWave];
+        const uint64_t q = __ballot(found != INT64_MAX);
+        const int64_t wf = q ? readlane_i64(found, __builtin_ctzll(q)) : INT64_MAX;
+        lds_sync();
+        if ((threadIdx.x & (kWave - 1)) == 0) s_found[threadIdx.x / kWave] = wf;
+        lds_sync();
+        int64_t r = s_found[0];
+#pragma unroll
+        for (int w = 1; w < NT / kWave; ++w) r = s_found[w] < r ? s_found[w] : r;
         // rounding left the target past every thread: the tile's last positive element
         result = r != INT64_MAX ? r : block_max_i64<NT>(last_positive(sp, V, u));
       }
@@ -337,43 +339,44 @@ __device__ __forceinline__ void exchange(Exchange& x, uint64_t payload, uint64_t
   exchange_n<1>(x, payload, 0ull, s_words, nullptr);
 }
 
-// Slice values v_l = s_val[l] (l < G, in slice order): every wave computes
-// the same inclusive scan, so every thread gets the same total, and, for a
-// target, the slice holding it and the offset into it.  Rounding past the
-// end picks the end of the last slice with positive weight.
-__device__ __forceinline__ double slice_scan(const double* s_val, int G, double target, int* pick, double* loc) {
+// Slice values of the last exchange as every wave holds them: lane l < G
+// has slice l's value v and the inclusive prefix inc over slices 0..l (the
+// same in every wave, so every thread takes the same decisions).
+struct SliceSums {
+  double v, inc;
+};
+
+// Scan of the lanes' slice values; returns the total.
+__device__ __forceinline__ double scan_slices(double v, int G, SliceSums* ss) {
+  ss->v = v;
+  ss->inc = wave_incl_scan(v);
+  return readlane_d(ss->inc, G - 1);
+}
+
+// The slice holding `target` (0 <= target < total) and the offset into
+// it; rounding past the end picks the end of the last slice with positive
+// weight.
+__device__ __forceinline__ void pick_slice(const SliceSums& ss, int G, double target, int* pick, double* loc) {
   const int l = threadIdx.x & (kWave - 1);
-  const double v = l < G ? s_val[l] : 0.0;
-  double inc = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const double y = __shfl_up(inc, o, kWave);
-    if (l >= o) inc += y;
-  }
-  const double total = __shfl(inc, G - 1, kWave);
-  const uint64_t over = __ballot(l < G && inc > target);
+  const uint64_t over = __ballot(l < G && ss.inc > target);
   if (over) {
     const int p = __builtin_ctzll(over);
     *pick = p;
-    *loc = target - (__shfl(inc, p, kWave) - __shfl(v, p, kWave));
+    *loc = target - (readlane_d(ss.inc, p) - readlane_d(ss.v, p));
   } else {
-    const uint64_t pos = __ballot(l < G && v > 0.0);
+    const uint64_t pos = __ballot(l < G && ss.v > 0.0);
     const int p = pos ? 63 - __builtin_clzll(pos) : 0;
     *pick = p;
-    *loc = __shfl(v, p, kWave);  // its end
+    *loc = readlane_d(ss.v, p);  // its end
   }
-  return total;
 }
 
-// Exchange slice sums: every thread gets the total; s_val[0..G) holds the
-// slice values (for a later slice_scan).
-__device__ __forceinline__ double exchange_sum(Exchange& x, double mine, uint64_t* s_words, double* s_val) {
+// Exchange slice sums: every thread gets the total, and ss the scan for a
+// later pick_slice.
+__device__ __forceinline__ double exchange_sum(Exchange& x, double mine, uint64_t* s_words, SliceSums* ss) {
   exchange(x, pack_sum(mine), s_words);
-  if ((int)threadIdx.x < x.G) s_val[threadIdx.x] = unpack_sum(s_words[threadIdx.x]);
-  lds_sync();
-  int pick;
-  double loc;
-  return slice_scan(s_val, x.G, 0.0, &pick, &loc);
+  const int l = threadIdx.x & (kWave - 1);
+  return scan_slices(l < x.G ? unpack_sum(s_words[l]) : 0.0, x.G, ss);
 }
 
 // Exchange slice maxima: every thread gets the maximum.
@@ -385,23 +388,18 @@ __device__ __forceinline__ float exchange_max(Exchange& x, float mine, uint64_t*
 }
 
 // Exchange slice statistics (max m_l, sum s_l of 2^(z c - c m_l)): every
-// thread gets the row maximum M; s_val[0..G) holds the slice weights
-// s_l 2^(c m_l - c M) (for a later slice_scan) and the total is returned.
+// thread gets the row maximum M and the total of the slice weights
+// s_l 2^(c m_l - c M), and ss their scan for a later pick_slice.
 __device__ __forceinline__ double exchange_stats(Exchange& x, const Partial& mine, float c, uint64_t* s_w0,
-                                                 uint64_t* s_w1, double* s_val, float* M_out) {
+                                                 uint64_t* s_w1, SliceSums* ss, float* M_out) {
   exchange_n<2>(x, pack_max(mine.m), pack_sum(mine.s), s_w0, s_w1);
   const int l = threadIdx.x & (kWave - 1);
   const float m = l < x.G ? unpack_max(s_w0[l]) : kNegInf;
   const float M = wave_fmax(m);
   *M_out = M;
-  if ((int)threadIdx.x < x.G)
-    s_val[threadIdx.x] = (m == kNegInf || M == kNegInf)
-                             ? 0.0
-                             : unpack_sum(s_w1[threadIdx.x]) * exp2((double)(c * m) - (double)(c * M));
-  lds_sync();
-  int pick;
-  double loc;
-  return slice_scan(s_val, x.G, 0.0, &pick, &loc);
+  const double v =
+      (l >= x.G || m == kNegInf || M == kNegInf) ? 0.0 : unpack_sum(s_w1[l]) * exp2((double)(c * m) - (double)(c * M));
+  return scan_slices(v, x.G, ss);
 }
 
 // Zero n slot words, spread over the blocks of a launch that precedes the
