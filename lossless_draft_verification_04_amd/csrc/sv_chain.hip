@@ -84,30 +84,36 @@ __device__ __forceinline__ RowStat merge_staged(const StagedParts& st, bool stag
 }
 
 // Parts per row that a lane merges straight from memory (more are staged in
-// LDS by the whole block first).
-constexpr int kDirectParts = 4;
+// LDS by the whole block first): a lane loads the parts of two rows, or of
+// one row in point-mass mode.
+template <bool PM>
+constexpr int direct_parts() {
+  return PM ? 8 : 4;
+}
 
-// Parts [0, n) at gp, 1 <= n <= kDirectParts, as 16-byte vectors: every
-// load is issued at once and unconditionally (clamped indexes), so the
-// merge waits for one round trip.
-__device__ __forceinline__ void load_parts(const Partial* gp, int n, u32x4 (&v)[kDirectParts]) {
+// Parts [0, n) at gp, 1 <= n <= N, as 16-byte vectors: every load is
+// issued at once and unconditionally (clamped indexes), so the merge waits
+// for one round trip.
+template <int N>
+__device__ __forceinline__ void load_parts(const Partial* gp, int n, u32x4 (&v)[N]) {
 #pragma unroll
-  for (int i = 0; i < kDirectParts; ++i)
+  for (int i = 0; i < N; ++i)
     v[i] = *reinterpret_cast<const u32x4*>(gp + (i < n ? i : n - 1));  // written by the previous launch
 }
 
 // Row statistic from loaded parts (the arithmetic of merge_staged).
-__device__ __forceinline__ RowStat merge_loaded(const u32x4 (&v)[kDirectParts], int n, float c) {
-  float m[kDirectParts];
-  double sum[kDirectParts];
+template <int N>
+__device__ __forceinline__ RowStat merge_loaded(const u32x4 (&v)[N], int n, float c) {
+  float m[N];
+  double sum[N];
 #pragma unroll
-  for (int i = 0; i < kDirectParts; ++i) {
+  for (int i = 0; i < N; ++i) {
     m[i] = __uint_as_float(v[i][0]);
     sum[i] = __longlong_as_double((long long)(((uint64_t)v[i][3] << 32) | v[i][2]));
   }
   float M = kNegInf;
 #pragma unroll
-  for (int i = 0; i < kDirectParts; ++i)
+  for (int i = 0; i < N; ++i)
     if (i < n) M = fmaxf(M, m[i]);
   RowStat r;
   r.pad = 0.f;
@@ -123,7 +129,7 @@ __device__ __forceinline__ RowStat merge_loaded(const u32x4 (&v)[kDirectParts], 
   }
   double S = 0.0;
 #pragma unroll
-  for (int i = 0; i < kDirectParts; ++i)
+  for (int i = 0; i < N; ++i)
     if (i < n && m[i] != kNegInf) S += sum[i] * exp2((double)(c * m[i]) - (double)r.cm);
   r.S = S;
   return r;
@@ -148,7 +154,7 @@ struct Decided {
 // rejection (lane 0 when every draft is accepted) writes the candidate's
 // draw job, so the only block barrier is the one before the longest
 // candidate is picked (plus the staging barrier when a row has more than
-// kDirectParts parts).  The writer block reports errors and, unless the
+// direct_parts() parts).  The writer block reports errors and, unless the
 // outputs are deferred (d.deferred), stores them; chain_outputs stores
 // deferred ones.  Returns the kept candidate's job (in LDS).
 template <int DT, bool PM>
@@ -160,7 +166,8 @@ __device__ const Job* chain_decide(const ChainParams& a, int b, bool writer, Dec
   const int Kg = a.K * a.gamma;
   const int rows = PM ? Kg : Kg + a.gamma;
   const int nparts = rows * a.nch1;
-  const bool direct = a.nch1 <= kDirectParts;
+  constexpr int kDP = direct_parts<PM>();
+  const bool direct = a.nch1 <= kDP;
   const bool staged = !direct && nparts <= kStage;
   const Partial* pb = static_cast<const Partial*>(a.part1) + (int64_t)b * nparts;
   const int lane = threadIdx.x & (kWave - 1);
@@ -196,11 +203,11 @@ __device__ const Job* chain_decide(const ChainParams& a, int b, bool writer, Dec
       const float zp = a.zg[o];
       const float zq = PM ? 0.f : a.zq[o];
       if (direct) {
-        u32x4 vp[kDirectParts], vq[kDirectParts];
+        u32x4 vp[kDP], vq[PM ? 1 : kDP];
         load_parts(pb + first_p, a.nch1, vp);
-        if (!PM) load_parts(pb + first_q, a.nch1, vq);
+        if constexpr (!PM) load_parts(pb + first_q, a.nch1, vq);
         sp = merge_loaded(vp, a.nch1, a.c);
-        if (!PM) sq = merge_loaded(vq, a.nch1, a.c);
+        if constexpr (!PM) sq = merge_loaded(vq, a.nch1, a.c);
       } else {
         sp = merge_staged(st, staged, pb, first_p, a.nch1, a.c);
         if (!PM) sq = merge_staged(st, staged, pb, first_q, a.nch1, a.c);

@@ -270,12 +270,182 @@ __device__ TopPair wave_list_scan(const Src src, int64_t v0, int64_t v1, int V, 
   return TopPair{lv, li};
 }
 
-// The wave's list of the F best values of [v0, v1).  (Per-lane lists were
-// measured ten times slower on the fan-out rows: some lane of the 64 inserts
-// at nearly every element, so the whole wave runs the insertion.)
+// The block's list of the F best values of [v0, v1) (F <= 64; every wave
+// of the block calls it with the same arguments).  Block thread t owns the
+// vectors v0 + t + k * NT.
+//  Pass 1 streams the range once; each thread keeps only its best element
+//  (value desc, then vector asc), about one max and one compare per vector.
+//  The block's F best threads by that element are the only threads that can
+//  own a top-F value: a value owned by any other thread is beaten by the F
+//  selected threads' bests.  So
+//  pass 2 re-reads just those threads' vectors (F times the range / NT
+//  vectors, mostly still in L2), spread over the waves; each wave lists
+//  the values of its share that reach the F-th selected best, inserting
+//  each with a lane shift.
+// Each wave returns its list (lane l = l-th best); the block's top F is the
+// top F of the waves' lists.  (Keeping running top-F lists during the
+// stream instead costs an insertion per new record, about F ln(n / F) per
+// list, which dominated at F >= 4.)
+template <int NT, int E, class Src>
+__device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V, int F) {
+  constexpr int NW = NT / kWave;
+  constexpr int kWin = 4;  // vectors in flight per thread
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wave = threadIdx.x / kWave;
+  const int tid = threadIdx.x;
+  __shared__ float s_m[NT];
+  __shared__ int32_t s_mv[NT];
+  __shared__ int32_t s_sel[kWave];
+  __shared__ int s_nsel;
+  __shared__ float s_tf;
+  float lv = kNegInf;
+  int32_t li = kNoIdx;
+  if (F <= 0) return TopPair{lv, li};
+  // pass 1: this thread's best element, as (value, vector offset)
+  float m = kNegInf;
+  int32_t mv = kNoIdx;
+  if (v0 < v1) {  // block-uniform
+    typename Src::Data d[kWin];
+    int64_t v = v0 + tid;
+#pragma unroll
+    for (int u = 0; u < kWin; ++u) {
+      const int64_t a = v + (int64_t)u * NT;
+      d[u] = src.load(a < v1 ? a : v1 - 1);  // clamped: every load is issued
+    }
+    for (; v < v1; v += (int64_t)kWin * NT) {
+      typename Src::Data nx[kWin];
+#pragma unroll
+      for (int u = 0; u < kWin; ++u) {
+        const int64_t a = v + (int64_t)(kWin + u) * NT;
+        nx[u] = src.load(a < v1 ? a : v1 - 1);
+      }
+#pragma unroll
+      for (int u = 0; u < kWin; ++u) {
+        const int64_t vu = v + (int64_t)u * NT;
+        if (vu < v1) {
+          float x[E];
+          src.values(d[u], vu, x);
+          float vm = x[0];
+#pragma unroll
+          for (int e = 1; e < E; ++e) vm = fmaxf(vm, x[e]);
+          // a vector always holds a listable element unless -inf is not listed
+          const bool has = !Src::kSkipNegInf || vm > kNegInf;
+          if (has && (mv == kNoIdx || vm > m)) {
+            m = vm;
+            mv = (int32_t)(vu - v0);
+          }
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < kWin; ++u) d[u] = nx[u];
+    }
+  }
+  s_m[tid] = m;
+  s_mv[tid] = mv;
+  lds_sync();
+  // the F best threads (wave 0: F rounds of a wave-wide selection over the
+  // NW entries each lane holds)
+  if (wave == 0) {
+    float em[NW];
+    int32_t ev_i[NW];
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      em[w] = s_m[w * kWave + lane];
+      ev_i[w] = s_mv[w * kWave + lane];
+    }
+    uint32_t taken = 0;
+    int n = 0;
+    float tf = kNegInf;
+    for (; n < F; ++n) {
+      float bv = kNegInf;
+      int32_t bi = kNoIdx;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float ev = em[w];
+        const int32_t ei = ev_i[w];
+        if (!((taken >> w) & 1u) && ei != kNoIdx && (bi == kNoIdx || top_better(ev, ei, bv, bi))) {
+          bv = ev;
+          bi = ei;
+        }
+      }
+      float wv = bv;
+      int32_t wi = bi;
+      wave_best(wv, wi);
+      if (wi == kNoIdx) break;  // fewer than F threads hold an element
+      const int owner = wi % NT;  // the thread whose vectors hold it
+      if (lane == (owner & (kWave - 1))) taken |= 1u << (owner / kWave);
+      if (lane == 0) s_sel[n] = owner;
+      tf = wv;
+    }
+    if (lane == 0) {
+      s_nsel = n;
+      s_tf = n == F ? tf : kNegInf;  // fewer threads than F: every listable value qualifies
+    }
+  }
+  lds_sync();
+  // pass 2: the selected threads' vectors, kWin per thread at a time
+  const int nsel = s_nsel;
+  const float tf = s_tf;
+  const int64_t span = v1 - v0;
+  const int64_t nk = (span + NT - 1) / NT;  // vectors per thread at most
+  const int64_t total = (int64_t)nsel * nk;
+  int count = 0;
+  for (int64_t base = 0; base < total; base += (int64_t)kWin * NT) {
+    typename Src::Data d[kWin];
+    int64_t rel[kWin];
+#pragma unroll
+    for (int u = 0; u < kWin; ++u) {
+      const int64_t t = base + (int64_t)u * NT + tid;
+      rel[u] = -1;
+      if (t < total) {
+        const int s = (int)(t / nk);
+        const int64_t r = s_sel[s] + (t - (int64_t)s * nk) * NT;
+        if (r < span) rel[u] = r;
+      }
+      d[u] = src.load(v0 + (rel[u] >= 0 ? rel[u] : 0));
+    }
+#pragma unroll
+    for (int u = 0; u < kWin; ++u) {
+      float x[E];
+      uint32_t mine = 0;
+      if (rel[u] >= 0) {
+        const int64_t vv = v0 + rel[u];
+        src.values(d[u], vv, x);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (x[e] >= tf && vv * E + e < V && (!Src::kSkipNegInf || x[e] > kNegInf)) mine |= 1u << e;
+      }
+      uint64_t cm = __ballot(mine != 0);
+      while (cm) {
+        const int sl = __builtin_ctzll(cm);
+        cm &= cm - 1;
+        uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)mine, sl);
+        const int64_t vs = v0 + readlane_i64(rel[u], sl);
+        while (bits) {
+          const int e = __builtin_ctz(bits);
+          bits &= bits - 1;
+          float xe = 0.f;
+#pragma unroll
+          for (int q = 0; q < E; ++q)
+            if (q == e) xe = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[q]), sl));
+          const int32_t ie = (int32_t)(vs * E + e);
+          const float fv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), F - 1));
+          const int32_t fi = __builtin_amdgcn_readlane(li, F - 1);
+          if (count < F || top_better(xe, ie, fv, fi)) {
+            wave_insert(lv, li, xe, ie, F, lane);
+            if (count < F) ++count;
+          }
+        }
+      }
+    }
+  }
+  return TopPair{lv, li};
+}
+
+// Per-wave lists whose merge is the block's top F of [v0, v1).
 template <int NT, int E, class Src>
 __device__ TopPair wave_topk_scan(const Src src, int64_t v0, int64_t v1, int V, int F) {
-  return wave_list_scan<NT, E>(src, v0, v1, V, F);
+  return block_topk_scan<NT, E>(src, v0, v1, V, F);
 }
 
 }  // namespace sv
