@@ -176,7 +176,8 @@ sv_status plan_fanout(sv_dtype dt, int32_t R, int32_t V, int32_t F_max, Plan* pl
   if (R < 0 || V < 1 || F_max < 1) return SV_EINVAL;
   if (R > (int32_t)kWsCounters || V > SV_MAX_V || F_max > SV_MAX_FANOUT) return SV_EUNSUPPORTED;
   pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
-  split(R, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
+  // 512-thread blocks: half the usual block count
+  split(R, pl->nvec, stats_blocks() / 2, &pl->nch1, &pl->vpc1);
   pl->grid1 = (int64_t)R * pl->nch1;
   if (pl->grid1 > INT32_MAX) return SV_EUNSUPPORTED;
   size_t off = kWsFixed;

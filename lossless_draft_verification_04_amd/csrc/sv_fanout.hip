@@ -4,17 +4,17 @@
 // the draft logits at every lookahead position k.  Here: for each row r the
 // F[r] largest logits, value descending, index ascending on ties.
 //
-// One launch: a block per (row part).  Each wave keeps its current top-F in
-// registers and streams its share of the part in increasing index order
-// (sv_topk.hpp); the block merges its waves' lists; the last block of a row
-// merges the parts' lists and writes them.
+// One launch: a block per (row part).  The block finds its part's top F in
+// two passes (sv_topk.hpp) and merges its waves' lists; a row in one part
+// is written by its block, otherwise the last block of the row merges the
+// parts' lists and writes them.
 #include "sv_device.hpp"
 #include "sv_internal.h"
 #include "sv_topk.hpp"
 
 namespace sv {
 
-constexpr int kFNT = 256;
+constexpr int kFNT = 512;
 
 template <int DT>
 __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
@@ -58,6 +58,14 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
         if (t.idx == kNoIdx || (ti != kNoIdx && !top_better(t.val, t.idx, tv, ti))) break;
         wave_insert(lv, li, t.val, t.idx, F, lane);
       }
+  }
+  if (a.nch == 1) {  // the whole row: no parts to merge
+    if (wave == 0 && lane < a.F_max) {
+      const bool keep = lane < F && li != kNoIdx;
+      a.out_ids[(int64_t)r * a.F_max + lane] = keep ? li : -1;
+      if (a.out_vals) a.out_vals[(int64_t)r * a.F_max + lane] = keep ? lv : kNegInf;
+    }
+    return;
   }
   if (wave == 0 && lane < a.F_max) put_entry(parts + (int64_t)ch * a.F_max + lane, lane < F ? lv : kNegInf,
                                              lane < F ? li : kNoIdx);
