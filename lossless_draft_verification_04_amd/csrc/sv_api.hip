@@ -251,6 +251,14 @@ sv_status plan_branch(sv_dtype dt, int32_t B, int32_t gamma, int32_t V, int32_t 
   const int64_t rows = (int64_t)B * (gamma + 1);
   split(rows, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
   split(B, pl->nvec, stats_blocks(), &pl->nch2, &pl->vpc2);
+  // fork parts of at most 4 vectors per thread keep their vectors in
+  // registers for the top-k's second pass; take them when that at most
+  // doubles the part count
+  constexpr int64_t kForkHeldVecs = 4 * 256;
+  if (pl->vpc2 > kForkHeldVecs && (pl->nvec + kForkHeldVecs - 1) / kForkHeldVecs <= 2 * (int64_t)pl->nch2) {
+    pl->vpc2 = kForkHeldVecs;
+    pl->nch2 = (int32_t)((pl->nvec + kForkHeldVecs - 1) / kForkHeldVecs);
+  }
   pl->grid1 = rows * pl->nch1;
   pl->grid2 = (int64_t)B * pl->nch2;
   if (pl->grid1 > INT32_MAX || pl->grid2 > INT32_MAX) return SV_EUNSUPPORTED;
