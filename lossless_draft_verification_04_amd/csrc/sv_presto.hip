@@ -32,7 +32,8 @@
 
 namespace sv {
 
-constexpr int kPNT = 256;
+constexpr int kPNT = 256;   // expansion block
+constexpr int kPFT = 1024;  // final block: one per sequence, on an otherwise idle device
 constexpr int kStageE = 1024;  // proposal entries the final launch stages at once
 constexpr int kMaxParts = 64;  // statistics parts per row (the plan caps it)
 constexpr float kLn2 = 0.69314718055994531f;
@@ -215,16 +216,26 @@ __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
   }
 }
 
+// Order key of a candidate at position pos of the ranking array: priority
+// descending, then position ascending, as one unsigned compare (floats map
+// to unsigned integers in their order, -0 as +0; -inf is above the empty
+// key 0).
+__device__ __forceinline__ uint64_t rank_key(float v, int pos) {
+  const uint32_t bits = __float_as_uint(v == 0.f ? 0.f : v);
+  const uint32_t o = (bits & 0x80000000u) ? ~bits : (bits | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)pos);
+}
+
 // One block per sequence (after the expansion launch): every node's s and S,
 // each leaf's part lists merged into its top k, and those into the
 // sequence's top b.
-__global__ __launch_bounds__(kPNT) void presto_final_kernel(PrestoParams a) {
+__global__ __launch_bounds__(kPFT) void presto_final_kernel(PrestoParams a) {
   const int b = blockIdx.x;
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int64_t rowbase = (int64_t)b * a.N;
   __shared__ int32_t s_par[SV_MAX_N];  // parents, each clamped below its node
-  for (int i = threadIdx.x; i < a.N; i += kPNT) {
+  for (int i = threadIdx.x; i < a.N; i += kPFT) {
     const int32_t p = a.parent[rowbase + i];
     const bool ok = i == 0 || (p >= 0 && p < i);
     if (!ok) set_error(a.err, SV_DERR_TREE);
@@ -236,14 +247,14 @@ __global__ __launch_bounds__(kPNT) void presto_final_kernel(PrestoParams a) {
   __shared__ int s_dep[SV_MAX_N];
   __shared__ uint8_t s_leaf[SV_MAX_N];
   __shared__ int s_changed;
-  for (int i = threadIdx.x; i < a.N; i += kPNT) {
+  for (int i = threadIdx.x; i < a.N; i += kPFT) {
     s_leaf[i] = 1;
     s_dep[i] = i == 0 ? 0 : -1;
   }
   lds_sync();
-  for (int i = 1 + threadIdx.x; i < a.N; i += kPNT) s_leaf[s_par[i]] = 0;
+  for (int i = 1 + threadIdx.x; i < a.N; i += kPFT) s_leaf[s_par[i]] = 0;
   lds_sync();
-  for (int i = threadIdx.x; i < 2 * a.N; i += kPNT) {
+  for (int i = threadIdx.x; i < 2 * a.N; i += kPFT) {
     const int node = i >> 1, which = i & 1;
     if (!s_leaf[node]) s_off[which][node] = row_offset(a, rowbase + node, which);
   }
@@ -251,7 +262,7 @@ __global__ __launch_bounds__(kPNT) void presto_final_kernel(PrestoParams a) {
   // the children's gathered logits and lambda per level, in LDS for the
   // level loop
   __shared__ float s_zt[SV_MAX_N], s_zd[SV_MAX_N], s_lam[SV_MAX_N];
-  for (int i = threadIdx.x; i < a.N; i += kPNT) {
+  for (int i = threadIdx.x; i < a.N; i += kPFT) {
     s_zt[i] = a.zc[rowbase + i];
     s_zd[i] = a.zc[(int64_t)a.B * a.N + rowbase + i];
     s_lam[i] = a.lam[(i + 1 < a.D ? i + 1 : a.D) - 1];  // depth i + 1
@@ -265,7 +276,7 @@ __global__ __launch_bounds__(kPNT) void presto_final_kernel(PrestoParams a) {
   for (int level = 1;; ++level) {
     if (threadIdx.x == 0) s_changed = 0;
     lds_sync();
-    for (int i = 1 + threadIdx.x; i < a.N; i += kPNT) {
+    for (int i = 1 + threadIdx.x; i < a.N; i += kPFT) {
       const int p = s_par[i];
       if (s_dep[i] < 0 && s_dep[p] == level - 1) {
         const float zp = s_zt[i], zq = s_zd[i];
@@ -285,29 +296,33 @@ __global__ __launch_bounds__(kPNT) void presto_final_kernel(PrestoParams a) {
     lds_sync();
     if (!s_changed) break;
   }
-  for (int i = threadIdx.x; i < a.N; i += kPNT) {
+  for (int i = threadIdx.x; i < a.N; i += kPFT) {
     if (a.out_s) a.out_s[rowbase + i] = s_s[i];
     if (a.out_S) a.out_S[rowbase + i] = s_S[i];
   }
   // Proposals: every leaf's list of k (merged by the expansion launch),
   // staged in LDS in chunks of whole leaves with all loads in flight
-  // together.  The valid entries of a chunk, compacted, and the current top b
-  // are ranked against each other: each counts the candidates that beat it,
-  // eight at a time, with (node, token) packed into one 64-bit key so that
-  // the order is (priority descending, key ascending); every key is
-  // distinct, so the ranks are too, and those below b form the new top b.
+  // together.  The current top b and the chunk's valid entries are laid out
+  // in (node, token) order -- the top b first (earlier chunks hold smaller
+  // nodes, and equal priorities among them are already in key order), then
+  // each leaf's entries sorted by token -- so that the order (priority
+  // descending, (node, token) ascending) is one 64-bit compare of
+  // (ordered priority bits, inverted position).  Every candidate counts the
+  // candidates that beat it; ranks are distinct, and those below b form the
+  // new top b.
   const TopEntry* all = static_cast<const TopEntry*>(a.leaf_lists) + rowbase * a.k;
   const int per_leaf = a.k;
   const int leaves_per_chunk = kStageE / per_leaf;
   __shared__ float c_v[kStageE];
   __shared__ int32_t c_t[kStageE];
-  // candidates: the chunk's kept entries, then the top b, padded to a multiple of 8
+  // candidates: the top b, then the chunk's kept entries, padded to a multiple of 8
   __shared__ float k_v[kStageE + SV_MAX_FANOUT + 8];
   __shared__ int64_t k_key[kStageE + SV_MAX_FANOUT + 8];
+  __shared__ uint64_t k_ord[kStageE + SV_MAX_FANOUT + 16];  // 8 spare keys for the read-ahead
   __shared__ float top_v[SV_MAX_FANOUT];
   __shared__ int32_t top_n[SV_MAX_FANOUT], top_t[SV_MAX_FANOUT];
   __shared__ int s_nk;
-  for (int j = threadIdx.x; j < a.b_top; j += kPNT) {
+  for (int j = threadIdx.x; j < a.b_top; j += kPFT) {
     top_v[j] = kNegInf;
     top_n[j] = kNoIdx;
     top_t[j] = kNoIdx;
@@ -316,7 +331,7 @@ __global__ __launch_bounds__(kPNT) void presto_final_kernel(PrestoParams a) {
     const int n1 = n0 + leaves_per_chunk < a.N ? n0 + leaves_per_chunk : a.N;
     const int ne = (n1 - n0) * per_leaf;
     lds_sync();  // the previous chunk is consumed
-    for (int e = threadIdx.x; e < ne; e += kPNT) {
+    for (int e = threadIdx.x; e < ne; e += kPFT) {
       TopEntry t;
       t.val = kNegInf;
       t.idx = kNoIdx;
@@ -325,56 +340,74 @@ __global__ __launch_bounds__(kPNT) void presto_final_kernel(PrestoParams a) {
       c_t[e] = t.idx;
     }
     if (threadIdx.x == 0) s_nk = 0;
+    // the top b first (empty entries never win and are not ranked)
+    for (int j = threadIdx.x; j < a.b_top; j += kPFT) {
+      const bool top = top_n[j] != kNoIdx;
+      k_v[j] = top_v[j];
+      k_key[j] = top ? (((int64_t)top_n[j] << 32) | (uint32_t)top_t[j]) : INT64_MAX;
+      k_ord[j] = top ? rank_key(top_v[j], j) : 0ull;
+    }
     lds_sync();
-    // compact the valid entries in index order
-    for (int e0 = 0; e0 < ne; e0 += kPNT) {
+    // the kept entries after them, each leaf's by token
+    for (int e0 = 0; e0 < ne; e0 += kPFT) {
       const int e = e0 + (int)threadIdx.x;
       const int keep = (e < ne && c_t[e] != kNoIdx) ? 1 : 0;
       double before;
-      const int total = (int)block_exclusive_scan<kPNT>((double)keep, &before);
+      const int total = (int)block_exclusive_scan<kPFT>((double)keep, &before);
       if (keep) {
-        const int at = s_nk + (int)before;
+        // within the leaf: kept entries before this one, and those with a smaller token
+        const int l0 = e - e % per_leaf;
+        int prior = 0, smaller = 0;
+        for (int q = l0; q < l0 + per_leaf; ++q) {
+          const int32_t tq = c_t[q];
+          prior += (int)((q < e) & (tq != kNoIdx));
+          smaller += (int)((tq != kNoIdx) & (tq < c_t[e]));
+        }
+        const int at = a.b_top + s_nk + (int)before - prior + smaller;
         const int node = n0 + e / per_leaf;
-        k_v[at] = s_S[node] + c_v[e] * kLn2;
+        const float v = s_S[node] + c_v[e] * kLn2;
+        k_v[at] = v;
         k_key[at] = ((int64_t)node << 32) | (uint32_t)c_t[e];
+        k_ord[at] = rank_key(v, at);
       }
       lds_sync();
       if (threadIdx.x == 0) s_nk += total;
       lds_sync();
     }
-    const int nk = s_nk;
-    const int nc = (nk + a.b_top + 7) & ~7;
-    for (int j = threadIdx.x; j < nc - nk; j += kPNT) {
-      const bool top = j < a.b_top && top_n[j] != kNoIdx;
-      k_v[nk + j] = top ? top_v[j] : kNegInf;
-      k_key[nk + j] = top ? (((int64_t)top_n[j] << 32) | (uint32_t)top_t[j]) : INT64_MAX;
+    const int nc = (a.b_top + s_nk + 7) & ~7;
+    for (int j = a.b_top + s_nk + (int)threadIdx.x; j < nc; j += kPFT) {
+      k_key[j] = INT64_MAX;
+      k_ord[j] = 0ull;
     }
     lds_sync();
-    for (int i = threadIdx.x; i < nc; i += kPNT) {
-      const float vi = k_v[i];
+    for (int i = threadIdx.x; i < nc; i += kPFT) {
       const int64_t ki = k_key[i];
       if (ki == INT64_MAX) continue;
+      const uint64_t oi = k_ord[i];
+      // the next eight keys are read while these are compared (LDS latency
+      // hidden); nc is a multiple of 8 and the array has 8 spare keys
       int rank = 0;
+      uint64_t oj[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) oj[q] = k_ord[q];
       for (int j0 = 0; j0 < nc; j0 += 8) {
-        float vj[8];
-        int64_t kj[8];
+        uint64_t on[8];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) {
-          vj[q] = k_v[j0 + q];
-          kj[q] = k_key[j0 + q];
-        }
+        for (int q = 0; q < 8; ++q) on[q] = k_ord[j0 + 8 + q];
 #pragma unroll
-        for (int q = 0; q < 8; ++q) rank += (vj[q] > vi || (vj[q] == vi && kj[q] < ki)) ? 1 : 0;
+        for (int q = 0; q < 8; ++q) rank += (int)(oj[q] > oi);
+#pragma unroll
+        for (int q = 0; q < 8; ++q) oj[q] = on[q];
       }
       if (rank < a.b_top) {
-        top_v[rank] = vi;
+        top_v[rank] = k_v[i];
         top_n[rank] = (int32_t)(ki >> 32);
         top_t[rank] = (int32_t)(ki & 0xffffffff);
       }
     }
   }
   lds_sync();
-  for (int j = threadIdx.x; j < a.b_top; j += kPNT) {
+  for (int j = threadIdx.x; j < a.b_top; j += kPFT) {
     const bool has = top_n[j] != kNoIdx;
     a.out_node[(int64_t)b * a.b_top + j] = has ? top_n[j] : -1;
     a.out_tok[(int64_t)b * a.b_top + j] = has ? top_t[j] : -1;
@@ -392,7 +425,7 @@ hipError_t launch_presto(const PrestoParams& p, const TreeParams& stats, sv_dtyp
     presto_expand_kernel<SV_F32><<<dim3((unsigned)plan.grid2), dim3(kPNT), 0, s>>>(p);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
-  presto_final_kernel<<<dim3((unsigned)p.B), dim3(kPNT), 0, s>>>(p);
+  presto_final_kernel<<<dim3((unsigned)p.B), dim3(kPFT), 0, s>>>(p);
   return hipGetLastError();
 }
 
