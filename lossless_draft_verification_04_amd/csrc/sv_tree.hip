@@ -43,7 +43,7 @@
 
 namespace sv {
 
-constexpr int kTNT = 256;
+constexpr int kTNT = 512;
 constexpr int kTU = 4;
 constexpr int kGather = SV_MAX_N / kTNT;  // candidate children per stats thread
 
