@@ -36,7 +36,7 @@ __device__ __forceinline__ uint32_t count_before(const u32x4 d, int64_t v, int V
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int64_t i = v * E + e;
-    c += (i < V && (x[e] > zt || (x[e] == zt && i < t))) ? 1u : 0u;
+    c += (uint32_t)((i < V) & ((x[e] > zt) | ((x[e] == zt) & (i < t))));  // no branches
   }
   return c;
 }
@@ -48,6 +48,9 @@ __global__ __launch_bounds__(kCNT) void cache_rank_kernel(CacheParams a) {
   const int ch = (int)(bid - (int64_t)b * a.nch);
   const int32_t n = a.n[b], t = a.t[b];
   const bool ok = n >= 0 && n <= a.K && t >= 0 && t < a.V;
+  // the fan-out of position n (F is given exactly when out_hit is), loaded
+  // now so the last block does not wait for it after its fetch-add
+  const int32_t Fn = (ok && threadIdx.x == 0 && a.F != nullptr) ? a.F[n] : 0;
   uint32_t cnt = 0;
   if (ok) {
     const void* row = row_ptr(a.drf, (int64_t)b * (a.K + 1) + n, a.sb);
@@ -76,7 +79,7 @@ __global__ __launch_bounds__(kCNT) void cache_rank_kernel(CacheParams a) {
     if ((uint32_t)(old >> 32) == (uint32_t)(a.nch - 1)) {
       const int32_t rank = (int32_t)((uint32_t)old + total);
       a.out_rank[b] = ok ? rank : -1;
-      if (a.out_hit) a.out_hit[b] = ok && rank < a.F[n] ? 1 : 0;
+      if (a.out_hit) a.out_hit[b] = ok && rank < Fn ? 1 : 0;
       if (!ok) set_error(a.err, SV_DERR_TOKEN);
       __hip_atomic_store(word, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }

@@ -14,7 +14,7 @@
 
 namespace sv {
 
-constexpr int kGNT = 256;
+constexpr int kGNT = 192;
 constexpr int kGU = 4;
 
 struct ArgPart {
@@ -149,8 +149,10 @@ __global__ __launch_bounds__(kGNT) void greedy_kernel(GreedyParams a) {
   if (threadIdx.x == 0) put_arg(parts + (int64_t)j * a.nch + ch, part);
   if (!arrive_last<kGNT>(&a.cnt[b], (uint32_t)per_seq)) return;
 
-  __shared__ int32_t g[SV_MAX_GAMMA + 1];
+  __shared__ int32_t g[SV_MAX_GAMMA + 1], s_tok[SV_MAX_GAMMA];
   for (int jj = threadIdx.x; jj < rows; jj += kGNT) {
+    // the drafted token is loaded with the row's parts (one round of loads)
+    const int32_t x = jj < a.gamma ? a.tok[(int64_t)b * a.gamma + jj] : 0;
     const ArgPart* pr = parts + (int64_t)jj * a.nch;
     const ArgPart p0 = get_arg(pr);
     float bv = p0.val;
@@ -163,19 +165,24 @@ __global__ __launch_bounds__(kGNT) void greedy_kernel(GreedyParams a) {
       }
     }
     g[jj] = bi;
+    if (jj < a.gamma) {
+      s_tok[jj] = x;
+      if (x < 0 || x >= a.V) set_error(a.err, SV_DERR_TOKEN);
+    }
     if (a.out_argmax) a.out_argmax[(int64_t)b * rows + jj] = bi;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
-    int n = 0;
-    while (n < a.gamma && a.tok[(int64_t)b * a.gamma + n] == g[n]) ++n;
-    for (int jj = 0; jj < a.gamma; ++jj) {
-      const int32_t x = a.tok[(int64_t)b * a.gamma + jj];
-      if (x < 0 || x >= a.V) set_error(a.err, SV_DERR_TOKEN);
+  if (threadIdx.x < kWave) {
+    // n = leading matches: a ballot of the mismatches (gamma <= 64)
+    const int l = threadIdx.x;
+    const uint64_t miss = __ballot(l < a.gamma && s_tok[l] != g[l]);
+    int n = miss ? __builtin_ctzll(miss) : a.gamma;
+    if (n > a.gamma) n = a.gamma;
+    if (l == 0) {
+      a.out_n[b] = n;
+      a.out_tok[b] = g[n];
+      __hip_atomic_store(&a.cnt[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    a.out_n[b] = n;
-    a.out_tok[b] = g[n];
-    __hip_atomic_store(&a.cnt[b], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
