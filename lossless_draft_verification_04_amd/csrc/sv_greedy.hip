@@ -33,9 +33,9 @@ __device__ __forceinline__ ArgPart get_arg(const ArgPart* src) {
   return v;
 }
 
-// (value desc, index asc)
+// (value desc, index asc), without branches
 __device__ __forceinline__ bool arg_better(float va, int64_t ia, float vb, int64_t ib) {
-  return va > vb || (va == vb && ia < ib);
+  return (va > vb) | ((va == vb) & (ia < ib));
 }
 
 template <int DT>
