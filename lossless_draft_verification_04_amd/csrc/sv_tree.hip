@@ -119,20 +119,24 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
 constexpr int kWNT = 256;  // walk block
 
 // Children of `node` in increasing index (from the staged parent array) into
-// s_kids; returns their count (the same in every thread).
+// s_kids; returns their count (the same in every thread).  The first wave
+// finds them with one ballot per 64 candidates, so the block waits at one
+// barrier; every wave has finished with the previous node's list (each
+// node's processing ends at a barrier).
 __device__ int node_children(int node, int N, const int32_t* s_par, int* s_kids, int* s_cnt) {
-  if (threadIdx.x == 0) *s_cnt = 0;
-  lds_sync();
-  for (int base = node + 1; base < N; base += kWNT) {
-    const int i = base + (int)threadIdx.x;
-    const int flag = (i < N) && s_par[i] == node;
-    double excl;
-    const double tot = block_exclusive_scan<kWNT>((double)flag, &excl);
-    if (flag) s_kids[*s_cnt + (int)excl] = i;
-    lds_sync();
-    if (threadIdx.x == 0) *s_cnt += (int)tot;
-    lds_sync();
+  if (threadIdx.x < kWave) {
+    const int lane = threadIdx.x;
+    int cnt = 0;
+    for (int base = node + 1; base < N; base += kWave) {
+      const int i = base + lane;
+      const bool flag = (i < N) & (s_par[i < N ? i : N - 1] == node);
+      const uint64_t m = __ballot(flag);
+      if (flag) s_kids[cnt + __popcll(m & ((1ull << lane) - 1))] = i;
+      cnt += __popcll(m);
+    }
+    if (lane == 0) *s_cnt = cnt;
   }
+  lds_sync();
   return *s_cnt;
 }
 
@@ -186,6 +190,8 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   __shared__ double s_S[2][SV_MAX_N];
   __shared__ double s_pt[SV_MAX_N], s_qt[SV_MAX_N];  // each child's p and q under its parent's rows
   __shared__ float s_r[SV_MAX_N];
+  __shared__ int s_first[SV_MAX_N];  // each node's first child (N: none)
+  __shared__ int s_tried[SV_MAX_N];  // children tried so far, in order (their outputs are stored at the end)
   __shared__ uint64_t s_w0[kMaxG], s_w1[kMaxG];
   SliceSums ss;  // the slices' values of the last exchange
   __shared__ int s_cnt;
@@ -199,6 +205,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     s_par[i] = a.parent[rowbase + i];
     s_zp[i] = zc[i];
     s_zq[i] = zc[(int64_t)a.B * a.N + i];
+    s_first[i] = a.N;
   }
   for (int r = threadIdx.x; r < 2 * (a.N - 1); r += kWNT) {
     const int u = r >> 1, which = r & 1;
@@ -244,13 +251,31 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     s_pt[i] = pt;
     s_qt[i] = qt;
     s_r[i] = (float)uniform24(a.seed, (uint32_t)i, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
+    if (s_par[i] >= 0 && s_par[i] < i) atomicMin(&s_first[s_par[i]], i);
   }
   lds_sync();
 
   int node = 0, depth = 0;
+  int ntried = 0;  // entries of s_tried (the same in every thread)
   int64_t t = -1;
   Slice<DT, kWNT, HELD> sl;
   for (;;) {
+    // a node whose first child is accepted at its first try needs no pass
+    // over the logits: follow such nodes on the staged p, q and uniforms (the
+    // test is the general loop's first iteration, with c = 0 and D = 1; an
+    // accepted child has p > 0, so only the draft row can lack mass)
+    for (;;) {
+      const int fc = s_first[node];
+      if (fc >= a.N || depth >= a.max_depth || !((double)s_r[fc] < accept_ratio(s_pt[fc], s_qt[fc]))) break;
+      if (threadIdx.x == 0) {
+        s_tried[ntried] = fc;
+        s_path[depth] = fc;
+        if (writer && !(s_S[1][node] > 0.0)) set_error(a.err, SV_DERR_ROW);
+      }
+      ++ntried;
+      ++depth;
+      node = fc;
+    }
     const int nk = node_children(node, a.N, s_par, s_kids, &s_cnt);
     const void* rowP = row_ptr(a.tgt, rowbase + node, a.tgt_sb);
     if (nk == 0 || depth >= a.max_depth) {
@@ -284,11 +309,8 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     for (int kk = 0; kk < nk; ++kk) {
       const int cn = s_kids[kk];
       const double pt = s_pt[cn], qt = s_qt[cn];
-      if (writer && threadIdx.x == 0) {
-        if (__builtin_isnan(s_zp[cn])) set_error(a.err, SV_DERR_TOKEN);
-        if (a.out_p) a.out_p[rowbase + cn] = (float)pt;
-        if (a.out_q) a.out_q[rowbase + cn] = (float)qt;
-      }
+      if (threadIdx.x == 0) s_tried[ntried] = cn;
+      ++ntried;
       const double pcur = fmax(0.0, pt - c * qt) / D;
       if ((double)s_r[cn] < accept_ratio(pcur, qt)) {
         accepted = cn;
@@ -331,6 +353,12 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     for (int d = threadIdx.x; d < a.max_depth; d += kWNT)
       a.out_path[(int64_t)b * a.max_depth + d] = d < depth ? s_path[d] : -1;
     if (threadIdx.x == 0) a.out_len[b] = depth;
+    for (int k = threadIdx.x; k < ntried; k += kWNT) {
+      const int cn = s_tried[k];
+      if (__builtin_isnan(s_zp[cn])) set_error(a.err, SV_DERR_TOKEN);
+      if (a.out_p) a.out_p[rowbase + cn] = (float)s_pt[cn];
+      if (a.out_q) a.out_q[rowbase + cn] = (float)s_qt[cn];
+    }
   }
   if (t >= 0 && threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
 }
@@ -357,9 +385,12 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
   __shared__ float s_zp[SV_MAX_N];   // each child's logit under its parent's target row
   __shared__ float s_cm[SV_MAX_N];   // target row statistics of the nodes with children
   __shared__ double s_S[SV_MAX_N];
-  __shared__ double s_pt[SV_MAX_N];  // the current node's children, in order: p(x_i)
-  __shared__ double s_w[SV_MAX_N];   // w(x_i) when child i is tried (0 for a repeated token)
-  __shared__ float s_r[SV_MAX_N];
+  __shared__ double s_pt[SV_MAX_N];  // each child's p under its parent's target row
+  __shared__ double s_w[SV_MAX_N];   // the current node's children, in order: w(x_i) when child i is
+                                     // tried (0 for a repeated token)
+  __shared__ float s_r[SV_MAX_N];    // each child's acceptance uniform
+  __shared__ int s_first[SV_MAX_N];  // each node's first child (N: none)
+  __shared__ int s_tried[SV_MAX_N];  // children tried so far, in order (their outputs are stored at the end)
   __shared__ int32_t s_ex[SV_MAX_N];  // rejected tokens inside this block's slice
   __shared__ uint64_t s_w0[kMaxG], s_w1[kMaxG];
   SliceSums ss;  // the slices' values of the last exchange
@@ -371,6 +402,7 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
     s_par[i] = a.parent[rowbase + i];
     s_tok[i] = a.tok[rowbase + i];
     s_zp[i] = zc[i];
+    s_first[i] = a.N;
   }
   for (int u = threadIdx.x; u < a.N - 1; u += kWNT) {
     const Partial* pr = parts + (rowbase + u) * a.nch;  // written by the previous launch
@@ -396,11 +428,42 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
   if (writer)
     for (int i = 1 + threadIdx.x; i < a.N; i += kWNT)
       if (s_par[i] < 0 || s_par[i] >= i) set_error(a.err, SV_DERR_TREE);
+  // every child's p under its parent's target row and its uniform, once for
+  // the whole tree (indexed by node)
+  for (int i = 1 + threadIdx.x; i < a.N; i += kWNT) {
+    const bool valid = s_par[i] >= 0 && s_par[i] < i;
+    const int u = valid ? s_par[i] : 0;
+    RowStat P;
+    P.cm = s_cm[u];
+    P.S = s_S[u];
+    P.pad = 0.f;
+    const float zp = s_zp[i];
+    s_pt[i] = __builtin_isnan(zp) ? 0.0 : prob_of(zp, a.c, P);
+    s_r[i] = (float)uniform24(a.seed, (uint32_t)i, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
+    if (valid) atomicMin(&s_first[u], i);
+  }
+  lds_sync();
 
   int node = 0, depth = 0;
+  int ntried = 0;  // entries of s_tried (the same in every thread)
   int64_t t = -1;
   Slice<DT, kWNT, HELD> sl;
   for (;;) {
+    // a node whose first child is accepted needs no list of its children:
+    // follow such nodes on the staged p and uniforms (the test is the
+    // general loop's first iteration, with D = 1; an accepted child has
+    // p > 0, so its parent's row has mass)
+    for (;;) {
+      const int fc = s_first[node];
+      if (fc >= a.N || depth >= a.max_depth || !((double)s_r[fc] < accept_ratio(s_pt[fc] / 1.0, 1.0))) break;
+      if (threadIdx.x == 0) {
+        s_tried[ntried] = fc;
+        s_path[depth] = fc;
+      }
+      ++ntried;
+      ++depth;
+      node = fc;
+    }
     const int nk = node_children(node, a.N, s_par, s_kids, &s_cnt);
     const void* rowP = row_ptr(a.tgt, rowbase + node, a.tgt_sb);
     if (nk == 0 || depth >= a.max_depth) {
@@ -418,14 +481,10 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
     // an earlier sibling carries the same token
     for (int k = threadIdx.x; k < nk; k += kWNT) {
       const int cn = s_kids[k];
-      const float zp = s_zp[cn];
-      const double pt = __builtin_isnan(zp) ? 0.0 : prob_of(zp, a.c, P);
       const int32_t tk = s_tok[cn];
       bool repeated = false;
       for (int j = 0; j < k && !repeated; ++j) repeated = s_tok[s_kids[j]] == tk;
-      s_pt[k] = pt;
-      s_w[k] = repeated ? 0.0 : pt;
-      s_r[k] = (float)uniform24(a.seed, (uint32_t)cn, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
+      s_w[k] = repeated ? 0.0 : s_pt[cn];
     }
     lds_sync();
     double D = 1.0;
@@ -433,19 +492,15 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
     for (int kk = 0; kk < nk; ++kk) {
       const double w = s_w[kk];
       const double ar = D > 0.0 ? accept_ratio(w / D, 1.0) : 0.0;
-      if ((double)s_r[kk] < ar) {
+      if ((double)s_r[s_kids[kk]] < ar) {
         accepted = s_kids[kk];
         tried = kk + 1;
         break;
       }
       D -= w;
     }
-    if (writer)
-      for (int k = threadIdx.x; k < tried; k += kWNT) {
-        const int cn = s_kids[k];
-        if (__builtin_isnan(s_zp[cn])) set_error(a.err, SV_DERR_TOKEN);
-        if (a.out_p) a.out_p[rowbase + cn] = (float)s_pt[k];
-      }
+    for (int k = threadIdx.x; k < tried; k += kWNT) s_tried[ntried + k] = s_kids[k];
+    ntried += tried;
     if (accepted >= 0) {
       if (threadIdx.x == 0) s_path[depth] = accepted;
       ++depth;
@@ -497,6 +552,11 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
     for (int d = threadIdx.x; d < a.max_depth; d += kWNT)
       a.out_path[(int64_t)b * a.max_depth + d] = d < depth ? s_path[d] : -1;
     if (threadIdx.x == 0) a.out_len[b] = depth;
+    for (int k = threadIdx.x; k < ntried; k += kWNT) {
+      const int cn = s_tried[k];
+      if (__builtin_isnan(s_zp[cn])) set_error(a.err, SV_DERR_TOKEN);
+      if (a.out_p) a.out_p[rowbase + cn] = (float)s_pt[cn];
+    }
   }
   if (t >= 0 && threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
 }
