@@ -90,6 +90,15 @@ def test_chain_full_batched_workload():
     PT.device_error_clear()
 
 
+def test_chain_parts_merged_from_memory():
+    # one sequence, 126 rows of 9 parts each: 1134 parts, more than the decide
+    # stages in LDS, so every row statistic is merged from device memory
+    wl = W.chain_zipf(B=1, gamma=63, V=80000, T=0.9, seed=19)
+    for seed, rnd in [(0, 0), (2, 1)]:
+        PT.chain(wl, seed, rnd)
+    PT.device_error_clear()
+
+
 def test_chain_out_of_range_token_sets_error_and_rejects():
     wl = W.chain_zipf(B=2, gamma=4, V=4096, T=1.0, seed=15)
     wl.tensors["tok"][1, 0] = 4096
@@ -123,6 +132,21 @@ def test_multi_k1_matches_chain_on_gpu():
     m = svx.sv_verify_multi(g["tgt"][:, None], g["drf"], g["tok"][:, None].contiguous(), 1.0, seed=3, round_=4)
     assert torch.equal(c["n"], m["n"]) and torch.equal(c["tok"], m["tok"])
     assert torch.equal(c["p"], m["p"][:, 0]) and (m["k"] == 0).all()
+
+
+def test_multi_parts_merged_from_memory():
+    # one sequence of 5 x 40 rows in 6 parts each: 1200 parts (merged from memory)
+    wl = W.multi_zipf(B=1, K=4, gamma=40, V=50000, T=1.0, seed=23)
+    for seed in (0, 5):
+        PT.multi(wl, seed, 2)
+    PT.device_error_clear()
+
+
+def test_multi_max_candidates_and_gamma():
+    # K = SV_MAX_K and gamma = SV_MAX_GAMMA: sixteen candidates per wave of the decide
+    wl = W.multi_zipf(B=2, K=64, gamma=64, V=2003, T=1.0, seed=24)
+    PT.multi(wl, 3, 0)
+    PT.device_error_clear()
 
 
 def test_multi_full_workload():
