@@ -36,6 +36,9 @@ constexpr int kPNT = 256;   // expansion block
 constexpr int kPFT = 1024;  // final block: one per sequence, on an otherwise idle device
 constexpr int kStageE = 1024;  // proposal entries the final launch stages at once
 constexpr int kMaxParts = 64;  // statistics parts per row (the plan caps it)
+constexpr int kFinalParts = 2048;  // statistics parts the final launch stages in LDS (2 rows per node)
+static_assert(kStageE <= kPFT, "a thread of the final launch prefetches at most one entry of the first chunk");
+static_assert(SV_MAX_N % kPFT == 0 && kFinalParts % kPFT == 0, "whole loads per thread");
 constexpr float kLn2 = 0.69314718055994531f;
 
 hipError_t launch_tree_stats(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
@@ -96,6 +99,20 @@ __device__ float row_offset(const PrestoParams& a, int64_t node_row, int which) 
   const RowStat st = merge_parts(static_cast<const Partial*>(a.part) + (node_row * 2 + which) * a.nch1, a.nch1, a.c);
   if (!(st.S > 0.0)) return __builtin_huge_valf();
   return (float)((double)st.cm + log2(st.S));
+}
+
+// The same offset from n parts staged in LDS (merge_parts' arithmetic, in
+// part order).
+__device__ float row_offset_staged(const Partial* pp, int n, float c) {
+  float M = kNegInf;
+  for (int i = 0; i < n; ++i) M = fmaxf(M, pp[i].m);
+  if (M == kNegInf) return __builtin_huge_valf();
+  const float cm = c * M;
+  double S = 0.0;
+  for (int i = 0; i < n; ++i)
+    if (pp[i].m != kNegInf) S += pp[i].s * exp2((double)(c * pp[i].m) - (double)cm);
+  if (!(S > 0.0)) return __builtin_huge_valf();
+  return (float)((double)cm + log2(S));
 }
 
 // Lambda of a node at depth d >= 1.
@@ -235,67 +252,116 @@ __global__ __launch_bounds__(kPFT) void presto_final_kernel(PrestoParams a) {
   const int wave = threadIdx.x / kWave;
   const int64_t rowbase = (int64_t)b * a.N;
   __shared__ int32_t s_par[SV_MAX_N];  // parents, each clamped below its node
-  for (int i = threadIdx.x; i < a.N; i += kPFT) {
-    const int32_t p = a.parent[rowbase + i];
-    const bool ok = i == 0 || (p >= 0 && p < i);
-    if (!ok) set_error(a.err, SV_DERR_TREE);
-    s_par[i] = (i > 0 && ok) ? p : 0;
-  }
-  lds_sync();
   __shared__ float s_off[2][SV_MAX_N];  // row offsets of the nodes with children (target, draft)
   __shared__ float s_s[SV_MAX_N], s_S[SV_MAX_N];
   __shared__ int s_dep[SV_MAX_N];
   __shared__ uint8_t s_leaf[SV_MAX_N];
-  __shared__ int s_changed;
-  for (int i = threadIdx.x; i < a.N; i += kPFT) {
-    s_leaf[i] = 1;
-    s_dep[i] = i == 0 ? 0 : -1;
+  // the children's gathered logits and lambda per level, in LDS for the
+  // level loop
+  __shared__ float s_zt[SV_MAX_N], s_zd[SV_MAX_N], s_lam[SV_MAX_N];
+  __shared__ Partial s_pp[kFinalParts];  // every row's statistics parts, when they fit
+  const int np = 2 * a.N * a.nch1;
+  const bool staged = np <= kFinalParts;  // block-uniform
+  const int per_leaf = a.k;
+  const int leaves_per_chunk = kStageE / per_leaf;
+  const TopEntry* all = static_cast<const TopEntry*>(a.leaf_lists) + rowbase * a.k;
+  // one round of loads, every one issued before any is used: the parents,
+  // the children's gathered logits, lambda, the rows' statistics parts
+  // (written two launches earlier) and this thread's entry of the first
+  // chunk of proposals (whether its node is a leaf is known only later)
+  constexpr int kPerThread = SV_MAX_N / kPFT;
+  constexpr int kPartsPerThread = kFinalParts / kPFT;
+  int32_t r_par[kPerThread];
+  float r_zt[kPerThread], r_zd[kPerThread], r_lam[kPerThread];
+  u32x4 r_pp[kPartsPerThread];
+  const u32x4* gparts = reinterpret_cast<const u32x4*>(static_cast<const Partial*>(a.part) + rowbase * 2 * a.nch1);
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int i = (int)threadIdx.x + q * kPFT;
+    const int ic = i < a.N ? i : a.N - 1;
+    r_par[q] = a.parent[rowbase + ic];
+    r_zt[q] = a.zc[rowbase + ic];
+    r_zd[q] = a.zc[(int64_t)a.B * a.N + rowbase + ic];
+    r_lam[q] = a.lam[(ic + 1 < a.D ? ic + 1 : a.D) - 1];  // depth i + 1
+  }
+  if (staged) {
+#pragma unroll
+    for (int q = 0; q < kPartsPerThread; ++q) {
+      const int j = (int)threadIdx.x + q * kPFT;
+      r_pp[q] = gparts[j < np ? j : np - 1];
+    }
+  }
+  const int ne0 = (a.N < leaves_per_chunk ? a.N : leaves_per_chunk) * per_leaf;  // <= kStageE = kPFT
+  const TopEntry pre = get_entry(all + ((int)threadIdx.x < ne0 ? (int)threadIdx.x : 0));
+#pragma unroll
+  for (int q = 0; q < kPerThread; ++q) {
+    const int i = (int)threadIdx.x + q * kPFT;
+    if (i < a.N) {
+      const int32_t p = r_par[q];
+      const bool ok = i == 0 || (p >= 0 && p < i);
+      if (!ok) set_error(a.err, SV_DERR_TREE);
+      s_par[i] = (i > 0 && ok) ? p : 0;
+      s_leaf[i] = 1;
+      s_dep[i] = i == 0 ? 0 : -1;
+      s_zt[i] = r_zt[q];
+      s_zd[i] = r_zd[q];
+      s_lam[i] = r_lam[q];
+    }
+  }
+  if (staged) {
+#pragma unroll
+    for (int q = 0; q < kPartsPerThread; ++q) {
+      const int j = (int)threadIdx.x + q * kPFT;
+      if (j < np) {
+        s_pp[j].m = __uint_as_float(r_pp[q][0]);
+        s_pp[j].pad = 0.f;
+        s_pp[j].s = __longlong_as_double((long long)(((uint64_t)r_pp[q][3] << 32) | r_pp[q][2]));
+      }
+    }
   }
   lds_sync();
   for (int i = 1 + threadIdx.x; i < a.N; i += kPFT) s_leaf[s_par[i]] = 0;
   lds_sync();
   for (int i = threadIdx.x; i < 2 * a.N; i += kPFT) {
     const int node = i >> 1, which = i & 1;
-    if (!s_leaf[node]) s_off[which][node] = row_offset(a, rowbase + node, which);
+    if (!s_leaf[node])
+      s_off[which][node] = staged ? row_offset_staged(s_pp + (node * 2 + which) * a.nch1, a.nch1, a.c)
+                                  : row_offset(a, rowbase + node, which);
   }
   lds_sync();
-  // the children's gathered logits and lambda per level, in LDS for the
-  // level loop
-  __shared__ float s_zt[SV_MAX_N], s_zd[SV_MAX_N], s_lam[SV_MAX_N];
-  for (int i = threadIdx.x; i < a.N; i += kPFT) {
-    s_zt[i] = a.zc[rowbase + i];
-    s_zd[i] = a.zc[(int64_t)a.B * a.N + rowbase + i];
-    s_lam[i] = a.lam[(i + 1 < a.D ? i + 1 : a.D) - 1];  // depth i + 1
-  }
-  lds_sync();
-  // depth and path score, level by level (parents precede children)
-  if (threadIdx.x == 0) {
-    s_s[0] = 0.f;
-    s_S[0] = 0.f;
-  }
-  for (int level = 1;; ++level) {
-    if (threadIdx.x == 0) s_changed = 0;
-    lds_sync();
-    for (int i = 1 + threadIdx.x; i < a.N; i += kPFT) {
-      const int p = s_par[i];
-      if (s_dep[i] < 0 && s_dep[p] == level - 1) {
-        const float zp = s_zt[i], zq = s_zd[i];
-        float sc;
-        if (__builtin_isnan(zp) || __builtin_isnan(zq)) {
-          set_error(a.err, SV_DERR_TOKEN);
-          sc = kNegInf;
-        } else {
-          sc = proxy_log2(zp, zq, a.c, s_off[0][p], s_off[1][p], s_lam[level - 1]) * kLn2;
-        }
-        s_s[i] = sc;
-        s_S[i] = s_S[p] + sc;
-        s_dep[i] = level;
-        s_changed = 1;
-      }
+  // depth and path score, level by level (parents precede children), by
+  // the first wave alone: its lanes' LDS accesses are performed in program
+  // order, so a level needs no block barrier, only a vote on whether any
+  // node was placed
+  if (wave == 0) {
+    if (lane == 0) {
+      s_s[0] = 0.f;
+      s_S[0] = 0.f;
     }
-    lds_sync();
-    if (!s_changed) break;
+    for (int level = 1;; ++level) {
+      __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront", "local");  // the previous level's writes first
+      int placed = 0;
+      for (int i = 1 + lane; i < a.N; i += kWave) {
+        const int p = s_par[i];
+        if (s_dep[i] < 0 && s_dep[p] == level - 1) {
+          const float zp = s_zt[i], zq = s_zd[i];
+          float sc;
+          if (__builtin_isnan(zp) || __builtin_isnan(zq)) {
+            set_error(a.err, SV_DERR_TOKEN);
+            sc = kNegInf;
+          } else {
+            sc = proxy_log2(zp, zq, a.c, s_off[0][p], s_off[1][p], s_lam[level - 1]) * kLn2;
+          }
+          s_s[i] = sc;
+          s_S[i] = s_S[p] + sc;
+          s_dep[i] = level;
+          placed = 1;
+        }
+      }
+      if (!__any(placed)) break;
+    }
   }
+  lds_sync();
   for (int i = threadIdx.x; i < a.N; i += kPFT) {
     if (a.out_s) a.out_s[rowbase + i] = s_s[i];
     if (a.out_S) a.out_S[rowbase + i] = s_S[i];
@@ -310,15 +376,13 @@ __global__ __launch_bounds__(kPFT) void presto_final_kernel(PrestoParams a) {
   // (ordered priority bits, inverted position).  Every candidate counts the
   // candidates that beat it; ranks are distinct, and those below b form the
   // new top b.
-  const TopEntry* all = static_cast<const TopEntry*>(a.leaf_lists) + rowbase * a.k;
-  const int per_leaf = a.k;
-  const int leaves_per_chunk = kStageE / per_leaf;
   __shared__ float c_v[kStageE];
   __shared__ int32_t c_t[kStageE];
   // candidates: the top b, then the chunk's kept entries, padded to a multiple of 8
   __shared__ float k_v[kStageE + SV_MAX_FANOUT + 8];
   __shared__ int64_t k_key[kStageE + SV_MAX_FANOUT + 8];
   __shared__ uint64_t k_ord[kStageE + SV_MAX_FANOUT + 16];  // 8 spare keys for the read-ahead
+  __shared__ int s_rank[kStageE + SV_MAX_FANOUT + 8];  // each candidate's count of better keys
   __shared__ float top_v[SV_MAX_FANOUT];
   __shared__ int32_t top_n[SV_MAX_FANOUT], top_t[SV_MAX_FANOUT];
   __shared__ int s_nk;
@@ -335,7 +399,8 @@ __global__ __launch_bounds__(kPFT) void presto_final_kernel(PrestoParams a) {
       TopEntry t;
       t.val = kNegInf;
       t.idx = kNoIdx;
-      if (s_leaf[n0 + e / per_leaf]) t = get_entry(all + (int64_t)n0 * per_leaf + e);
+      // the first chunk's entry was loaded with the tree (e is this thread's index there)
+      if (s_leaf[n0 + e / per_leaf]) t = n0 == 0 ? pre : get_entry(all + (int64_t)n0 * per_leaf + e);
       c_v[e] = t.val;
       c_t[e] = t.idx;
     }
@@ -379,18 +444,25 @@ __global__ __launch_bounds__(kPFT) void presto_final_kernel(PrestoParams a) {
       k_key[j] = INT64_MAX;
       k_ord[j] = 0ull;
     }
+    for (int j = threadIdx.x; j < nc; j += kPFT) s_rank[j] = 0;
     lds_sync();
-    for (int i = threadIdx.x; i < nc; i += kPFT) {
-      const int64_t ki = k_key[i];
-      if (ki == INT64_MAX) continue;
+    // every candidate counts the keys above its own, in S segments of the
+    // key array at once (S threads per candidate, so that the whole block
+    // compares); a segment is a whole number of 8-key groups, and the next
+    // eight keys are read while these are compared (the array has 8 spare
+    // keys past nc)
+    const int S = nc <= kPFT / 2 ? kPFT / nc : 1;
+    const int L = ((nc + S - 1) / S + 7) & ~7;
+    for (int t = threadIdx.x; t < nc * S; t += kPFT) {
+      const int i = t % nc, seg = t / nc;
+      const int j_lo = seg * L, j_hi = j_lo + L < nc ? j_lo + L : nc;
+      if (k_key[i] == INT64_MAX || j_lo >= j_hi) continue;
       const uint64_t oi = k_ord[i];
-      // the next eight keys are read while these are compared (LDS latency
-      // hidden); nc is a multiple of 8 and the array has 8 spare keys
       int rank = 0;
       uint64_t oj[8];
 #pragma unroll
-      for (int q = 0; q < 8; ++q) oj[q] = k_ord[q];
-      for (int j0 = 0; j0 < nc; j0 += 8) {
+      for (int q = 0; q < 8; ++q) oj[q] = k_ord[j_lo + q];
+      for (int j0 = j_lo; j0 < j_hi; j0 += 8) {
         uint64_t on[8];
 #pragma unroll
         for (int q = 0; q < 8; ++q) on[q] = k_ord[j0 + 8 + q];
@@ -399,7 +471,13 @@ __global__ __launch_bounds__(kPFT) void presto_final_kernel(PrestoParams a) {
 #pragma unroll
         for (int q = 0; q < 8; ++q) oj[q] = on[q];
       }
-      if (rank < a.b_top) {
+      if (rank) atomicAdd(&s_rank[i], rank);
+    }
+    lds_sync();
+    for (int i = threadIdx.x; i < nc; i += kPFT) {
+      const int64_t ki = k_key[i];
+      const int rank = s_rank[i];
+      if (ki != INT64_MAX && rank < a.b_top) {
         top_v[rank] = k_v[i];
         top_n[rank] = (int32_t)(ki >> 32);
         top_t[rank] = (int32_t)(ki & 0xffffffff);
