@@ -76,6 +76,16 @@ def test_chain_one_draw_block_per_sequence():
     PT.device_error_clear()
 
 
+def test_chain_and_multi_at_the_sequence_limit():
+    # SV_MAX_SEQ sequences: the largest grids the entry points accept (one
+    # draw block per sequence, more blocks than the device holds at once)
+    wl = W.chain_normal(B=32768, gamma=1, V=3, T=1.0, dtype="bf16", seed=201)
+    PT.chain(wl, 1, 0)
+    PT.chain_pm(wl, 1, 0)
+    PT.multi(W.multi_zipf(B=32768, K=2, gamma=1, V=4, T=1.0, seed=203), 2, 0)
+    PT.device_error_clear()
+
+
 def test_chain_streamed_slices():
     # slices longer than a block holds in registers: the streamed draw
     wl = W.chain_zipf(B=400, gamma=2, V=50000, T=0.9, seed=18)
@@ -202,6 +212,24 @@ def test_tree_small_shapes():
 def test_tree_many_sequences(B):
     wl = W.tree_zipf(B=B, N=12, max_depth=5, V=2500, T=1.0, seed=44 + B)
     PT.tree(wl, 3, 0)
+    PT.device_error_clear()
+
+
+def test_tree_at_the_sequence_limit():
+    wl = W.tree_zipf(B=32768, N=3, max_depth=2, V=5, T=1.0, seed=202, F0=2)
+    PT.tree(wl, 1, 0)
+    PT.tree_pm(wl, 1, 0)
+    PT.device_error_clear()
+
+
+def test_fanout_at_the_row_limit():
+    g = torch.Generator().manual_seed(204)
+    R, V = 65536, 9
+    Vs = W.padded_stride(V, "f32")
+    x = torch.zeros(R, Vs, dtype=torch.float32)[:, :V]
+    x.copy_(torch.randn(R, V, generator=g))
+    F = torch.randint(0, 5, (R,), generator=g, dtype=torch.int32)
+    PT.fanout(x, F, 4)
     PT.device_error_clear()
 
 
