@@ -233,6 +233,27 @@ def test_fanout_at_the_row_limit():
     PT.device_error_clear()
 
 
+def test_vocabulary_limit():
+    # V = SV_MAX_V = 2^24: rows of 32 MB (bf16), streamed slices and many row
+    # parts.  T = 0.5 and these seeds keep every decision and draw margin
+    # above the exception threshold (n = 0, 1 and 2 of 2 for the chain), so
+    # the tokens are compared, not excepted.
+    V = 1 << 24
+    wl = W.chain_normal(B=1, gamma=2, V=V, T=0.5, dtype="bf16", seed=205)
+    for seed in (4, 5, 6):
+        _, ref = PT.chain(wl, seed, 0)
+        assert ref["mdec"].min() >= PT.MARGIN and ref["mcdf"].min() >= PT.MARGIN
+        PT.chain_pm(wl, seed, 0)
+    PT.greedy(W.greedy_zipf(B=1, gamma=2, V=V, seed=206))
+    tw = W.tree_zipf(B=1, N=3, max_depth=2, V=V, T=0.5, seed=207, F0=2)
+    for seed in (5, 6):
+        _, ref = PT.tree(tw, seed, 0)
+        assert ref["mdec"].min() >= PT.MARGIN and ref["mcdf"].min() >= PT.MARGIN
+        PT.tree_pm(tw, seed, 0)
+    PT.fanout(tw.tensors["drf"].reshape(3, V), torch.tensor([5, 0, 64], dtype=torch.int32), 64)
+    PT.device_error_clear()
+
+
 def test_tree_streamed_slices():
     # slices longer than a block holds in registers: the streamed walk
     wl = W.tree_zipf(B=70, N=10, max_depth=4, V=40000, T=1.0, seed=47)
