@@ -47,19 +47,11 @@ __device__ __forceinline__ float vec_max(const float* x) {
   return m;
 }
 
-template <int DT>
-__device__ __forceinline__ void load_masked(const void* row, int V, int64_t v, float* x) {
-  constexpr int E = Fmt<DT>::kPerVec;
-  unpack<DT>(load_vec(row, v), x);
-  if ((v + 1) * E > V) {
-#pragma unroll
-    for (int e = 0; e < E; ++e)
-      if (v * E + e >= V) x[e] = kNegInf;
-  }
-}
-
 // Lowest index of the maximum over vectors [v0, v1) of one row; every thread
-// returns the block's answer.
+// returns the block's answer.  Each thread keeps the raw bits of its best
+// vector, so the lowest index inside it is found without reading it again
+// (a re-read bypasses the caches like the stream and costs a whole memory
+// line per thread).
 template <int DT, int NT, int U>
 __device__ ArgPart range_argmax(const void* row, int V, int64_t v0, int64_t v1) {
   constexpr int E = Fmt<DT>::kPerVec;
@@ -67,6 +59,7 @@ __device__ ArgPart range_argmax(const void* row, int V, int64_t v0, int64_t v1) 
   const int64_t vf = v1 < nfull ? v1 : nfull;
   float bv = kNegInf;
   int64_t bvec = -1;
+  u32x4 bd = u32x4{0u, 0u, 0u, 0u};
   int64_t v = v0 + threadIdx.x;
   for (; v + (int64_t)(U - 1) * NT < vf; v += (int64_t)U * NT) {
     u32x4 d[U];
@@ -80,22 +73,35 @@ __device__ ArgPart range_argmax(const void* row, int V, int64_t v0, int64_t v1) 
       if (bvec < 0 || m > bv) {
         bv = m;
         bvec = v + (int64_t)u * NT;
+        bd = d[u];
       }
     }
   }
   for (; v < v1; v += NT) {
+    const u32x4 d = load_vec(row, v);
     float x[E];
-    load_masked<DT>(row, V, v, x);
+    unpack<DT>(d, x);
+    if ((v + 1) * E > V) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (v * E + e >= V) x[e] = kNegInf;
+    }
     const float m = vec_max<DT>(x);
     if (bvec < 0 || m > bv) {
       bv = m;
       bvec = v;
+      bd = d;
     }
   }
   int64_t bidx = INT64_MAX;
   if (bvec >= 0) {
     float x[E];
-    load_masked<DT>(row, V, bvec, x);
+    unpack<DT>(bd, x);
+    if ((bvec + 1) * E > V) {
+#pragma unroll
+      for (int e = 0; e < E; ++e)
+        if (bvec * E + e >= V) x[e] = kNegInf;
+    }
 #pragma unroll
     for (int e = E - 1; e >= 0; --e)
       if (x[e] == bv) bidx = bvec * E + e;
