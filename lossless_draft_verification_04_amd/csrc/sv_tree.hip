@@ -83,13 +83,15 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
   }
   // the first part of the row gathers its logits at the children's tokens
   // (NaN for a token outside the vocabulary); the loads are issued before the
-  // stream and their bits used after it, so no wait precedes the stream
+  // stream and their bits used after it, so no wait precedes the stream.
+  // Candidates that are not children all read element 0: every distinct
+  // gathered address costs a whole memory line.
   uint32_t zg[kGather];
   if (ch == 0) {  // block-uniform; the loads are unconditional (clamped token) so none waits for another
 #pragma unroll
     for (int k = 0; k < kGather; ++k) {
       const int32_t x = xk[k];
-      zg[k] = load_bits<DT>(row, x >= 0 && x < a.V ? x : 0);
+      zg[k] = load_bits<DT>(row, (pk[k] >= 0) & (x >= 0) & (x < a.V) ? x : 0);
     }
   }
   const int64_t v0 = (int64_t)ch * a.vpc;
