@@ -84,8 +84,8 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
   // the first part of the row gathers its logits at the children's tokens
   // (NaN for a token outside the vocabulary); the loads are issued before the
   // stream and their bits used after it, so no wait precedes the stream.
-  // Candidates that are not children all read element 0: every distinct
-  // gathered address costs a whole memory line.
+  // Candidates that are not children all read element 0, so the block
+  // issues no more distinct gathers than it has children.
   uint32_t zg[kGather];
   if (ch == 0) {  // block-uniform; the loads are unconditional (clamped token) so none waits for another
 #pragma unroll
