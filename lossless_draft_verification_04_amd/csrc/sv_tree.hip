@@ -91,7 +91,7 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
 #pragma unroll
     for (int k = 0; k < kGather; ++k) {
       const int32_t x = xk[k];
-      zg[k] = load_bits<DT>(row, (pk[k] >= 0) & (x >= 0) & (x < a.V) ? x : 0);
+      zg[k] = load_bits<DT>(row, ((pk[k] >= 0) & (x >= 0) & (x < a.V)) ? x : 0);
     }
   }
   const int64_t v0 = (int64_t)ch * a.vpc;

@@ -206,16 +206,25 @@ def lookahead_rows(wl: Workload) -> torch.Tensor:
     return out
 
 
-def greedy_zipf(B=64, gamma=32, V=151936, dtype="bf16", seed=1003, match0=0.9, decay=0.95) -> Workload:
-    """Greedy window: planted unique row maxima; draft matches with probability match0 * decay^j."""
+def greedy_zipf(B=64, gamma=32, V=151936, dtype="bf16", seed=1003, match0=0.9, decay=0.95,
+                plant=True) -> Workload:
+    """Greedy window: the draft matches the target row's argmax with probability match0 * decay^j.
+
+    plant=True puts a unique maximum (+1.0 over the row's top) at a random index of every row.
+    plant=False keeps the Zipf + Gumbel rows as stored, so that rounding to the storage dtype leaves
+    ties at the row maximum in some rows; the draft's "match" token is then the first maximal index
+    of the stored row (the generator's choice of draft tokens, not a verification result)."""
     gen = _gen(seed)
     _, tgt = _alloc_rows((B, gamma + 1), V, dtype)
     planted = torch.randint(0, V, (B, gamma + 1), generator=gen, dtype=torch.int64)
     for b in range(B):
         t32 = zipf_rows(gamma + 1, V, gen)
-        top = t32.max(dim=1).values
-        t32[torch.arange(gamma + 1), planted[b]] = top + 1.0
+        if plant:
+            top = t32.max(dim=1).values
+            t32[torch.arange(gamma + 1), planted[b]] = top + 1.0
         tgt[b].copy_(t32)
+        if not plant:
+            planted[b] = torch.argmax(tgt[b].to(torch.float32), dim=1)
     j = torch.arange(1, gamma + 1, dtype=torch.float64)
     p_match = match0 * decay ** j
     hit = torch.rand(B, gamma, generator=gen, dtype=torch.float64) < p_match[None, :]
@@ -225,7 +234,7 @@ def greedy_zipf(B=64, gamma=32, V=151936, dtype="bf16", seed=1003, match0=0.9, d
     if V == 1:
         other = g.clone()
     tok = torch.where(hit, g, other).to(torch.int32)
-    return Workload("greedy", dict(B=B, gamma=gamma, V=V, dtype=dtype, seed=seed),
+    return Workload("greedy", dict(B=B, gamma=gamma, V=V, dtype=dtype, seed=seed, plant=plant),
                     dict(tgt=tgt, tok=tok, planted=planted.to(torch.int32)))
 
 

@@ -77,6 +77,10 @@ MUTANTS = [
      "for (int v = 0; v < in.V; ++v) w[v] = p[v];", TREE_PINS),
     ("multi ties to highest k", "if (results[k].n > best_n) {", "if (results[k].n >= best_n) {",
      [pins.test_multi_k1_is_chain_and_each_candidate_is_its_chain]),
+    ("multi draws from the first candidate's rows", "out_tok[b] = results[best_k].t;", "out_tok[b] = results[0].t;",
+     [pins.test_multi_k1_is_chain_and_each_candidate_is_its_chain]),
+    ("multi draws from the last candidate's rows", "out_tok[b] = results[best_k].t;",
+     "out_tok[b] = results[K - 1].t;", [pins.test_multi_k1_is_chain_and_each_candidate_is_its_chain]),
     ("greedy ties to highest index", "    if (z > best) {\n      best = z;", "    if (z >= best) {\n      best = z;",
      [pins.test_greedy_ties_lowest_index_and_signed_zero, pins.test_greedy_equals_chain_on_one_hot_rows]),
     ("fan-out unstable order", "std::stable_sort(idx.begin(), idx.end(), [&](int a, int b) { return z[a] > z[b]; });",

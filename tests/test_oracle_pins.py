@@ -268,18 +268,35 @@ def test_greedy_ties_lowest_index_and_signed_zero():
 # Multi-candidate and tree reductions
 # --------------------------------------------------------------------------
 def test_multi_k1_is_chain_and_each_candidate_is_its_chain():
+    """SpecDiff-2 page, Core method: the kept candidate is verified as a chain (draft-then-verify page §2.1),
+    so for any K its n is that candidate's own chain n and the emitted token is the chain's draw on ITS rows
+    (its target row n+1 against the shared draft row, or its bonus row) with the sequence's one sampling
+    uniform."""
     rng = np.random.default_rng(9)
-    B, K, gamma, V = 6, 4, 5, 40
+    B, K, gamma, V = 40, 4, 5, 40
     tgt = rng.normal(0, 2, (B, K, gamma + 1, V))
     drf = tgt[:, 0, :gamma] + rng.normal(0, 1, (B, gamma, V))
-    tok = rng.integers(0, V, (B, K, gamma)).astype(np.int32)
+    # drafts drawn near the target's mode so that streaks differ between candidates
+    tok = np.argmax(tgt[:, :, :gamma] + rng.gumbel(0, 1.5, (B, K, gamma, V)), axis=-1).astype(np.int32)
     om = oracle.verify_multi(tgt, drf, tok, 0.9, 77, 5, "f64")
+    alone = []
     for k in range(K):
-        # candidate k alone, with the acceptance uniforms drawn at counter k
+        # candidate k alone, with the acceptance uniforms drawn at counter k and the shared sampling uniform
         r = np.array([[oracle.uniform(77, j + 1, b, k, 5, 0) for j in range(gamma)] for b in range(B)])
         o1 = oracle.verify_multi(tgt[:, k:k + 1].copy(), drf, tok[:, k:k + 1].copy(), 0.9, 77, 5, "f64",
                                  r=r[:, None, :])
         assert np.array_equal(o1["n"], om["n_cand"][:, k])
+        alone.append(o1)
+    ks = om["k"]
+    for b in range(B):
+        o1 = alone[ks[b]]
+        assert om["t"][b] == o1["t"][b] and om["mcdf"][b] == o1["mcdf"][b]
+        assert om["rows"][b] == o1["rows"][b]
+    # the draw is not a candidate-independent quantity here: a kept candidate other than the first and the
+    # last occurs, and another candidate's draw would have given another token
+    assert np.any((ks != 0) & (ks != K - 1))
+    for other in (0, K - 1):
+        assert np.any(np.array([alone[other]["t"][b] != om["t"][b] for b in range(B)]) & (ks != other))
     assert np.array_equal(om["n"], om["n_cand"].max(1))
     assert np.array_equal(om["k"], np.argmax(om["n_cand"], 1))  # lowest k among the longest
     o1 = oracle.verify_multi(tgt[:, :1].copy(), drf, tok[:, :1].copy(), 0.9, 77, 5, "f64")
