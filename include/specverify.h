@@ -208,6 +208,27 @@ sv_status sv_verify_tree(const void* tgt, const void* drf, sv_dtype dt, int64_t 
                          int32_t* out_tok, float* out_p, float* out_q, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * sv_verify_chain for callers that cannot allocate device memory (code under
+ * HIP graph capture, tight serving loops, harnesses that forbid hipMalloc):
+ * the same computation, arguments and outputs, with no workspace argument.
+ * Its scratch space is a device array of SV_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; the call allocates and
+ * frees nothing.  Shapes whose chain workspace (sv_workspace_size with
+ * SV_OP_CHAIN) exceeds that size are rejected with SV_EUNSUPPORTED before
+ * anything is enqueued.  Every call on one GPU uses that GPU's array: calls
+ * that overlap in time on one GPU (other streams, other host threads) race
+ * and must be ordered by the caller.  Device-side input errors are OR-ed into
+ * *out_err (a device int32 the caller zeroes before the call; NULL: not
+ * reported).  The array is looked up on the first call on each device (with
+ * that device current); SV_EHIP if that lookup fails.
+ */
+#define SV_NOALLOC_SCRATCH_BYTES (8u << 20)
+sv_status sv_verify_chain_noalloc(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride,
+                                  int64_t drf_stride, const int32_t* draft_tok, int32_t B, int32_t gamma, int32_t V,
+                                  float T, uint64_t seed, uint32_t round, int32_t* out_n, int32_t* out_tok,
+                                  float* out_p, float* out_q, int32_t* out_err, void* stream);
+
+/*
  * Point-mass ("greedy acceptance") chain verification: SpecDiff-2 page, Core
  * method, read as the draft-then-verify page's §2.1 step with the draft
  * distribution a point mass at the drafted token (q = delta_x).  Lossless for

@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 
 #include "sv_device.hpp"
 #include "sv_internal.h"
@@ -362,7 +363,7 @@ static sv_status verify_chain_like(const void* tgt, const void* drf, sv_dtype dt
                                    int64_t drf_stride, const int32_t* tok, int32_t B, int32_t K, int32_t gamma,
                                    int32_t V, float T, uint64_t seed, uint32_t round, int32_t* out_k, int32_t* out_n,
                                    int32_t* out_tok, int32_t* out_n_cand, float* out_p, float* out_q, bool pm,
-                                   void* ws, size_t ws_bytes, void* stream) {
+                                   void* ws, size_t ws_bytes, void* stream, int32_t* err = nullptr) {
   Plan pl;
   sv_status st = plan_chain(dt, B, K, gamma, V, pm, &pl);
   if (st != SV_OK) return st;
@@ -392,7 +393,7 @@ static sv_status verify_chain_like(const void* tgt, const void* drf, sv_dtype dt
   p.out_n_cand = out_n_cand;
   p.out_p = out_p;
   p.out_q = out_q;
-  p.err = reinterpret_cast<int32_t*>(w);
+  p.err = err ? err : reinterpret_cast<int32_t*>(w);
   p.part1 = w + pl.off_part1;
   p.zg = reinterpret_cast<float*>(w + pl.off_part2);
   p.zq = p.zg + (int64_t)B * K * gamma;
@@ -411,6 +412,58 @@ sv_status sv_verify_chain(const void* tgt, const void* drf, sv_dtype dt, int64_t
                           size_t ws_bytes, void* stream) {
   return verify_chain_like(tgt, drf, dt, tgt_stride, drf_stride, draft_tok, B, 1, gamma, V, T, seed, round, nullptr,
                            out_n, out_tok, nullptr, out_p, out_q, false, ws, ws_bytes, stream);
+}
+
+// ---------------------------------------------------------------------------
+// Allocation-free chain verification.  The scratch space is this file-scope
+// device array: each GPU the library runs on holds its own copy until the
+// process ends.  In host code `scratch` names a host-side stand-in, not device
+// memory, so the array is only ever reached through the device address that
+// hipGetSymbolAddress returns, looked up once per device with that device
+// current and kept per device.
+// ---------------------------------------------------------------------------
+namespace {
+constexpr size_t kScratchBytes = SV_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) unsigned char scratch[kScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// The current device's copy of the array (null if the lookup fails).
+void* scratch_for_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return nullptr;
+    g_scratch_ptr[dev] = ptr;
+  }
+  return g_scratch_ptr[dev];
+}
+}  // namespace
+
+sv_status sv_verify_chain_noalloc(const void* tgt, const void* drf, sv_dtype dt, int64_t tgt_stride,
+                                  int64_t drf_stride, const int32_t* draft_tok, int32_t B, int32_t gamma, int32_t V,
+                                  float T, uint64_t seed, uint32_t round, int32_t* out_n, int32_t* out_tok,
+                                  float* out_p, float* out_q, int32_t* out_err, void* stream) {
+  // the shape's scratch need, checked before any HIP call
+  Plan pl;
+  sv_status st = plan_chain(dt, B, 1, gamma, V, false, &pl);
+  if (st != SV_OK) return st;
+  if (pl.bytes > kScratchBytes) return SV_EUNSUPPORTED;
+  if (B == 0) return verify_chain_like(tgt, drf, dt, tgt_stride, drf_stride, draft_tok, B, 1, gamma, V, T, seed,
+                                       round, nullptr, out_n, out_tok, nullptr, out_p, out_q, false, nullptr, 0,
+                                       stream);
+  void* ws = scratch_for_current_device();
+  if (!ws) return SV_EHIP;
+  // every part, gathered logit and slot word the kernels read is written
+  // earlier in the same call (the slot words by the statistics launch), so
+  // the previous call's contents need no clearing; device errors go to
+  // out_err, or to the array's own error word, which is never read
+  return verify_chain_like(tgt, drf, dt, tgt_stride, drf_stride, draft_tok, B, 1, gamma, V, T, seed, round, nullptr,
+                           out_n, out_tok, nullptr, out_p, out_q, false, ws, kScratchBytes, stream, out_err);
 }
 
 sv_status sv_verify_chain_pm(const void* tgt, sv_dtype dt, int64_t tgt_stride, const int32_t* draft_tok, int32_t B,

@@ -51,6 +51,8 @@ _SIGS = {
                          _P, _P, _P, _sz, _P], _i32),
     "sv_verify_tree": ([_P, _P, _i32, _i64, _i64, _P, _P, _i32, _i32, _i32, _i32, _f32, _u64, _u32, _P, _P, _P,
                         _P, _P, _P, _sz, _P], _i32),
+    "sv_verify_chain_noalloc": ([_P, _P, _i32, _i64, _i64, _P, _i32, _i32, _i32, _f32, _u64, _u32, _P, _P, _P, _P,
+                                 _P, _P], _i32),
     "sv_verify_chain_pm": ([_P, _i32, _i64, _P, _i32, _i32, _i32, _f32, _u64, _u32, _P, _P, _P, _P, _sz, _P], _i32),
     "sv_verify_tree_pm": ([_P, _i32, _i64, _P, _P, _i32, _i32, _i32, _i32, _f32, _u64, _u32, _P, _P, _P, _P, _P,
                            _sz, _P], _i32),
@@ -170,6 +172,32 @@ def sv_verify_chain(tgt, drf, tok, T, seed=0, round_=0, want_pq=True, workspace=
     _check(_lib.sv_verify_chain(_ptr(tgt), _ptr(drf), dt, _row_stride(tgt, "tgt"), _row_stride(drf, "drf"),
                                 _ptr(tok), B, gamma, V, float(T), int(seed), int(round_), _ptr(out_n), _ptr(out_tok),
                                 _ptr(p), _ptr(q), _ptr(ws), ws.numel(), _stream(dev)), "sv_verify_chain")
+    return dict(n=out_n, tok=out_tok, p=p, q=q)
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20
+
+
+def sv_verify_chain_noalloc(tgt, drf, tok, T, seed=0, round_=0, want_pq=True, out_err=None):
+    """sv_verify_chain through the allocation-free entry point: the library's own per-GPU scratch array, no
+    workspace.  out_err: optional zeroed device int32 tensor [1] that receives the device error bits."""
+    B, g1, V = tgt.shape
+    gamma = g1 - 1
+    if tuple(drf.shape) != (B, gamma, V) or drf.dtype != tgt.dtype:
+        raise SpecVerifyError(SV_EINVAL, f"drf shape {tuple(drf.shape)} / dtype does not match tgt")
+    _i32_tensor(tok, (B, gamma), "tok")
+    if out_err is not None:
+        _i32_tensor(out_err, (1,), "out_err")
+    dt = _dtype_code(tgt)
+    dev = tgt.device
+    out_n = torch.empty(B, dtype=torch.int32, device=dev)
+    out_tok = torch.empty(B, dtype=torch.int32, device=dev)
+    p = torch.empty(B, gamma, dtype=torch.float32, device=dev) if want_pq else None
+    q = torch.empty(B, gamma, dtype=torch.float32, device=dev) if want_pq else None
+    _check(_lib.sv_verify_chain_noalloc(_ptr(tgt), _ptr(drf), dt, _row_stride(tgt, "tgt"), _row_stride(drf, "drf"),
+                                        _ptr(tok), B, gamma, V, float(T), int(seed), int(round_), _ptr(out_n),
+                                        _ptr(out_tok), _ptr(p), _ptr(q), _ptr(out_err), _stream(dev)),
+           "sv_verify_chain_noalloc")
     return dict(n=out_n, tok=out_tok, p=p, q=q)
 
 

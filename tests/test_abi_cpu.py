@@ -29,7 +29,7 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 16
+    assert len(names) == 17
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(svx.EXPORTED)
@@ -216,3 +216,17 @@ def test_binding_rejects_bad_layouts_on_cpu_tensors():
         svx._row_stride(x.transpose(1, 2), "x")
     with pytest.raises(svx.SpecVerifyError):
         svx._row_stride(torch.zeros(2, 6, 64, dtype=torch.bfloat16)[:, :5], "x")  # rows not evenly spaced
+
+
+def test_noalloc_rejects_shapes_beyond_its_scratch_before_any_hip_call():
+    """sv_verify_chain_noalloc checks dtype, sizes and its scratch limit on the host (nothing enqueued)."""
+    p = ctypes.c_void_p(16)
+    need = ws_size(svx.SV_OP_CHAIN, svx.SV_BF16, 32768, 1, 64, 152064)[1]
+    assert need > svx.NOALLOC_SCRATCH_BYTES
+    st = L.sv_verify_chain_noalloc(p, p, svx.SV_BF16, 152064, 152064, p, 32768, 64, 152064, 1.0, 0, 0, p, p, None,
+                                   None, None, None)
+    assert st == svx.SV_EUNSUPPORTED
+    assert L.sv_verify_chain_noalloc(p, p, 7, 16, 16, p, 1, 1, 16, 1.0, 0, 0, p, p, None, None, None,
+                                     None) == svx.SV_EDTYPE
+    assert L.sv_verify_chain_noalloc(p, p, svx.SV_BF16, 16, 16, p, 1, 65, 16, 1.0, 0, 0, p, p, None, None, None,
+                                     None) == svx.SV_EUNSUPPORTED
