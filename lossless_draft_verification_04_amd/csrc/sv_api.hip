@@ -394,6 +394,7 @@ static sv_status verify_chain_like(const void* tgt, const void* drf, sv_dtype dt
   p.out_p = out_p;
   p.out_q = out_q;
   p.err = err ? err : reinterpret_cast<int32_t*>(w);
+  p.knobs = err ? nullptr : reinterpret_cast<const uint32_t*>(w);
   p.part1 = w + pl.off_part1;
   p.zg = reinterpret_cast<float*>(w + pl.off_part2);
   p.zq = p.zg + (int64_t)B * K * gamma;
@@ -548,6 +549,7 @@ static sv_status verify_tree_like(const void* tgt, const void* drf, sv_dtype dt,
   p.out_p = out_p;
   p.out_q = out_q;
   p.err = reinterpret_cast<int32_t*>(w);
+  p.knobs = reinterpret_cast<const uint32_t*>(w);
   p.slots = w + pl.off_jobs;
   p.zc = reinterpret_cast<float*>(w + pl.off_part2);
   p.part = w + pl.off_part1;
@@ -665,6 +667,7 @@ sv_status sv_presto_score(const void* tgt, const void* drf, sv_dtype dt, int64_t
   t.V = V;
   t.c = log2e_over(T);
   t.err = reinterpret_cast<int32_t*>(w);
+  t.knobs = nullptr;
   t.part = w + pl.off_part1;
   t.zc = reinterpret_cast<float*>(w + pl.off_part2);
   t.slots = w + pl.off_jobs;  // the expansion's per-node arrival counters

@@ -370,7 +370,7 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
   const int64_t spv = (a.nvec + a.G - 1) / a.G;
   const int64_t v0 = (int64_t)g * spv < a.nvec ? (int64_t)g * spv : a.nvec;
   const int64_t v1 = v0 + spv < a.nvec ? v0 + spv : a.nvec;
-  Exchange x = make_exchange(a.slots, a.err, b, a.G, g);
+  Exchange x = make_exchange(a.slots, a.err, a.knobs, b, a.G, g);
   const bool resid = !PM && jb.rowQ >= 0 && jb.SP > 0.0 && jb.SQ > 0.0;
   const bool pm_resid = PM && jb.SP > 0.0;  // a rejection, in a row with mass
   DrawSpec sp = job_spec<DT>(a, jb, 0.f);

@@ -31,6 +31,7 @@ struct ChainParams {
   float* out_p;
   float* out_q;
   int32_t* err;
+  const uint32_t* knobs;  // workspace header (wait bound, test switch), or null
   void* part1;     // stats parts, [B][rows][nch1]
   float* zg;       // target logits of the drafted tokens, [B][K][gamma]
   float* zq;       // draft logits of the drafted tokens, [B][K][gamma]
@@ -73,6 +74,7 @@ struct TreeParams {
   float* out_p;
   float* out_q;
   int32_t* err;
+  const uint32_t* knobs;  // workspace header (wait bound, test switch), or null
   void* part;
   float* zc;       // each child's logits under its parent's rows, [2][B][N] (target, draft)
   void* slots;     // walk slot words, [B][G][4], zeroed by the stats launch

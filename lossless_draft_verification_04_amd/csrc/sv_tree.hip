@@ -177,7 +177,7 @@ template <int DT, bool HELD>
 __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   const int b = blockIdx.x / a.G;
   const int g = blockIdx.x - b * a.G;
-  Exchange x = make_exchange(a.slots, a.err, b, a.G, g);
+  Exchange x = make_exchange(a.slots, a.err, a.knobs, b, a.G, g);
   const int64_t spv = (a.nvec + a.G - 1) / a.G;
   const int64_t v0 = (int64_t)g * spv < a.nvec ? (int64_t)g * spv : a.nvec;
   const int64_t v1 = v0 + spv < a.nvec ? v0 + spv : a.nvec;
@@ -371,7 +371,7 @@ template <int DT, bool HELD>
 __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
   const int b = blockIdx.x / a.G;
   const int g = blockIdx.x - b * a.G;
-  Exchange x = make_exchange(a.slots, a.err, b, a.G, g);
+  Exchange x = make_exchange(a.slots, a.err, a.knobs, b, a.G, g);
   const int64_t spv = (a.nvec + a.G - 1) / a.G;
   const int64_t v0 = (int64_t)g * spv < a.nvec ? (int64_t)g * spv : a.nvec;
   const int64_t v1 = v0 + spv < a.nvec ? v0 + spv : a.nvec;

@@ -18,8 +18,10 @@
 // per block and no separate arrival counter.  Two pass parities keep a slow
 // block's slot from being overwritten while it is still read.  The G blocks
 // of a sequence must be resident together (the host sizes G so that the
-// whole launch fits on the device); waits are bounded and a block that waits
-// too long sets SV_DERR_TIMEOUT and stops waiting.
+// whole launch fits on an otherwise idle device); waits are bounded and a
+// block that waits too long sets SV_DERR_TIMEOUT and stops waiting, leaving
+// that sequence's outputs invalid (a kernel on another stream that holds
+// compute units long enough can cause this).
 #pragma once
 
 #include "sv_device.hpp"
@@ -269,13 +271,24 @@ struct Exchange {
   uint64_t* slots;  // [2 parities][G][2 words] of this sequence, zero at launch
   int32_t* err;
   int G, g;
-  int pass;   // exchanges so far
-  bool late;  // a wait ran out: later exchanges do not wait (first wave only)
+  int pass;        // exchanges so far
+  bool late;       // a wait ran out: later exchanges do not wait (first wave only)
+  bool withhold;   // test switch: this block never publishes
+  uint32_t limit;  // polls before a wait gives up
 };
 
 constexpr int kSlotWords = 4;  // slot words per block of a launch (2 parities x 2 words)
 
-__device__ __forceinline__ Exchange make_exchange(void* slots, int32_t* err, int b, int G, int g) {
+// Workspace header words read by the waits (word 0 is the error word):
+// [1] the number of polls after which a wait gives up (0: kSpinLimit);
+// [2] nonzero: the last block of sequence 0 never publishes, so that its
+//     partners' waits run out -- a switch for tests of the bounded waits
+//     (every kernel still exits).  knobs may be null (the defaults).
+constexpr int kKnobSpin = 1;
+constexpr int kKnobWithhold = 2;
+
+__device__ __forceinline__ Exchange make_exchange(void* slots, int32_t* err, const uint32_t* knobs, int b, int G,
+                                                  int g) {
   Exchange x;
   x.slots = static_cast<uint64_t*>(slots) + (int64_t)b * kSlotWords * G;
   x.err = err;
@@ -283,6 +296,9 @@ __device__ __forceinline__ Exchange make_exchange(void* slots, int32_t* err, int
   x.g = g;
   x.pass = 0;
   x.late = false;
+  const uint32_t spin = knobs ? knobs[kKnobSpin] : 0u;
+  x.limit = spin ? spin : kSpinLimit;
+  x.withhold = knobs && knobs[kKnobWithhold] != 0u && b == 0 && G > 1 && g == G - 1;
   return x;
 }
 
@@ -306,7 +322,7 @@ __device__ __forceinline__ void exchange_n(Exchange& x, uint64_t p0, uint64_t p1
     uint64_t w0 = p0, w1 = p1;
     bool ok = (l >= x.G) || (l == x.g);
     if (x.G > 1) {
-      if (l == x.g) {
+      if (l == x.g && !x.withhold) {
         st_dev(set + 2 * l, p0 | tag);
         if (NW == 2) st_dev(set + 2 * l + 1, p1 | tag);
       }
@@ -318,7 +334,7 @@ __device__ __forceinline__ void exchange_n(Exchange& x, uint64_t p0, uint64_t p1
           ok = (w0 & kTagMask) == tag && (NW == 1 || (w1 & kTagMask) == tag);
         }
         if (__all(ok) || x.late) break;
-        if (++spins > kSpinLimit) {
+        if (++spins > x.limit) {
           if (l == 0) set_error(x.err, SV_DERR_TIMEOUT);
           x.late = true;
           break;

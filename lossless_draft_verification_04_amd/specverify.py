@@ -32,7 +32,7 @@ SV_OK, SV_EINVAL, SV_EDTYPE, SV_EALIGN, SV_EWORKSPACE, SV_EUNSUPPORTED, SV_EHIP 
 SV_F32, SV_BF16 = 0, 1
 (SV_OP_CHAIN, SV_OP_GREEDY, SV_OP_MULTI, SV_OP_TREE, SV_OP_FANOUT, SV_OP_CHAIN_PM, SV_OP_TREE_PM,
  SV_OP_CACHE, SV_OP_PRESTO, SV_OP_BRANCH) = range(10)
-DERR_TOKEN, DERR_TREE, DERR_FANOUT, DERR_ROW = 1, 2, 4, 8
+DERR_TOKEN, DERR_TREE, DERR_FANOUT, DERR_ROW, DERR_TIMEOUT = 1, 2, 4, 8, 16
 
 _P = ctypes.c_void_p
 _i32, _i64, _u32, _u64, _f32, _f64, _sz = (ctypes.c_int32, ctypes.c_int64, ctypes.c_uint32, ctypes.c_uint64,
@@ -81,6 +81,37 @@ class SpecVerifyError(RuntimeError):
 def _check(status, what):
     if status != SV_OK:
         raise SpecVerifyError(status, what)
+
+
+class DeviceError(RuntimeError):
+    """Device-side input error bits (DERR_*) reported by a call in checked mode."""
+
+    def __init__(self, flags, what):
+        names = [n for n, b in (("token", DERR_TOKEN), ("tree", DERR_TREE), ("fanout", DERR_FANOUT),
+                                ("row", DERR_ROW), ("timeout", DERR_TIMEOUT)) if flags & b]
+        super().__init__(f"{what}: device error word {flags} ({', '.join(names)}); outputs of the call are invalid")
+        self.flags = flags
+
+
+_CHECKED = False
+
+
+def set_checked(on: bool = True) -> None:
+    """Checked mode: after every call, synchronise its stream and raise DeviceError if the workspace's device
+    error word is set (and clear it).  Off by default: a call is then asynchronous and the word is read only
+    through sv_get_device_error."""
+    global _CHECKED
+    _CHECKED = bool(on)
+
+
+def _checked(device, what, workspace=None):
+    if not _CHECKED:
+        return
+    ws = workspace if workspace is not None else Workspace.get(device, 0)
+    flags = _i32(0)
+    _check(_lib.sv_get_device_error(_ptr(ws), ctypes.byref(flags), _stream(device)), "sv_get_device_error")
+    if flags.value:
+        raise DeviceError(flags.value, what)
 
 
 def _dtype_code(t: torch.Tensor) -> int:
@@ -172,6 +203,7 @@ def sv_verify_chain(tgt, drf, tok, T, seed=0, round_=0, want_pq=True, workspace=
     _check(_lib.sv_verify_chain(_ptr(tgt), _ptr(drf), dt, _row_stride(tgt, "tgt"), _row_stride(drf, "drf"),
                                 _ptr(tok), B, gamma, V, float(T), int(seed), int(round_), _ptr(out_n), _ptr(out_tok),
                                 _ptr(p), _ptr(q), _ptr(ws), ws.numel(), _stream(dev)), "sv_verify_chain")
+    _checked(dev, "sv_verify_chain", workspace)
     return dict(n=out_n, tok=out_tok, p=p, q=q)
 
 
@@ -216,6 +248,7 @@ def sv_verify_chain_pm(tgt, tok, T, seed=0, round_=0, want_p=True, workspace=Non
     _check(_lib.sv_verify_chain_pm(_ptr(tgt), dt, _row_stride(tgt, "tgt"), _ptr(tok), B, gamma, V, float(T),
                                    int(seed), int(round_), _ptr(out_n), _ptr(out_tok), _ptr(p), _ptr(ws),
                                    ws.numel(), _stream(dev)), "sv_verify_chain_pm")
+    _checked(dev, "sv_verify_chain_pm", workspace)
     return dict(n=out_n, tok=out_tok, p=p)
 
 
@@ -232,6 +265,7 @@ def sv_verify_greedy(tgt, tok, want_argmax=True, workspace=None):
     am = torch.empty(B, g1, dtype=torch.int32, device=dev) if want_argmax else None
     _check(_lib.sv_verify_greedy(_ptr(tgt), dt, _row_stride(tgt, "tgt"), _ptr(tok), B, gamma, V, _ptr(out_n),
                                  _ptr(out_tok), _ptr(am), _ptr(ws), ws.numel(), _stream(dev)), "sv_verify_greedy")
+    _checked(dev, "sv_verify_greedy", workspace)
     return dict(n=out_n, tok=out_tok, argmax=am)
 
 
@@ -254,6 +288,7 @@ def sv_verify_multi(tgt, drf, tok, T, seed=0, round_=0, want_pq=True, workspace=
                                 _ptr(tok), B, K, gamma, V, float(T), int(seed), int(round_), _ptr(out["k"]),
                                 _ptr(out["n"]), _ptr(out["tok"]), _ptr(out["n_cand"]), _ptr(out["p"]),
                                 _ptr(out["q"]), _ptr(ws), ws.numel(), _stream(dev)), "sv_verify_multi")
+    _checked(dev, "sv_verify_multi", workspace)
     return out
 
 
@@ -276,6 +311,7 @@ def sv_verify_tree(tgt, drf, node_tok, parent, max_depth, T, seed=0, round_=0, w
                                _ptr(node_tok), _ptr(parent), B, N, int(max_depth), V, float(T), int(seed),
                                int(round_), _ptr(out["len"]), _ptr(out["path"]), _ptr(out["tok"]), _ptr(out["p"]),
                                _ptr(out["q"]), _ptr(ws), ws.numel(), _stream(dev)), "sv_verify_tree")
+    _checked(dev, "sv_verify_tree", workspace)
     return out
 
 
@@ -295,6 +331,7 @@ def sv_verify_tree_pm(tgt, node_tok, parent, max_depth, T, seed=0, round_=0, wan
                                   int(max_depth), V, float(T), int(seed), int(round_), _ptr(out["len"]),
                                   _ptr(out["path"]), _ptr(out["tok"]), _ptr(out["p"]), _ptr(ws), ws.numel(),
                                   _stream(dev)), "sv_verify_tree_pm")
+    _checked(dev, "sv_verify_tree_pm", workspace)
     return out
 
 
@@ -310,6 +347,7 @@ def sv_fanout_topk(logits, F, F_max, want_vals=True, workspace=None):
     vals = torch.empty(R, F_max, dtype=torch.float32, device=dev) if want_vals else None
     _check(_lib.sv_fanout_topk(_ptr(logits), dt, _row_stride(logits, "logits"), R, V, _ptr(F), int(F_max), _ptr(ids),
                                _ptr(vals), _ptr(ws), ws.numel(), _stream(dev)), "sv_fanout_topk")
+    _checked(dev, "sv_fanout_topk", workspace)
     return ids, vals
 
 
@@ -328,6 +366,7 @@ def sv_cache_hit_test(drf, n, t, F=None, workspace=None):
     hit = torch.empty(B, dtype=torch.int32, device=dev) if F is not None else None
     _check(_lib.sv_cache_hit_test(_ptr(drf), dt, _row_stride(drf, "drf"), B, K1 - 1, V, _ptr(n), _ptr(t), _ptr(F),
                                   _ptr(rank), _ptr(hit), _ptr(ws), ws.numel(), _stream(dev)), "sv_cache_hit_test")
+    _checked(dev, "sv_cache_hit_test", workspace)
     return dict(rank=rank, hit=hit)
 
 
@@ -353,6 +392,7 @@ def sv_presto_score(tgt, drf, node_tok, parent, T, lam, k, b_top, want_scores=Tr
                                 _ptr(node_tok), _ptr(parent), B, N, V, float(T), _ptr(lam), lam.numel(), int(k),
                                 int(b_top), _ptr(out["s"]), _ptr(out["S"]), _ptr(out["node"]), _ptr(out["tok"]),
                                 _ptr(out["score"]), _ptr(ws), ws.numel(), _stream(dev)), "sv_presto_score")
+    _checked(dev, "sv_presto_score", workspace)
     return out
 
 
@@ -374,6 +414,7 @@ def sv_branch_fork(drf, tok, T, eps, k_max, cls=None, workspace=None):
     _check(_lib.sv_branch_fork(_ptr(drf), dt, _row_stride(drf, "drf"), _ptr(tok), _ptr(cls), B, gamma, V, float(T),
                                float(eps), int(k_max), _ptr(out["pos"]), _ptr(out["qb"]), _ptr(out["k"]),
                                _ptr(out["ids"]), _ptr(ws), ws.numel(), _stream(dev)), "sv_branch_fork")
+    _checked(dev, "sv_branch_fork", workspace)
     return out
 
 
