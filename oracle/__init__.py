@@ -78,6 +78,11 @@ def _load(path):
 def lib():
     global _lib
     if _lib is None:
+        # SV_ORACLE_LIB: another build of sv_oracle.cpp (the sanitizer test's ASan/UBSan build)
+        other = os.environ.get("SV_ORACLE_LIB")
+        if other:
+            _lib = _load(other)
+            return _lib
         if not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
             build(force=True)
         _lib = _load(_LIB)
