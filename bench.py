@@ -222,7 +222,7 @@ def bench_greedy(wl, steps, warmup):
     pos = p["B"] * p["gamma"]
     alg = p["B"] * (p["gamma"] + 1) * p["V"] * esize(p["dtype"])
     return dict(positions_per_call=pos, positions_per_s=pos / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
-                alg_bytes=alg, mean_accepted=float(out["n"].float().mean().item()), copies=len(copies))
+                alg_bytes=alg, mean_accepted=float(out["n"].float().mean().item()), copies=len(copies), _out=out)
 
 
 def bench_multi(wl, steps, warmup):
@@ -240,7 +240,7 @@ def bench_multi(wl, steps, warmup):
     alg = (B * K * g + B * g) * row + sum(2 if int(x) < g else 1 for x in n) * row
     pos = B * K * g
     return dict(positions_per_call=pos, positions_per_s=pos / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
-                alg_bytes=alg, mean_accepted=float(n.mean()), copies=len(copies))
+                alg_bytes=alg, mean_accepted=float(n.mean()), copies=len(copies), _out=out)
 
 
 def tree_alg_bytes(wl, out):
@@ -285,7 +285,7 @@ def bench_tree(wl, steps, warmup):
     wall, ev_ms = time_graphs(fn, copies, steps, warmup)
     pos = p["B"] * (p["N"] - 1)
     return dict(positions_per_call=pos, positions_per_s=pos / (wall * 1e-3), ms_per_step=wall, call_ms=ev_ms,
-                alg_bytes=alg, mean_accepted=float(out["len"].float().mean().item()), copies=len(copies))
+                alg_bytes=alg, mean_accepted=float(out["len"].float().mean().item()), copies=len(copies), _out=out)
 
 
 def bench_tree_pm(wl, steps, warmup):
@@ -437,13 +437,184 @@ def bench_fanout(wl, steps, warmup):
 
 
 def summarize(r):
-    d = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+    d = {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items() if not k.startswith("_")}
     d["achieved_GBps"] = round(r["alg_bytes"] / (r["call_ms"] * 1e-3) / 1e9, 1)
     d["frac_of_peak"] = round(d["achieved_GBps"] / HBM_PEAK_GBS, 4)
     return d
 
 
+# ------------------------------------------------------------------ acceptance statistics (outside the timed region)
+def acceptance_by_position(n, gamma):
+    """alpha_j, j = 1..gamma: the fraction of windows that reached position j (n >= j - 1) and accepted it
+    (n >= j); the draft-then-verify page §2.2's per-position acceptance, realised."""
+    n = np.asarray(n).reshape(-1)
+    out = []
+    for j in range(1, gamma + 1):
+        reached = int((n >= j - 1).sum())
+        out.append(round(float((n >= j).sum()) / reached, 4) if reached else None)
+    return out
+
+
+def overlap_by_position(T, pairs):
+    """beta_j = sum_v min(p_j(v), q_j(v)) = 1 - TV(p_j, q_j) (draft-then-verify page §2.2), the acceptance rate
+    of position j when the draft is drawn from q_j, from the stored logits in fp64.  pairs[j]: the (target row,
+    draft row) CPU tensors of position j."""
+    out = []
+    for j, rows in enumerate(pairs):
+        vals = []
+        for zt, zd in rows:
+            a = zt.to(torch.float64) / T
+            b = zd.to(torch.float64) / T
+            pa = torch.softmax(a, 0)
+            pb = torch.softmax(b, 0)
+            vals.append(float(torch.minimum(pa, pb).sum()))
+        out.append(round(float(np.mean(vals)), 4))
+    return out
+
+
+def chain_rounds(wl, g, rounds, seed=0):
+    """Accepted counts of `rounds` verification calls on one input copy (rounds 0.. : fresh uniforms)."""
+    T = float(np.float32(wl.params["T"]))
+    ns = [svx.sv_verify_chain(g["tgt"], g["drf"], g["tok"], T, seed=seed, round_=r, want_pq=False)["n"]
+          for r in range(rounds)]
+    return torch.stack(ns).cpu().numpy()
+
+
+def multi_rounds(wl, g, rounds, seed=0):
+    T = float(np.float32(wl.params["T"]))
+    ns = [svx.sv_verify_multi(g["tgt"], g["drf"], g["tok"], T, seed=seed, round_=r, want_pq=False)["n_cand"]
+          for r in range(rounds)]
+    return torch.stack(ns).cpu().numpy()
+
+
+STAT_KIND = {"chain_small_f32": "chain", "greedy_window": "greedy", "multi_candidate": "multi", "tree": "tree"}
+
+
+def chain_stats(wl, rounds):
+    """alpha_j over `rounds` rounds of fresh uniforms on the benchmarked inputs, the mean accepted length, and
+    beta_j of the stored rows (draft-then-verify page §2.2; the SpecDiff-2 page's position-wise acceptance)."""
+    p = wl.params
+    g = wl.to("cuda")
+    n = chain_rounds(wl, g, rounds)
+    tgt, drf = wl.tensors["tgt"], wl.tensors["drf"]
+    B, gamma = p["B"], p["gamma"]
+    T = float(np.float32(p["T"]))
+    beta = overlap_by_position(T, [[(tgt[b, j], drf[b, j]) for b in range(B)] for j in range(gamma)])
+    out = dict(rounds=rounds, alpha_j=acceptance_by_position(n, gamma), mean_accepted=round(float(n.mean()), 3),
+               beta_j=beta, beta_mean=round(float(np.mean(beta)), 4))
+    del g
+    return out
+
+
+def small_chain_beta(instances=64):
+    """beta of the small chain generator over `instances` seeds (one sequence each), per position and overall."""
+    rows = [[] for _ in range(W.CHAIN_SMALL["gamma"])]
+    for s in range(instances):
+        w = W.chain_normal(**W.CHAIN_SMALL, seed=1000 + s)
+        for j in range(W.CHAIN_SMALL["gamma"]):
+            rows[j].append((w.tensors["tgt"][0, j], w.tensors["drf"][0, j]))
+    beta = overlap_by_position(float(np.float32(W.CHAIN_SMALL["T"])), rows)
+    return dict(instances=instances, beta_j=beta, beta_mean=round(float(np.mean(beta)), 4))
+
+
+def greedy_stats(wl, rounds):
+    """Greedy verification has no uniforms: alpha_j is the realised match rate at position j over the window's
+    sequences, beside the generator's planted match probability 0.9 * 0.95^j."""
+    g = wl.to("cuda")
+    n = svx.sv_verify_greedy(g["tgt"], g["tok"], want_argmax=False)["n"].cpu().numpy()
+    gamma = wl.params["gamma"]
+    del g
+    return dict(alpha_j=acceptance_by_position(n, gamma), mean_accepted=round(float(n.mean()), 3),
+                planted_match_j=[round(0.9 * 0.95 ** j, 4) for j in range(1, gamma + 1)])
+
+
+def multi_stats(wl, rounds):
+    """alpha_j per candidate chain (all K candidates' accepted counts pooled) and of the kept candidate, over
+    `rounds` rounds of fresh uniforms, and the kept candidate's mean accepted length."""
+    g = wl.to("cuda")
+    T = float(np.float32(wl.params["T"]))
+    nc, kept = [], []
+    for r in range(rounds):
+        o = svx.sv_verify_multi(g["tgt"], g["drf"], g["tok"], T, seed=0, round_=r, want_pq=False)
+        nc.append(o["n_cand"].cpu().numpy())
+        kept.append(o["n"].cpu().numpy())
+    nc, kept = np.stack(nc), np.stack(kept)
+    gamma = wl.params["gamma"]
+    del g
+    return dict(rounds=rounds, alpha_j_per_candidate=acceptance_by_position(nc, gamma),
+                alpha_j_kept=acceptance_by_position(kept, gamma), mean_accepted_per_candidate=round(float(nc.mean()), 3),
+                mean_accepted_kept=round(float(kept.mean()), 3))
+
+
+def tree_stats(wl, rounds):
+    """Accepted depth over `rounds` rounds: the fraction of walks that reached depth d and went one deeper."""
+    g = wl.to("cuda")
+    p = wl.params
+    T = float(np.float32(p["T"]))
+    L = np.stack([svx.sv_verify_tree(g["tgt"], g["drf"], g["tok"], g["parent"], p["max_depth"], T, seed=0,
+                                     round_=r, want_pq=False)["len"].cpu().numpy() for r in range(rounds)])
+    del g
+    return dict(rounds=rounds, alpha_d=acceptance_by_position(L, p["max_depth"]), mean_depth=round(float(L.mean()), 3))
+
+
 # ------------------------------------------------------------------ CPU oracle
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def margin_counts(excepted, mismatch):
+    """Near-margin sequences (a decision with |r - a| < 1e-6 or a draw within 1e-6 of a CDF edge in the
+    oracle's fp64 arithmetic) and the GPU/oracle mismatches among them and outside them."""
+    excepted = np.asarray(excepted, bool)
+    mismatch = np.asarray(mismatch, bool)
+    return dict(sequences=int(excepted.size), near_margin=int(excepted.sum()),
+                mismatches_near_margin=int((mismatch & excepted).sum()),
+                mismatches_outside=int((mismatch & ~excepted).sum()))
+
+
+def oracle_parity(runs):
+    """The oracle on the exact inputs each benchmarked call verified (copy 0, same seed and round), compared
+    with the GPU outputs of that call."""
+    import oracle
+    res = {}
+    for name, (kind, wl, out) in runs.items():
+        p = wl.params
+        t0 = time.perf_counter()
+        if kind == "chain":
+            ref = oracle.verify_chain(W.to_numpy_logits(wl.tensors["tgt"]), W.to_numpy_logits(wl.tensors["drf"]),
+                                      wl.tensors["tok"].numpy(), float(np.float32(p["T"])), 0, 0, p["dtype"])
+            n, t = out["n"].cpu().numpy(), out["tok"].cpu().numpy()
+            r = margin_counts((ref["mdec"] < 1e-6) | (ref["mcdf"] < 1e-6), (n != ref["n"]) | (t != ref["t"]))
+        elif kind == "multi":
+            ref = oracle.verify_multi(W.to_numpy_logits(wl.tensors["tgt"]), W.to_numpy_logits(wl.tensors["drf"]),
+                                      wl.tensors["tok"].numpy(), float(np.float32(p["T"])), 0, 0, p["dtype"])
+            k, n, t = (out[x].cpu().numpy() for x in ("k", "n", "tok"))
+            r = margin_counts((ref["mdec"] < 1e-6) | (ref["mcdf"] < 1e-6),
+                              (k != ref["k"]) | (n != ref["n"]) | (t != ref["t"]))
+        elif kind == "tree":
+            ref = oracle.verify_tree(W.to_numpy_logits(wl.tensors["tgt"]), W.to_numpy_logits(wl.tensors["drf"]),
+                                     wl.tensors["tok"].numpy(), wl.tensors["parent"].numpy(), p["max_depth"],
+                                     float(np.float32(p["T"])), 0, 0, p["dtype"])
+            L, path, t = out["len"].cpu().numpy(), out["path"].cpu().numpy(), out["tok"].cpu().numpy()
+            r = margin_counts((ref["mdec"] < 1e-6) | (ref["mcdf"] < 1e-6),
+                              (L != ref["len"]) | (t != ref["t"]) | (path != ref["path"]).any(1))
+        else:  # greedy: no uniforms, so no margin; every output compared
+            ref = oracle.verify_greedy(W.to_numpy_logits(wl.tensors["tgt"]), wl.tensors["tok"].numpy(), p["dtype"])
+            n, t = out["n"].cpu().numpy(), out["tok"].cpu().numpy()
+            r = margin_counts(np.zeros(len(n), bool), (n != ref["n"]) | (t != ref["t"]))
+        r["oracle_s"] = round(time.perf_counter() - t0, 2)
+        res[name] = r
+        log(f"oracle parity {name}: {r}")
+    return res
+
+
 def cpu_baseline(wl, budget_s):
     import oracle
     p = wl.params
@@ -460,7 +631,53 @@ def cpu_baseline(wl, budget_s):
     pos = reps * p["B"] * p["gamma"]
     return dict(value=round(pos / el, 1), unit="positions/s", cores=1, kind="oracle",
                 sample=f"the full {p['B']}-sequence batch of the benchmarked workload, {reps} pass(es), {el:.1f} s, "
-                       f"single-threaded fp64 C++")
+                       f"single-threaded fp64 C++",
+                cpu_model=cpu_model(), nproc=os.cpu_count())
+
+
+# ------------------------------------------------------------------ read probe
+PROBE_SHAPES = [  # (label, blocks, mode, unroll, chunk bytes)
+    ("ranges_1024_u4", 1024, 0, 4, 0), ("ranges_2048_u4", 2048, 0, 4, 0), ("ranges_4096_u4", 4096, 0, 4, 0),
+    ("ranges_1024_u8", 1024, 0, 8, 0), ("ranges_2048_u2", 2048, 0, 2, 0),
+    ("xcd_ranges_1024_u4", 1024, 1, 4, 0), ("xcd_ranges_2048_u4", 2048, 1, 4, 0),
+    ("queue_1024_64K_u4", 1024, 2, 4, 1 << 16), ("queue_1024_128K_u4", 1024, 2, 4, 1 << 17),
+    ("queue_2048_32K_u4", 2048, 2, 4, 1 << 15), ("queue_768_64K_u8", 768, 2, 8, 1 << 16),
+]
+
+
+def read_probe(sizes_mb=(311, 642), reps=30, shapes=None):
+    """HBM read rate of sv_read_probe (the statistics kernels' load pattern) over buffers of the headline's row
+    bytes and the greedy window's, for several launch shapes, rotating copies so that the last-level cache cannot
+    serve repeats.  The statistics kernel's own shape is ranges_1024_u4."""
+    sink = torch.zeros(4, dtype=torch.int32, device="cuda")
+    res = {}
+    for mb in sizes_mb:
+        nbytes = mb * 1000 * 1000 // 16 * 16
+        copies = [torch.empty(nbytes // 4, dtype=torch.int32, device="cuda").random_() for _ in
+                  range(max(2, int(np.ceil(ROTATE_BYTES / nbytes))))]
+        for label, blocks, mode, unroll, chunk in (shapes or PROBE_SHAPES):
+            call = lambda i: svx.sv_read_probe(copies[i % len(copies)], sink, blocks, mode, unroll, chunk)
+            for i in range(6):
+                call(i)
+            torch.cuda.synchronize()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            for i in range(reps):
+                call(i)
+            b.record()
+            torch.cuda.synchronize()
+            us = a.elapsed_time(b) * 1e3 / reps
+            gbs = nbytes / (us * 1e-6) / 1e9
+            res[f"{mb}MB/{label}"] = dict(us=round(us, 2), GBps=round(gbs, 1), frac_of_peak=round(gbs / HBM_PEAK_GBS, 4))
+            log(f"read probe {mb} MB {label}: {us:.2f} us, {gbs:.1f} GB/s")
+        del copies
+        torch.cuda.empty_cache()
+    assert int(sink[1].item()) == 0 and int(sink[2].item()) == 0, "probe counters not returned to zero"
+    best = {}
+    for mb in sizes_mb:
+        k = max((x for x in res if x.startswith(f"{mb}MB/")), key=lambda x: res[x]["GBps"])
+        best[f"{mb}MB"] = dict(shape=k.split("/", 1)[1], **res[k])
+    return dict(shapes=res, best=best)
 
 
 def main():
@@ -474,6 +691,11 @@ def main():
     ap.add_argument("--eager", action="store_true", help="time eager calls instead of graph replays (profiling runs)")
     ap.add_argument("--copy-probe-mib", type=int, default=0, help="also run copies of this size (counter calibration)")
     ap.add_argument("--source-hash", action="store_true", help="print the kernel-source hash and exit")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="run only the HBM read probe (311 MB and 642 MB buffers) and print its JSON line")
+    ap.add_argument("--no-read-probe", action="store_true", help="leave the read probe out of the default run")
+    ap.add_argument("--no-stats", action="store_true", help="skip the acceptance statistics and the oracle parity")
+    ap.add_argument("--stat-rounds", type=int, default=32, help="verification rounds behind each alpha_j")
     args = ap.parse_args()
     if args.source_hash:
         print(kernel_source_hash())
@@ -486,19 +708,29 @@ def main():
         sys.exit(2)
     torch.cuda.init()
     dev_name = torch.cuda.get_device_name(0)
+    if args.read_probe:
+        log("read probe: sv_read_probe over rotating buffers")
+        print(json.dumps({"read_probe": read_probe(), "device": dev_name, "peak_GBps": HBM_PEAK_GBS}), flush=True)
+        return
 
     log("generating the batched chain workload (B=32, gamma=16, V=152064, bf16)")
     wl = W.chain_zipf(**W.CHAIN_BATCHED)
-    r, _ = bench_chain(wl, args.steps, args.warmup)
+    r, head_out = bench_chain(wl, args.steps, args.warmup)
     head = summarize(r)
     log(f"chain_batched: {head}")
+    runs = {"chain_batched": ("chain", wl, head_out)}
+    stats = {}
+    if not args.no_stats:
+        stats["chain_batched"] = chain_stats(wl, args.stat_rounds)
+        log(f"chain_batched statistics: {stats['chain_batched']}")
 
     variants = {}
     if not args.no_variants:
         steps_v = max(10, args.steps // 2)
         warm_v = max(3, args.warmup // 2)
         for name, mk, fn in [
-            ("chain_small_f32", lambda: W.chain_normal(**W.CHAIN_SMALL), lambda w: bench_chain(w, steps_v, warm_v)[0]),
+            ("chain_small_f32", lambda: W.chain_normal(**W.CHAIN_SMALL),
+             lambda w: (lambda ro: {**ro[0], "_out": ro[1]})(bench_chain(w, steps_v, warm_v))),
             ("chain_pm_batched", lambda: wl, lambda w: bench_chain_pm(w, steps_v, warm_v)),
             ("greedy_window", lambda: W.greedy_zipf(**W.GREEDY_WINDOW), lambda w: bench_greedy(w, steps_v, warm_v)),
             ("multi_candidate", lambda: W.multi_zipf(**W.MULTI_CAND), lambda w: bench_multi(w, steps_v, warm_v)),
@@ -506,8 +738,17 @@ def main():
         ]:
             log(f"generating {name}")
             w = mk()
-            variants[name] = summarize(fn(w))
+            res = fn(w)
+            variants[name] = summarize(res)
             log(f"{name}: {variants[name]}")
+            if not args.no_stats and name in STAT_KIND:
+                kind = STAT_KIND[name]
+                runs[name] = (kind, w, res["_out"])
+                stats[name] = {"chain": chain_stats, "greedy": greedy_stats, "multi": multi_stats,
+                               "tree": tree_stats}[kind](w, args.stat_rounds)
+                if name == "chain_small_f32":
+                    stats[name]["generator"] = small_chain_beta()
+                log(f"{name} statistics: {stats[name]}")
             if name == "chain_pm_batched":
                 log("generating the lookahead row for the cache hit test")
                 wc = W.chain_zipf(**W.CHAIN_BATCHED, lookahead_row=True)
@@ -534,6 +775,15 @@ def main():
         log("timing the CPU oracle")
         cpu = cpu_baseline(wl, args.cpu_budget)
         cpu["cores"] = 1
+        if not args.no_stats:
+            log("the oracle on the benchmarked inputs (near-margin decisions and mismatches)")
+            for name, rec in oracle_parity(runs).items():
+                stats.setdefault(name, {})["oracle_parity"] = rec
+
+    probe = None
+    if not args.no_read_probe:
+        log("read probe beside the headline (311 MB: the headline's streamed row bytes)")
+        probe = read_probe(sizes_mb=(311,))
 
     rl = roofline(r["alg_bytes"], r["call_ms"])
     rl["kernel"] = ("sv_verify_chain call (row-statistics kernel + draw kernel); duration = HIP events around the "
@@ -561,6 +811,8 @@ def main():
                    "eager_ms_per_step": round(r["eager_ms_per_step"], 5)},
         "roofline": rl,
         "cpu_baseline": cpu,
+        "statistics": stats or None,
+        "read_probe": probe,
         "variants": variants,
     }
     print(json.dumps(line), flush=True)

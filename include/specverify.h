@@ -383,6 +383,25 @@ sv_status sv_branch_fork(const void* drf, sv_dtype dt, int64_t stride, const int
                          float* out_qb, int32_t* out_k, int32_t* out_ids, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * Measurement aid (not a step of the method): reads the 16-byte vectors at
+ * `buf` (DEVICE, 16-byte aligned; `bytes` rounded down to a multiple of 16)
+ * with the row statistics kernels' load pattern -- 16-byte non-temporal
+ * loads, `unroll` (2, 4 or 8) in flight per thread and the next `unroll`
+ * issued before the current ones are used, blocks of 256 threads -- so that
+ * the HBM read rate a launch shape reaches on this device can be timed beside
+ * those kernels.  `mode` 0: `blocks` blocks over contiguous ranges; 1: the
+ * same ranges grouped so that each of the 8 XCDs streams one contiguous
+ * eighth (`blocks` a multiple of 8); 2: `blocks` persistent blocks taking
+ * chunks of `chunk_bytes` (a multiple of 16, at least 4096) from a
+ * device-wide counter.  `sink` (DEVICE, 3 x uint32, zero before the first
+ * call) holds a store sink and mode 2's counters, which the kernel returns to
+ * zero as it exits; calls that share a sink must not overlap.  SV_EINVAL on
+ * any other argument value.  Asynchronous on `stream`.
+ */
+sv_status sv_read_probe(const void* buf, size_t bytes, int32_t blocks, int32_t mode, int32_t unroll,
+                        size_t chunk_bytes, void* sink, void* stream);
+
+/*
  * Host helper, SSD / Saguaro review Theorem 12: F_k = ceil(F0 * a_p^(k/(1+r)))
  * for k < K; F_K uses the capped term F0 * a_p^(K/(1+r)) * (1-a_p)^(-1/(1+r))
  * when capped_last != 0, the plain term otherwise.  Writes K+1 values to the

@@ -63,6 +63,7 @@ _SIGS = {
     "sv_branch_fork": ([_P, _i32, _i64, _P, _P, _i32, _i32, _i32, _f32, _f32, _i32, _P, _P, _P, _P, _P, _sz, _P],
                        _i32),
     "sv_geometric_fanout": ([_i32, _f64, _f64, _i32, _i32, ctypes.POINTER(_i32)], _i32),
+    "sv_read_probe": ([_P, _sz, _i32, _i32, _i32, _sz, _P, _P], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -416,6 +417,14 @@ def sv_branch_fork(drf, tok, T, eps, k_max, cls=None, workspace=None):
                                _ptr(out["ids"]), _ptr(ws), ws.numel(), _stream(dev)), "sv_branch_fork")
     _checked(dev, "sv_branch_fork", workspace)
     return out
+
+
+def sv_read_probe(buf: torch.Tensor, sink: torch.Tensor, blocks=1024, mode=0, unroll=4, chunk_bytes=1 << 16):
+    """Read every 16-byte vector of buf in the statistics kernels' load pattern (a bandwidth probe).  sink: int32
+    [>= 3] on the device, zero before the first call (mode 2's counters; the kernel leaves them at zero)."""
+    assert sink.numel() >= 3 and sink.element_size() == 4 and sink.device == buf.device
+    _check(_lib.sv_read_probe(_ptr(buf), buf.numel() * buf.element_size(), int(blocks), int(mode), int(unroll),
+                              int(chunk_bytes), _ptr(sink), _stream(buf.device)), "sv_read_probe")
 
 
 def sv_geometric_fanout(F0, a_p, r, K, capped_last=False):

@@ -268,7 +268,9 @@ def presto(wl, lam, k, b_top, T=None):
         cls = np.zeros(b_top + extra, int)
         for i in range(1, n_ref):
             tol = SCORE_ULP * (pw(rn[b, i]) + pw(rn[b, i - 1]))
-            cls[i] = cls[i - 1] + (0 if abs(rs[b, i] - rs[b, i - 1]) <= tol else 1)
+            # equal scores (two -inf among them) tie; otherwise within the score tolerance
+            tied = rs[b, i] == rs[b, i - 1] or abs(rs[b, i] - rs[b, i - 1]) <= tol
+            cls[i] = cls[i - 1] + (0 if tied else 1)
         ref_score = {(int(rn[b, i]), int(rt[b, i])): rs[b, i] for i in range(n_ref)}
         for j, (u, t) in enumerate(got):
             assert (u, t) in ref_score, f"presto sequence {b}: gpu proposal {(u, t)} not among the oracle's"
