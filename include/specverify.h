@@ -58,15 +58,18 @@
  *    [0, V); every row has a finite logit; tree parent arrays valid.  A
  *    violation never causes an out-of-bounds access: it sets a bit in the
  *    error word and the affected decision rejects.
- *  - Cross-block waits.  The draw launch of the chain entry points (chain,
- *    point-mass chain, multi, noalloc) and the walk launch of the tree entry
- *    points split each sequence over G blocks that exchange partial sums and
- *    wait for each other.  G is chosen so that the whole launch is resident
- *    at once on an otherwise idle device.  A kernel running concurrently on
- *    another stream can keep some of those blocks from starting; the waiting
- *    blocks then give up after a bounded number of polls, set
- *    SV_DERR_TIMEOUT, and that call's outputs are invalid.  The call still
- *    completes and leaves the workspace ready for the next one.
+ *  - Cross-block waits.  The chain entry points (chain, point-mass chain,
+ *    multi, noalloc) run one launch whose draw blocks wait until every
+ *    statistics block of their sequence has counted its arrival; they and
+ *    the walk launch of the tree entry points split each sequence's final
+ *    draw over G blocks that exchange partial sums and wait for each other.
+ *    G is chosen so that all draw (walk) blocks are resident at once on an
+ *    otherwise idle device once the statistics blocks, which never wait,
+ *    are done.  A kernel running concurrently on another stream can keep
+ *    some of those blocks from starting; the waiting blocks then give up
+ *    after a bounded number of polls, set SV_DERR_TIMEOUT, and that call's
+ *    outputs are invalid.  The call still completes and leaves the
+ *    workspace ready for the next one.
  *  - Workspace header: 32-bit word 0 is the device error word; word 1 bounds
  *    the polls of a cross-block wait (0: the default, 2^22) and word 2 is a
  *    test switch that stops the last block of sequence 0 from publishing

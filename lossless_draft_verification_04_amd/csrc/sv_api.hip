@@ -116,14 +116,12 @@ sv_status plan_chain(sv_dtype dt, int32_t B, int32_t K, int32_t gamma, int32_t V
   const int64_t rows = (int64_t)B * (K + (pm ? 0 : 1)) * gamma;
   split(rows, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
   pl->grid1 = rows * pl->nch1;
-  if (pl->grid1 > INT32_MAX || (int64_t)B * kMaxG > INT32_MAX) return SV_EUNSUPPORTED;
+  if (pl->grid1 + (int64_t)B * kMaxG > INT32_MAX) return SV_EUNSUPPORTED;
   size_t off = kWsFixed;
   pl->off_part1 = off;
   off = align_up(off + (size_t)rows * pl->nch1 * sizeof(Partial), 256);
   pl->off_part2 = off;  // gathered logits of the drafted tokens (target, then draft)
   off = align_up(off + (size_t)2 * B * K * gamma * sizeof(float), 256);
-  pl->off_jobs = off;   // draw slot words
-  off = align_up(off + (size_t)B * kSlotWords * g_cap(B) * sizeof(uint64_t), 256);
   pl->bytes = off;
   return SV_OK;
 }
@@ -395,13 +393,25 @@ static sv_status verify_chain_like(const void* tgt, const void* drf, sv_dtype dt
   p.out_q = out_q;
   p.err = err ? err : reinterpret_cast<int32_t*>(w);
   p.knobs = err ? nullptr : reinterpret_cast<const uint32_t*>(w);
+  // counter region (zero between calls): arrivals and draw exits, B
+  // counters each (64 bytes apart for small batches), then the exchange
+  // slots, which the kernel also leaves zero
+  p.cnt = reinterpret_cast<uint32_t*>(w + kWsHeader);
+  p.cstride = B <= 512 ? 16 : 1;
+  p.slots = w + kWsHeader + align_up((size_t)8 * B * p.cstride, 256);
   p.part1 = w + pl.off_part1;
   p.zg = reinterpret_cast<float*>(w + pl.off_part2);
   p.zq = p.zg + (int64_t)B * K * gamma;
-  p.slots = w + pl.off_jobs;
   p.nch1 = pl.nch1;
+  p.grid1 = pl.grid1;
   p.pm = pm;
-  pick_slices(B, pl.nvec, chain_draw_capacity(dt, true, pm), chain_draw_capacity(dt, false, pm), &p.G, &p.held);
+  p.xcd = B % 8 == 0;
+  // all B * G draw blocks fit on the device at once (once the statistics
+  // blocks, which are placed first and never wait, have finished)
+  pick_slices(B, pl.nvec, chain_capacity(dt, true, pm), chain_capacity(dt, false, pm), &p.G, &p.held);
+  if (p.G > 1 && align_up((size_t)8 * B * p.cstride, 256) + (size_t)kSlotWords * 8 * B * p.G >
+                     kWsCounters * sizeof(uint32_t))
+    return SV_EUNSUPPORTED;  // not reached: B * G <= 4096 and B <= 2048 whenever G > 1
   p.vpc1 = pl.vpc1;
   p.nvec = pl.nvec;
   return launch_chain(p, dt, pl, static_cast<hipStream_t>(stream)) == hipSuccess ? SV_OK : SV_EHIP;
@@ -459,10 +469,11 @@ sv_status sv_verify_chain_noalloc(const void* tgt, const void* drf, sv_dtype dt,
                                        stream);
   void* ws = scratch_for_current_device();
   if (!ws) return SV_EHIP;
-  // every part, gathered logit and slot word the kernels read is written
-  // earlier in the same call (the slot words by the statistics launch), so
-  // the previous call's contents need no clearing; device errors go to
-  // out_err, or to the array's own error word, which is never read
+  // every part and gathered logit the kernel reads is written earlier in
+  // the same call, and its arrival counters and exchange slots start at
+  // zero (the array starts zeroed and every call leaves them zero), so the
+  // previous call's contents need no clearing; device errors go to out_err,
+  // or to the array's own error word, which is never read
   return verify_chain_like(tgt, drf, dt, tgt_stride, drf_stride, draft_tok, B, 1, gamma, V, T, seed, round, nullptr,
                            out_n, out_tok, nullptr, out_p, out_q, false, ws, kScratchBytes, stream, out_err);
 }

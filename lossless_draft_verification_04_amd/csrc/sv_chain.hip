@@ -4,20 +4,34 @@
 // residual norm(max(0, p - q)), bonus row p_{gamma+1}); SpecDiff-2 page, Core
 // method (K candidates over shared draft marginals, keep the longest streak).
 //
-// Two launches per call:
-//  1. stats: one block per (row part); every needed logit row (target rows
-//     1..gamma of every candidate, draft rows 1..gamma) is streamed once with
-//     16-byte loads and reduced to a mergeable (max, sum 2^(z c - c max))
-//     part.  No cross-block hand-off.
-//  2. draw: G blocks per sequence.  Every block merges the sequence's parts,
-//     gathers p(x_j) and q(x_j), draws the acceptance uniforms, finds each
-//     candidate's first rejection with a wave ballot and keeps the best
-//     candidate: the same decisions in every block (block 0 writes them).
-//     Each block then loads its slice of the rows the final draw needs into
-//     registers, the slice sums are exchanged, and the block whose slice
-//     holds u * S searches it (sv_walk.hpp).
-// The bonus row p_{gamma+1} is only read when every draft of the kept
-// candidate is accepted.
+// One launch per call, with two kinds of block.
+//  - Statistics blocks (the first grid1): one per row part.  Every needed
+//    logit row (target rows 1..gamma of every candidate, draft rows 1..gamma)
+//    is streamed once with 16-byte loads and reduced to a mergeable
+//    (max, sum 2^(z c - c max)) part; the first part of a row also gathers
+//    the drafted tokens' logits in it.  The block then counts one arrival
+//    for its sequence and exits (nothing waits).  When the batch is a
+//    multiple of 8 sequences, all statistics blocks of a sequence sit on one
+//    XCD (blocks are dealt to the 8 XCDs in turn), so sequences finish at
+//    their XCD's pace and most draws run while other XCDs still stream.
+//  - Draw blocks (the next B * G): G per sequence, spread over the XCDs.
+//    Each waits until its sequence's parts have all arrived, merges them,
+//    draws the acceptance uniforms, finds each candidate's first rejection
+//    with a wave ballot and keeps the best candidate (the same decisions in
+//    every block; one block stores them).  It then loads its slice of the
+//    rows the final draw needs into registers, the slice sums are exchanged,
+//    and the block whose slice holds u * S searches it (sv_walk.hpp).  The
+//    bonus row p_{gamma+1} is only read when every draft of the kept
+//    candidate is accepted.
+// Each XCD places its blocks in index order, so every statistics block is
+// placed before any draw block.  Draw blocks wait only on statistics blocks
+// (which never wait) and on their own sequence's draw blocks, and the host
+// keeps B * G within the blocks the device holds at once, so once the
+// statistics blocks are done every draw block is resident.  Every wait is
+// bounded.  The last draw block of a sequence to exit takes the arrivals
+// back off the counter and clears the sequence's exchange slots, so both
+// are zero when the next call starts (they live in the workspace's counter
+// region, which every entry point leaves zero).
 //
 // Point-mass mode (SpecDiff-2 page, Core method: the chosen draft token is
 // accepted with the verifier's own probability, the residual is resampled on
@@ -34,6 +48,16 @@ namespace sv {
 
 constexpr int kNT = 256;
 constexpr int kU = 4;
+
+__device__ __forceinline__ void st_dev32(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t ld_dev32(const uint32_t* p) {
+  return __hip_atomic_load(const_cast<uint32_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t add_dev32(uint32_t* p, uint32_t v) {
+  return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
 
 struct Job {
   int64_t rowP;  // target row of the draw
@@ -91,14 +115,18 @@ constexpr int direct_parts() {
   return PM ? 8 : 4;
 }
 
-// Parts [0, n) at gp, 1 <= n <= N, as 16-byte vectors: every load is
+// Parts [0, n) at gp, 1 <= n <= N, as 16-byte vectors, read with
+// device-scope loads (written by other blocks of this launch): every load is
 // issued at once and unconditionally (clamped indexes), so the merge waits
 // for one round trip.
 template <int N>
 __device__ __forceinline__ void load_parts(const Partial* gp, int n, u32x4 (&v)[N]) {
 #pragma unroll
-  for (int i = 0; i < N; ++i)
-    v[i] = *reinterpret_cast<const u32x4*>(gp + (i < n ? i : n - 1));  // written by the previous launch
+  for (int i = 0; i < N; ++i) {
+    const uint64_t* w = reinterpret_cast<const uint64_t*>(gp + (i < n ? i : n - 1));
+    const uint64_t w0 = ld_dev(w), w1 = ld_dev(w + 1);
+    v[i] = u32x4{(uint32_t)w0, (uint32_t)(w0 >> 32), (uint32_t)w1, (uint32_t)(w1 >> 32)};
+  }
 }
 
 // Row statistic from loaded parts (the arithmetic of merge_staged).
@@ -148,7 +176,9 @@ struct Decided {
   bool deferred;
 };
 
-// Decisions of sequence b (identical in every block that makes them).  Wave
+// Decisions of sequence b (identical in every block that makes them; parts
+// and gathered logits were written by statistics blocks of this launch and
+// are read with device-scope loads).  Wave
 // k takes candidate k: lane j merges the statistics of its target and draft
 // rows j, decides position j + 1, and the lane at the candidate's first
 // rejection (lane 0 when every draft is accepted) writes the candidate's
@@ -175,7 +205,7 @@ __device__ const Job* chain_decide(const ChainParams& a, int b, bool writer, Dec
 
   if (staged) {
     for (int i = threadIdx.x; i < nparts; i += kNT) {
-      const Partial pi = pb[i];  // written by the previous launch
+      const Partial pi = get_partial(pb + i);
       st.m[i] = pi.m;
       st.s[i] = pi.s;
     }
@@ -200,8 +230,8 @@ __device__ const Job* chain_decide(const ChainParams& a, int b, bool writer, Dec
       // the drafted token, its gathered logits (stats pass) and the rows'
       // parts: one round of independent loads
       x = a.tok[o];
-      const float zp = a.zg[o];
-      const float zq = PM ? 0.f : a.zq[o];
+      const float zp = __uint_as_float(ld_dev32(reinterpret_cast<const uint32_t*>(a.zg) + o));
+      const float zq = PM ? 0.f : __uint_as_float(ld_dev32(reinterpret_cast<const uint32_t*>(a.zq) + o));
       if (direct) {
         u32x4 vp[kDP], vq[PM ? 1 : kDP];
         load_parts(pb + first_p, a.nch1, vp);
@@ -292,13 +322,23 @@ __device__ void chain_outputs(const ChainParams& a, int b, const Decided& d) {
   }
 }
 
+// Statistics block: one row part, then one arrival for its sequence.
 template <int DT>
-__global__ __launch_bounds__(kNT) void chain_stats_kernel(ChainParams a) {
+__device__ void stats_role(const ChainParams& a) {
   const int rows = a.pm ? a.K * a.gamma : (a.K + 1) * a.gamma;
   const int64_t per_seq = (int64_t)rows * a.nch1;
   const int64_t bid = blockIdx.x;
-  const int b = (int)(bid / per_seq);
-  const int64_t rem = bid - (int64_t)b * per_seq;
+  int b;
+  int64_t rem;
+  if (a.xcd) {
+    // blocks are dealt to the 8 XCDs in turn: XCD x streams sequences x, x + 8, ...
+    const int64_t i = bid >> 3;
+    b = (int)(bid & 7) + 8 * (int)(i / per_seq);
+    rem = i % per_seq;
+  } else {
+    b = (int)(bid / per_seq);
+    rem = bid - (int64_t)b * per_seq;
+  }
   const int lr = (int)(rem / a.nch1);
   const int ch = (int)(rem - (int64_t)lr * a.nch1);
   const int Kg = a.K * a.gamma;
@@ -327,9 +367,15 @@ __global__ __launch_bounds__(kNT) void chain_stats_kernel(ChainParams a) {
   const int64_t v1 = v0 + a.vpc1 < a.nvec ? v0 + a.vpc1 : a.nvec;
   uint32_t zbits = 0;
   const Partial part = range_stats<DT, kNT, kU>(row, a.V, v0, v1, a.c, zo >= 0, x, &zbits);
-  if (threadIdx.x == 0) put_partial(static_cast<Partial*>(a.part1) + (int64_t)b * per_seq + (int64_t)lr * a.nch1 + ch, part);
-  if (zo >= 0) (is_tgt ? a.zg : a.zq)[zo] = (x >= 0 && x < a.V) ? bits_value<DT>(zbits) : 0.f;
-  zero_slots(a.slots, (int64_t)a.B * kSlotWords * a.G, bid, kNT);  // for the draw launch
+  // every store of this block is made by wave 0 (K <= 64 gathering threads)
+  if (threadIdx.x < kWave) {
+    if (threadIdx.x == 0) put_partial(static_cast<Partial*>(a.part1) + (int64_t)b * per_seq + (int64_t)lr * a.nch1 + ch, part);
+    if (zo >= 0)
+      st_dev32(reinterpret_cast<uint32_t*>(is_tgt ? a.zg : a.zq) + zo,
+               __float_as_uint((x >= 0 && x < a.V) ? bits_value<DT>(zbits) : 0.f));
+    __builtin_amdgcn_s_waitcnt(0);  // the wave's stores are complete (device-visible)
+    if (threadIdx.x == 0) add_dev32(a.cnt + (int64_t)b * a.cstride, 1u);
+  }
 }
 
 template <int DT>
@@ -356,21 +402,37 @@ __device__ DrawSpec job_spec(const ChainParams& a, const Job& jb, float cm_plain
   return sp;
 }
 
-// Draw: G blocks per sequence, each deciding the sequence and owning one
-// slice of the draw row(s).
+// Wave 0 waits until every part of sequence b has arrived; false if the wait
+// ran out.  Far from done (under half the parts in), one poll per couple of
+// microseconds.
+__device__ bool wait_parts(const ChainParams& a, int b, uint32_t limit) {
+  const uint32_t* arrivals = a.cnt + (int64_t)b * a.cstride;
+  const uint32_t total = (uint32_t)(a.pm ? a.K * a.gamma : (a.K + 1) * a.gamma) * (uint32_t)a.nch1;
+  uint32_t spins = 0;
+  for (;;) {
+    uint32_t c = 0;
+    if ((threadIdx.x & (kWave - 1)) == 0) c = ld_dev32(arrivals);
+    c = __builtin_amdgcn_readfirstlane(c);
+    if (c >= total) return true;
+    const bool near = 2u * c >= total;
+    spins += near ? 1u : 8u;
+    if (spins > limit) return false;
+    if (near)
+      __builtin_amdgcn_s_sleep(2);
+    else
+      __builtin_amdgcn_s_sleep(63);
+  }
+}
+
+// The decisions and the draw of one draw block (all its waits bounded).
 template <int DT, bool HELD, bool PM>
-__global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
-  const int b = blockIdx.x / a.G;
-  const int g = blockIdx.x - b * a.G;
-  __shared__ uint64_t s_words[kMaxG], s_w1[kMaxG];
-  SliceSums ss;  // the slices' values of the last exchange
-  __shared__ Decided dec;
+__device__ void draw_body(const ChainParams& a, int b, int g, Exchange& x, Decided& dec, uint64_t* s_words,
+                          uint64_t* s_w1, SliceSums& ss) {
   const Job* pj = chain_decide<DT, PM>(a, b, g == 0, dec);
   const Job jb = *pj;
   const int64_t spv = (a.nvec + a.G - 1) / a.G;
   const int64_t v0 = (int64_t)g * spv < a.nvec ? (int64_t)g * spv : a.nvec;
   const int64_t v1 = v0 + spv < a.nvec ? v0 + spv : a.nvec;
-  Exchange x = make_exchange(a.slots, a.err, a.knobs, b, a.G, g);
   const bool resid = !PM && jb.rowQ >= 0 && jb.SP > 0.0 && jb.SQ > 0.0;
   const bool pm_resid = PM && jb.SP > 0.0;  // a rejection, in a row with mass
   DrawSpec sp = job_spec<DT>(a, jb, 0.f);
@@ -421,41 +483,86 @@ __global__ __launch_bounds__(kNT) void chain_draw_kernel(ChainParams a) {
   }
 }
 
+// Draw block g of sequence b: decides the sequence and owns one slice of the
+// draw row(s).
+template <int DT, bool HELD, bool PM>
+__device__ void draw_role(const ChainParams& a, int d, Decided& dec) {
+  const int b = d / a.G;
+  const int g = d - b * a.G;
+  __shared__ uint64_t s_words[kMaxG], s_w1[kMaxG];
+  __shared__ int s_ok, s_last;
+  SliceSums ss;  // the slices' values of the last exchange
+  Exchange x = make_exchange(a.slots, a.err, a.knobs, b, a.G, g);
+  if (threadIdx.x < kWave) {
+    const bool ok = wait_parts(a, b, x.limit);
+    if (threadIdx.x == 0) {
+      s_ok = ok;
+      if (!ok) set_error(a.err, SV_DERR_TIMEOUT);
+    }
+  }
+  __syncthreads();
+  if (s_ok) draw_body<DT, HELD, PM>(a, b, g, x, dec, s_words, s_w1, ss);
+  // exits: the last draw block of the sequence takes its arrivals back off
+  // the counter (late ones, after a timed-out wait, bring it to zero too)
+  // and clears its exchange slots for the next call
+  if (threadIdx.x == 0) {
+    // wave 0 made every slot store of this block: they are complete before
+    // the exit counts, so the clearing below lands after them
+    __builtin_amdgcn_s_waitcnt(0);
+    uint32_t* exits = a.cnt + (int64_t)(a.B + b) * a.cstride;
+    s_last = add_dev32(exits, 1u) == (uint32_t)a.G - 1u;
+    if (s_last) {
+      st_dev32(exits, 0u);
+      const uint32_t total = (uint32_t)(a.pm ? a.K * a.gamma : (a.K + 1) * a.gamma) * (uint32_t)a.nch1;
+      __hip_atomic_fetch_sub(a.cnt + (int64_t)b * a.cstride, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+  if (s_last && a.G > 1) {
+    uint64_t* slots = static_cast<uint64_t*>(a.slots) + (int64_t)b * kSlotWords * a.G;
+    for (int i = threadIdx.x; i < kSlotWords * a.G; i += kNT) st_dev(slots + i, 0ull);
+  }
+}
+
+template <int DT, bool HELD, bool PM>
+__global__ __launch_bounds__(kNT) void chain_kernel(ChainParams a) {
+  __shared__ Decided dec;
+  if ((int64_t)blockIdx.x < a.grid1)
+    stats_role<DT>(a);
+  else
+    draw_role<DT, HELD, PM>(a, (int)((int64_t)blockIdx.x - a.grid1), dec);
+}
+
 template <int DT>
-hipError_t launch_chain_t(const ChainParams& p, const Plan& plan, hipStream_t s) {
-  chain_stats_kernel<DT><<<dim3((unsigned)plan.grid1), dim3(kNT), 0, s>>>(p);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  // B * G <= the blocks the device holds at once (chosen by the caller): a
-  // sequence's blocks are resident together on an otherwise idle device,
-  // and their waits are bounded either way
-  const dim3 grid((unsigned)p.B * p.G);
+hipError_t launch_chain_t(const ChainParams& p, hipStream_t s) {
+  const dim3 grid((unsigned)(p.grid1 + (int64_t)p.B * p.G));
   if (p.pm) {
     if (p.held)
-      chain_draw_kernel<DT, true, true><<<grid, dim3(kNT), 0, s>>>(p);
+      chain_kernel<DT, true, true><<<grid, dim3(kNT), 0, s>>>(p);
     else
-      chain_draw_kernel<DT, false, true><<<grid, dim3(kNT), 0, s>>>(p);
+      chain_kernel<DT, false, true><<<grid, dim3(kNT), 0, s>>>(p);
   } else {
     if (p.held)
-      chain_draw_kernel<DT, true, false><<<grid, dim3(kNT), 0, s>>>(p);
+      chain_kernel<DT, true, false><<<grid, dim3(kNT), 0, s>>>(p);
     else
-      chain_draw_kernel<DT, false, false><<<grid, dim3(kNT), 0, s>>>(p);
+      chain_kernel<DT, false, false><<<grid, dim3(kNT), 0, s>>>(p);
   }
   return hipGetLastError();
 }
 
 hipError_t launch_chain(const ChainParams& p, sv_dtype dt, const Plan& plan, hipStream_t s) {
-  return dt == SV_BF16 ? launch_chain_t<SV_BF16>(p, plan, s) : launch_chain_t<SV_F32>(p, plan, s);
+  (void)plan;
+  return dt == SV_BF16 ? launch_chain_t<SV_BF16>(p, s) : launch_chain_t<SV_F32>(p, s);
 }
 
 template <int DT, bool PM>
-const void* draw_fn(bool held) {
-  return held ? reinterpret_cast<const void*>(&chain_draw_kernel<DT, true, PM>)
-              : reinterpret_cast<const void*>(&chain_draw_kernel<DT, false, PM>);
+const void* chain_fn(bool held) {
+  return held ? reinterpret_cast<const void*>(&chain_kernel<DT, true, PM>)
+              : reinterpret_cast<const void*>(&chain_kernel<DT, false, PM>);
 }
 
-// Blocks of the draw kernel the device holds at once.
-int chain_draw_capacity(sv_dtype dt, bool held, bool pm) {
+// Blocks of the chain kernel the device holds at once.
+int chain_capacity(sv_dtype dt, bool held, bool pm) {
   static int cache[2][2][2][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
@@ -463,9 +570,9 @@ int chain_draw_capacity(sv_dtype dt, bool held, bool pm) {
   if (c == 0) {
     const void* fn;
     if (dt == SV_BF16)
-      fn = pm ? draw_fn<SV_BF16, true>(held) : draw_fn<SV_BF16, false>(held);
+      fn = pm ? chain_fn<SV_BF16, true>(held) : chain_fn<SV_BF16, false>(held);
     else
-      fn = pm ? draw_fn<SV_F32, true>(held) : draw_fn<SV_F32, false>(held);
+      fn = pm ? chain_fn<SV_F32, true>(held) : chain_fn<SV_F32, false>(held);
     c = device_capacity(fn, kNT, dev);
   }
   return c;

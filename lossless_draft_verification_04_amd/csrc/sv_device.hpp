@@ -307,79 +307,108 @@ struct RowStat {
   double S;  // sum_v 2^(z_v c - cm); 0 if the row has no finite logit
 };
 
+// Buffer resource over `bytes` bytes at `base` (raw, untyped: the gfx9
+// word-3 format).  A load at an offset past `bytes` returns zeros without a
+// memory access, so a prefetch past the end of a range needs no clamp.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t range_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
+}
+// One 16-byte non-temporal load at byte offset `off` of a range.
+__device__ __forceinline__ u32x4 load_range(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2);
+}
+
+// Fold U vectors of one row into this thread's running (m, s): m the
+// largest logit so far, s the sum of 2^(z c - c m).  MASK: vectors whose
+// index first + u * NT is past the range (nv) count as -inf.
+template <int DT, int NT, int U, bool MASK>
+__device__ __forceinline__ void fold_vectors(const u32x4 (&d)[U], int64_t first, int64_t nv, float c, float& m,
+                                             float& s) {
+  constexpr int E = Fmt<DT>::kPerVec;
+  float x[U * E];
+#pragma unroll
+  for (int u = 0; u < U; ++u) unpack<DT>(d[u], x + u * E);
+  if constexpr (MASK) {
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (first + (int64_t)u * NT >= nv)
+#pragma unroll
+        for (int e = 0; e < E; ++e) x[u * E + e] = kNegInf;
+  }
+  float gm = x[0];
+#pragma unroll
+  for (int e = 1; e < U * E; ++e) gm = fmaxf(gm, x[e]);
+  if (gm > m) {
+    s *= fast_exp2(c * m - c * gm);
+    m = gm;
+  }
+  if (m != kNegInf) {
+    const float cm = c * m;
+    float t[U * E];
+#pragma unroll
+    for (int e = 0; e < U * E; ++e) t[e] = fast_exp2(__builtin_fmaf(x[e], c, -cm));
+#pragma unroll
+    for (int w = U * E / 2; w > 0; w >>= 1)
+#pragma unroll
+      for (int e = 0; e < w; ++e) t[e] += t[e + w];
+    s += t[0];
+  }
+}
+
 // Online (max, sum) over vectors [v0, v1) of one row by a block of NT
-// threads; U vectors in flight per thread.  Every thread returns the
-// block's partial.  A thread with `gather` set also loads the bits of
-// element gx of the row (clamped into [0, V)) into *gbits; the load is
-// issued after the first vectors of the stream, so waiting for gx (loaded by
-// the caller) does not hold back the stream, and nothing waits for the
-// gathered bits before the caller uses them.
+// threads; U vectors in flight per thread, the next U issued before the
+// current ones are folded.  Every thread runs the same number of groups of
+// U * NT vectors (the last one masked), so no thread ends with a serial
+// tail of dependent loads; prefetches past the range read zeros from the
+// buffer resource and are never folded.  Every thread returns the block's
+// partial.  A thread with `gather` set also loads the bits of element gx of
+// the row (clamped into [0, V)) into *gbits; the load is issued after the
+// first vectors of the stream, so waiting for gx (loaded by the caller) does
+// not hold back the stream, and nothing waits for the gathered bits before
+// the caller uses them.
 template <int DT, int NT, int U>
 __device__ Partial range_stats(const void* row, int V, int64_t v0, int64_t v1, float c, bool gather = false,
                                int32_t gx = 0, uint32_t* gbits = nullptr) {
   constexpr int E = Fmt<DT>::kPerVec;
+  constexpr int64_t kGroup = (int64_t)U * NT;
   const int tid = threadIdx.x;
   const int64_t nfull = V / E;
   const int64_t vf = v1 < nfull ? v1 : nfull;
   float m = kNegInf;
   float s = 0.f;
-  int64_t v = v0 + tid;
   bool gathered = !gather;
-  if (v + (int64_t)(U - 1) * NT < vf) {
-    // software pipelined: the next U vectors are in flight while these are
-    // reduced (the prefetch past the end is clamped to the last full vector)
+  if (vf > v0) {
+    // full vectors [v0, vf): at most 2^24 / 4 vectors, so byte offsets fit 32 bits
+    const int64_t nv = vf - v0;
+    const __amdgpu_buffer_rsrc_t rs = range_rsrc(static_cast<const u32x4*>(row) + v0, (uint32_t)(nv * 16));
+    const int64_t full = nv / kGroup;
+    uint32_t off = (uint32_t)tid * 16u;
     u32x4 cur[U];
 #pragma unroll
-    for (int u = 0; u < U; ++u) cur[u] = load_vec(row, v + (int64_t)u * NT);
+    for (int u = 0; u < U; ++u) cur[u] = load_range(rs, off + (uint32_t)(u * NT * 16));
     if (!gathered) {
       *gbits = load_bits<DT>(row, gx >= 0 && gx < V ? gx : 0);
       gathered = true;
     }
-    for (;;) {
-      const int64_t vn = v + (int64_t)U * NT;
-      const bool more = vn + (int64_t)(U - 1) * NT < vf;
+    for (int64_t k = 0; k < full; ++k) {
+      off += (uint32_t)(kGroup * 16);
       u32x4 nxt[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        const int64_t a = vn + (int64_t)u * NT;
-        nxt[u] = load_vec(row, a < vf ? a : vf - 1);
-      }
-      float x[U * E];
-#pragma unroll
-      for (int u = 0; u < U; ++u) unpack<DT>(cur[u], x + u * E);
-      float gm = x[0];
-#pragma unroll
-      for (int e = 1; e < U * E; ++e) gm = fmaxf(gm, x[e]);
-      if (gm > m) {
-        s *= fast_exp2(c * m - c * gm);
-        m = gm;
-      }
-      if (m != kNegInf) {
-        const float cm = c * m;
-        float t[U * E];
-#pragma unroll
-        for (int e = 0; e < U * E; ++e) t[e] = fast_exp2(__builtin_fmaf(x[e], c, -cm));
-#pragma unroll
-        for (int w = U * E / 2; w > 0; w >>= 1)
-#pragma unroll
-          for (int e = 0; e < w; ++e) t[e] += t[e + w];
-        s += t[0];
-      }
-      v = vn;
-      if (!more) break;
+      for (int u = 0; u < U; ++u) nxt[u] = load_range(rs, off + (uint32_t)(u * NT * 16));
+      fold_vectors<DT, NT, U, false>(cur, 0, nv, c, m, s);
 #pragma unroll
       for (int u = 0; u < U; ++u) cur[u] = nxt[u];
     }
+    if (full * kGroup < nv) fold_vectors<DT, NT, U, true>(cur, full * kGroup + tid, nv, c, m, s);
   }
   if (!gathered) *gbits = load_bits<DT>(row, gx >= 0 && gx < V ? gx : 0);
-  for (; v < v1; v += NT) {
+  if (v1 > nfull && tid == 0) {
+    // the row's last vector, holding fewer than E logits (v1 = nfull + 1)
     float x[E];
-    unpack<DT>(load_vec(row, v), x);
-    if (v >= nfull) {
+    unpack<DT>(load_vec(row, nfull), x);
 #pragma unroll
-      for (int e = 0; e < E; ++e)
-        if (v * E + e >= V) x[e] = kNegInf;
-    }
+    for (int e = 0; e < E; ++e)
+      if (nfull * E + e >= V) x[e] = kNegInf;
     float gm = x[0];
 #pragma unroll
     for (int e = 1; e < E; ++e) gm = fmaxf(gm, x[e]);

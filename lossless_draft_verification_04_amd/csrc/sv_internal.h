@@ -32,14 +32,18 @@ struct ChainParams {
   float* out_q;
   int32_t* err;
   const uint32_t* knobs;  // workspace header (wait bound, test switch), or null
+  uint32_t* cnt;   // counter region: arrivals of sequence b at [b * cstride], draw exits at [(B + b) * cstride]
+  int32_t cstride;
   void* part1;     // stats parts, [B][rows][nch1]
   float* zg;       // target logits of the drafted tokens, [B][K][gamma]
   float* zq;       // draft logits of the drafted tokens, [B][K][gamma]
-  void* slots;     // draw slot words, [B][G][4], zeroed by the stats launch
+  void* slots;     // draw slot words, [B][G][4], in the counter region (zero between calls)
   int32_t nch1;
   int32_t G;       // draw blocks per sequence
+  int64_t grid1;   // statistics blocks (the draw blocks follow them)
   bool held;       // slices of at most kSliceTiles tiles, held in registers
   bool pm;         // point-mass acceptance: target rows only
+  bool xcd;        // a sequence's statistics blocks share one XCD (B a multiple of 8)
   int64_t vpc1, nvec;
 };
 
@@ -184,9 +188,9 @@ hipError_t launch_presto(const PrestoParams& p, const TreeParams& stats, sv_dtyp
                          hipStream_t s);
 hipError_t launch_fill_zero(void* ws, size_t bytes, hipStream_t s);
 
-// Blocks of one launch of the draw / walk kernel (held or streamed slices)
-// the current device holds at once (0 if unknown).
-int chain_draw_capacity(sv_dtype dt, bool held, bool pm);
+// Blocks of one launch of the chain kernel or the walk kernel (held or
+// streamed slices) the current device holds at once (0 if unknown).
+int chain_capacity(sv_dtype dt, bool held, bool pm);
 int tree_walk_capacity(sv_dtype dt, bool held, bool pm);
 
 // Blocks of kernel fn (block of nt threads) device dev holds at once.

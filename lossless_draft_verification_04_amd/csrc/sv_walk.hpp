@@ -10,8 +10,9 @@
 // and the blocks exchange the slice sums; the block whose slice holds u * S
 // searches it.
 //
-// Exchange: two 64-bit slot words per (sequence, pass parity, block), zeroed
-// by the call's first launch.  After a pass each block stores its value(s)
+// Exchange: two 64-bit slot words per (sequence, pass parity, block), zero
+// when the exchange starts (the tree's first launch zeroes them; the chain
+// kernel keeps its slots zero between calls).  After a pass each block stores its value(s)
 // with the pass's tag in the low byte (a double with its 8 lowest mantissa
 // bits replaced, or a float in the high half) and its first wave polls the G
 // slots of the pass until every tag matches: one or two device-scope stores
@@ -268,7 +269,7 @@ struct Slice {
 
 // Exchange state of one block.
 struct Exchange {
-  uint64_t* slots;  // [2 parities][G][2 words] of this sequence, zero at launch
+  uint64_t* slots;  // [2 parities][G][2 words] of this sequence, zero at the start
   int32_t* err;
   int G, g;
   int pass;        // exchanges so far
