@@ -65,7 +65,7 @@ __device__ RowStat staged_stat(const Partial* st, bool staged, const Partial* gp
   double S = 0.0;
   if (M != kNegInf)
     for (int i = 0; i < n; ++i)
-      if (st[first + i].m != kNegInf) S += st[first + i].s * exp2((double)(c * st[first + i].m) - (double)r.cm);
+      if (st[first + i].m != kNegInf) S += st[first + i].s * exp2_d((double)(c * st[first + i].m) - (double)r.cm);
   r.S = S;
   return r;
 }

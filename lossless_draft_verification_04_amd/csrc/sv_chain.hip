@@ -102,7 +102,7 @@ __device__ __forceinline__ RowStat merge_staged(const StagedParts& st, bool stag
   r.cm = c * M;
   double S = 0.0;
   for (int i = 0; i < n; ++i)
-    if (st.m[first + i] != kNegInf) S += st.s[first + i] * exp2((double)(c * st.m[first + i]) - (double)r.cm);
+    if (st.m[first + i] != kNegInf) S += st.s[first + i] * exp2_d((double)(c * st.m[first + i]) - (double)r.cm);
   r.S = S;
   return r;
 }
@@ -158,7 +158,7 @@ __device__ __forceinline__ RowStat merge_loaded(const u32x4 (&v)[N], int n, floa
   double S = 0.0;
 #pragma unroll
   for (int i = 0; i < N; ++i)
-    if (i < n && m[i] != kNegInf) S += sum[i] * exp2((double)(c * m[i]) - (double)r.cm);
+    if (i < n && m[i] != kNegInf) S += sum[i] * exp2_d((double)(c * m[i]) - (double)r.cm);
   r.S = S;
   return r;
 }
@@ -203,6 +203,16 @@ __device__ const Job* chain_decide(const ChainParams& a, int b, bool writer, Dec
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
 
+  // the first candidate's token and gathered logits are loaded before the
+  // parts are staged, so that both travel in one round of loads
+  int32_t x_pre = 0;
+  uint32_t zp_pre = 0, zq_pre = 0;
+  if (wave < a.K && lane < a.gamma) {
+    const int64_t o = ((int64_t)b * a.K + wave) * a.gamma + lane;
+    x_pre = a.tok[o];
+    zp_pre = ld_dev32(reinterpret_cast<const uint32_t*>(a.zg) + o);
+    if (!PM) zq_pre = ld_dev32(reinterpret_cast<const uint32_t*>(a.zq) + o);
+  }
   if (staged) {
     for (int i = threadIdx.x; i < nparts; i += kNT) {
       const Partial pi = get_partial(pb + i);
@@ -229,10 +239,18 @@ __device__ const Job* chain_decide(const ChainParams& a, int b, bool writer, Dec
       const double r = uniform24(a.seed, (uint32_t)(j + 1), (uint32_t)b, (uint32_t)k, a.round, 0);
       // the drafted token, its gathered logits (stats pass) and the rows'
       // parts: one round of independent loads
-      x = a.tok[o];
-      const float zp = __uint_as_float(ld_dev32(reinterpret_cast<const uint32_t*>(a.zg) + o));
-      const float zq = PM ? 0.f : __uint_as_float(ld_dev32(reinterpret_cast<const uint32_t*>(a.zq) + o));
-      if (direct) {
+      const bool pre = k == wave;
+      x = pre ? x_pre : a.tok[o];
+      const float zp = __uint_as_float(pre ? zp_pre : ld_dev32(reinterpret_cast<const uint32_t*>(a.zg) + o));
+      const float zq =
+          PM ? 0.f : __uint_as_float(pre ? zq_pre : ld_dev32(reinterpret_cast<const uint32_t*>(a.zq) + o));
+      if (a.nch1 == 1) {  // whole rows: one part each
+        u32x4 vp[1], vq[1];
+        load_parts(pb + first_p, 1, vp);
+        if constexpr (!PM) load_parts(pb + first_q, 1, vq);
+        sp = merge_loaded(vp, 1, a.c);
+        if constexpr (!PM) sq = merge_loaded(vq, 1, a.c);
+      } else if (direct) {
         u32x4 vp[kDP], vq[PM ? 1 : kDP];
         load_parts(pb + first_p, a.nch1, vp);
         if constexpr (!PM) load_parts(pb + first_q, a.nch1, vq);
@@ -403,8 +421,8 @@ __device__ DrawSpec job_spec(const ChainParams& a, const Job& jb, float cm_plain
 }
 
 // Wave 0 waits until every part of sequence b has arrived; false if the wait
-// ran out.  Far from done (under half the parts in), one poll per couple of
-// microseconds.
+// ran out.  Far from done (under half the parts in), polls are spaced about
+// half a microsecond apart.
 __device__ bool wait_parts(const ChainParams& a, int b, uint32_t limit) {
   const uint32_t* arrivals = a.cnt + (int64_t)b * a.cstride;
   const uint32_t total = (uint32_t)(a.pm ? a.K * a.gamma : (a.K + 1) * a.gamma) * (uint32_t)a.nch1;
@@ -415,12 +433,37 @@ __device__ bool wait_parts(const ChainParams& a, int b, uint32_t limit) {
     c = __builtin_amdgcn_readfirstlane(c);
     if (c >= total) return true;
     const bool near = 2u * c >= total;
-    spins += near ? 1u : 8u;
+    spins += near ? 1u : 4u;
     if (spins > limit) return false;
     if (near)
       __builtin_amdgcn_s_sleep(2);
     else
-      __builtin_amdgcn_s_sleep(63);
+      __builtin_amdgcn_s_sleep(16);
+  }
+}
+
+// A draw block of sequence b is done with the sequence's counters and
+// exchange slots (block-uniform call).  The last one takes the arrivals back
+// off the counter (late ones, after a timed-out wait, bring it to zero too)
+// and clears the exchange slots for the next call.
+__device__ void draw_exit(const ChainParams& a, int b) {
+  __shared__ int s_last;
+  if (threadIdx.x == 0) {
+    // wave 0 made every slot store of this block: they are complete before
+    // the exit counts, so the clearing below lands after them
+    __builtin_amdgcn_s_waitcnt(0);
+    uint32_t* exits = a.cnt + (int64_t)(a.B + b) * a.cstride;
+    s_last = add_dev32(exits, 1u) == (uint32_t)a.G - 1u;
+    if (s_last) {
+      st_dev32(exits, 0u);
+      const uint32_t total = (uint32_t)(a.pm ? a.K * a.gamma : (a.K + 1) * a.gamma) * (uint32_t)a.nch1;
+      __hip_atomic_fetch_sub(a.cnt + (int64_t)b * a.cstride, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  lds_sync();
+  if (s_last && a.G > 1) {
+    uint64_t* slots = static_cast<uint64_t*>(a.slots) + (int64_t)b * kSlotWords * a.G;
+    for (int i = threadIdx.x; i < kSlotWords * a.G; i += kNT) st_dev(slots + i, 0ull);
   }
 }
 
@@ -474,6 +517,7 @@ __device__ void draw_body(const ChainParams& a, int b, int g, Exchange& x, Decid
   int pick;
   double loc;
   pick_slice(ss, x.G, jb.u * total, &pick, &loc);
+  draw_exit(a, b);  // the slots are read no more: the search works on registers
   // a block other than the searching one stores the deferred outputs
   if (g == (x.G > 1 && pick == 0 ? 1 : 0)) chain_outputs<PM>(a, b, dec);
   if (pick == g) {
@@ -490,7 +534,7 @@ __device__ void draw_role(const ChainParams& a, int d, Decided& dec) {
   const int b = d / a.G;
   const int g = d - b * a.G;
   __shared__ uint64_t s_words[kMaxG], s_w1[kMaxG];
-  __shared__ int s_ok, s_last;
+  __shared__ int s_ok;
   SliceSums ss;  // the slices' values of the last exchange
   Exchange x = make_exchange(a.slots, a.err, a.knobs, b, a.G, g);
   if (threadIdx.x < kWave) {
@@ -501,27 +545,8 @@ __device__ void draw_role(const ChainParams& a, int d, Decided& dec) {
     }
   }
   __syncthreads();
-  if (s_ok) draw_body<DT, HELD, PM>(a, b, g, x, dec, s_words, s_w1, ss);
-  // exits: the last draw block of the sequence takes its arrivals back off
-  // the counter (late ones, after a timed-out wait, bring it to zero too)
-  // and clears its exchange slots for the next call
-  if (threadIdx.x == 0) {
-    // wave 0 made every slot store of this block: they are complete before
-    // the exit counts, so the clearing below lands after them
-    __builtin_amdgcn_s_waitcnt(0);
-    uint32_t* exits = a.cnt + (int64_t)(a.B + b) * a.cstride;
-    s_last = add_dev32(exits, 1u) == (uint32_t)a.G - 1u;
-    if (s_last) {
-      st_dev32(exits, 0u);
-      const uint32_t total = (uint32_t)(a.pm ? a.K * a.gamma : (a.K + 1) * a.gamma) * (uint32_t)a.nch1;
-      __hip_atomic_fetch_sub(a.cnt + (int64_t)b * a.cstride, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-  __syncthreads();
-  if (s_last && a.G > 1) {
-    uint64_t* slots = static_cast<uint64_t*>(a.slots) + (int64_t)b * kSlotWords * a.G;
-    for (int i = threadIdx.x; i < kSlotWords * a.G; i += kNT) st_dev(slots + i, 0ull);
-  }
+  if (s_ok) draw_body<DT, HELD, PM>(a, b, g, x, dec, s_words, s_w1, ss);  // counts the exit itself
+  if (!s_ok) draw_exit(a, b);
 }
 
 template <int DT, bool HELD, bool PM>

@@ -92,6 +92,16 @@ __device__ __forceinline__ float bits_value(uint32_t w) {
 // below 2^-126 of the row maximum and do not matter to any sum here).
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
+// 2^x for a double x <= 0 whose exact value is wanted to fp32 accuracy
+// (rescaling one part's sum to another shift when parts merge): the
+// fraction goes through the fp32 unit and the integer part is exact, so the
+// relative error is that of one v_exp_f32 (about 1e-7) for any x, where an
+// fp32 argument would lose digits of x itself.
+__device__ __forceinline__ double exp2_d(double x) {
+  const double n = floor(x);
+  return ldexp((double)__builtin_amdgcn_exp2f((float)(x - n)), (int)fmax(n, -2000.0));
+}
+
 // ---------------------------------------------------------------------------
 // Philox4x32-10 (Salmon, Moraes, Dror, Shaw, SC'11): ten rounds of
 // (c0,c1,c2,c3) -> (hi(B c2)^c1^k0, lo(B c2), hi(A c0)^c3^k1, lo(A c0)),
@@ -659,7 +669,7 @@ __device__ inline RowStat merge_parts(const Partial* parts, int n, float c) {
   for (int i = 0; i < n; ++i) {
     const Partial pi = get_partial(parts + i);
     if (pi.m == kNegInf) continue;
-    S += pi.s * exp2((double)(c * pi.m) - (double)r.cm);
+    S += pi.s * exp2_d((double)(c * pi.m) - (double)r.cm);
   }
   r.S = S;
   return r;

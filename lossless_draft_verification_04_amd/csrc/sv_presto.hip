@@ -110,7 +110,7 @@ __device__ float row_offset_staged(const Partial* pp, int n, float c) {
   const float cm = c * M;
   double S = 0.0;
   for (int i = 0; i < n; ++i)
-    if (pp[i].m != kNegInf) S += pp[i].s * exp2((double)(c * pp[i].m) - (double)cm);
+    if (pp[i].m != kNegInf) S += pp[i].s * exp2_d((double)(c * pp[i].m) - (double)cm);
   if (!(S > 0.0)) return __builtin_huge_valf();
   return (float)((double)cm + log2(S));
 }
@@ -166,7 +166,7 @@ __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
       const float cm = a.c * M;
       double S = 0.0;
       for (int i = 0; i < a.nch1; ++i)
-        if (pp[i].m != kNegInf) S += pp[i].s * exp2((double)(a.c * pp[i].m) - (double)cm);
+        if (pp[i].m != kNegInf) S += pp[i].s * exp2_d((double)(a.c * pp[i].m) - (double)cm);
       if (S > 0.0) off = (float)((double)cm + log2(S));
     }
     s_offs[threadIdx.x] = off;

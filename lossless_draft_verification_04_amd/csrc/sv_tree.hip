@@ -223,7 +223,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       } else {
         for (int i = 0; i < a.nch; ++i) {
           const Partial pi = pr[i];
-          if (pi.m != kNegInf) S += pi.s * exp2((double)(a.c * pi.m) - (double)cm);
+          if (pi.m != kNegInf) S += pi.s * exp2_d((double)(a.c * pi.m) - (double)cm);
         }
       }
     }
@@ -419,7 +419,7 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
       } else {
         for (int i = 0; i < a.nch; ++i) {
           const Partial pi = pr[i];
-          if (pi.m != kNegInf) S += pi.s * exp2((double)(a.c * pi.m) - (double)cm);
+          if (pi.m != kNegInf) S += pi.s * exp2_d((double)(a.c * pi.m) - (double)cm);
         }
       }
     }

@@ -415,7 +415,7 @@ __device__ __forceinline__ double exchange_stats(Exchange& x, const Partial& min
   const float M = wave_fmax(m);
   *M_out = M;
   const double v =
-      (l >= x.G || m == kNegInf || M == kNegInf) ? 0.0 : unpack_sum(s_w1[l]) * exp2((double)(c * m) - (double)(c * M));
+      (l >= x.G || m == kNegInf || M == kNegInf) ? 0.0 : unpack_sum(s_w1[l]) * exp2_d((double)(c * m) - (double)(c * M));
   return scan_slices(v, x.G, ss);
 }
 
