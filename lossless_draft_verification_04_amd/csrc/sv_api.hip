@@ -151,9 +151,9 @@ sv_status plan_tree(sv_dtype dt, int32_t B, int32_t N, int32_t V, bool pm, Plan*
   pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
   const int64_t rows = (int64_t)B * N * (pm ? 1 : 2);
   // only rows of nodes with children are streamed (about half of them in a
-  // bushy tree): aim the part count at twice the usual block target, in
-  // blocks of twice the usual size
-  split(rows, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
+  // bushy tree), by the blocks at the front of the grid: aim the block count
+  // at twice the usual target, so that about the usual number stream
+  split(rows, pl->nvec, 2 * stats_blocks(), &pl->nch1, &pl->vpc1);
   if (pl->nch1 > kWalkMaxParts) {
     pl->vpc1 = (pl->nvec + kWalkMaxParts - 1) / kWalkMaxParts;
     pl->nch1 = (int32_t)((pl->nvec + pl->vpc1 - 1) / pl->vpc1);

@@ -11,13 +11,13 @@
 // residual; a node without children gives the bonus draw from its target row.
 //
 // Two launches per call:
-//  1. stats: a block per (node, target|draft, row part), laid out node-major
-//     so that the low-numbered nodes (parents precede their children, so in a
-//     breadth-first numbering these are the ones with children) are
-//     dispatched first and spread evenly over the compute units; blocks of
-//     nodes without children exit at once.  A working block streams its part
-//     of the row once; the first part of a row also gathers the row's logits
-//     at the node's children's tokens.
+//  1. stats: a block per (k, sequence, target|draft, row part), where block
+//     k of a sequence streams its k-th node with children (found from the
+//     parent array in LDS).  The layout is k-major, so the blocks that stream
+//     come first and spread evenly over the compute units; blocks past a
+//     sequence's last node with children exit at once.  A working block
+//     streams its part of the row once; the first part of a row also gathers
+//     the row's logits at the node's children's tokens.
 //  2. walk: G blocks per sequence replay the walk in lockstep.  Each stages
 //     the tree, every node's row statistics and every child's logits in LDS
 //     once and computes every child's p, q and uniform there; at a node it
@@ -56,30 +56,58 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
   const int which = a.pm ? 0 : (int)(rest & 1);
   if (!a.pm) rest >>= 1;
   const int b = (int)(rest % a.B);
-  const int u = (int)(rest / a.B);
+  const int k = (int)(rest / a.B);  // this block streams the k-th node with children of sequence b
   const int64_t rowbase = (int64_t)b * a.N;
-  const void* row = which ? row_ptr(a.drf, rowbase + u, a.drf_sb) : row_ptr(a.tgt, rowbase + u, a.tgt_sb);
-  // children of u among the candidates i = u + 1 + tid + k * kTNT: every
-  // parent and token is loaded in one round (clamped indexes), so the block
-  // waits for one round trip before it knows whether it streams
-  int32_t pk[kGather], xk[kGather];
-#pragma unroll
-  for (int k = 0; k < kGather; ++k) {
-    const int i = u + 1 + (int)threadIdx.x + k * kTNT;
-    const int ic = i < a.N ? i : a.N - 1;
-    pk[k] = a.parent[rowbase + ic];
-    xk[k] = a.tok[rowbase + ic];
+  // the sequence's tree in LDS (one round of loads); blocks are laid out
+  // k-major, so the blocks that stream come first and spread evenly over the
+  // compute units, and the blocks past a sequence's last node with children
+  // (the end of the grid, mostly) exit at once
+  __shared__ int32_t s_par[SV_MAX_N], s_tok[SV_MAX_N];
+  __shared__ int s_has[SV_MAX_N];
+  __shared__ int s_u;
+  for (int i = threadIdx.x; i < a.N; i += kTNT) {
+    s_par[i] = a.parent[rowbase + i];
+    s_tok[i] = a.tok[rowbase + i];
+    s_has[i] = a.all_rows ? 1 : 0;
   }
-  int has_kids = 0;
-#pragma unroll
-  for (int k = 0; k < kGather; ++k) {
-    const int i = u + 1 + (int)threadIdx.x + k * kTNT;
-    if (i < a.N && pk[k] == u) has_kids = 1;
-    else pk[k] = -1;  // not a child of u
+  __syncthreads();
+  if (!a.all_rows)
+    for (int i = 1 + (int)threadIdx.x; i < a.N; i += kTNT) {
+      const int pi = s_par[i];
+      if (pi >= 0 && pi < i) s_has[pi] = 1;  // every writer stores the same value
+    }
+  __syncthreads();
+  if (threadIdx.x < kWave) {
+    // the k-th flagged node in index order: one ballot per 64 nodes
+    const int lane = threadIdx.x;
+    int cnt = 0, found = -1;
+    for (int base = 0; base < a.N && found < 0; base += kWave) {
+      const int i = base + lane;
+      uint64_t m = __ballot(i < a.N && s_has[i < a.N ? i : 0]);
+      const int c = __popcll(m);
+      if (k < cnt + c) {
+        for (int r = k - cnt; r > 0; --r) m &= m - 1;
+        found = base + __builtin_ctzll(m);
+      }
+      cnt += c;
+    }
+    if (lane == 0) s_u = found;
   }
-  if (!a.all_rows && !__syncthreads_or(has_kids)) {
+  __syncthreads();
+  const int u = s_u;
+  if (u < 0) {
     zero_slots(a.slots, a.nzero, bid, kTNT);  // for the walk launch
     return;
+  }
+  const void* row = which ? row_ptr(a.drf, rowbase + u, a.drf_sb) : row_ptr(a.tgt, rowbase + u, a.tgt_sb);
+  // children of u among the candidates i = u + 1 + tid + j * kTNT
+  int32_t pk[kGather], xk[kGather];
+#pragma unroll
+  for (int j = 0; j < kGather; ++j) {
+    const int i = u + 1 + (int)threadIdx.x + j * kTNT;
+    const bool kid = i < a.N && s_par[i < a.N ? i : 0] == u;
+    pk[j] = kid ? u : -1;
+    xk[j] = kid ? s_tok[i] : 0;
   }
   // the first part of the row gathers its logits at the children's tokens
   // (NaN for a token outside the vocabulary); the loads are issued before the
@@ -89,9 +117,9 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
   uint32_t zg[kGather];
   if (ch == 0) {  // block-uniform; the loads are unconditional (clamped token) so none waits for another
 #pragma unroll
-    for (int k = 0; k < kGather; ++k) {
-      const int32_t x = xk[k];
-      zg[k] = load_bits<DT>(row, ((pk[k] >= 0) & (x >= 0) & (x < a.V)) ? x : 0);
+    for (int j = 0; j < kGather; ++j) {
+      const int32_t x = xk[j];
+      zg[j] = load_bits<DT>(row, ((pk[j] >= 0) & (x >= 0) & (x < a.V)) ? x : 0);
     }
   }
   const int64_t v0 = (int64_t)ch * a.vpc;
@@ -101,10 +129,10 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
   float* zc = a.zc + (int64_t)which * a.B * a.N + rowbase;
   if (ch == 0) {
 #pragma unroll
-    for (int k = 0; k < kGather; ++k) {
-      const int32_t x = xk[k];
-      if (pk[k] >= 0)
-        zc[u + 1 + (int)threadIdx.x + k * kTNT] = (x >= 0 && x < a.V) ? bits_value<DT>(zg[k]) : __builtin_nanf("");
+    for (int j = 0; j < kGather; ++j) {
+      const int32_t x = xk[j];
+      if (pk[j] >= 0)
+        zc[u + 1 + (int)threadIdx.x + j * kTNT] = (x >= 0 && x < a.V) ? bits_value<DT>(zg[j]) : __builtin_nanf("");
     }
   }
   zero_slots(a.slots, a.nzero, bid, kTNT);  // for the walk launch
