@@ -16,6 +16,8 @@ namespace sv {
 
 namespace {
 
+constexpr int kSmallPartVecs = 4096;  // largest part (vectors) the chain plan forms to keep parts per row direct
+constexpr int64_t kSmallDrawVecs = 131072;  // B * vectors per row at or below which the chain draw uses full tiles
 constexpr int kBlockVecs = 1024;   // smallest row part (vectors): 4 in flight per thread of a 256-thread block
 constexpr int kMaxResident = 4096;  // bound on the blocks of a draw / walk launch (two slot words each)
 
@@ -115,6 +117,14 @@ sv_status plan_chain(sv_dtype dt, int32_t B, int32_t K, int32_t gamma, int32_t V
   pl->nvec = (V + per_vec(dt) - 1) / per_vec(dt);
   const int64_t rows = (int64_t)B * (K + (pm ? 0 : 1)) * gamma;
   split(rows, pl->nvec, stats_blocks(), &pl->nch1, &pl->vpc1);
+  // few short rows: at most the parts a draw block merges straight from
+  // registers (4 per row, 8 in point-mass mode), which saves the draw blocks
+  // a staging round when each part stays small
+  const int32_t direct = pm ? 8 : 4;
+  if (pl->nch1 > direct && (pl->nvec + direct - 1) / direct <= kSmallPartVecs) {
+    pl->vpc1 = (pl->nvec + direct - 1) / direct;
+    pl->nch1 = (int32_t)((pl->nvec + pl->vpc1 - 1) / pl->vpc1);
+  }
   pl->grid1 = rows * pl->nch1;
   if (pl->grid1 + (int64_t)B * kMaxG > INT32_MAX) return SV_EUNSUPPORTED;
   size_t off = kWsFixed;
@@ -409,6 +419,12 @@ static sv_status verify_chain_like(const void* tgt, const void* drf, sv_dtype dt
   // all B * G draw blocks fit on the device at once (once the statistics
   // blocks, which are placed first and never wait, have finished)
   pick_slices(B, pl.nvec, chain_capacity(dt, true, pm), chain_capacity(dt, false, pm), &p.G, &p.held);
+  if ((int64_t)B * pl.nvec <= kSmallDrawVecs && p.held) {
+    // little to draw from: blocks of kSliceTiles full tiles each, so that
+    // fewer blocks take part in each exchange
+    const int64_t g = (pl.nvec + (int64_t)kSliceTiles * 256 - 1) / ((int64_t)kSliceTiles * 256);
+    if (g < p.G) p.G = g < 1 ? 1 : (int32_t)g;
+  }
   if (p.G > 1 && align_up((size_t)8 * B * p.cstride, 256) + (size_t)kSlotWords * 8 * B * p.G >
                      kWsCounters * sizeof(uint32_t))
     return SV_EUNSUPPORTED;  // not reached: B * G <= 4096 and B <= 2048 whenever G > 1

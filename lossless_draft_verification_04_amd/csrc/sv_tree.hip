@@ -314,8 +314,10 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       break;
     }
     const void* rowQ = row_ptr(a.drf, rowbase + node, a.drf_sb);
-    // the held slice of the node's row pair is loaded at the first rejection
-    bool loaded = false;
+    // the held slice of the node's row pair is loaded on entering the node,
+    // so that the loads travel while the first children are tested
+    sl.load(rowP, rowQ, v0, v1);
+    bool loaded = true;
     RowStat P, Q;
     P.cm = s_cm[0][node];
     P.S = s_S[0][node];
