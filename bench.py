@@ -786,8 +786,8 @@ def main():
         probe = read_probe(sizes_mb=(311,))
 
     rl = roofline(r["alg_bytes"], r["call_ms"])
-    rl["kernel"] = ("sv_verify_chain call (row-statistics kernel + draw kernel); duration = HIP events around the "
-                    "graph replays on the launch stream / calls")
+    rl["kernel"] = ("sv_verify_chain call (one chain_kernel launch: statistics blocks, then draw blocks); duration = "
+                    "HIP events around the graph replays on the launch stream / calls")
     rl["alg_bytes_per_call"] = int(r["alg_bytes"])
     line = {
         "metric": METRIC,
