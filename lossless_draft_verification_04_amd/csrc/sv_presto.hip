@@ -194,9 +194,9 @@ __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
     if (!empty) {
       const TopPair t =
           lam == 0.f
-              ? wave_topk_scan<kPNT, E, false>(ProxyValues<DT, true>{rowP, rowQ, a.V, 0.f, 0.f}, v0, v1, a.V, a.k)
-              : wave_topk_scan<kPNT, E, false>(ProxyValues<DT, false>{rowP, rowQ, a.V, (offP - offQ) / a.c, lam},
-                                               v0, v1, a.V, a.k);
+              ? wave_topk_scan<kPNT, E, false, 4>(ProxyValues<DT, true>{rowP, rowQ, a.V, 0.f, 0.f}, v0, v1, a.V, a.k)
+              : wave_topk_scan<kPNT, E, false, 4>(ProxyValues<DT, false>{rowP, rowQ, a.V, (offP - offQ) / a.c, lam},
+                                                  v0, v1, a.V, a.k);
       lv = t.v;
       li = t.i;
     }

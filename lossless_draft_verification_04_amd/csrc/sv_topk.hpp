@@ -230,10 +230,11 @@ __device__ __forceinline__ void insert_flagged(const float (&x)[E], uint32_t min
 // stream instead costs an insertion per new record, about F ln(n / F) per
 // list, which dominated at F >= 4.)  MAY_HOLD = false drops the register
 // path (it keeps kWin vectors live across the selection).
-template <int NT, int E, bool MAY_HOLD, class Src>
+template <int NT, int E, bool MAY_HOLD, int KEEP, class Src>
 __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V, int F) {
   constexpr int NW = NT / kWave;
-  constexpr int kWin = 4;  // vectors in flight per thread
+  constexpr int kWin = 4;   // vectors in flight per thread
+  constexpr int kKeep = KEEP > 0 ? KEEP : 1;  // best vectors a thread remembers for pass 2
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int tid = threadIdx.x;
@@ -241,7 +242,8 @@ __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V,
   __shared__ int32_t s_mv[NT];
   __shared__ uint8_t s_pick[NT];
   __shared__ int32_t s_sel[kWave];
-  __shared__ int s_nsel;
+  __shared__ int32_t s_rr[kWave * kKeep];  // vectors pass 2 reads again (offsets in the range)
+  __shared__ int s_nsel, s_nrr, s_full;
   __shared__ float s_tf;
   float lv = kNegInf;
   int32_t li = kNoIdx;
@@ -249,9 +251,16 @@ __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V,
   const int64_t span = v1 - v0;
   const int64_t nk = (span + NT - 1) / NT;  // vectors per thread at most
   const bool held = MAY_HOLD && nk <= kWin;  // block-uniform
-  // pass 1: this thread's best element, as (value, vector offset)
-  float m = kNegInf;
-  int32_t mv = kNoIdx;
+  // pass 1: this thread's kKeep best vectors by their largest element, as
+  // (value, vector offset), best first (equal values: lower offset first);
+  // the first is the thread's best element
+  float bm[kKeep];
+  int32_t bo[kKeep];
+#pragma unroll
+  for (int i = 0; i < kKeep; ++i) {
+    bm[i] = kNegInf;
+    bo[i] = kNoIdx;
+  }
   typename Src::Data d[kWin];
   if (span > 0) {  // block-uniform
 #pragma unroll
@@ -279,9 +288,20 @@ __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V,
           for (int e = 1; e < E; ++e) vm = fmaxf(vm, x[e]);
           // a vector always holds a listable element unless -inf is not listed
           const bool has = !Src::kSkipNegInf || vm > kNegInf;
-          if (has && (mv == kNoIdx || vm > m)) {
-            m = vm;
-            mv = (int32_t)(vu - v0);
+          if (has) {
+            // insertion by carrying the displaced entry down the list
+            float cv = vm;
+            int32_t co = (int32_t)(vu - v0);
+#pragma unroll
+            for (int i = 0; i < kKeep; ++i) {
+              const bool t = (bo[i] == kNoIdx) | top_better(cv, co, bm[i], bo[i]);
+              const float sv = bm[i];
+              const int32_t so = bo[i];
+              bm[i] = t ? cv : bm[i];
+              bo[i] = t ? co : bo[i];
+              cv = t ? sv : cv;
+              co = t ? so : co;
+            }
           }
         }
       }
@@ -290,9 +310,15 @@ __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V,
       for (int u = 0; u < kWin; ++u) d[u] = nx[u];
     }
   }
+  const float m = bm[0];
+  const int32_t mv = bo[0];
   s_m[tid] = m;
   s_mv[tid] = mv;
   s_pick[tid] = 0;
+  if (tid == 0) {
+    s_nrr = 0;
+    s_full = 0;
+  }
   lds_sync();
   // the F best threads (wave 0: F rounds of a wave-wide selection over the
   // NW entries each lane holds)
@@ -354,7 +380,41 @@ __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V,
     }
     return TopPair{lv, li};
   }
-  // pass 2 re-read: the selected threads' vectors, kWin per thread at a time
+  // pass 2 re-read, short form (KEEP > 0): each selected thread lists its
+  // kept vectors whose largest element reaches the F-th selected best; only
+  // a thread with more such vectors than it kept needs all its vectors read
+  // again
+  if (KEEP == 0 && tid == 0) s_full = 1;
+  if (KEEP > 0 && s_pick[tid]) {
+    if (nk > kKeep && bo[kKeep - 1] != kNoIdx && bm[kKeep - 1] >= tf) {
+      s_full = 1;  // every writer stores the same value
+    } else {
+#pragma unroll
+      for (int i = 0; i < kKeep; ++i)
+        if (bo[i] != kNoIdx && bm[i] >= tf) s_rr[atomicAdd(&s_nrr, 1)] = bo[i];
+    }
+  }
+  lds_sync();
+  if (!s_full) {
+    const int nrr = s_nrr;
+    for (int base = 0; base < nrr; base += NT) {  // block-uniform
+      const int t = base + tid;
+      const int64_t vs = t < nrr ? v0 + s_rr[t] : -1;
+      typename Src::Data dd;
+      if (vs >= 0) dd = src.load(vs);
+      float x[E];
+      uint32_t mine = 0;
+      if (vs >= 0) {
+        src.values(dd, vs, x);
+#pragma unroll
+        for (int e = 0; e < E; ++e)
+          if (x[e] >= tf && vs * E + e < V && (!Src::kSkipNegInf || x[e] > kNegInf)) mine |= 1u << e;
+      }
+      insert_flagged<E>(x, mine, vs, F, lv, li, &count, lane);
+    }
+    return TopPair{lv, li};
+  }
+  // pass 2 re-read, full form: the selected threads' vectors, kWin per thread at a time
   const int nsel = s_nsel;
   const int64_t total = (int64_t)nsel * nk;
   for (int64_t base = 0; base < total; base += (int64_t)kWin * NT) {
@@ -386,10 +446,14 @@ __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V,
   return TopPair{lv, li};
 }
 
-// Per-wave lists whose merge is the block's top F of [v0, v1).
-template <int NT, int E, bool MAY_HOLD = true, class Src>
+// Per-wave lists whose merge is the block's top F of [v0, v1).  KEEP > 0:
+// every thread remembers its KEEP best vectors, so that pass 2 reads again
+// only the vectors that can hold a top-F value (each 16-byte re-read costs a
+// whole memory line); the bookkeeping costs pass 1 a few operations per
+// vector, which pays where pass 2 would re-read a large share of the range.
+template <int NT, int E, bool MAY_HOLD = true, int KEEP = 0, class Src>
 __device__ TopPair wave_topk_scan(const Src src, int64_t v0, int64_t v1, int V, int F) {
-  return block_topk_scan<NT, E, MAY_HOLD>(src, v0, v1, V, F);
+  return block_topk_scan<NT, E, MAY_HOLD, KEEP>(src, v0, v1, V, F);
 }
 
 }  // namespace sv
