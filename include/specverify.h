@@ -63,6 +63,9 @@
  *    statistics block of their sequence has counted its arrival; they and
  *    the walk launch of the tree entry points split each sequence's final
  *    draw over G blocks that exchange partial sums and wait for each other.
+ *    Small chain calls (K = 1, at most 9 rows per sequence to hold, B * V
+ *    small) instead run G blocks per sequence that each hold a slice of
+ *    every row: they exchange their row statistics, then their draw sums.
  *    G is chosen so that all draw (walk) blocks are resident at once on an
  *    otherwise idle device once the statistics blocks, which never wait,
  *    are done.  A kernel running concurrently on another stream can keep

@@ -9,7 +9,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libspecverify.so")
-SOURCES = ["sv_api.hip", "sv_chain.hip", "sv_greedy.hip", "sv_tree.hip", "sv_fanout.hip", "sv_cache.hip", "sv_presto.hip", "sv_branch.hip", "sv_probe.hip"]
+SOURCES = ["sv_api.hip", "sv_chain.hip", "sv_chain_small.hip", "sv_greedy.hip", "sv_tree.hip", "sv_fanout.hip", "sv_cache.hip", "sv_presto.hip", "sv_branch.hip", "sv_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

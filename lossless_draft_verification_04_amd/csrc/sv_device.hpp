@@ -214,6 +214,67 @@ __device__ __forceinline__ int64_t readlane_i64(int64_t v, int l) {
   return (int64_t)(((uint64_t)hi << 32) | lo);
 }
 
+// Reductions of N values per lane at once, each left in every lane, by DPP
+// lane movement: two quad permutations (lane i with i^1, then with i^2),
+// then the half-row and row mirrors, give every lane of a 16-lane row its
+// row's total; the four row totals are then read as scalars and combined in
+// a fixed order.  At each step the two lanes of a pair combine the same two
+// operands, so all lanes end with the same bits, and the N reductions'
+// steps interleave (no LDS traffic, no wait between steps of one value).
+constexpr int kDppQuadXor1 = 0xB1;  // quad_perm [1,0,3,2]
+constexpr int kDppQuadXor2 = 0x4E;  // quad_perm [2,3,0,1]
+constexpr int kDppRowMirror = 0x140, kDppRowHalfMirror = 0x141;
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+template <int N>
+__device__ __forceinline__ void rows_fmax_all(float (&v)[N]) {
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] = fmaxf(v[r], dpp_f<kDppQuadXor1>(v[r]));
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] = fmaxf(v[r], dpp_f<kDppQuadXor2>(v[r]));
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] = fmaxf(v[r], dpp_f<kDppRowHalfMirror>(v[r]));
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] = fmaxf(v[r], dpp_f<kDppRowMirror>(v[r]));
+#pragma unroll
+  for (int r = 0; r < N; ++r)
+    v[r] = fmaxf(fmaxf(readlane_f(v[r], 0), readlane_f(v[r], 16)), fmaxf(readlane_f(v[r], 32), readlane_f(v[r], 48)));
+}
+template <int N>
+__device__ __forceinline__ void rows_fsum_all(float (&v)[N]) {
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] += dpp_f<kDppQuadXor1>(v[r]);
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] += dpp_f<kDppQuadXor2>(v[r]);
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] += dpp_f<kDppRowHalfMirror>(v[r]);
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] += dpp_f<kDppRowMirror>(v[r]);
+#pragma unroll
+  for (int r = 0; r < N; ++r)
+    v[r] = (readlane_f(v[r], 0) + readlane_f(v[r], 16)) + (readlane_f(v[r], 32) + readlane_f(v[r], 48));
+}
+template <int N>
+__device__ __forceinline__ void rows_sum_all(double (&v)[N]) {
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] += dpp_d<kDppQuadXor1, 0xF>(v[r], 0.0);
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] += dpp_d<kDppQuadXor2, 0xF>(v[r], 0.0);
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] += dpp_d<kDppRowHalfMirror, 0xF>(v[r], 0.0);
+#pragma unroll
+  for (int r = 0; r < N; ++r) v[r] += dpp_d<kDppRowMirror, 0xF>(v[r], 0.0);
+#pragma unroll
+  for (int r = 0; r < N; ++r)
+    v[r] = (readlane_d(v[r], 0) + readlane_d(v[r], 16)) + (readlane_d(v[r], 32) + readlane_d(v[r], 48));
+}
+
 __device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);

@@ -64,13 +64,13 @@ __device__ void block_scan_vec(const double* v, double* excl, double* out) {
 }
 
 // One block's slice [v0, v1) of a row pair (rowQ null: a single row).
-// HELD: the slice spans at most kSliceTiles tiles and is kept in registers;
+// HELD: the slice spans at most TILES tiles and is kept in registers;
 // otherwise it is streamed from memory on each use (separate kernels, so the
 // streaming code's registers do not add to the held ones).
-template <int DT, int NT, bool HELD>
+template <int DT, int NT, bool HELD, int TILES = kSliceTiles>
 struct Slice {
   static constexpr int E = Fmt<DT>::kPerVec;
-  static constexpr int kT = HELD ? kSliceTiles : 1;
+  static constexpr int kT = HELD ? TILES : 1;
   u32x4 p[kT], q[kT];
   double own[kT];   // this thread's weight sum per tile (last prepare)
   double excl[kT];  // the weight of the tile's earlier threads (last prepare)

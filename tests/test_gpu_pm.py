@@ -74,7 +74,9 @@ def test_chain_pm_equals_chain_with_one_hot_drafts():
         b = svx.sv_verify_chain_pm(g["tgt"], g["tok"], T, seed=seed, round_=rnd)
         torch.cuda.synchronize()
         assert torch.equal(a["n"], b["n"]) and torch.equal(a["tok"], b["tok"])
-        assert torch.equal(a["p"], b["p"])
+        # the two calls may take different launch plans (the point-mass call holds 9 rows per block and
+        # takes the small-call path), so p agrees to the rounding of the row statistics, not bit for bit
+        assert torch.allclose(a["p"], b["p"], rtol=1e-6, atol=0.0)
         assert (a["q"] == 1.0).all()
     PT.device_error_clear()
 

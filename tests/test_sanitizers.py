@@ -15,7 +15,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 CSRC = os.path.join(ROOT, "lossless_draft_verification_04_amd", "csrc")
-SOURCES = ["sv_api.hip", "sv_chain.hip", "sv_greedy.hip", "sv_tree.hip", "sv_fanout.hip", "sv_cache.hip",
+SOURCES = ["sv_api.hip", "sv_chain.hip", "sv_chain_small.hip", "sv_greedy.hip", "sv_tree.hip", "sv_fanout.hip", "sv_cache.hip",
            "sv_presto.hip", "sv_branch.hip", "sv_probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 SAN_ENV = dict(ASAN_OPTIONS="detect_leaks=0:abort_on_error=1", UBSAN_OPTIONS="halt_on_error=1:print_stacktrace=1")
