@@ -37,7 +37,7 @@ struct ChainParams {
   void* part1;     // stats parts, [B][rows][nch1]
   float* zg;       // target logits of the drafted tokens, [B][K][gamma]
   float* zq;       // draft logits of the drafted tokens, [B][K][gamma]
-  void* slots;     // draw slot words, [B][G][4], in the counter region (zero between calls)
+  void* slots;     // draw slot words, [B][G][kSlotWords], in the counter region (zero between calls)
   int32_t nch1;
   int32_t G;       // draw blocks per sequence
   int64_t grid1;   // statistics blocks (the draw blocks follow them)
@@ -81,7 +81,7 @@ struct TreeParams {
   const uint32_t* knobs;  // workspace header (wait bound, test switch), or null
   void* part;
   float* zc;       // each child's logits under its parent's rows, [2][B][N] (target, draft)
-  void* slots;     // walk slot words, [B][G][4], zeroed by the stats launch
+  void* slots;     // walk slot words, [B][G][kSlotWords], zeroed by the stats launch
   int64_t nzero;   // 64-bit words of `slots` the stats launch zeroes
   int32_t nch;
   int32_t G;       // walk blocks per sequence

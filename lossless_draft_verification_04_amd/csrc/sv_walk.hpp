@@ -269,7 +269,7 @@ struct Slice {
 
 // Exchange state of one block.
 struct Exchange {
-  uint64_t* slots;  // [2 parities][G][2 words] of this sequence, zero at the start
+  uint64_t* slots;  // [2 parities][G][kSlotPad words, 2 used] of this sequence, zero at the start
   int32_t* err;
   int G, g;
   int pass;        // exchanges so far
@@ -278,7 +278,12 @@ struct Exchange {
   uint32_t limit;  // polls before a wait gives up
 };
 
-constexpr int kSlotWords = 4;  // slot words per block of a launch (2 parities x 2 words)
+// Each block's slot words sit kSlotPad words (64 B) apart, so no two blocks
+// store to one 64-byte span: with 16-byte slots, 8 blocks' stores and every
+// block's polls met in one cache line, which measured 0.25-0.5 us slower per
+// exchange of 16-64 blocks.
+constexpr int kSlotPad = 8;
+constexpr int kSlotWords = 2 * kSlotPad;  // slot words per block of a launch (2 parities)
 
 // Workspace header words read by the waits (word 0 is the error word):
 // [1] the number of polls after which a wait gives up (0: kSpinLimit);
@@ -319,19 +324,19 @@ __device__ __forceinline__ void exchange_n(Exchange& x, uint64_t p0, uint64_t p1
   lds_sync();  // every wave is done with the previous exchange's words
   if (threadIdx.x < kWave) {
     const int l = threadIdx.x;
-    uint64_t* set = x.slots + (int64_t)(x.pass & 1) * 2 * x.G;
+    uint64_t* set = x.slots + (int64_t)(x.pass & 1) * kSlotPad * x.G;
     uint64_t w0 = p0, w1 = p1;
     bool ok = (l >= x.G) || (l == x.g);
     if (x.G > 1) {
       if (l == x.g && !x.withhold) {
-        st_dev(set + 2 * l, p0 | tag);
-        if (NW == 2) st_dev(set + 2 * l + 1, p1 | tag);
+        st_dev(set + kSlotPad * l, p0 | tag);
+        if (NW == 2) st_dev(set + kSlotPad * l + 1, p1 | tag);
       }
       uint32_t spins = 0;
       for (;;) {
         if (!ok) {
-          w0 = ld_dev(set + 2 * l);
-          if (NW == 2) w1 = ld_dev(set + 2 * l + 1);
+          w0 = ld_dev(set + kSlotPad * l);
+          if (NW == 2) w1 = ld_dev(set + kSlotPad * l + 1);
           ok = (w0 & kTagMask) == tag && (NW == 1 || (w1 & kTagMask) == tag);
         }
         if (__all(ok) || x.late) break;
