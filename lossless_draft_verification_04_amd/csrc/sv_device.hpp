@@ -169,11 +169,6 @@ __device__ __forceinline__ T wave_min(T v) {
   for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o, kWave));
   return v;
 }
-__device__ __forceinline__ float wave_fmax(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
 // Lane movement by DPP (gfx9 encodings): row_shr:n shifts within 16-lane
 // rows, row_bcast:15 / row_bcast:31 broadcast lane 15 of each row to the
 // next row / lane 31 to rows 2 and 3.  Lanes without a source, and rows
@@ -275,10 +270,16 @@ __device__ __forceinline__ void rows_sum_all(double (&v)[N]) {
     v[r] = (readlane_d(v[r], 0) + readlane_d(v[r], 16)) + (readlane_d(v[r], 32) + readlane_d(v[r], 48));
 }
 
+// One value per lane: the wave's maximum / sum, in every lane.
+__device__ __forceinline__ float wave_fmax(float v) {
+  float a[1] = {v};
+  rows_fmax_all(a);
+  return a[0];
+}
 __device__ __forceinline__ double wave_sum(double v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-  return v;
+  double a[1] = {v};
+  rows_sum_all(a);
+  return a[0];
 }
 
 template <int NT>

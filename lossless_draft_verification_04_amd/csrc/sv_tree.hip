@@ -336,7 +336,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     sp.ex = nullptr;
     sp.nex = 0;
     double c = 0.0, D = 1.0;
-    bool sums_current = false;  // the slice holds the sums of the current residual
+    bool sums_current = false;  // the last exchange holds the slices' sums of the current residual
     int accepted = -1;
     for (int kk = 0; kk < nk; ++kk) {
       const int cn = s_kids[kk];
@@ -354,7 +354,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
         sl.load(rowP, rowQ, v0, v1);
         loaded = true;
       }
-      const double Dn = exchange_sum(x, sl.prepare(sp, a.V), s_w0, &ss);
+      const double Dn = exchange_sum(x, sl.total(sp, a.V), s_w0, &ss);
       if (Dn > 0.0) {
         c = cnext;
         D = Dn;
@@ -370,14 +370,19 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       lds_sync();
       continue;
     }
-    // every child rejected: draw from (p - c q)^+
+    // every child rejected: draw from (p - c q)^+; the rejection passes
+    // exchanged only the slices' totals, so the searching block prepares its
+    // slice's prefixes first
     sp.coef = (float)c;
     if (!loaded) sl.load(rowP, rowQ, v0, v1);  // (not reached: the last child was rejected)
-    if (!sums_current) D = exchange_sum(x, sl.prepare(sp, a.V), s_w0, &ss);
+    if (!sums_current) D = exchange_sum(x, sl.total(sp, a.V), s_w0, &ss);
     int pick;
     double loc;
     pick_slice(ss, x.G, us * D, &pick, &loc);
-    if (pick == g) t = sl.search(sp, a.V, loc);
+    if (pick == g) {
+      sl.prepare(sp, a.V);
+      t = sl.search(sp, a.V, loc);
+    }
     break;
   }
   lds_sync();

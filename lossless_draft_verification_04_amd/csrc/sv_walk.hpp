@@ -38,13 +38,13 @@ constexpr uint64_t kTagMask = 0xffull;
 // their block totals (out; waves in index order), with one block barrier
 // pair for all N.
 template <int NT, int N>
-__device__ void block_scan_vec(const double* v, double* excl, double* out) {
+__device__ void block_scan_vec(const double* v, double* excl, double* out, int n = N) {
   __shared__ double red[NT / kWave][N];
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
   double inc[N];
 #pragma unroll
-  for (int i = 0; i < N; ++i) inc[i] = wave_incl_scan(v[i]);
+  for (int i = 0; i < N; ++i) inc[i] = i < n ? wave_incl_scan(v[i]) : 0.0;  // n: entries in use (block-uniform)
   lds_sync();
   if (lane == kWave - 1)
 #pragma unroll
@@ -138,11 +138,32 @@ struct Slice {
         for (int e = 0; e < E; ++e) own[u] += (double)w[e];
       }
     }
-    block_scan_vec<NT, kT>(own, excl, tot);
+    // tiles past the slice's end are empty in every thread: not scanned
+    const int used = (int)((v1 - v0 + NT - 1) / NT);
+    block_scan_vec<NT, kT>(own, excl, tot, used < kT ? used : kT);
     double total = 0.0;
 #pragma unroll
     for (int u = 0; u < kT; ++u) total += tot[u];
     return total;
+  }
+
+  // The block's weight sum of sp over the slice, as prepare returns it but
+  // without the per-tile prefixes a search needs (for passes whose sums are
+  // only exchanged; a search needs a prepare with the same sp first).
+  __device__ __forceinline__ double total(const DrawSpec& sp, int V) const {
+    if constexpr (!HELD) return range_weight_sum<DT, NT>(sp, V, v0, v1);
+    double s = 0.0;
+#pragma unroll
+    for (int u = 0; u < kT; ++u) {
+      int64_t v;
+      if (valid(u, &v)) {
+        float w[E];
+        draw_weights_from<DT>(sp, V, v, p[u], q[u], w);
+#pragma unroll
+        for (int e = 0; e < E; ++e) s += (double)w[e];
+      }
+    }
+    return block_sum<NT>(s);
   }
 
   // (max, sum 2^(z c - c max)) of row P over the slice.
