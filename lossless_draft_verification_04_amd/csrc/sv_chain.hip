@@ -167,6 +167,15 @@ __device__ __forceinline__ RowStat merge_loaded(const u32x4 (&v)[N], int n, floa
 // the per-position outputs wait in pq until after the draw's exchange, so
 // that no block carries stores into the loads and exchange on the critical
 // path (a wait for a load also waits for earlier stores here).
+// What a draw block computes before it waits for the statistics: the draw
+// uniform, and (wave k < K, lane j < gamma) candidate k's drafted token x_{k,j}
+// and its acceptance uniform.
+struct Early {
+  double u;
+  double r;
+  int32_t x;
+};
+
 struct Decided {
   StagedParts st;
   int n[SV_MAX_K];  // first rejection (accepted count) per candidate
@@ -188,7 +197,7 @@ struct Decided {
 // outputs are deferred (d.deferred), stores them; chain_outputs stores
 // deferred ones.  Returns the kept candidate's job (in LDS).
 template <int DT, bool PM>
-__device__ const Job* chain_decide(const ChainParams& a, int b, bool writer, Decided& d) {
+__device__ const Job* chain_decide(const ChainParams& a, int b, bool writer, Decided& d, const Early& e) {
   StagedParts& st = d.st;
   int* sN = d.n;
   Job* sJob = d.job;
@@ -203,13 +212,13 @@ __device__ const Job* chain_decide(const ChainParams& a, int b, bool writer, Dec
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
 
-  // the first candidate's token and gathered logits are loaded before the
-  // parts are staged, so that both travel in one round of loads
-  int32_t x_pre = 0;
+  // the first candidate's gathered logits are loaded before the parts are
+  // staged, so that both travel in one round of loads (its token came
+  // before the wait)
+  const int32_t x_pre = e.x;
   uint32_t zp_pre = 0, zq_pre = 0;
   if (wave < a.K && lane < a.gamma) {
     const int64_t o = ((int64_t)b * a.K + wave) * a.gamma + lane;
-    x_pre = a.tok[o];
     zp_pre = ld_dev32(reinterpret_cast<const uint32_t*>(a.zg) + o);
     if (!PM) zq_pre = ld_dev32(reinterpret_cast<const uint32_t*>(a.zq) + o);
   }
@@ -229,14 +238,12 @@ __device__ const Job* chain_decide(const ChainParams& a, int b, bool writer, Dec
     sp.S = 0.0;
     sq.S = 1.0;  // point mass: q(x) = 1
     int32_t x = -1;
-    // the draw uniform (only the job's lane uses it), computed while the
-    // loads below are in flight
-    const double u = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
+    const double u = e.u;  // the draw uniform (only the job's lane uses it)
     if (lane < a.gamma) {
       const int j = lane;
       const int64_t o = ((int64_t)b * a.K + k) * a.gamma + j;
       const int first_p = (k * a.gamma + j) * a.nch1, first_q = (Kg + j) * a.nch1;
-      const double r = uniform24(a.seed, (uint32_t)(j + 1), (uint32_t)b, (uint32_t)k, a.round, 0);
+      const double r = k == wave ? e.r : uniform24(a.seed, (uint32_t)(j + 1), (uint32_t)b, (uint32_t)k, a.round, 0);
       // the drafted token, its gathered logits (stats pass) and the rows'
       // parts: one round of independent loads
       const bool pre = k == wave;
@@ -470,8 +477,8 @@ __device__ void draw_exit(const ChainParams& a, int b) {
 // The decisions and the draw of one draw block (all its waits bounded).
 template <int DT, bool HELD, bool PM>
 __device__ void draw_body(const ChainParams& a, int b, int g, Exchange& x, Decided& dec, uint64_t* s_words,
-                          uint64_t* s_w1, SliceSums& ss) {
-  const Job* pj = chain_decide<DT, PM>(a, b, g == 0, dec);
+                          uint64_t* s_w1, SliceSums& ss, const Early& e) {
+  const Job* pj = chain_decide<DT, PM>(a, b, g == 0, dec, e);
   const Job jb = *pj;
   const int64_t spv = (a.nvec + a.G - 1) / a.G;
   const int64_t v0 = (int64_t)g * spv < a.nvec ? (int64_t)g * spv : a.nvec;
@@ -531,12 +538,35 @@ __device__ void draw_body(const ChainParams& a, int b, int g, Exchange& x, Decid
 // draw row(s).
 template <int DT, bool HELD, bool PM>
 __device__ void draw_role(const ChainParams& a, int d, Decided& dec) {
-  const int b = d / a.G;
-  const int g = d - b * a.G;
+  // with sequences grouped by XCD, a sequence's draw blocks sit on the XCD
+  // that streamed its rows (the grid before them is a multiple of 8 blocks,
+  // so d and the block index agree mod 8): they start as that XCD's
+  // statistics blocks end, whatever the other XCDs still stream
+  int b, g;
+  if (a.xcd) {
+    const int i = d >> 3;
+    b = (d & 7) + 8 * (i / a.G);
+    g = i - (i / a.G) * a.G;
+  } else {
+    b = d / a.G;
+    g = d - b * a.G;
+  }
   __shared__ uint64_t s_words[kMaxG], s_w1[kMaxG];
   __shared__ int s_ok;
   SliceSums ss;  // the slices' values of the last exchange
   Exchange x = make_exchange(a.slots, a.err, a.knobs, b, a.G, g);
+  // everything that does not depend on the statistics, while they stream
+  Early e;
+  e.u = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
+  e.r = 1.0;
+  e.x = 0;
+  {
+    const int lane = threadIdx.x & (kWave - 1), wave = threadIdx.x / kWave;
+    if (wave < a.K && lane < a.gamma) {
+      e.x = a.tok[((int64_t)b * a.K + wave) * a.gamma + lane];
+      e.r = uniform24(a.seed, (uint32_t)(lane + 1), (uint32_t)b, (uint32_t)wave, a.round, 0);
+    }
+  }
   if (threadIdx.x < kWave) {
     const bool ok = wait_parts(a, b, x.limit);
     if (threadIdx.x == 0) {
@@ -545,7 +575,7 @@ __device__ void draw_role(const ChainParams& a, int d, Decided& dec) {
     }
   }
   __syncthreads();
-  if (s_ok) draw_body<DT, HELD, PM>(a, b, g, x, dec, s_words, s_w1, ss);  // counts the exit itself
+  if (s_ok) draw_body<DT, HELD, PM>(a, b, g, x, dec, s_words, s_w1, ss, e);  // counts the exit itself
   if (!s_ok) draw_exit(a, b);
 }
 
