@@ -148,6 +148,35 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
 // ---------------------------------------------------------------------------
 constexpr int kWNT = 256;  // walk block
 
+// Staging of a walk block in one round of loads, for trees whose nodes and
+// rows fit one per thread and whose rows have at most kStageParts parts:
+// thread t loads node t's entries and row t's parts before it uses any, and
+// draws child t's uniform while they travel.  (Otherwise a loop per kind of
+// entry.)
+constexpr int kStageParts = 4;
+
+// A row's statistic (c max, S) from its n <= kStageParts parts in registers,
+// merged in part order as the loop over parts in memory does.
+__device__ __forceinline__ void merge_held(const Partial (&pv)[kStageParts], int n, float c, float* cm, double* S) {
+  float M = kNegInf;
+#pragma unroll
+  for (int i = 0; i < kStageParts; ++i)
+    if (i < n) M = fmaxf(M, pv[i].m);
+  *cm = 0.f;
+  *S = 0.0;
+  if (M == kNegInf) return;
+  *cm = c * M;
+  if (n == 1) {
+    *S = pv[0].s;
+    return;
+  }
+  double sum = 0.0;
+#pragma unroll
+  for (int i = 0; i < kStageParts; ++i)
+    if (i < n && pv[i].m != kNegInf) sum += pv[i].s * exp2_d((double)(c * pv[i].m) - (double)*cm);
+  *S = sum;
+}
+
 // Children of `node` in increasing index (from the staged parent array) into
 // s_kids; returns their count (the same in every thread).  The first wave
 // finds them with one ballot per 64 candidates, so the block waits at one
@@ -231,13 +260,41 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   // round of loads (parts and logits of nodes without children were not
   // written and are never used)
   const float* zc = a.zc + rowbase;
-  for (int i = threadIdx.x; i < a.N; i += kWNT) {
-    s_par[i] = a.parent[rowbase + i];
-    s_zp[i] = zc[i];
-    s_zq[i] = zc[(int64_t)a.B * a.N + i];
-    s_first[i] = a.N;
+  const bool one_round = a.N <= kWNT && 2 * (a.N - 1) <= kWNT && a.nch <= kStageParts;  // block-uniform
+  if (one_round) {
+    const int t = threadIdx.x;
+    int32_t par = 0;
+    float zp = 0.f, zq = 0.f;
+    Partial pv[kStageParts];
+    if (t < a.N) {
+      par = a.parent[rowbase + t];
+      zp = zc[t];
+      zq = zc[(int64_t)a.B * a.N + t];
+    }
+    if (t < 2 * (a.N - 1)) {
+      const Partial* pr = parts + ((rowbase + (t >> 1)) * 2 + (t & 1)) * a.nch;  // written by the previous launch
+#pragma unroll
+      for (int i = 0; i < kStageParts; ++i) pv[i] = pr[i < a.nch ? i : a.nch - 1];
+    }
+    float r = 0.f;
+    if (t >= 1 && t < a.N) r = (float)uniform24(a.seed, (uint32_t)t, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
+    if (t < a.N) {
+      s_par[t] = par;
+      s_zp[t] = zp;
+      s_zq[t] = zq;
+      s_first[t] = a.N;
+      s_r[t] = r;
+    }
+    if (t < 2 * (a.N - 1)) merge_held(pv, a.nch, a.c, &s_cm[t & 1][t >> 1], &s_S[t & 1][t >> 1]);
   }
-  for (int r = threadIdx.x; r < 2 * (a.N - 1); r += kWNT) {
+  if (!one_round)
+    for (int i = threadIdx.x; i < a.N; i += kWNT) {
+      s_par[i] = a.parent[rowbase + i];
+      s_zp[i] = zc[i];
+      s_zq[i] = zc[(int64_t)a.B * a.N + i];
+      s_first[i] = a.N;
+    }
+  for (int r = one_round ? kWNT : threadIdx.x; r < 2 * (a.N - 1); r += kWNT) {
     const int u = r >> 1, which = r & 1;
     const Partial* pr = parts + ((rowbase + u) * 2 + which) * a.nch;  // written by the previous launch
     float M = kNegInf;
@@ -280,7 +337,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     }
     s_pt[i] = pt;
     s_qt[i] = qt;
-    s_r[i] = (float)uniform24(a.seed, (uint32_t)i, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
+    if (!one_round) s_r[i] = (float)uniform24(a.seed, (uint32_t)i, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
     if (s_par[i] >= 0 && s_par[i] < i) atomicMin(&s_first[s_par[i]], i);
   }
   lds_sync();
@@ -435,13 +492,41 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
   const double us = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
 
   const float* zc = a.zc + rowbase;
-  for (int i = threadIdx.x; i < a.N; i += kWNT) {
-    s_par[i] = a.parent[rowbase + i];
-    s_tok[i] = a.tok[rowbase + i];
-    s_zp[i] = zc[i];
-    s_first[i] = a.N;
+  const bool one_round = a.N <= kWNT && a.nch <= kStageParts;  // block-uniform
+  if (one_round) {
+    const int t = threadIdx.x;
+    int32_t par = 0, tok = 0;
+    float zp = 0.f;
+    Partial pv[kStageParts];
+    if (t < a.N) {
+      par = a.parent[rowbase + t];
+      tok = a.tok[rowbase + t];
+      zp = zc[t];
+    }
+    if (t < a.N - 1) {
+      const Partial* pr = parts + (rowbase + t) * a.nch;  // written by the previous launch
+#pragma unroll
+      for (int i = 0; i < kStageParts; ++i) pv[i] = pr[i < a.nch ? i : a.nch - 1];
+    }
+    float r = 0.f;
+    if (t >= 1 && t < a.N) r = (float)uniform24(a.seed, (uint32_t)t, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
+    if (t < a.N) {
+      s_par[t] = par;
+      s_tok[t] = tok;
+      s_zp[t] = zp;
+      s_first[t] = a.N;
+      s_r[t] = r;
+    }
+    if (t < a.N - 1) merge_held(pv, a.nch, a.c, &s_cm[t], &s_S[t]);
   }
-  for (int u = threadIdx.x; u < a.N - 1; u += kWNT) {
+  if (!one_round)
+    for (int i = threadIdx.x; i < a.N; i += kWNT) {
+      s_par[i] = a.parent[rowbase + i];
+      s_tok[i] = a.tok[rowbase + i];
+      s_zp[i] = zc[i];
+      s_first[i] = a.N;
+    }
+  for (int u = one_round ? kWNT : threadIdx.x; u < a.N - 1; u += kWNT) {
     const Partial* pr = parts + (rowbase + u) * a.nch;  // written by the previous launch
     float M = kNegInf;
     for (int i = 0; i < a.nch; ++i) M = fmaxf(M, pr[i].m);
@@ -476,7 +561,7 @@ __global__ __launch_bounds__(kWNT) void tree_pm_walk_kernel(TreeParams a) {
     P.pad = 0.f;
     const float zp = s_zp[i];
     s_pt[i] = __builtin_isnan(zp) ? 0.0 : prob_of(zp, a.c, P);
-    s_r[i] = (float)uniform24(a.seed, (uint32_t)i, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
+    if (!one_round) s_r[i] = (float)uniform24(a.seed, (uint32_t)i, (uint32_t)b, 0, a.round, 0);  // exact: 24-bit grid
     if (valid) atomicMin(&s_first[u], i);
   }
   lds_sync();
