@@ -25,10 +25,17 @@ FLAGS = [
 ]
 
 
-def build(verbose: bool = False) -> str:
+LIB_TIMELINE = os.path.join(HERE, "libspecverify_timeline.so")
+
+
+def build(verbose: bool = False, timeline: bool = False) -> str:
+    """Build the library; timeline=True builds the measurement variant with per-block wall-clock stamps
+    (libspecverify_timeline.so, -DSV_TIMELINE) beside it."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, *FLAGS, "-I" + os.path.join(ROOT, "include"), *srcs, "-o", tmp]
+    lib = LIB_TIMELINE if timeline else LIB
+    tmp = lib + ".tmp"
+    cmd = [HIPCC, *FLAGS, *(["-DSV_TIMELINE"] if timeline else []), "-I" + os.path.join(ROOT, "include"), *srcs,
+           "-o", tmp]
     res = subprocess.run(cmd, capture_output=True, text=True)
     noise = "is not a recognized feature for this target"
     err = "\n".join(ln for ln in (res.stdout + res.stderr).splitlines() if noise not in ln)
@@ -36,9 +43,9 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{err}")
     if verbose and err.strip():
         print(err, file=sys.stderr)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, timeline="--timeline" in sys.argv[1:]))

@@ -804,3 +804,17 @@ int32_t sv_geometric_fanout(int32_t F0, double a_p, double r, int32_t K, int32_t
 }
 
 }  // extern "C"
+
+extern "C" sv_status sv_timeline_set(void* buf, uint64_t records) {
+#ifdef SV_TIMELINE
+  if (!buf) records = 0;
+  if (sv::timeline_set_chain(buf, records) != hipSuccess || sv::timeline_set_chain_small(buf, records) != hipSuccess ||
+      sv::timeline_set_tree(buf, records) != hipSuccess)
+    return SV_EHIP;
+  return SV_OK;
+#else
+  (void)buf;
+  (void)records;
+  return SV_EUNSUPPORTED;
+#endif
+}

@@ -352,6 +352,7 @@ template <int DT>
 __device__ void stats_role(const ChainParams& a) {
   const int rows = a.pm ? a.K * a.gamma : (a.K + 1) * a.gamma;
   const int64_t per_seq = (int64_t)rows * a.nch1;
+  SV_STAMP_START(0);
   const int64_t bid = blockIdx.x;
   int b;
   int64_t rem;
@@ -392,6 +393,8 @@ __device__ void stats_role(const ChainParams& a) {
   const int64_t v1 = v0 + a.vpc1 < a.nvec ? v0 + a.vpc1 : a.nvec;
   uint32_t zbits = 0;
   const Partial part = range_stats<DT, kNT, kU>(row, a.V, v0, v1, a.c, zo >= 0, x, &zbits);
+  SV_STAMP(0, 1);
+  SV_STAMP_TAG(0, 1, b);
   // every store of this block is made by wave 0 (K <= 64 gathering threads)
   if (threadIdx.x < kWave) {
     if (threadIdx.x == 0) put_partial(static_cast<Partial*>(a.part1) + (int64_t)b * per_seq + (int64_t)lr * a.nch1 + ch, part);
@@ -401,6 +404,7 @@ __device__ void stats_role(const ChainParams& a) {
     __builtin_amdgcn_s_waitcnt(0);  // the wave's stores are complete (device-visible)
     if (threadIdx.x == 0) add_dev32(a.cnt + (int64_t)b * a.cstride, 1u);
   }
+  SV_STAMP_FLUSH(0);
 }
 
 template <int DT>
@@ -480,6 +484,7 @@ __device__ void draw_body(const ChainParams& a, int b, int g, Exchange& x, Decid
                           uint64_t* s_w1, SliceSums& ss, const Early& e) {
   const Job* pj = chain_decide<DT, PM>(a, b, g == 0, dec, e);
   const Job jb = *pj;
+  SV_STAMP(0, 2);
   const int64_t spv = (a.nvec + a.G - 1) / a.G;
   const int64_t v0 = (int64_t)g * spv < a.nvec ? (int64_t)g * spv : a.nvec;
   const int64_t v1 = v0 + spv < a.nvec ? v0 + spv : a.nvec;
@@ -504,7 +509,9 @@ __device__ void draw_body(const ChainParams& a, int b, int g, Exchange& x, Decid
       total = exchange_sum(x, sl.prepare(sp, a.V), s_words, &ss);
     }
   } else if (resid) {
-    total = exchange_sum(x, sl.prepare(sp, a.V), s_words, &ss);
+    const double mine = sl.prepare(sp, a.V);
+    SV_STAMP(0, 3);
+    total = exchange_sum(x, mine, s_words, &ss);
     if (!(total > 0.0)) {
       // residual mass rounded to 0: draw from p_{n+1} itself
       sp.rowQ = nullptr;
@@ -521,6 +528,7 @@ __device__ void draw_body(const ChainParams& a, int b, int g, Exchange& x, Decid
     sp.invSP = 1.f;
     plain = true;
   }
+  SV_STAMP(0, 4);
   int pick;
   double loc;
   pick_slice(ss, x.G, jb.u * total, &pick, &loc);
@@ -531,6 +539,7 @@ __device__ void draw_body(const ChainParams& a, int b, int g, Exchange& x, Decid
     if (plain) sl.prepare(sp, a.V);  // the owner's weights under the row's shift
     const int64_t t = sl.search(sp, a.V, loc);
     if (threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
+    SV_STAMP(0, 5);
   }
 }
 
@@ -554,6 +563,8 @@ __device__ void draw_role(const ChainParams& a, int d, Decided& dec) {
   __shared__ uint64_t s_words[kMaxG], s_w1[kMaxG];
   __shared__ int s_ok;
   SliceSums ss;  // the slices' values of the last exchange
+  SV_STAMP_START(0);
+  SV_STAMP_TAG(0, 2, b);
   Exchange x = make_exchange(a.slots, a.err, a.knobs, b, a.G, g);
   // everything that does not depend on the statistics, while they stream
   Early e;
@@ -575,8 +586,11 @@ __device__ void draw_role(const ChainParams& a, int d, Decided& dec) {
     }
   }
   __syncthreads();
+  SV_STAMP(0, 1);
   if (s_ok) draw_body<DT, HELD, PM>(a, b, g, x, dec, s_words, s_w1, ss, e);  // counts the exit itself
   if (!s_ok) draw_exit(a, b);
+  SV_STAMP(0, 6);
+  SV_STAMP_FLUSH(0);
 }
 
 template <int DT, bool HELD, bool PM>
@@ -604,6 +618,8 @@ hipError_t launch_chain_t(const ChainParams& p, hipStream_t s) {
   }
   return hipGetLastError();
 }
+
+SV_TIMELINE_SETTER(timeline_set_chain)
 
 hipError_t launch_chain(const ChainParams& p, sv_dtype dt, const Plan& plan, hipStream_t s) {
   (void)plan;

@@ -94,6 +94,8 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
   const int spv = (nvec + a.G - 1) / a.G;
   const int v0 = g * spv < nvec ? g * spv : nvec;
   const int v1 = v0 + spv < nvec ? v0 + spv : nvec;
+  SV_STAMP_START(0);
+  SV_STAMP_TAG(0, 3, b);
   uint64_t* words1 = small_slots(a, b);
   Exchange x = make_exchange(a.slots, a.err, a.knobs, b, a.G, g);
   x.slots = words1 + (int64_t)a.G * kSmallW;
@@ -158,6 +160,7 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
     mw[r] = mt[r];
   }
   rows_fmax_all(mw);
+  SV_STAMP(0, 1);
   float sw[kSmallRows];
 #pragma unroll
   for (int r = 0; r < kSmallRows; ++r) sw[r] = mt[r] == kNegInf ? 0.f : st[r] * fast_exp2(a.c * mt[r] - a.c * mw[r]);
@@ -171,6 +174,7 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
       s_ws[wave][r] = sw[r];
     }
   lds_sync();
+  SV_STAMP(0, 2);
 
   // the first round: thread r publishes row r's part as two tagged words
   const uint64_t tag1 = 1;
@@ -190,6 +194,7 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
       st_dev(words1 + (int64_t)g * kSmallW + 2 * r + 1, pack_sum(S) | tag1);
     }
   }
+  SV_STAMP(0, 3);
   // the waves share the wait and the merge: wave w takes rows w, w + 4,
   // w + 8 (those below R); lane q < G polls block q's two words of each
   constexpr int kRW = (kSmallRows + kW - 1) / kW;
@@ -254,6 +259,7 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
     }
   }
   lds_sync();
+  SV_STAMP(0, 4);
   bool any_late = false;
 #pragma unroll
   for (int w = 0; w < kW; ++w) any_late |= s_late[w] != 0;
@@ -289,6 +295,7 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
   const int32_t xn = __builtin_amdgcn_readlane(xt, n < a.gamma ? n : 0);
   if (threadIdx.x == 0) s_ex = (n < a.gamma && xn >= 0 && xn < a.V) ? xn : -1;
 
+  SV_STAMP(0, 5);
   // the draw: target row n (the bonus row when n = gamma), with draft row n
   // for a residual
   const int rP = n;
@@ -358,6 +365,7 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
     if (g == 0 && threadIdx.x == 0 && !(SP > 0.0)) set_error(a.err, SV_DERR_ROW);
     total = exchange_sum(x, sl.prepare(sp, a.V), s_words, &ss);
   }
+  SV_STAMP(0, 6);
   int pick;
   double loc;
   pick_slice(ss, x.G, us * total, &pick, &loc);
@@ -376,7 +384,11 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
     if (threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
   }
   small_exit_end(a, b, exits);
+  SV_STAMP(0, 7);
+  SV_STAMP_FLUSH(0);
 }
+
+SV_TIMELINE_SETTER(timeline_set_chain_small)
 
 hipError_t launch_chain_small(const ChainParams& p, sv_dtype dt, hipStream_t s) {
   const dim3 grid((unsigned)p.B * p.G), block(kSNT);

@@ -12,6 +12,73 @@
 
 namespace sv {
 
+// ---------------------------------------------------------------------------
+// Timeline builds (-DSV_TIMELINE, libspecverify_timeline.so): thread 0 of a
+// block keeps the 100 MHz wall clock (s_memrealtime) of each phase end in slot
+// k of the block's 16-slot record, written at the block's end to record
+// base + blockIdx.x of a buffer the host registers (sv_timeline_set).  Slot 15
+// holds a tag: role | seq << 8 | XCD << 40.  In the normal build the stamps
+// compile to nothing.
+// ---------------------------------------------------------------------------
+constexpr int kTimelineSlots = 16;
+#ifdef SV_TIMELINE
+static __device__ uint64_t* g_timeline;
+static __device__ uint64_t g_timeline_records;  // records the buffer holds
+// A block's stamps wait in LDS and go to memory once, at the block's end
+// (SV_STAMP_FLUSH): a global store in the middle of a kernel would be waited
+// for by the next wait on a load (this chip counts stores and loads together).
+__device__ __forceinline__ uint64_t* timeline_lds() {
+  __shared__ uint64_t s_tl[kTimelineSlots];
+  return s_tl;
+}
+__device__ __forceinline__ void timeline_put(int k, uint64_t v) {
+  if (threadIdx.x == 0) timeline_lds()[k] = v;
+}
+__device__ __forceinline__ void timeline_flush(uint64_t base) {
+  const uint64_t r = base + blockIdx.x;
+  if (threadIdx.x == 0 && g_timeline && r < g_timeline_records)
+    for (int k = 0; k < kTimelineSlots; ++k) g_timeline[r * kTimelineSlots + k] = timeline_lds()[k];
+}
+__device__ __forceinline__ void timeline_clear() {
+  if (threadIdx.x == 0)
+    for (int k = 0; k < kTimelineSlots; ++k) timeline_lds()[k] = 0;
+}
+#define SV_STAMP_START(base) (::sv::timeline_clear(), ::sv::timeline_put(0, __builtin_amdgcn_s_memrealtime()))
+#define SV_STAMP(base, k) ::sv::timeline_put((k), __builtin_amdgcn_s_memrealtime())
+#define SV_STAMP_VAL(base, k, v) ::sv::timeline_put((k), (uint64_t)(v))
+#define SV_STAMP_TAG(base, role, seq)                                                               \
+  ::sv::timeline_put(15, (uint64_t)(role) | ((uint64_t)(uint32_t)(seq) << 8) |                     \
+                             ((uint64_t)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xf) << 40))
+#define SV_STAMP_FLUSH(base) ::sv::timeline_flush(base)
+// Registers the stamp buffer of this translation unit (host side).
+#define SV_TIMELINE_SETTER(name)                                                                    \
+  hipError_t name(void* p, uint64_t records) {                                                      \
+    const hipError_t e = hipMemcpyToSymbol(HIP_SYMBOL(g_timeline), &p, sizeof(p));                  \
+    return e != hipSuccess ? e : hipMemcpyToSymbol(HIP_SYMBOL(g_timeline_records), &records, sizeof(records)); \
+  }
+// Accumulated intervals of a repeated phase (two kinds), per block.
+struct Lap {
+  uint64_t t = 0, sum[2] = {0, 0};
+  __device__ __forceinline__ void start() { t = __builtin_amdgcn_s_memrealtime(); }
+  __device__ __forceinline__ void lap(int i) {
+    const uint64_t u = __builtin_amdgcn_s_memrealtime();
+    sum[i] += u - t;
+    t = u;
+  }
+};
+#else
+#define SV_STAMP_START(base) ((void)0)
+#define SV_STAMP(base, k) ((void)0)
+#define SV_STAMP_VAL(base, k, v) ((void)0)
+#define SV_STAMP_TAG(base, role, seq) ((void)0)
+#define SV_STAMP_FLUSH(base) ((void)0)
+#define SV_TIMELINE_SETTER(name)
+struct Lap {
+  __device__ __forceinline__ void start() {}
+  __device__ __forceinline__ void lap(int) {}
+};
+#endif
+
 constexpr int kWave = 64;
 constexpr float kNegInf = -__builtin_huge_valf();
 

@@ -44,6 +44,7 @@
 namespace sv {
 
 constexpr int kTNT = 512;
+constexpr uint64_t kTimelineWalkBase = 16384;  // timeline records of the walk launch (the stats launch's start at 0)
 constexpr int kTU = 4;
 constexpr int kGather = SV_MAX_N / kTNT;  // candidate children per stats thread
 
@@ -58,6 +59,7 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
   const int b = (int)(rest % a.B);
   const int k = (int)(rest / a.B);  // this block streams the k-th node with children of sequence b
   const int64_t rowbase = (int64_t)b * a.N;
+  SV_STAMP_START(0);
   // the sequence's tree in LDS (one round of loads); blocks are laid out
   // k-major, so the blocks that stream come first and spread evenly over the
   // compute units, and the blocks past a sequence's last node with children
@@ -125,6 +127,8 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
   const int64_t v0 = (int64_t)ch * a.vpc;
   const int64_t v1 = v0 + a.vpc < a.nvec ? v0 + a.vpc : a.nvec;
   const Partial part = range_stats<DT, kTNT, kTU>(row, a.V, v0, v1, a.c);
+  SV_STAMP(0, 1);
+  SV_STAMP_TAG(0, 4, b);
   if (threadIdx.x == 0) put_partial(static_cast<Partial*>(a.part) + ((rowbase + u) * nw + which) * a.nch + ch, part);
   float* zc = a.zc + (int64_t)which * a.B * a.N + rowbase;
   if (ch == 0) {
@@ -136,6 +140,7 @@ __global__ __launch_bounds__(kTNT) void tree_stats_kernel(TreeParams a) {
     }
   }
   zero_slots(a.slots, a.nzero, bid, kTNT);  // for the walk launch
+  SV_STAMP_FLUSH(0);
 }
 
 // ---------------------------------------------------------------------------
@@ -255,6 +260,10 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   SliceSums ss;  // the slices' values of the last exchange
   __shared__ int s_cnt;
   const double us = uniform24(a.seed, 0, (uint32_t)b, 0, a.round, 1);
+  SV_STAMP_START(kTimelineWalkBase);
+  SV_STAMP_TAG(kTimelineWalkBase, 5, b);
+  Lap lp;        // rejection passes: summing the residual, exchanging the sums
+  int npass = 0;
 
   // the tree, the gathered logits and every node's row statistic, in one
   // round of loads (parts and logits of nodes without children were not
@@ -341,6 +350,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     if (s_par[i] >= 0 && s_par[i] < i) atomicMin(&s_first[s_par[i]], i);
   }
   lds_sync();
+  SV_STAMP(kTimelineWalkBase, 1);
 
   int node = 0, depth = 0;
   int ntried = 0;  // entries of s_tried (the same in every thread)
@@ -411,7 +421,12 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
         sl.load(rowP, rowQ, v0, v1);
         loaded = true;
       }
-      const double Dn = exchange_sum(x, sl.total(sp, a.V), s_w0, &ss);
+      lp.start();
+      const double mine = sl.total(sp, a.V);
+      lp.lap(0);
+      const double Dn = exchange_sum(x, mine, s_w0, &ss);
+      lp.lap(1);
+      ++npass;
       if (Dn > 0.0) {
         c = cnext;
         D = Dn;
@@ -442,6 +457,11 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     }
     break;
   }
+  SV_STAMP_VAL(kTimelineWalkBase, 2, lp.sum[0]);
+  SV_STAMP_VAL(kTimelineWalkBase, 3, lp.sum[1]);
+  SV_STAMP_VAL(kTimelineWalkBase, 4, npass);
+  SV_STAMP(kTimelineWalkBase, 5);
+  SV_STAMP_VAL(kTimelineWalkBase, 6, depth);
   lds_sync();
   if (writer) {
     for (int d = threadIdx.x; d < a.max_depth; d += kWNT)
@@ -455,6 +475,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     }
   }
   if (t >= 0 && threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
+  SV_STAMP_FLUSH(kTimelineWalkBase);
 }
 
 // Point-mass walk.  The G blocks of a sequence replay the same scalar
@@ -714,6 +735,8 @@ hipError_t launch_tree_t(const TreeParams& p, const Plan& plan, hipStream_t s) {
   }
   return hipGetLastError();
 }
+
+SV_TIMELINE_SETTER(timeline_set_tree)
 
 hipError_t launch_tree(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s) {
   return dt == SV_BF16 ? launch_tree_t<SV_BF16>(p, plan, s) : launch_tree_t<SV_F32>(p, plan, s);

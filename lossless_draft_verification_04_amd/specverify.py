@@ -19,7 +19,8 @@ import threading
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libspecverify.so")
+# SV_LIBRARY selects another build of the library (the timeline build), by path
+_LIB_PATH = os.environ.get("SV_LIBRARY") or os.path.join(_HERE, "libspecverify.so")
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
@@ -64,6 +65,7 @@ _SIGS = {
                        _i32),
     "sv_geometric_fanout": ([_i32, _f64, _f64, _i32, _i32, ctypes.POINTER(_i32)], _i32),
     "sv_read_probe": ([_P, _sz, _i32, _i32, _i32, _sz, _P, _P], _i32),
+    "sv_timeline_set": ([_P, ctypes.c_uint64], _i32),
 }
 for _name, (_args, _res) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -425,6 +427,17 @@ def sv_read_probe(buf: torch.Tensor, sink: torch.Tensor, blocks=1024, mode=0, un
     assert sink.numel() >= 3 and sink.element_size() == 4 and sink.device == buf.device
     _check(_lib.sv_read_probe(_ptr(buf), buf.numel() * buf.element_size(), int(blocks), int(mode), int(unroll),
                               int(chunk_bytes), _ptr(sink), _stream(buf.device)), "sv_read_probe")
+
+
+def sv_timeline_set(buf):
+    """Register a device buffer (uint64 [records, 16], zero-filled) for the timeline build's per-block stamps,
+    or None to stop.  Raises on a library built without timelines (SV_EUNSUPPORTED)."""
+    if buf is None:
+        _check(_lib.sv_timeline_set(None, 0), "sv_timeline_set")
+        return
+    assert buf.dtype == torch.int64 and buf.is_contiguous() and buf.numel() % 16 == 0
+    torch.cuda.synchronize(buf.device)
+    _check(_lib.sv_timeline_set(_ptr(buf), buf.numel() // 16), "sv_timeline_set")
 
 
 def sv_geometric_fanout(F0, a_p, r, K, capped_last=False):

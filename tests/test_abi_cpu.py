@@ -29,10 +29,15 @@ def declared_functions():
 
 def test_every_declared_function_is_exported():
     names = declared_functions()
-    assert len(names) == 18
+    assert len(names) == 19
     for n in names:
         assert hasattr(L, n), n
     assert set(names) == set(svx.EXPORTED)
+
+
+def test_timeline_setter_is_a_stub_in_the_normal_build():
+    # only the timeline build (-DSV_TIMELINE) records; the normal library refuses without touching the GPU
+    assert svx._lib.sv_timeline_set(None, 0) == svx.SV_EUNSUPPORTED
 
 
 def test_version_and_status_strings():
