@@ -809,7 +809,7 @@ extern "C" sv_status sv_timeline_set(void* buf, uint64_t records) {
 #ifdef SV_TIMELINE
   if (!buf) records = 0;
   if (sv::timeline_set_chain(buf, records) != hipSuccess || sv::timeline_set_chain_small(buf, records) != hipSuccess ||
-      sv::timeline_set_tree(buf, records) != hipSuccess)
+      sv::timeline_set_tree(buf, records) != hipSuccess || sv::timeline_set_fanout(buf, records) != hipSuccess)
     return SV_EHIP;
   return SV_OK;
 #else

@@ -21,6 +21,8 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
   constexpr int E = Fmt<DT>::kPerVec;
   const int r = blockIdx.x / a.nch;
   const int ch = blockIdx.x - r * a.nch;
+  SV_STAMP_START(0);
+  SV_STAMP_TAG(0, 6, r);
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   int F = a.F[r];
@@ -38,6 +40,7 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
     lv = t.v;
     li = t.i;
   }
+  SV_STAMP(0, 4);
   // merge the block's waves into wave 0's list
   __shared__ TopEntry s_list[kFNT / kWave][SV_MAX_FANOUT];
   __syncthreads();
@@ -65,6 +68,8 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
       a.out_ids[(int64_t)r * a.F_max + lane] = keep ? li : -1;
       if (a.out_vals) a.out_vals[(int64_t)r * a.F_max + lane] = keep ? lv : kNegInf;
     }
+    SV_STAMP(0, 5);
+    SV_STAMP_FLUSH(0);
     return;
   }
   if (wave == 0 && lane < a.F_max) put_entry(parts + (int64_t)ch * a.F_max + lane, lane < F ? lv : kNegInf,
@@ -82,6 +87,8 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
     if (lane == 0) __hip_atomic_store(&a.cnt[r], 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
+
+SV_TIMELINE_SETTER(timeline_set_fanout)
 
 hipError_t launch_fanout(const FanoutParams& p, sv_dtype dt, const Plan& plan, hipStream_t s) {
   if (dt == SV_BF16)

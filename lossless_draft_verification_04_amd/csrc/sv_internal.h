@@ -184,6 +184,7 @@ hipError_t launch_chain(const ChainParams& p, sv_dtype dt, const Plan& plan, hip
 hipError_t timeline_set_chain(void* p, uint64_t records);
 hipError_t timeline_set_chain_small(void* p, uint64_t records);
 hipError_t timeline_set_tree(void* p, uint64_t records);
+hipError_t timeline_set_fanout(void* p, uint64_t records);
 #endif
 // Small calls (sv_chain_small.hip): each of G blocks per sequence holds its
 // slice (at most kSmallTiles tiles of 256 vectors) of every row the step may

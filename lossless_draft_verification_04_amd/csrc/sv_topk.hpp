@@ -310,6 +310,7 @@ __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V,
       for (int u = 0; u < kWin; ++u) d[u] = nx[u];
     }
   }
+  SV_STAMP(0, 2);  // (timeline builds) this thread's pass 1 is done
   const float m = bm[0];
   const int32_t mv = bo[0];
   s_m[tid] = m;
@@ -320,6 +321,7 @@ __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V,
     s_full = 0;
   }
   lds_sync();
+  SV_STAMP(0, 6);  // (timeline builds) every thread's pass 1 is done
   // the F best threads (wave 0: F rounds of a wave-wide selection over the
   // NW entries each lane holds)
   if (wave == 0) {
@@ -360,6 +362,7 @@ __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V,
     }
   }
   lds_sync();
+  SV_STAMP(0, 3);  // (timeline builds) the F best threads are selected
   const float tf = s_tf;
   int count = 0;
   if (MAY_HOLD && held) {

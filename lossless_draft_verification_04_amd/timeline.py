@@ -1,4 +1,4 @@
-"""Per-phase wall-clock timelines of the chain, small-call chain and tree kernels (a measurement tool).
+"""Per-phase wall-clock timelines of the chain, small-call chain, tree and fan-out kernels (a measurement tool).
 
 Uses the timeline build of the library, in which thread 0 of every block stores the 100 MHz wall clock at the
 end of each phase (`sv_timeline_set` in include/specverify.h).  On a GPU:
@@ -144,6 +144,39 @@ def tree(stamps, reps):
     return lines
 
 
+def fanout(stamps, reps):
+    wl = W.tree_zipf(**W.TREE_FANOUT)
+    B, N, V = wl.tensors["drf"].shape
+    F = torch.tensor([W.fanout_schedule(8, 0.7, 1.0, 9)[d] for d in wl.tensors["depth"].reshape(-1).tolist()],
+                     dtype=torch.int32, device="cuda")
+    x = wl.to("cuda")["drf"].reshape(B * N, V)
+    fn = lambda: svx.sv_fanout_topk(x, F, 8, want_vals=False)  # noqa: E731
+    for _ in range(5):
+        fn()
+    torch.cuda.synchronize()
+    names = ["start", "thread 0 pass 1", "all pass 1", "threads selected", "scan done", "written"]
+    cols_of = [0, 2, 6, 3, 4, 5]
+    lines = [f"## fan-out, {B * N} tree draft rows, V={V} bf16", "",
+             "| call | blocks | " + " | ".join(names) + " |", "|---|---|" + "---|" * len(names)]
+    for rep in range(reps):
+        _, st, role, _, _ = stamps.take(fn)
+        Bk = np.nonzero(role == 6)[0]
+        t0 = st[Bk, 0].min()
+        cols = []
+        for c in cols_of:
+            v = st[Bk, c]
+            v = v[v > 0]
+            cols.append(f"{np.median((v - t0) * TICK_US):.2f} / {((v.max() - t0) * TICK_US):.2f}" if len(v) else "—")
+        lines.append(f"| {rep} | {len(Bk)} | " + " | ".join(cols) + " |")
+        d = (st[Bk, 4] - st[Bk, 6]) * TICK_US
+        lines.append("")
+        lines.append(f"per block, all pass 1 to scan done: median {np.median(d):.2f}, max {d.max():.2f}; "
+                     f"selection (all pass 1 to selected): median {np.median((st[Bk, 3] - st[Bk, 6]) * TICK_US):.2f}")
+        lines.append("")
+    lines += ["(median / max over the blocks)", ""]
+    return lines
+
+
 def main(argv=None):
     argv = sys.argv[1:] if argv is None else argv
     reps = int(argv[0]) if argv else 2
@@ -151,7 +184,7 @@ def main(argv=None):
         raise SystemExit("timeline: needs a GPU")
     stamps = Stamps(torch.device("cuda", 0))
     lines = ["# Kernel timelines (timeline build, wall-clock stamps per block)", ""]
-    for part in (chain, small, tree):
+    for part in (chain, small, tree, fanout):
         lines += part(stamps, reps)
         print("\n".join(lines), flush=True)
         lines = []
