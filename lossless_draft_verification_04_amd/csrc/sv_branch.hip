@@ -137,29 +137,14 @@ __global__ __launch_bounds__(kBNT) void branch_fork_kernel(BranchParams a) {
   const int64_t v0 = (int64_t)ch * a.vpc2;
   const int64_t v1 = v0 + a.vpc2 < a.nvec ? v0 + a.vpc2 : a.nvec;
   {
-    const TopPair t = wave_topk_scan<kBNT, E>(RowValues<DT>{row, a.V}, v0, v1, a.V, k);
+    const TopPair t = block_topk<kBNT, E>(RowValues<DT>{row, a.V}, v0, v1, a.V, k);
     lv = t.v;
     li = t.i;
   }
-  __shared__ TopEntry s_list[kBNT / kWave][SV_MAX_FANOUT];
-  lds_sync();
-  if (lane < SV_MAX_FANOUT) {
-    s_list[wave][lane].val = lv;
-    s_list[wave][lane].idx = li;
-  }
-  lds_sync();
+  // wave 0 holds the part's list
   TopEntry* lists = static_cast<TopEntry*>(a.lists) + (int64_t)b * a.nch2 * a.k_max;
-  if (wave == 0) {
-    for (int w = 1; w < kBNT / kWave; ++w)
-      for (int e = 0; e < k; ++e) {
-        const TopEntry t = s_list[w][e];
-        const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), k - 1));
-        const int32_t ti = __builtin_amdgcn_readlane(li, k - 1);
-        if (t.idx == kNoIdx || (ti != kNoIdx && !top_better(t.val, t.idx, tv, ti))) break;
-        wave_insert(lv, li, t.val, t.idx, k, lane);
-      }
-    if (lane < a.k_max) put_entry(lists + (int64_t)ch * a.k_max + lane, lane < k ? lv : kNegInf, lane < k ? li : kNoIdx);
-  }
+  if (wave == 0 && lane < a.k_max)
+    put_entry(lists + (int64_t)ch * a.k_max + lane, lane < k ? lv : kNegInf, lane < k ? li : kNoIdx);
   if (!arrive_last<kBNT>(&a.cnt[b], (uint32_t)a.nch2)) return;
   if (wave == 0) {
     float fv = kNegInf;

@@ -34,6 +34,10 @@ __device__ __forceinline__ uint64_t* timeline_lds() {
 __device__ __forceinline__ void timeline_put(int k, uint64_t v) {
   if (threadIdx.x == 0) timeline_lds()[k] = v;
 }
+// Slot k <- the latest of the values the block's waves put there.
+__device__ __forceinline__ void timeline_last(int k, uint64_t v) {
+  if ((threadIdx.x & 63) == 0) atomicMax(reinterpret_cast<unsigned long long*>(&timeline_lds()[k]), (unsigned long long)v);
+}
 __device__ __forceinline__ void timeline_flush(uint64_t base) {
   const uint64_t r = base + blockIdx.x;
   if (threadIdx.x == 0 && g_timeline && r < g_timeline_records)
@@ -46,6 +50,7 @@ __device__ __forceinline__ void timeline_clear() {
 #define SV_STAMP_START(base) (::sv::timeline_clear(), ::sv::timeline_put(0, __builtin_amdgcn_s_memrealtime()))
 #define SV_STAMP(base, k) ::sv::timeline_put((k), __builtin_amdgcn_s_memrealtime())
 #define SV_STAMP_VAL(base, k, v) ::sv::timeline_put((k), (uint64_t)(v))
+#define SV_STAMP_LAST(base, k) ::sv::timeline_last((k), __builtin_amdgcn_s_memrealtime())
 #define SV_STAMP_TAG(base, role, seq)                                                               \
   ::sv::timeline_put(15, (uint64_t)(role) | ((uint64_t)(uint32_t)(seq) << 8) |                     \
                              ((uint64_t)(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 0xf) << 40))
@@ -70,6 +75,7 @@ struct Lap {
 #define SV_STAMP_START(base) ((void)0)
 #define SV_STAMP(base, k) ((void)0)
 #define SV_STAMP_VAL(base, k, v) ((void)0)
+#define SV_STAMP_LAST(base, k) ((void)0)
 #define SV_STAMP_TAG(base, role, seq) ((void)0)
 #define SV_STAMP_FLUSH(base) ((void)0)
 #define SV_TIMELINE_SETTER(name)

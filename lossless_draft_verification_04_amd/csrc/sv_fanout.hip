@@ -4,10 +4,9 @@
 // the draft logits at every lookahead position k.  Here: for each row r the
 // F[r] largest logits, value descending, index ascending on ties.
 //
-// One launch: a block per (row part).  The block finds its part's top F in
-// two passes (sv_topk.hpp) and merges its waves' lists; a row in one part
-// is written by its block, otherwise the last block of the row merges the
-// parts' lists and writes them.
+// One launch: a block per (row part).  The block finds its part's top F
+// (sv_topk.hpp); a row in one part is written by its block, otherwise the
+// last block of the row merges the parts' lists and writes them.
 #include "sv_device.hpp"
 #include "sv_internal.h"
 #include "sv_topk.hpp"
@@ -36,32 +35,13 @@ __global__ __launch_bounds__(kFNT) void fanout_kernel(FanoutParams a) {
   const int64_t v0 = (int64_t)ch * a.vpc;
   const int64_t v1 = v0 + a.vpc < a.nvec ? v0 + a.vpc : a.nvec;
   if (F > 0) {
-    const TopPair t = wave_topk_scan<kFNT, E>(RowValues<DT>{row, a.V}, v0, v1, a.V, F);
+    const TopPair t = block_topk<kFNT, E>(RowValues<DT>{row, a.V}, v0, v1, a.V, F);
     lv = t.v;
     li = t.i;
   }
   SV_STAMP(0, 4);
-  // merge the block's waves into wave 0's list
-  __shared__ TopEntry s_list[kFNT / kWave][SV_MAX_FANOUT];
-  __syncthreads();
-  if (lane < SV_MAX_FANOUT) {
-    s_list[wave][lane].val = lv;
-    s_list[wave][lane].idx = li;
-  }
-  __syncthreads();
+  // wave 0 holds the part's list
   TopEntry* parts = static_cast<TopEntry*>(a.part) + (int64_t)r * a.nch * a.F_max;
-  if (wave == 0 && F > 0) {
-    // each list is sorted: stop at its first entry that does not beat the
-    // current F-th best
-    for (int w = 1; w < kFNT / kWave; ++w)
-      for (int e = 0; e < F; ++e) {
-        const TopEntry t = s_list[w][e];
-        const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), F - 1));
-        const int32_t ti = __builtin_amdgcn_readlane(li, F - 1);
-        if (t.idx == kNoIdx || (ti != kNoIdx && !top_better(t.val, t.idx, tv, ti))) break;
-        wave_insert(lv, li, t.val, t.idx, F, lane);
-      }
-  }
   if (a.nch == 1) {  // the whole row: no parts to merge
     if (wave == 0 && lane < a.F_max) {
       const bool keep = lane < F && li != kNoIdx;

@@ -194,30 +194,15 @@ __global__ __launch_bounds__(kPNT) void presto_expand_kernel(PrestoParams a) {
     if (!empty) {
       const TopPair t =
           lam == 0.f
-              ? wave_topk_scan<kPNT, E, false, 4>(ProxyValues<DT, true>{rowP, rowQ, a.V, 0.f, 0.f}, v0, v1, a.V, a.k)
-              : wave_topk_scan<kPNT, E, false, 4>(ProxyValues<DT, false>{rowP, rowQ, a.V, (offP - offQ) / a.c, lam},
-                                                  v0, v1, a.V, a.k);
+              ? block_topk<kPNT, E, false>(ProxyValues<DT, true>{rowP, rowQ, a.V, 0.f, 0.f}, v0, v1, a.V, a.k)
+              : block_topk<kPNT, E, false>(ProxyValues<DT, false>{rowP, rowQ, a.V, (offP - offQ) / a.c, lam},
+                                              v0, v1, a.V, a.k);
       lv = t.v;
       li = t.i;
     }
-    // logit units -> log2 of the proxy weight
+    // wave 0 holds the part's list; logit units -> log2 of the proxy weight
     if (li != kNoIdx) lv = __builtin_fmaf(lv, a.c, -offQ);
-    __shared__ TopEntry s_list[kPNT / kWave][SV_MAX_FANOUT];
-    lds_sync();
-    if (lane < SV_MAX_FANOUT) {
-      s_list[wave][lane].val = lv;
-      s_list[wave][lane].idx = li;
-    }
-    lds_sync();
     if (wave == 0) {
-      for (int w = 1; w < kPNT / kWave; ++w)
-        for (int e = 0; e < a.k; ++e) {
-          const TopEntry t = s_list[w][e];
-          const float tv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), a.k - 1));
-          const int32_t ti = __builtin_amdgcn_readlane(li, a.k - 1);
-          if (t.idx == kNoIdx || (ti != kNoIdx && !top_better(t.val, t.idx, tv, ti))) break;
-          wave_insert(lv, li, t.val, t.idx, a.k, lane);
-        }
       if (a.nch2 == 1 && lane < a.k) put_entry(static_cast<TopEntry*>(a.leaf_lists) + (rowbase + u) * a.k + lane, lv, li);
       if (a.nch2 > 1 && lane < a.k) put_entry(lists + lane, lv, li);
     }

@@ -3,12 +3,13 @@
 // fork and the PRESTO expansion.
 //
 // Lists live in registers, one entry per lane (lane i = i-th best).  The scan
-// takes two passes (block_topk_scan): every thread first keeps only the best
-// element of the vectors it owns, the block selects the F threads with the
-// best such elements by F rounds of a wave-wide DPP reduction, and only
-// those threads' vectors are looked at again and their qualifying values
-// inserted with a lane shift.  Lists from other blocks are merged by the same
-// selection rounds (wave_merge_entries).
+// (block_topk) takes two passes: every thread first keeps only the best
+// element of the vectors it owns; each wave bounds the block's F-th best from
+// below by its own F best threads; only the threads whose best reaches the
+// bound are looked at again, their values at or above it are listed in LDS,
+// and one wave picks the F best of the list.  Entries compare as one 64-bit
+// key (top_key).  Lists from other blocks are merged by rounds of a
+// wave-wide selection (wave_merge_entries).
 #pragma once
 
 #include "sv_device.hpp"
@@ -50,7 +51,6 @@ template <int CTRL, int ROWS>
 __device__ __forceinline__ float dpp_f(float old, float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(old), __float_as_int(v), CTRL, ROWS, 0xF, false));
 }
-constexpr int kWaveShr1 = 0x138;  // lane l takes lane l - 1
 constexpr int kRowShr = 0x110;    // + n: lane l takes lane l - n within its row of 16
 constexpr int kRowBcast15 = 0x142, kRowBcast31 = 0x143;
 
@@ -77,26 +77,6 @@ __device__ __forceinline__ void wave_best(float& v, int32_t& i) {
   best_step<kRowBcast31, 0xC>(v, i);
   v = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), kWave - 1));
   i = __builtin_amdgcn_readlane(i, kWave - 1);
-}
-
-// Insert (v, i) into the wave's sorted list (lane l holds entry l; lanes
-// >= F hold the empty entry).  Wave-uniform arguments.
-__device__ __forceinline__ void wave_insert(float& lv, int32_t& li, float v, int32_t i, int F, int lane) {
-  const bool here = top_better(v, i, lv, li) & (lane < F);
-  const uint64_t m = __ballot(here);
-  if (!m) return;
-  const int pos = __builtin_ctzll(m);
-  const float up_v = dpp_f<kWaveShr1, 0xF>(lv, lv);
-  const int32_t up_i = dpp_i<kWaveShr1, 0xF>(li, li);
-  if (lane < F) {
-    if (lane > pos) {
-      lv = up_v;
-      li = up_i;
-    } else if (lane == pos) {
-      lv = v;
-      li = i;
-    }
-  }
 }
 
 // One logit row as a value source (elements past V read as -inf; -inf
@@ -170,7 +150,7 @@ __device__ __forceinline__ void wave_merge_entries(const TopEntry* src, int n, i
   }
 }
 
-// A value source for the scans below provides
+// A value source for the scan below provides
 //   using Data = ...;                        one vector's raw data
 //   Data load(int64_t v) const;              the loads of vector v
 //   void values(const Data&, int64_t v, float* x) const;
@@ -182,91 +162,199 @@ struct TopPair {
   int32_t i;
 };
 
-// Insert the values of one vector per lane that `mine` flags (lane l's
-// vector is vector vs of the range; x its E values) into the wave's list of
-// F entries; *count is the number of entries held (wave-uniform).
-template <int E>
-__device__ __forceinline__ void insert_flagged(const float (&x)[E], uint32_t mine, int64_t vs, int F, float& lv,
-                                               int32_t& li, int* count, int lane) {
-  uint64_t cm = __ballot(mine != 0);
-  while (cm) {
-    const int sl = __builtin_ctzll(cm);
-    cm &= cm - 1;
-    uint32_t bits = (uint32_t)__builtin_amdgcn_readlane((int)mine, sl);
-    const int64_t v = readlane_i64(vs, sl);
-    while (bits) {
-      const int e = __builtin_ctz(bits);
-      bits &= bits - 1;
-      float xe = 0.f;
-#pragma unroll
-      for (int q = 0; q < E; ++q)
-        if (q == e) xe = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x[q]), sl));
-      const int32_t ie = (int32_t)(v * E + e);
-      const float fv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lv), F - 1));
-      const int32_t fi = __builtin_amdgcn_readlane(li, F - 1);
-      if (*count < F || top_better(xe, ie, fv, fi)) {
-        wave_insert(lv, li, xe, ie, F, lane);
-        if (*count < F) ++*count;
-      }
+// Order key of an entry (value descending, index ascending) as one unsigned
+// 64-bit compare, larger = better: the value's bits map to unsigned integers
+// in the value order (-0 keyed as +0, so equal values tie), and the index is
+// complemented (a lower index keys higher; kNoIdx keys below every element
+// index).  Key 0 is below every entry and stands for "none".
+__device__ __forceinline__ uint64_t top_key(float v, int32_t i) {
+  const uint32_t b = __float_as_uint(v == 0.f ? 0.f : v);
+  const uint32_t o = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+  return ((uint64_t)o << 32) | (uint64_t)(~(uint32_t)i);
+}
+__device__ __forceinline__ int32_t key_index(uint64_t k) { return (int32_t)~(uint32_t)k; }
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t k, int l) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)k, l);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(k >> 32), l);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// k <- the larger of itself and the key DPP pattern CTRL brings in.
+template <int CTRL, int ROWS>
+__device__ __forceinline__ void key_max_step(uint64_t& k) {
+  const int32_t lo = (int32_t)(uint32_t)k;
+  const int32_t hi = (int32_t)(uint32_t)(k >> 32);
+  const uint64_t o = ((uint64_t)(uint32_t)dpp_i<CTRL, ROWS>(hi, hi) << 32) | (uint32_t)dpp_i<CTRL, ROWS>(lo, lo);
+  k = o > k ? o : k;
+}
+// The wave's largest key, in every lane (full exec): within rows of 16, then
+// across rows, ending in lane 63.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
+  key_max_step<kRowShr + 1, 0xF>(k);
+  key_max_step<kRowShr + 2, 0xF>(k);
+  key_max_step<kRowShr + 4, 0xF>(k);
+  key_max_step<kRowShr + 8, 0xF>(k);
+  key_max_step<kRowBcast15, 0xA>(k);
+  key_max_step<kRowBcast31, 0xC>(k);
+  return readlane_u64(k, kWave - 1);
+}
+
+// Candidate entries a block collects for its final selection (LDS).
+constexpr int kCand = 512;
+
+// A listed candidate: the value's bits (low word) and its index (high word).
+__device__ __forceinline__ uint64_t pack_cand(float v, int32_t i) {
+  return ((uint64_t)(uint32_t)i << 32) | __float_as_uint(v);
+}
+__device__ __forceinline__ float cand_value(uint64_t c) { return __uint_as_float((uint32_t)c); }
+__device__ __forceinline__ uint64_t cand_key(uint64_t c) { return top_key(cand_value(c), (int32_t)(c >> 32)); }
+
+// The F best of n candidates (cand in LDS; n <= kCand) as the wave's list:
+// lane l <- the l-th best, empty entries past the n-th.  Returns the F-th
+// best key (0 when n < F).  Up to 64 candidates: every candidate counts the
+// candidates with a larger key (its rank) and moves to the lane of that
+// rank; more: F rounds of a wave-wide maximum over kCand / 64 keys per lane.
+__device__ __forceinline__ uint64_t wave_select(const uint64_t* cand, int n, int F, int lane, float& lv,
+                                                int32_t& li) {
+  lv = kNegInf;
+  li = kNoIdx;
+  if (n <= kWave) {
+    const uint64_t c = lane < n ? cand[lane] : 0ull;
+    const uint64_t k = lane < n ? cand_key(c) : 0ull;
+    int above = 0;
+    for (int j = 0; j < n; ++j) above += readlane_u64(k, j) > k ? 1 : 0;
+    const int rank = lane < n ? above : lane;
+    // the ranks are a permutation of the lanes: a forward permute puts
+    // every candidate in the lane of its rank
+    const int to = rank * 4;
+    const uint32_t klo = (uint32_t)__builtin_amdgcn_ds_permute(to, (int)(uint32_t)k);
+    const uint32_t khi = (uint32_t)__builtin_amdgcn_ds_permute(to, (int)(uint32_t)(k >> 32));
+    const float pv = __int_as_float(__builtin_amdgcn_ds_permute(to, (int)(uint32_t)c));
+    const uint64_t pk = ((uint64_t)khi << 32) | klo;
+    if (lane < n && lane < F) {
+      lv = pv;
+      li = key_index(pk);
     }
+    return n >= F ? readlane_u64(pk, F - 1) : 0ull;
+  }
+  constexpr int H = kCand / kWave;
+  uint64_t hk[H];
+#pragma unroll
+  for (int h = 0; h < H; ++h) {
+    const int e = h * kWave + lane;
+    hk[h] = e < n ? cand_key(cand[e]) : 0ull;
+  }
+  uint64_t kth = 0;
+  for (int r = 0; r < F; ++r) {
+    uint64_t b = 0;
+    int bh = 0;
+#pragma unroll
+    for (int h = 0; h < H; ++h) {
+      const bool t = hk[h] > b;
+      b = t ? hk[h] : b;
+      bh = t ? h : bh;
+    }
+    const uint64_t w = wave_max_key(b);
+    if (w == 0) return 0ull;  // fewer than F candidates
+    const int owner = __builtin_ctzll(__ballot(b == w));  // keys are unique
+    const float wv = cand_value(cand[__builtin_amdgcn_readlane(bh, owner) * kWave + owner]);
+#pragma unroll
+    for (int h = 0; h < H; ++h) hk[h] = hk[h] == w ? 0ull : hk[h];
+    if (lane == r) {
+      lv = wv;
+      li = key_index(w);
+    }
+    kth = w;
+  }
+  return kth;
+}
+
+// Flag the values of vector vs (vs < 0: none; d its data) whose keys reach
+// tau and append them to the candidate list (every append is counted; past
+// kCand only the count grows).  Branch-free per value: a value's key is its
+// order bits (-0 as +0) over its complemented index.
+template <int E, class Src>
+__device__ __forceinline__ void flag_candidates(const Src& src, const typename Src::Data& d, int64_t vs, int V,
+                                                uint64_t tau, uint64_t* cand, int* nc) {
+  if (vs < 0) return;
+  float x[E];
+  src.values(d, vs, x);
+  const int32_t i0 = (int32_t)(vs * E);
+  uint32_t mine = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const uint32_t b = __float_as_uint(x[e] + 0.f);  // -0 + 0 = +0
+    const uint32_t o = b ^ ((uint32_t)((int32_t)b >> 31) | 0x80000000u);
+    const uint64_t key = ((uint64_t)o << 32) | (uint32_t)~(uint32_t)(i0 + e);
+    const bool ok = (i0 + e < V) & (!Src::kSkipNegInf | (x[e] > kNegInf)) & (key >= tau);
+    mine |= (uint32_t)ok << e;
+  }
+  if (!mine) return;
+  const int pos = atomicAdd(nc, __builtin_popcount(mine));
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int p = pos + __builtin_popcount(mine & ((1u << e) - 1u));
+    if (((mine >> e) & 1u) & (p < kCand)) cand[p] = pack_cand(x[e], i0 + e);
   }
 }
 
-// The block's top F values of [v0, v1) as per-wave lists (F <= 64; every
-// wave of the block calls it with the same arguments).  Block thread t owns
-// the vectors v0 + t + k * NT.
-//  Pass 1 streams the range once; each thread keeps only its best element
-//  (value desc, then vector asc), about one max and one compare per vector.
-//  The block's F best threads by that element are the only threads that can
-//  own a top-F value: a value owned by any other thread is beaten by the F
-//  selected threads' bests.  So
-//  pass 2 looks again at just those threads' vectors -- still in registers
-//  when every thread owns at most kWin of them, else re-read (F times the
-//  range / NT vectors, mostly from L2) spread over the waves -- and each wave
-//  lists the values of its share that reach the F-th selected best,
-//  inserting each with a lane shift.
-// Each wave returns its list (lane l = l-th best); the block's top F is the
-// top F of the waves' lists.  (Keeping running top-F lists during the
-// stream instead costs an insertion per new record, about F ln(n / F) per
-// list, which dominated at F >= 4.)  MAY_HOLD = false drops the register
+// The block's top F values of [v0, v1) (F <= 64; every thread of the block
+// calls it with the same arguments): wave 0 returns the list (lane l = l-th
+// best, value descending, index ascending), the other waves empty entries.
+// Block thread t owns the vectors v0 + t + k * NT.
+//  Pass 1 streams the range once; each thread keeps only its best vector by
+//  largest element (value desc, then vector asc): one max and one compare
+//  per vector.  Its "thread key" is the key of that value at the vector's
+//  first element index, a bound from above on the key of every element the
+//  thread owns.
+//  Bound: the block's threads form 64 groups of NT / 64; p is the largest
+//  value such that at least F groups hold a thread whose best value reaches
+//  it, so F distinct elements reach p and every top-F value is at least p
+//  (tau = the key of value p at the lowest-keyed index).
+//  Pass 2 looks again at the vectors of the threads whose key reaches tau --
+//  still in registers when every thread owns at most kWin of them, else
+//  re-read by the thread's wave -- and lists every value whose key reaches
+//  tau in LDS.  The F best listed values are the block's top F.  If more
+//  than kCand values are listed (many ties at p), tau rises to the F-th best
+//  key among the kept ones (again a bound from below on the top F), and
+//  pass 2 is repeated.
+// Outside the register path every thread keeps its best vector's data in
+// registers and the largest value of its other vectors, so that pass 2 reads
+// memory again only for a thread whose other vectors can hold a value at or
+// above tau (then all its vectors).  MAY_HOLD = false drops the register
 // path (it keeps kWin vectors live across the selection).
-template <int NT, int E, bool MAY_HOLD, int KEEP, class Src>
-__device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V, int F) {
-  constexpr int NW = NT / kWave;
+template <int NT, int E, bool MAY_HOLD = true, class Src>
+__device__ __forceinline__ TopPair block_topk(const Src src, int64_t v0, int64_t v1, int V, int F) {
   constexpr int kWin = 4;   // vectors in flight per thread
-  constexpr int kKeep = KEEP > 0 ? KEEP : 1;  // best vectors a thread remembers for pass 2
   const int lane = threadIdx.x & (kWave - 1);
   const int wave = threadIdx.x / kWave;
   const int tid = threadIdx.x;
-  __shared__ float s_m[NT];
-  __shared__ int32_t s_mv[NT];
-  __shared__ uint8_t s_pick[NT];
-  __shared__ int32_t s_sel[kWave];
-  __shared__ int32_t s_rr[kWave * kKeep];  // vectors pass 2 reads again (offsets in the range)
-  __shared__ int s_nsel, s_nrr, s_full;
-  __shared__ float s_tf;
+  __shared__ uint64_t s_cand[kCand];
+  __shared__ uint32_t s_gm[kWave];
+  __shared__ uint64_t s_tau;
+  __shared__ int s_nc;
   float lv = kNegInf;
   int32_t li = kNoIdx;
   if (F <= 0) return TopPair{lv, li};
   const int64_t span = v1 - v0;
   const int64_t nk = (span + NT - 1) / NT;  // vectors per thread at most
   const bool held = MAY_HOLD && nk <= kWin;  // block-uniform
-  // pass 1: this thread's kKeep best vectors by their largest element, as
-  // (value, vector offset), best first (equal values: lower offset first);
-  // the first is the thread's best element
-  float bm[kKeep];
-  int32_t bo[kKeep];
-#pragma unroll
-  for (int i = 0; i < kKeep; ++i) {
-    bm[i] = kNegInf;
-    bo[i] = kNoIdx;
-  }
+  // pass 1: this thread's best vector by its largest element (value desc,
+  // then vector offset asc): value bm, offset bo, data bd; and the largest
+  // element of its other vectors, mdrop (NaN: none; fmaxf returns the other
+  // operand of a NaN)
+  float bm = kNegInf;
+  int32_t bo = kNoIdx;
+  typename Src::Data bd{};
+  float mdrop = __builtin_nanf("");
   typename Src::Data d[kWin];
   if (span > 0) {  // block-uniform
+    // loads past the range are not issued: a load left in flight at the end
+    // of the stream would be waited for after it
 #pragma unroll
     for (int u = 0; u < kWin; ++u) {
       const int64_t a = v0 + tid + (int64_t)u * NT;
-      d[u] = src.load(a < v1 ? a : v1 - 1);  // clamped: every load is issued
+      if (a < v1) d[u] = src.load(a);
     }
     for (int64_t v = v0 + tid; v < v1; v += (int64_t)kWin * NT) {
       typename Src::Data nx[kWin];
@@ -274,7 +362,7 @@ __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V,
 #pragma unroll
         for (int u = 0; u < kWin; ++u) {
           const int64_t a = v + (int64_t)(kWin + u) * NT;
-          nx[u] = src.load(a < v1 ? a : v1 - 1);
+          if (a < v1) nx[u] = src.load(a);
         }
       }
 #pragma unroll
@@ -289,19 +377,13 @@ __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V,
           // a vector always holds a listable element unless -inf is not listed
           const bool has = !Src::kSkipNegInf || vm > kNegInf;
           if (has) {
-            // insertion by carrying the displaced entry down the list
-            float cv = vm;
-            int32_t co = (int32_t)(vu - v0);
-#pragma unroll
-            for (int i = 0; i < kKeep; ++i) {
-              const bool t = (bo[i] == kNoIdx) | top_better(cv, co, bm[i], bo[i]);
-              const float sv = bm[i];
-              const int32_t so = bo[i];
-              bm[i] = t ? cv : bm[i];
-              bo[i] = t ? co : bo[i];
-              cv = t ? sv : cv;
-              co = t ? so : co;
-            }
+            const int32_t o = (int32_t)(vu - v0);
+            const bool t = (bo == kNoIdx) | top_better(vm, o, bm, bo);
+            // the value that is not the best from here on
+            if (!t | (bo != kNoIdx)) mdrop = fmaxf(mdrop, t ? bm : vm);
+            bm = t ? vm : bm;
+            bo = t ? o : bo;
+            if (t) bd = d[u];
           }
         }
       }
@@ -311,152 +393,108 @@ __device__ TopPair block_topk_scan(const Src src, int64_t v0, int64_t v1, int V,
     }
   }
   SV_STAMP(0, 2);  // (timeline builds) this thread's pass 1 is done
-  const float m = bm[0];
-  const int32_t mv = bo[0];
-  s_m[tid] = m;
-  s_mv[tid] = mv;
-  s_pick[tid] = 0;
-  if (tid == 0) {
-    s_nrr = 0;
-    s_full = 0;
+  SV_STAMP_LAST(0, 9);  // (timeline builds) the last wave's pass 1 is done
+  // the upper bound of vector offset o's element keys at value m
+  auto vec_key = [&](float m, int32_t o) { return top_key(m, (int32_t)((v0 + o) * E)); };
+  const uint64_t tkey = bo == kNoIdx ? 0ull : vec_key(bm, bo);
+  // the bound: the largest value p (in its key's upper 16 bits: exact for
+  // bf16 values) such that at least F of the block's 64 thread groups (GS
+  // consecutive threads each) hold a thread whose best value is at least p.
+  // F distinct elements reach p, so every top-F value is at least p:
+  // tau = key(p, lowest-keyed index).  Wave 0 finds p from the groups'
+  // maxima, one per lane, by a binary search on the bits.
+  constexpr int GS = NT / kWave;
+  static_assert(GS >= 1 && GS <= 16 && GS * kWave == NT, "64 groups of at most 16 threads");
+  {
+    uint64_t k = tkey;
+    if constexpr (GS >= 2) key_max_step<kRowShr + 1, 0xF>(k);
+    if constexpr (GS >= 4) key_max_step<kRowShr + 2, 0xF>(k);
+    if constexpr (GS >= 8) key_max_step<kRowShr + 4, 0xF>(k);
+    if constexpr (GS >= 16) key_max_step<kRowShr + 8, 0xF>(k);
+    if ((lane & (GS - 1)) == GS - 1) s_gm[tid / GS] = (uint32_t)(k >> 32);  // 0: the group holds nothing
   }
+  if (tid == 0) s_nc = 0;
   lds_sync();
-  SV_STAMP(0, 6);  // (timeline builds) every thread's pass 1 is done
-  // the F best threads (wave 0: F rounds of a wave-wide selection over the
-  // NW entries each lane holds)
+  SV_STAMP(0, 6);  // (timeline builds) the groups' maxima are known
   if (wave == 0) {
-    float em[NW];
-    int32_t ei[NW];
+    const uint32_t gh = s_gm[lane];
+    uint32_t p = 0;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) {
-      em[w] = s_m[w * kWave + lane];
-      ei[w] = s_mv[w * kWave + lane];
+    for (int bit = 31; bit >= 16; --bit) {
+      const uint32_t c = p | (1u << bit);
+      if (__builtin_popcountll(__ballot(gh >= c)) >= F) p = c;
     }
-    uint32_t taken = 0;
-    int n = 0;
-    float tf = kNegInf;
-    for (; n < F; ++n) {
-      float bv = kNegInf;
-      int32_t bi = kNoIdx;
-#pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const bool t = (((taken >> w) & 1u) == 0u) & top_better(em[w], ei[w], bv, bi);
-        bv = t ? em[w] : bv;
-        bi = t ? ei[w] : bi;
-      }
-      float wv = bv;
-      int32_t wi = bi;
-      wave_best(wv, wi);
-      if (wi == kNoIdx) break;  // fewer than F threads hold an element
-      const int owner = wi % NT;  // the thread whose vectors hold it
-      if (lane == (owner & (kWave - 1))) taken |= 1u << (owner / kWave);
-      if (lane == 0) {
-        s_sel[n] = owner;
-        s_pick[owner] = 1;
-      }
-      tf = wv;
-    }
-    if (lane == 0) {
-      s_nsel = n;
-      s_tf = n == F ? tf : kNegInf;  // fewer threads than F: every listable value qualifies
-    }
+    if (lane == 0) s_tau = (uint64_t)p << 32;  // the value p at the lowest key of any index
   }
   lds_sync();
-  SV_STAMP(0, 3);  // (timeline builds) the F best threads are selected
-  const float tf = s_tf;
-  int count = 0;
-  if (MAY_HOLD && held) {
-    // pass 2 from registers: the selected threads flag their own values
-    const bool picked = s_pick[tid] != 0;
+  SV_STAMP(0, 7);  // (timeline builds) the bound is known
+  uint64_t tau = s_tau;
+  int nc;
+  for (;;) {  // block-uniform; tau rises on every repetition
+    const bool sel = tkey != 0ull && tkey >= tau;
+    if (MAY_HOLD && held) {
+      // from registers: the selected threads flag their own values
 #pragma unroll
-    for (int u = 0; u < kWin; ++u) {
-      const int64_t vu = v0 + tid + (int64_t)u * NT;
-      float x[E];
-      uint32_t mine = 0;
-      if (picked && vu < v1) {
-        src.values(d[u], vu, x);
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          if (x[e] >= tf && vu * E + e < V && (!Src::kSkipNegInf || x[e] > kNegInf)) mine |= 1u << e;
+      for (int u = 0; u < kWin; ++u) {
+        const int64_t vu = v0 + tid + (int64_t)u * NT;
+        flag_candidates<E>(src, d[u], sel && vu < v1 ? vu : -1, V, tau, s_cand, &s_nc);
       }
-      insert_flagged<E>(x, mine, vu, F, lv, li, &count, lane);
-    }
-    return TopPair{lv, li};
-  }
-  // pass 2 re-read, short form (KEEP > 0): each selected thread lists its
-  // kept vectors whose largest element reaches the F-th selected best; only
-  // a thread with more such vectors than it kept needs all its vectors read
-  // again
-  if (KEEP == 0 && tid == 0) s_full = 1;
-  if (KEEP > 0 && s_pick[tid]) {
-    if (nk > kKeep && bo[kKeep - 1] != kNoIdx && bm[kKeep - 1] >= tf) {
-      s_full = 1;  // every writer stores the same value
     } else {
-#pragma unroll
-      for (int i = 0; i < kKeep; ++i)
-        if (bo[i] != kNoIdx && bm[i] >= tf) s_rr[atomicAdd(&s_nrr, 1)] = bo[i];
-    }
-  }
-  lds_sync();
-  if (!s_full) {
-    const int nrr = s_nrr;
-    for (int base = 0; base < nrr; base += NT) {  // block-uniform
-      const int t = base + tid;
-      const int64_t vs = t < nrr ? v0 + s_rr[t] : -1;
-      typename Src::Data dd;
-      if (vs >= 0) dd = src.load(vs);
-      float x[E];
-      uint32_t mine = 0;
-      if (vs >= 0) {
-        src.values(dd, vs, x);
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          if (x[e] >= tf && vs * E + e < V && (!Src::kSkipNegInf || x[e] > kNegInf)) mine |= 1u << e;
+      // only the best vector can reach tau unless another one can (its key
+      // is at most that of its value at the thread's first element index):
+      // the best from registers, else every vector from memory
+      const bool full = sel && mdrop == mdrop && top_key(mdrop, (int32_t)((v0 + tid) * E)) >= tau;
+      flag_candidates<E>(src, bd, sel && !full ? v0 + bo : -1, V, tau, s_cand, &s_nc);
+      // every vector of the wave's threads that may hold a dropped value,
+      // spread over the wave's lanes (one vector per lane at a time: rare)
+      const uint64_t fm = __ballot(full);
+      if (fm) {  // wave-uniform
+        const int nkk = (int)nk;
+        const int items = __builtin_popcountll(fm) * nkk;
+        for (int base = 0; base < items; base += kWave) {
+          const int t = base + lane;
+          const int j = t < items ? t / nkk : -1;
+          // the j-th such lane of the wave
+          int sl = 0;
+          uint64_t m = fm;
+          for (int q = 0; m; ++q) {
+            const int bl = __builtin_ctzll(m);
+            m &= m - 1;
+            sl = j == q ? bl : sl;
+          }
+          int64_t vs = -1;
+          if (j >= 0) {
+            const int64_t r = (int64_t)(wave * kWave + sl) + (int64_t)(t - j * nkk) * NT;
+            if (r < span) vs = v0 + r;
+          }
+          typename Src::Data dd;
+          if (vs >= 0) dd = src.load(vs);
+          flag_candidates<E>(src, dd, vs, V, tau, s_cand, &s_nc);
+        }
       }
-      insert_flagged<E>(x, mine, vs, F, lv, li, &count, lane);
     }
-    return TopPair{lv, li};
-  }
-  // pass 2 re-read, full form: the selected threads' vectors, kWin per thread at a time
-  const int nsel = s_nsel;
-  const int64_t total = (int64_t)nsel * nk;
-  for (int64_t base = 0; base < total; base += (int64_t)kWin * NT) {
-    int64_t vs[kWin];
-#pragma unroll
-    for (int u = 0; u < kWin; ++u) {
-      const int64_t t = base + (int64_t)u * NT + tid;
-      vs[u] = -1;
-      if (t < total) {
-        const int sidx = (int)(t / nk);
-        const int64_t r = s_sel[sidx] + (t - (int64_t)sidx * nk) * NT;
-        if (r < span) vs[u] = v0 + r;
+    SV_STAMP(0, 8);  // (timeline builds) thread 0's wave has listed its values
+    SV_STAMP_LAST(0, 10);  // (timeline builds) the last wave has listed its values
+    lds_sync();
+    nc = s_nc;
+    if (nc <= kCand) break;
+    // too many listed: raise tau to the F-th best kept key (kCand > F keys
+    // are kept, all at or above tau, so it rises)
+    if (wave == 0) {
+      float tv;
+      int32_t ti;
+      const uint64_t kth = wave_select(s_cand, kCand, F, lane, tv, ti);
+      if (lane == 0) {
+        s_tau = kth;
+        s_nc = 0;
       }
-      d[u] = src.load(vs[u] >= 0 ? vs[u] : v0);
     }
-#pragma unroll
-    for (int u = 0; u < kWin; ++u) {
-      float x[E];
-      uint32_t mine = 0;
-      if (vs[u] >= 0) {
-        src.values(d[u], vs[u], x);
-#pragma unroll
-        for (int e = 0; e < E; ++e)
-          if (x[e] >= tf && vs[u] * E + e < V && (!Src::kSkipNegInf || x[e] > kNegInf)) mine |= 1u << e;
-      }
-      insert_flagged<E>(x, mine, vs[u], F, lv, li, &count, lane);
-    }
+    lds_sync();
+    tau = s_tau;
   }
+  SV_STAMP(0, 3);  // (timeline builds) the candidates are listed
+  if (wave == 0) wave_select(s_cand, nc, F, lane, lv, li);
   return TopPair{lv, li};
-}
-
-// Per-wave lists whose merge is the block's top F of [v0, v1).  KEEP > 0:
-// every thread remembers its KEEP best vectors, so that pass 2 reads again
-// only the vectors that can hold a top-F value (each 16-byte re-read costs a
-// whole memory line); the bookkeeping costs pass 1 a few operations per
-// vector, which pays where pass 2 would re-read a large share of the range.
-template <int NT, int E, bool MAY_HOLD = true, int KEEP = 0, class Src>
-__device__ TopPair wave_topk_scan(const Src src, int64_t v0, int64_t v1, int V, int F) {
-  return block_topk_scan<NT, E, MAY_HOLD, KEEP>(src, v0, v1, V, F);
 }
 
 }  // namespace sv

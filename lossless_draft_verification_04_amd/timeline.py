@@ -154,8 +154,9 @@ def fanout(stamps, reps):
     for _ in range(5):
         fn()
     torch.cuda.synchronize()
-    names = ["start", "thread 0 pass 1", "all pass 1", "threads selected", "scan done", "written"]
-    cols_of = [0, 2, 6, 3, 4, 5]
+    names = ["start", "thread 0 pass 1", "group maxima", "bound", "wave 0 listed", "candidates listed", "selected",
+             "written"]
+    cols_of = [0, 2, 6, 7, 8, 3, 4, 5]
     lines = [f"## fan-out, {B * N} tree draft rows, V={V} bf16", "",
              "| call | blocks | " + " | ".join(names) + " |", "|---|---|" + "---|" * len(names)]
     for rep in range(reps):
@@ -168,10 +169,12 @@ def fanout(stamps, reps):
             v = v[v > 0]
             cols.append(f"{np.median((v - t0) * TICK_US):.2f} / {((v.max() - t0) * TICK_US):.2f}" if len(v) else "—")
         lines.append(f"| {rep} | {len(Bk)} | " + " | ".join(cols) + " |")
-        d = (st[Bk, 4] - st[Bk, 6]) * TICK_US
+        med = lambda a, b: np.median((st[Bk, b] - st[Bk, a]) * TICK_US)  # noqa: E731
         lines.append("")
-        lines.append(f"per block, all pass 1 to scan done: median {np.median(d):.2f}, max {d.max():.2f}; "
-                     f"selection (all pass 1 to selected): median {np.median((st[Bk, 3] - st[Bk, 6]) * TICK_US):.2f}")
+        lines.append(f"per block (medians): pass 1 of thread 0 to group maxima {med(2, 6):.2f} (last wave's pass 1 "
+                     f"{med(2, 9):.2f}), to the bound {med(6, 7):.2f}, to wave 0 listed {med(7, 8):.2f} (last wave "
+                     f"{med(7, 10):.2f}), to all listed {med(8, 3):.2f}, to selected {med(3, 4):.2f}, to written "
+                     f"{med(4, 5):.2f}")
         lines.append("")
     lines += ["(median / max over the blocks)", ""]
     return lines

@@ -306,6 +306,34 @@ def test_fanout_ties_zero_f_and_small_vocab():
     PT.fanout(small, torch.tensor([8, 3, 0, 5], dtype=torch.int32), 12)  # V < F_max
 
 
+def _concentrated_rows(g, R, V, E, dtype):
+    """Rows whose largest values all lie in the vectors (E elements each) with index mod 512 below 8, in
+    bands falling with that index: a block's few threads own far more top values than F."""
+    x = torch.randn(R, V, generator=g)
+    v = torch.arange(V) // E
+    lane = v % 512
+    hot = lane < 8
+    x[:, hot] += 100.0 - 2.0 * lane[hot].to(torch.float32)
+    Vs = W.padded_stride(V, dtype)
+    store = torch.zeros(R, Vs, dtype=torch.bfloat16 if dtype == "bf16" else torch.float32)
+    store[:, :V].copy_(x)
+    return store[:, :V]
+
+
+def test_fanout_concentrated_maxima_and_signed_zeros():
+    g = torch.Generator().manual_seed(53)
+    F = torch.tensor([8, 1, 64, 13, 2, 40], dtype=torch.int32)
+    PT.fanout(_concentrated_rows(g, 6, 128256, 8, "bf16"), F, 64)
+    PT.fanout(_concentrated_rows(g, 6, 50000, 4, "f32"), F, 64)
+    # zeros of both signs tie as values: index order decides
+    z = torch.zeros(3, 3000)
+    z[:, ::3] = -0.0
+    z[1, 2000:] = -1.0
+    z[2, :] = float("-inf")
+    z[2, 1234] = -0.0
+    PT.fanout(z, torch.tensor([9, 64, 3], dtype=torch.int32), 64)
+
+
 # ----------------------------------------------------------------- workspace
 def test_workspace_shared_across_ops_and_shapes():
     tw = W.tree_zipf(B=2, N=40, max_depth=8, V=8000, T=1.0, seed=61)
