@@ -187,18 +187,6 @@ __device__ __forceinline__ void key_max_step(uint64_t& k) {
   const uint64_t o = ((uint64_t)(uint32_t)dpp_i<CTRL, ROWS>(hi, hi) << 32) | (uint32_t)dpp_i<CTRL, ROWS>(lo, lo);
   k = o > k ? o : k;
 }
-// The wave's largest key, in every lane (full exec): within rows of 16, then
-// across rows, ending in lane 63.
-__device__ __forceinline__ uint64_t wave_max_key(uint64_t k) {
-  key_max_step<kRowShr + 1, 0xF>(k);
-  key_max_step<kRowShr + 2, 0xF>(k);
-  key_max_step<kRowShr + 4, 0xF>(k);
-  key_max_step<kRowShr + 8, 0xF>(k);
-  key_max_step<kRowBcast15, 0xA>(k);
-  key_max_step<kRowBcast31, 0xC>(k);
-  return readlane_u64(k, kWave - 1);
-}
-
 // Candidate entries a block collects for its final selection (LDS).
 constexpr int kCand = 512;
 
@@ -209,64 +197,48 @@ __device__ __forceinline__ uint64_t pack_cand(float v, int32_t i) {
 __device__ __forceinline__ float cand_value(uint64_t c) { return __uint_as_float((uint32_t)c); }
 __device__ __forceinline__ uint64_t cand_key(uint64_t c) { return top_key(cand_value(c), (int32_t)(c >> 32)); }
 
-// The F best of n candidates (cand in LDS; n <= kCand) as the wave's list:
-// lane l <- the l-th best, empty entries past the n-th.  Returns the F-th
-// best key (0 when n < F).  Up to 64 candidates: every candidate counts the
-// candidates with a larger key (its rank) and moves to the lane of that
-// rank; more: F rounds of a wave-wide maximum over kCand / 64 keys per lane.
-__device__ __forceinline__ uint64_t wave_select(const uint64_t* cand, int n, int F, int lane, float& lv,
-                                                int32_t& li) {
+// The F best of n <= 64 candidates (cand in LDS) as the wave's list: lane l
+// <- the l-th best, empty entries past the n-th.  Every candidate counts the
+// candidates with a larger key (its rank) and moves to the lane of that rank.
+__device__ __forceinline__ void wave_rank(const uint64_t* cand, int n, int F, int lane, float& lv, int32_t& li) {
   lv = kNegInf;
   li = kNoIdx;
-  if (n <= kWave) {
-    const uint64_t c = lane < n ? cand[lane] : 0ull;
-    const uint64_t k = lane < n ? cand_key(c) : 0ull;
+  const uint64_t c = lane < n ? cand[lane] : 0ull;
+  const uint64_t k = lane < n ? cand_key(c) : 0ull;
+  int above = 0;
+  for (int j = 0; j < n; ++j) above += readlane_u64(k, j) > k ? 1 : 0;
+  const int rank = lane < n ? above : lane;
+  // the ranks are a permutation of the lanes: a forward permute puts every
+  // candidate in the lane of its rank
+  const int to = rank * 4;
+  const uint32_t klo = (uint32_t)__builtin_amdgcn_ds_permute(to, (int)(uint32_t)k);
+  const uint32_t khi = (uint32_t)__builtin_amdgcn_ds_permute(to, (int)(uint32_t)(k >> 32));
+  const float pv = __int_as_float(__builtin_amdgcn_ds_permute(to, (int)(uint32_t)c));
+  if (lane < n && lane < F) {
+    lv = pv;
+    li = key_index(((uint64_t)khi << 32) | klo);
+  }
+}
+
+// The F best of n <= kCand candidates (cand in LDS), by the whole block
+// (every thread calls it): the thread holding candidate i counts the keys
+// above its own over all n (LDS broadcast reads), and the candidates ranked
+// below F land in out[rank].  Returns the F-th best key (0 when n < F).
+template <int NT>
+__device__ __forceinline__ uint64_t block_select(const uint64_t* cand, uint64_t* keys, uint64_t* out, int n, int F,
+                                                 uint64_t* s_kth) {
+  for (int i = threadIdx.x; i < n; i += NT) keys[i] = cand_key(cand[i]);
+  if (threadIdx.x == 0) *s_kth = 0ull;
+  lds_sync();
+  for (int i = threadIdx.x; i < n; i += NT) {
+    const uint64_t k = keys[i];
     int above = 0;
-    for (int j = 0; j < n; ++j) above += readlane_u64(k, j) > k ? 1 : 0;
-    const int rank = lane < n ? above : lane;
-    // the ranks are a permutation of the lanes: a forward permute puts
-    // every candidate in the lane of its rank
-    const int to = rank * 4;
-    const uint32_t klo = (uint32_t)__builtin_amdgcn_ds_permute(to, (int)(uint32_t)k);
-    const uint32_t khi = (uint32_t)__builtin_amdgcn_ds_permute(to, (int)(uint32_t)(k >> 32));
-    const float pv = __int_as_float(__builtin_amdgcn_ds_permute(to, (int)(uint32_t)c));
-    const uint64_t pk = ((uint64_t)khi << 32) | klo;
-    if (lane < n && lane < F) {
-      lv = pv;
-      li = key_index(pk);
-    }
-    return n >= F ? readlane_u64(pk, F - 1) : 0ull;
+    for (int j = 0; j < n; ++j) above += keys[j] > k ? 1 : 0;
+    if (above < F) out[above] = cand[i];
+    if (above == F - 1) *s_kth = k;
   }
-  constexpr int H = kCand / kWave;
-  uint64_t hk[H];
-#pragma unroll
-  for (int h = 0; h < H; ++h) {
-    const int e = h * kWave + lane;
-    hk[h] = e < n ? cand_key(cand[e]) : 0ull;
-  }
-  uint64_t kth = 0;
-  for (int r = 0; r < F; ++r) {
-    uint64_t b = 0;
-    int bh = 0;
-#pragma unroll
-    for (int h = 0; h < H; ++h) {
-      const bool t = hk[h] > b;
-      b = t ? hk[h] : b;
-      bh = t ? h : bh;
-    }
-    const uint64_t w = wave_max_key(b);
-    if (w == 0) return 0ull;  // fewer than F candidates
-    const int owner = __builtin_ctzll(__ballot(b == w));  // keys are unique
-    const float wv = cand_value(cand[__builtin_amdgcn_readlane(bh, owner) * kWave + owner]);
-#pragma unroll
-    for (int h = 0; h < H; ++h) hk[h] = hk[h] == w ? 0ull : hk[h];
-    if (lane == r) {
-      lv = wv;
-      li = key_index(w);
-    }
-    kth = w;
-  }
-  return kth;
+  lds_sync();
+  return *s_kth;
 }
 
 // Flag the values of vector vs (vs < 0: none; d its data) whose keys reach
@@ -307,14 +279,16 @@ __device__ __forceinline__ void flag_candidates(const Src& src, const typename S
 //  per vector.  Its "thread key" is the key of that value at the vector's
 //  first element index, a bound from above on the key of every element the
 //  thread owns.
-//  Bound: the block's threads form 64 groups of NT / 64; p is the largest
-//  value such that at least F groups hold a thread whose best value reaches
-//  it, so F distinct elements reach p and every top-F value is at least p
-//  (tau = the key of value p at the lowest-keyed index).
+//  Bound: the block's threads form groups (64 of them for F <= 8, more for
+//  larger F); p is the largest value such that at least F groups hold a
+//  thread whose best value reaches it, so F distinct elements reach p and
+//  every top-F value is at least p (tau = the key of value p at the
+//  lowest-keyed index).
 //  Pass 2 looks again at the vectors of the threads whose key reaches tau --
 //  still in registers when every thread owns at most kWin of them, else
 //  re-read by the thread's wave -- and lists every value whose key reaches
-//  tau in LDS.  The F best listed values are the block's top F.  If more
+//  tau in LDS.  The F best listed values are the block's top F (one wave
+//  ranks up to 64 of them, the block more).  If more
 //  than kCand values are listed (many ties at p), tau rises to the F-th best
 //  key among the kept ones (again a bound from below on the top F), and
 //  pass 2 is repeated.
@@ -330,7 +304,9 @@ __device__ __forceinline__ TopPair block_topk(const Src src, int64_t v0, int64_t
   const int wave = threadIdx.x / kWave;
   const int tid = threadIdx.x;
   __shared__ uint64_t s_cand[kCand];
-  __shared__ uint32_t s_gm[kWave];
+  __shared__ uint32_t s_gm[NT];
+  __shared__ uint64_t s_key[kCand];
+  __shared__ uint64_t s_sel[kWave];
   __shared__ uint64_t s_tau;
   __shared__ int s_nc;
   float lv = kNegInf;
@@ -398,31 +374,49 @@ __device__ __forceinline__ TopPair block_topk(const Src src, int64_t v0, int64_t
   auto vec_key = [&](float m, int32_t o) { return top_key(m, (int32_t)((v0 + o) * E)); };
   const uint64_t tkey = bo == kNoIdx ? 0ull : vec_key(bm, bo);
   // the bound: the largest value p (in its key's upper 16 bits: exact for
-  // bf16 values) such that at least F of the block's 64 thread groups (GS
+  // bf16 values) such that at least F of the block's 64 H thread groups (GS
   // consecutive threads each) hold a thread whose best value is at least p.
   // F distinct elements reach p, so every top-F value is at least p:
-  // tau = key(p, lowest-keyed index).  Wave 0 finds p from the groups'
-  // maxima, one per lane, by a binary search on the bits.
-  constexpr int GS = NT / kWave;
-  static_assert(GS >= 1 && GS <= 16 && GS * kWave == NT, "64 groups of at most 16 threads");
+  // tau = key(p, lowest-keyed index).  H grows with F (at least 8 groups per
+  // listed value, up to one thread per group), so the bound stays close to
+  // the F-th best value.  Wave 0 finds p from the groups' maxima, H per
+  // lane, by a binary search on the bits.
+  constexpr int kMaxH = NT / kWave;
+  static_assert(kMaxH >= 1 && kMaxH <= 16 && kMaxH * kWave == NT, "whole waves, at most 16");
+  int H = 1;
+  while (H < kMaxH && 8 * F > kWave * H) H *= 2;  // block-uniform
+  const int GS = NT / (kWave * H);
   {
     uint64_t k = tkey;
-    if constexpr (GS >= 2) key_max_step<kRowShr + 1, 0xF>(k);
-    if constexpr (GS >= 4) key_max_step<kRowShr + 2, 0xF>(k);
-    if constexpr (GS >= 8) key_max_step<kRowShr + 4, 0xF>(k);
-    if constexpr (GS >= 16) key_max_step<kRowShr + 8, 0xF>(k);
+    if (GS >= 2) key_max_step<kRowShr + 1, 0xF>(k);
+    if (GS >= 4) key_max_step<kRowShr + 2, 0xF>(k);
+    if (GS >= 8) key_max_step<kRowShr + 4, 0xF>(k);
+    if (GS >= 16) key_max_step<kRowShr + 8, 0xF>(k);
     if ((lane & (GS - 1)) == GS - 1) s_gm[tid / GS] = (uint32_t)(k >> 32);  // 0: the group holds nothing
   }
   if (tid == 0) s_nc = 0;
   lds_sync();
   SV_STAMP(0, 6);  // (timeline builds) the groups' maxima are known
   if (wave == 0) {
-    const uint32_t gh = s_gm[lane];
     uint32_t p = 0;
+    if (H == 1) {  // one group per lane (F <= 8)
+      const uint32_t gh = s_gm[lane];
 #pragma unroll
-    for (int bit = 31; bit >= 16; --bit) {
-      const uint32_t c = p | (1u << bit);
-      if (__builtin_popcountll(__ballot(gh >= c)) >= F) p = c;
+      for (int bit = 31; bit >= 16; --bit) {
+        const uint32_t c = p | (1u << bit);
+        if (__builtin_popcountll(__ballot(gh >= c)) >= F) p = c;
+      }
+    } else {
+      uint32_t gh[kMaxH];
+#pragma unroll
+      for (int h = 0; h < kMaxH; ++h) gh[h] = h < H ? s_gm[h * kWave + lane] : 0u;
+      for (int bit = 31; bit >= 16; --bit) {
+        const uint32_t c = p | (1u << bit);
+        int cnt = 0;
+#pragma unroll
+        for (int h = 0; h < kMaxH; ++h) cnt += __builtin_popcountll(__ballot(gh[h] >= c));  // empty groups are 0
+        if (cnt >= F) p = c;
+      }
     }
     if (lane == 0) s_tau = (uint64_t)p << 32;  // the value p at the lowest key of any index
   }
@@ -480,20 +474,20 @@ __device__ __forceinline__ TopPair block_topk(const Src src, int64_t v0, int64_t
     if (nc <= kCand) break;
     // too many listed: raise tau to the F-th best kept key (kCand > F keys
     // are kept, all at or above tau, so it rises)
-    if (wave == 0) {
-      float tv;
-      int32_t ti;
-      const uint64_t kth = wave_select(s_cand, kCand, F, lane, tv, ti);
-      if (lane == 0) {
-        s_tau = kth;
-        s_nc = 0;
-      }
-    }
+    tau = block_select<NT>(s_cand, s_key, s_sel, kCand, F, &s_tau);
+    if (tid == 0) s_nc = 0;
     lds_sync();
-    tau = s_tau;
   }
   SV_STAMP(0, 3);  // (timeline builds) the candidates are listed
-  if (wave == 0) wave_select(s_cand, nc, F, lane, lv, li);
+  if (nc <= kWave) {  // block-uniform
+    if (wave == 0) wave_rank(s_cand, nc, F, lane, lv, li);
+  } else {
+    block_select<NT>(s_cand, s_key, s_sel, nc, F, &s_tau);
+    if (wave == 0 && lane < F) {  // nc > 64 >= F: every lane below F has an entry
+      lv = cand_value(s_sel[lane]);
+      li = (int32_t)(s_sel[lane] >> 32);
+    }
+  }
   return TopPair{lv, li};
 }
 
