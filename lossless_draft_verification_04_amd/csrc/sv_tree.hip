@@ -355,6 +355,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
   int node = 0, depth = 0;
   int ntried = 0;  // entries of s_tried (the same in every thread)
   int64_t t = -1;
+  int nvisit = 0;  // (timeline builds) nodes entered
   Slice<DT, kWNT, HELD> sl;
   for (;;) {
     // a node whose first child is accepted at its first try needs no pass
@@ -374,6 +375,8 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       node = fc;
     }
     const int nk = node_children(node, a.N, s_par, s_kids, &s_cnt);
+    SV_STAMP(kTimelineWalkBase, 7 + (nvisit < 4 ? nvisit : 4));  // (timeline builds) a node's children are known
+    ++nvisit;
     const void* rowP = row_ptr(a.tgt, rowbase + node, a.tgt_sb);
     if (nk == 0 || depth >= a.max_depth) {
       if (nk > 0 && writer) set_error(a.err, SV_DERR_TREE);
@@ -446,6 +449,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
     // exchanged only the slices' totals, so the searching block prepares its
     // slice's prefixes first
     sp.coef = (float)c;
+    SV_STAMP(kTimelineWalkBase, 12);  // (timeline builds) every child rejected: the final draw starts
     if (!loaded) sl.load(rowP, rowQ, v0, v1);  // (not reached: the last child was rejected)
     if (!sums_current) D = exchange_sum(x, sl.total(sp, a.V), s_w0, &ss);
     int pick;
@@ -455,6 +459,7 @@ __global__ __launch_bounds__(kWNT) void tree_walk_kernel(TreeParams a) {
       sl.prepare(sp, a.V);
       t = sl.search(sp, a.V, loc);
     }
+    SV_STAMP(kTimelineWalkBase, 13);  // (timeline builds) the final draw is searched (its own block)
     break;
   }
   SV_STAMP_VAL(kTimelineWalkBase, 2, lp.sum[0]);

@@ -133,13 +133,20 @@ def tree(stamps, reps):
                      f"walk blocks {len(Wk)}")
         lines.append("statistics end, max per XCD: " + ", ".join(_fmt(e) for e in ends))
         lines.append("")
-        lines.append("| seq | walk start | staged | passes | summing (µs) | exchanging (µs) | end | depth |")
-        lines.append("|---|---|---|---|---|---|---|---|")
+        lines.append("| seq | walk start | staged | nodes entered (children known) | passes | summing (µs) | "
+                     "exchanging (µs) | final draw start | searched | end | depth |")
+        lines.append("|---|---|---|---|---|---|---|---|---|---|---|")
         for b in range(p["B"]):
             m = Wk[seq[Wk] == b]
-            lines.append(f"| {b} | {_fmt(u(st[m, 0].min()))} | {_fmt(u(st[m, 1].max()))} | {int(st[m, 4].max())} | "
-                         f"{st[m, 2].max() * TICK_US:.2f} | {st[m, 3].max() * TICK_US:.2f} | "
-                         f"{_fmt(u(st[m, 5].max()))} | {int(st[m, 6].max())} |")
+
+            def last(c):
+                v = st[m, c]
+                v = v[v > 0]
+                return u(v.max()) if len(v) else None
+            nodes = ", ".join(_fmt(last(c)).strip() for c in range(7, 12) if last(c) is not None)
+            lines.append(f"| {b} | {_fmt(u(st[m, 0].min()))} | {_fmt(u(st[m, 1].max()))} | {nodes} | "
+                         f"{int(st[m, 4].max())} | {st[m, 2].max() * TICK_US:.2f} | {st[m, 3].max() * TICK_US:.2f} | "
+                         f"{_fmt(last(12))} | {_fmt(last(13))} | {_fmt(u(st[m, 5].max()))} | {int(st[m, 6].max())} |")
         lines.append("")
     return lines
 
