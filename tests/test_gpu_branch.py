@@ -34,6 +34,30 @@ def test_branch_ragged_and_small_vocab(V, gamma, dtype):
     PT.device_error_clear()
 
 
+def _concentrate(x, seed):
+    """Raise the logits of the vectors (16 bytes each) whose index mod 256 is below 4, by 30-34: the largest
+    values of every row then sit in the vectors of four threads of each 256-thread block, far more of them
+    than any branch count."""
+    E = 8 if x.dtype == torch.bfloat16 else 4
+    v = torch.arange(x.shape[-1]) // E
+    hot = (v % 256) < 4
+    boost = torch.zeros(x.shape[-1])
+    boost[hot] = 30.0 + 4.0 * torch.rand(int(hot.sum()), generator=torch.Generator().manual_seed(seed))
+    out = torch.empty_like(x)
+    out.copy_((x.float() + boost).to(x.dtype))
+    return out
+
+
+def test_branch_concentrated_maxima_many_branches():
+    # up to 64 branches from rows whose top values crowd a few threads of a block: the scan lists more values
+    # than it keeps and raises its bound, and more than 64 candidates are ranked by the whole block
+    wl = W.chain_zipf(B=6, gamma=5, V=152064, T=1.0, seed=98, lookahead_row=True)
+    rows = _concentrate(W.lookahead_rows(wl), 11)
+    PT.branch(rows, wl.tensors["tok"], torch.ones(6, dtype=torch.int32), 1.0, 0.3, 64)
+    PT.branch(rows, wl.tensors["tok"], None, 1.0, 0.05, 40)
+    PT.device_error_clear()
+
+
 def test_branch_every_class():
     wl = W.chain_zipf(B=8, gamma=6, V=20000, T=1.0, seed=95, lookahead_row=True)
     rows = W.lookahead_rows(wl)

@@ -41,6 +41,22 @@ def test_presto_largest_lists():
     PT.device_error_clear()
 
 
+def test_presto_concentrated_proposals():
+    # the leaves' top proxies crowd the vectors of four threads of each block (vector index mod 256 below 4),
+    # with k = 64: the expansion scan raises its bound and ranks its candidates with the whole block
+    wl = W.tree_zipf(B=2, N=12, max_depth=4, V=128256, T=1.0, seed=87)
+    g = torch.Generator().manual_seed(12)
+    for key in ("tgt", "drf"):
+        x = wl.tensors[key]
+        v = torch.arange(x.shape[-1]) // 8
+        hot = (v % 256) < 4
+        boost = torch.zeros(x.shape[-1])
+        boost[hot] = 30.0 + 4.0 * torch.rand(int(hot.sum()), generator=g)
+        x.copy_((x.float() + boost).to(x.dtype))
+    PT.presto(wl, LAM, 64, 64)
+    PT.device_error_clear()
+
+
 def test_presto_masked_logits():
     wl = W.tree_zipf(B=4, N=20, max_depth=5, V=5003, T=1.0, seed=85)
     g = torch.Generator().manual_seed(9)
