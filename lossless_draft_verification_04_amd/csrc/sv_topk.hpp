@@ -3,13 +3,13 @@
 // fork and the PRESTO expansion.
 //
 // Lists live in registers, one entry per lane (lane i = i-th best).  The scan
-// (block_topk) takes two passes: every thread first keeps only the best
-// element of the vectors it owns; each wave bounds the block's F-th best from
-// below by its own F best threads; only the threads whose best reaches the
-// bound are looked at again, their values at or above it are listed in LDS,
-// and one wave picks the F best of the list.  Entries compare as one 64-bit
-// key (top_key).  Lists from other blocks are merged by rounds of a
-// wave-wide selection (wave_merge_entries).
+// (block_topk) takes two passes: every thread first keeps only its best
+// vector; groups of threads bound the block's F-th best value from below;
+// only the threads whose best reaches the bound are looked at again (from
+// registers, mostly), their values at or above it are listed in LDS, and
+// the list is ranked (by one wave, or by the block when it is long).
+// Entries compare as one 64-bit key (top_key).  Lists from other blocks are
+// merged by rounds of a wave-wide selection (wave_merge_entries).
 #pragma once
 
 #include "sv_device.hpp"
