@@ -454,19 +454,27 @@ __device__ bool wait_parts(const ChainParams& a, int b, uint32_t limit) {
 }
 
 // A draw block of sequence b is done with the sequence's counters and
-// exchange slots (block-uniform call).  The last one takes the arrivals back
-// off the counter (late ones, after a timed-out wait, bring it to zero too)
-// and clears the exchange slots for the next call.
-__device__ void draw_exit(const ChainParams& a, int b) {
+// exchange slots, in two steps.  draw_exit_begin (thread 0) counts the exit
+// once the block's slot stores are complete (wave 0 made them all) and
+// keeps the old count; the counting atomic is then in flight while the
+// block searches.  draw_exit_end (block-uniform) lets the last block of the
+// sequence take the arrivals back off the counter (late ones, after a
+// timed-out wait, bring it to zero too) and clear the exchange slots for the
+// next call.
+__device__ __forceinline__ uint32_t draw_exit_begin(const ChainParams& a, int b) {
+  uint32_t old = 0;
+  if (threadIdx.x == 0) {
+    __builtin_amdgcn_s_waitcnt(0);
+    old = add_dev32(a.cnt + (int64_t)(a.B + b) * a.cstride, 1u);
+  }
+  return old;
+}
+__device__ void draw_exit_end(const ChainParams& a, int b, uint32_t old) {
   __shared__ int s_last;
   if (threadIdx.x == 0) {
-    // wave 0 made every slot store of this block: they are complete before
-    // the exit counts, so the clearing below lands after them
-    __builtin_amdgcn_s_waitcnt(0);
-    uint32_t* exits = a.cnt + (int64_t)(a.B + b) * a.cstride;
-    s_last = add_dev32(exits, 1u) == (uint32_t)a.G - 1u;
+    s_last = old == (uint32_t)a.G - 1u;
     if (s_last) {
-      st_dev32(exits, 0u);
+      st_dev32(a.cnt + (int64_t)(a.B + b) * a.cstride, 0u);
       const uint32_t total = (uint32_t)(a.pm ? a.K * a.gamma : (a.K + 1) * a.gamma) * (uint32_t)a.nch1;
       __hip_atomic_fetch_sub(a.cnt + (int64_t)b * a.cstride, total, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
@@ -477,8 +485,8 @@ __device__ void draw_exit(const ChainParams& a, int b) {
     for (int i = threadIdx.x; i < kSlotWords * a.G; i += kNT) st_dev(slots + i, 0ull);
   }
 }
+__device__ __forceinline__ void draw_exit(const ChainParams& a, int b) { draw_exit_end(a, b, draw_exit_begin(a, b)); }
 
-// The decisions and the draw of one draw block (all its waits bounded).
 template <int DT, bool HELD, bool PM>
 __device__ void draw_body(const ChainParams& a, int b, int g, Exchange& x, Decided& dec, uint64_t* s_words,
                           uint64_t* s_w1, SliceSums& ss, const Early& e) {
@@ -532,7 +540,9 @@ __device__ void draw_body(const ChainParams& a, int b, int g, Exchange& x, Decid
   int pick;
   double loc;
   pick_slice(ss, x.G, jb.u * total, &pick, &loc);
-  draw_exit(a, b);  // the slots are read no more: the search works on registers
+  // the slots are read no more (the search works on registers): the exit
+  // counts while the block searches
+  const uint32_t exits = draw_exit_begin(a, b);
   // a block other than the searching one stores the deferred outputs
   if (g == (x.G > 1 && pick == 0 ? 1 : 0)) chain_outputs<PM>(a, b, dec);
   if (pick == g) {
@@ -541,6 +551,7 @@ __device__ void draw_body(const ChainParams& a, int b, int g, Exchange& x, Decid
     if (threadIdx.x == 0) a.out_tok[b] = (int32_t)t;
     SV_STAMP(0, 5);
   }
+  draw_exit_end(a, b, exits);
 }
 
 // Draw block g of sequence b: decides the sequence and owns one slice of the
