@@ -284,19 +284,18 @@ __device__ __forceinline__ void flag_candidates(const Src& src, const typename S
 //  thread whose best value reaches it, so F distinct elements reach p and
 //  every top-F value is at least p (tau = the key of value p at the
 //  lowest-keyed index).
-//  Pass 2 looks again at the vectors of the threads whose key reaches tau --
-//  still in registers when every thread owns at most kWin of them, else
-//  re-read by the thread's wave -- and lists every value whose key reaches
-//  tau in LDS.  The F best listed values are the block's top F (one wave
-//  ranks up to 64 of them, the block more).  If more
-//  than kCand values are listed (many ties at p), tau rises to the F-th best
-//  key among the kept ones (again a bound from below on the top F), and
-//  pass 2 is repeated.
-// Outside the register path every thread keeps its best vector's data in
-// registers and the largest value of its other vectors, so that pass 2 reads
-// memory again only for a thread whose other vectors can hold a value at or
-// above tau (then all its vectors).  MAY_HOLD = false drops the register
-// path (it keeps kWin vectors live across the selection).
+//  Pass 2 looks again at the vectors of the threads whose key reaches tau
+//  and lists every value whose key reaches tau in LDS.  When every thread
+//  owns at most kWin vectors they are all still in registers; otherwise each
+//  thread has kept its best vector's data and the largest value of its other
+//  vectors, so memory is read again (all the thread's vectors, spread over
+//  its wave) only for a thread whose other vectors can reach tau.  The F
+//  best listed values are the block's top F (one wave ranks up to 64 of
+//  them, the block more).  If more than kCand values are listed (many ties
+//  at p), tau rises to the F-th best key among the kept ones (again a bound
+//  from below on the top F), and pass 2 is repeated.
+// MAY_HOLD = false drops the all-in-registers path (it keeps kWin vectors
+// live across the selection).
 template <int NT, int E, bool MAY_HOLD = true, class Src>
 __device__ __forceinline__ TopPair block_topk(const Src src, int64_t v0, int64_t v1, int V, int F) {
   constexpr int kWin = 4;   // vectors in flight per thread
