@@ -49,15 +49,23 @@ def _fmt(v):
     return "—" if v is None or not np.isfinite(v) else f"{v:6.2f}"
 
 
-def chain(stamps, reps):
-    wl = W.chain_zipf(**W.CHAIN_BATCHED)
-    g = wl.to("cuda")
-    T = float(np.float32(wl.params["T"]))
-    fn = lambda: svx.sv_verify_chain(g["tgt"], g["drf"], g["tok"], T, want_pq=False)  # noqa: E731
+def chain(stamps, reps, multi=False):
+    if multi:
+        wl = W.multi_zipf(**W.MULTI_CAND)
+        g = wl.to("cuda")
+        T = float(np.float32(wl.params["T"]))
+        fn = lambda: svx.sv_verify_multi(g["tgt"], g["drf"], g["tok"], T, want_pq=False)  # noqa: E731
+        title = "## multi, B=16, K=8, gamma=16, V=128256 bf16"
+    else:
+        wl = W.chain_zipf(**W.CHAIN_BATCHED)
+        g = wl.to("cuda")
+        T = float(np.float32(wl.params["T"]))
+        fn = lambda: svx.sv_verify_chain(g["tgt"], g["drf"], g["tok"], T, want_pq=False)  # noqa: E731
+        title = "## chain, B=32, gamma=16, V=152064 bf16 (the headline batch)"
     for _ in range(5):
         fn()
     torch.cuda.synchronize()
-    lines = ["## chain, B=32, gamma=16, V=152064 bf16 (the headline batch)", ""]
+    lines = [title, ""]
     for rep in range(reps):
         out, st, role, seq, xcd = stamps.take(fn)
         S, D = np.nonzero(role == 1)[0], np.nonzero(role == 2)[0]
@@ -194,7 +202,7 @@ def main(argv=None):
         raise SystemExit("timeline: needs a GPU")
     stamps = Stamps(torch.device("cuda", 0))
     lines = ["# Kernel timelines (timeline build, wall-clock stamps per block)", ""]
-    for part in (chain, small, tree, fanout):
+    for part in (chain, lambda st, r: chain(st, r, multi=True), small, tree, fanout):
         lines += part(stamps, reps)
         print("\n".join(lines), flush=True)
         lines = []
