@@ -80,7 +80,7 @@ __device__ __forceinline__ u32x4 mask_from(u32x4 v, int n) {
   return v;
 }
 
-template <int DT, bool PM>
+template <int DT, bool PM, int TILES>
 __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
   constexpr int E = Fmt<DT>::kPerVec;
   constexpr int kW = kSNT / kWave;
@@ -106,12 +106,12 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
   // every tile of every held row at once, through buffer resources: rows
   // past R have an empty range and vectors past the row read zeros, without
   // a memory access or a branch
-  u32x4 d[kSmallRows][kSmallTiles];
+  u32x4 d[kSmallRows][TILES];
 #pragma unroll
   for (int r = 0; r < kSmallRows; ++r) {
     const __amdgpu_buffer_rsrc_t rs = range_rsrc(small_row<DT>(a, b, r < R ? r : 0), r < R ? (uint32_t)nvec * 16u : 0u);
 #pragma unroll
-    for (int u = 0; u < kSmallTiles; ++u) d[r][u] = load_range(rs, (uint32_t)(v0 + u * kSNT + (int)threadIdx.x) * 16u);
+    for (int u = 0; u < TILES; ++u) d[r][u] = load_range(rs, (uint32_t)(v0 + u * kSNT + (int)threadIdx.x) * 16u);
   }
   // the uniforms depend on nothing loaded: computed while the loads fly
   double rr = 1.0;
@@ -127,7 +127,7 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
   }
   // the slice's ragged end: vectors past the slice, and logits past V, become -inf
 #pragma unroll
-  for (int u = 0; u < kSmallTiles; ++u) {
+  for (int u = 0; u < TILES; ++u) {
     const int vi = v0 + u * kSNT + (int)threadIdx.x;
     const int nval = vi < v1 ? (a.V - vi * E < E ? a.V - vi * E : E) : 0;
     if (nval < E)
@@ -141,18 +141,18 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
   float mt[kSmallRows], mw[kSmallRows], st[kSmallRows];
 #pragma unroll
   for (int r = 0; r < kSmallRows; ++r) {
-    float z[kSmallTiles * E];
+    float z[TILES * E];
 #pragma unroll
-    for (int u = 0; u < kSmallTiles; ++u) unpack<DT>(d[r][u], z + u * E);
+    for (int u = 0; u < TILES; ++u) unpack<DT>(d[r][u], z + u * E);
     float m = z[0];
 #pragma unroll
-    for (int e = 1; e < kSmallTiles * E; ++e) m = fmaxf(m, z[e]);
+    for (int e = 1; e < TILES * E; ++e) m = fmaxf(m, z[e]);
     const float cm = m == kNegInf ? 0.f : a.c * m;
-    float t[kSmallTiles * E];
+    float t[TILES * E];
 #pragma unroll
-    for (int e = 0; e < kSmallTiles * E; ++e) t[e] = fast_exp2(__builtin_fmaf(z[e], a.c, -cm));
+    for (int e = 0; e < TILES * E; ++e) t[e] = fast_exp2(__builtin_fmaf(z[e], a.c, -cm));
 #pragma unroll
-    for (int w = kSmallTiles * E / 2; w > 0; w >>= 1)
+    for (int w = TILES * E / 2; w > 0; w >>= 1)
 #pragma unroll
       for (int e = 0; e < w; ++e) t[e] += t[e + w];
     mt[r] = r < R ? m : kNegInf;
@@ -308,20 +308,20 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
   const bool rows_ok = SP > 0.0 && (PM || n == a.gamma || SQ > 0.0);
   const bool resid = !PM && n < a.gamma && rows_ok;
   const bool pm_resid = PM && n < a.gamma && SP > 0.0;
-  Slice<DT, kSNT, true, kSmallTiles> sl;
+  Slice<DT, kSNT, true, TILES> sl;
   sl.rowP = small_row<DT>(a, b, rP);
   sl.rowQ = resid ? small_row<DT>(a, b, rQ) : nullptr;
   sl.v0 = v0;
   sl.v1 = v1 > v0 ? v1 : v0;
 #pragma unroll
-  for (int u = 0; u < kSmallTiles; ++u) {
+  for (int u = 0; u < TILES; ++u) {
     sl.p[u] = u32x4{0u, 0u, 0u, 0u};
     sl.q[u] = sl.p[u];
   }
 #pragma unroll
   for (int r = 0; r < kSmallRows; ++r)
 #pragma unroll
-    for (int u = 0; u < kSmallTiles; ++u) {
+    for (int u = 0; u < TILES; ++u) {
       if (r == rP) sl.p[u] = d[r][u];
       if (!PM && r == rQ) sl.q[u] = d[r][u];
     }
@@ -390,38 +390,44 @@ __global__ __launch_bounds__(kSNT) void chain_small_kernel(ChainParams a) {
 
 SV_TIMELINE_SETTER(timeline_set_chain_small)
 
-hipError_t launch_chain_small(const ChainParams& p, sv_dtype dt, hipStream_t s) {
+template <int TILES>
+static hipError_t launch_small_tiles(const ChainParams& p, sv_dtype dt, hipStream_t s) {
   const dim3 grid((unsigned)p.B * p.G), block(kSNT);
   if (dt == SV_BF16) {
     if (p.pm)
-      chain_small_kernel<SV_BF16, true><<<grid, block, 0, s>>>(p);
+      chain_small_kernel<SV_BF16, true, TILES><<<grid, block, 0, s>>>(p);
     else
-      chain_small_kernel<SV_BF16, false><<<grid, block, 0, s>>>(p);
+      chain_small_kernel<SV_BF16, false, TILES><<<grid, block, 0, s>>>(p);
   } else {
     if (p.pm)
-      chain_small_kernel<SV_F32, true><<<grid, block, 0, s>>>(p);
+      chain_small_kernel<SV_F32, true, TILES><<<grid, block, 0, s>>>(p);
     else
-      chain_small_kernel<SV_F32, false><<<grid, block, 0, s>>>(p);
+      chain_small_kernel<SV_F32, false, TILES><<<grid, block, 0, s>>>(p);
   }
   return hipGetLastError();
 }
 
+hipError_t launch_chain_small(const ChainParams& p, sv_dtype dt, int tiles, hipStream_t s) {
+  return tiles == 1 ? launch_small_tiles<1>(p, dt, s) : launch_small_tiles<kSmallTiles>(p, dt, s);
+}
+
+template <int TILES>
+static const void* small_kernel_fn(sv_dtype dt, bool pm) {
+  if (dt == SV_BF16)
+    return pm ? reinterpret_cast<const void*>(&chain_small_kernel<SV_BF16, true, TILES>)
+              : reinterpret_cast<const void*>(&chain_small_kernel<SV_BF16, false, TILES>);
+  return pm ? reinterpret_cast<const void*>(&chain_small_kernel<SV_F32, true, TILES>)
+            : reinterpret_cast<const void*>(&chain_small_kernel<SV_F32, false, TILES>);
+}
+
 // Blocks of the small-chain kernel the device holds at once.
-int chain_small_capacity(sv_dtype dt, bool pm) {
-  static int cache[2][2][64];
+int chain_small_capacity(sv_dtype dt, bool pm, int tiles) {
+  static int cache[2][2][2][64];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
-  int& c = cache[dt == SV_BF16][pm][dev];
-  if (c == 0) {
-    const void* fn;
-    if (dt == SV_BF16)
-      fn = pm ? reinterpret_cast<const void*>(&chain_small_kernel<SV_BF16, true>)
-              : reinterpret_cast<const void*>(&chain_small_kernel<SV_BF16, false>);
-    else
-      fn = pm ? reinterpret_cast<const void*>(&chain_small_kernel<SV_F32, true>)
-              : reinterpret_cast<const void*>(&chain_small_kernel<SV_F32, false>);
-    c = device_capacity(fn, kSNT, dev);
-  }
+  int& c = cache[tiles == 1][dt == SV_BF16][pm][dev];
+  if (c == 0)
+    c = device_capacity(tiles == 1 ? small_kernel_fn<1>(dt, pm) : small_kernel_fn<kSmallTiles>(dt, pm), kSNT, dev);
   return c;
 }
 

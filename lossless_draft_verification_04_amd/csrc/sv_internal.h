@@ -187,12 +187,12 @@ hipError_t timeline_set_tree(void* p, uint64_t records);
 hipError_t timeline_set_fanout(void* p, uint64_t records);
 #endif
 // Small calls (sv_chain_small.hip): each of G blocks per sequence holds its
-// slice (at most kSmallTiles tiles of 256 vectors) of every row the step may
+// slice (1 or kSmallTiles tiles of 256 vectors) of every row the step may
 // touch (at most kSmallRows rows: target 1..gamma+1, draft 1..gamma).
 constexpr int kSmallTiles = 2;
 constexpr int kSmallRows = 9;
-hipError_t launch_chain_small(const ChainParams& p, sv_dtype dt, hipStream_t s);
-int chain_small_capacity(sv_dtype dt, bool pm);
+hipError_t launch_chain_small(const ChainParams& p, sv_dtype dt, int tiles, hipStream_t s);
+int chain_small_capacity(sv_dtype dt, bool pm, int tiles);
 hipError_t launch_greedy(const GreedyParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
 hipError_t launch_tree(const TreeParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
 hipError_t launch_fanout(const FanoutParams& p, sv_dtype dt, const Plan& plan, hipStream_t s);
