@@ -20,8 +20,10 @@ NEG = float("-inf")
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
+# one 256-vector tile per block while a sequence's blocks number at most 64, else two: f32 V=65536 is 64
+# one-tile blocks, V=65537 33 two-tile blocks; bf16 V=262144 is 64 two-tile blocks
 @pytest.mark.parametrize("gamma,V,B", [(1, 1, 1), (1, 7, 3), (2, 100, 4), (3, 5000, 2), (4, 32000, 1),
-                                       (4, 65537, 1), (2, 262144, 1), (4, 9999, 8)])
+                                       (4, 65536, 1), (4, 65537, 1), (2, 262144, 1), (4, 9999, 8)])
 def test_small_chain_matches_oracle(dtype, gamma, V, B):
     wl = W.chain_normal(B=B, gamma=gamma, V=V, T=1.0, dtype=dtype, seed=400 + gamma * 7 + V % 97 + B)
     for seed, rnd in [(0, 0), (3, 1), (11, 5)]:
